@@ -1,0 +1,333 @@
+/*
+ * ubd.h - C ABI of libubd, a gfx950 (MI355X) implementation of one
+ * llama_decode step of a Llama-architecture transformer over ubatches with
+ * a KV cache.
+ *
+ * The calls follow the problem statement of the pages this library is built
+ * from:
+ *   [ENG]  "llama.cpp AI LLM Engine - how it works" (romankryvolapov.pages.dev)
+ *   [ARCH] "llama.cpp Architecture" (codeloopback.dev)
+ *   [DEC]  "Decode loop: batching, KV cache, memory management" (readoss.com)
+ *
+ * General rules
+ *   - Every call is host-side and single-threaded per context.  GPU work is
+ *     enqueued on the stream given at creation (NULL = the null stream) and
+ *     may still be running when a call returns; every reader of results
+ *     (logits, greedy ids, KV reads) synchronises that stream first.
+ *   - Pointers named "host" are host memory; "device" pointers are HIP
+ *     device memory of the model's device.  The library never frees memory
+ *     the caller passed in.
+ *   - No call aborts the process on user error.  Constructors return NULL
+ *     and set *status; other calls return the codes documented below.
+ *     ubd_last_error() gives a message for the most recent failure on the
+ *     calling thread.
+ */
+#ifndef UBD_H
+#define UBD_H
+
+#include <stdbool.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ubd_token;
+typedef int32_t ubd_pos;
+typedef int32_t ubd_seq_id;
+
+/* Storage types.  q8_0 is the 32-value int8 block with one f16 scale per
+ * block ([ARCH] Example 2: 34 bytes per 32 values); value = scale * code. */
+typedef enum ubd_type {
+    UBD_TYPE_F32 = 0,
+    UBD_TYPE_F16 = 1,
+    UBD_TYPE_BF16 = 2,
+    UBD_TYPE_Q8_0 = 3,
+} ubd_type;
+
+/* Largest n_seq_max accepted ([ENG] Step 7: n_seq_max must fit the
+ * library's sequence limit). */
+#define UBD_MAX_SEQ 256
+
+/* decode return codes ([ENG] Steps 11-12; [DEC] "Error recovery and state
+ * rollback") */
+#define UBD_OK 0
+#define UBD_NO_KV_SLOT 1     /* no room in the KV cache; state unchanged   */
+#define UBD_ABORTED 2        /* abort callback; done ubatches are kept     */
+#define UBD_INVALID -1       /* invalid batch or argument; state unchanged */
+#define UBD_ALLOC_FAILED -2  /* allocation / internal failure              */
+#define UBD_COMPUTE_FAILED -3 /* kernel or HIP failure; ubatch rolled back */
+
+/* ------------------------------------------------------------------ model */
+
+/* Hyperparameters ([ENG] Step 4 key list; [ARCH] Example 8 print_info).
+ * Derived: head_dim = n_embd / n_head, n_gqa = n_head / n_head_kv. */
+typedef struct ubd_hparams {
+    int32_t n_layer;
+    int32_t n_embd;
+    int32_t n_head;
+    int32_t n_head_kv;
+    int32_t n_ff;
+    int32_t n_vocab;
+    int32_t n_ctx_train;
+    float rms_eps;          /* RMSNorm epsilon (inside the square root)    */
+    float rope_freq_base;   /* RoPE theta base                             */
+    int32_t rope_type;      /* 0 = normal (adjacent pairs); only 0 exists  */
+} ubd_hparams;
+
+/* One weight tensor, named as in GGUF ([ENG] Step 6):
+ *   token_embd.weight, output_norm.weight, output.weight and, for every
+ *   layer N, blk.N.{attn_norm, attn_q, attn_k, attn_v, attn_output,
+ *   ffn_norm, ffn_gate, ffn_up, ffn_down}.weight
+ * Shapes use ggml's order ([ARCH] Example 4): ne[0] = values per row (the
+ * input dimension), ne[1] = rows (the output dimension); norm gains have
+ * ne = {n_embd, 1}.  Norm gains must be F32.  All 2-D matrices of a model
+ * share one type: F32, BF16 or Q8_0.
+ *   F32 / BF16: data = ne[1] rows of ne[0] values, row-major.
+ *   Q8_0:       data = int8 codes [ne[1]][ne[0]]; scales = f16 bit patterns
+ *               [ne[1]][ne[0] / 32]; ne[0] must be a multiple of 32.
+ * data / scales are host pointers unless on_device != 0.  They are copied
+ * during ubd_model_load and may be freed afterwards. */
+typedef struct ubd_tensor_src {
+    const char *name;
+    ubd_type type;
+    int64_t ne[2];
+    const void *data;
+    const void *scales;
+    int32_t on_device;
+} ubd_tensor_src;
+
+/* Device allocation hooks: alloc returns device memory of >= nbytes
+ * (256-byte aligned) or NULL; free releases it.  NULL hooks = hipMalloc /
+ * hipFree. */
+typedef void *(*ubd_alloc_fn)(size_t nbytes, void *user_data);
+typedef void (*ubd_free_fn)(void *ptr, void *user_data);
+
+typedef struct ubd_model_params {
+    int32_t device;         /* HIP device ordinal                          */
+    ubd_alloc_fn alloc;
+    ubd_free_fn free;
+    void *alloc_user_data;
+    void *stream;           /* hipStream_t for the weight upload           */
+} ubd_model_params;
+
+typedef struct ubd_model ubd_model;
+
+/* Load a model from the given tensors ([ENG] Steps 2-6, with host arrays
+ * standing in for the GGUF file).  Every tensor the architecture needs must
+ * be present exactly once with the expected shape.  Status: 0 ok; -1
+ * invalid (missing, duplicate, unknown or mis-shaped tensor, mixed matrix
+ * types, unsupported sizes: n_embd, n_head*head_dim, n_ff and n_vocab must
+ * be multiples of 16, head_dim must be 32, 64 or 128 and n_head / n_head_kv
+ * at most 32); -2 allocation or
+ * HIP failure.  Returns NULL on failure.  The model must outlive its
+ * contexts. */
+ubd_model *ubd_model_load(const ubd_hparams *hparams,
+                          const ubd_tensor_src *tensors, int32_t n_tensors,
+                          const ubd_model_params *params, int32_t *status);
+void ubd_model_free(ubd_model *model);
+/* Bytes of device memory held by the model's weights. */
+size_t ubd_model_size(const ubd_model *model);
+
+/* ---------------------------------------------------------------- context */
+
+/* Abort callback: polled before every ubatch; returning true stops the
+ * decode with UBD_ABORTED ([ENG] Steps 11-12). */
+typedef bool (*ubd_abort_fn)(void *user_data);
+
+/* Context parameters ([ENG] Step 7; [DEC] "Context construction"). */
+typedef struct ubd_context_params {
+    uint32_t n_ctx;          /* KV cells in total; 0 = n_ctx_train; padded
+                                up to a multiple of 256                    */
+    uint32_t n_batch;        /* most tokens per ubd_decode call            */
+    uint32_t n_ubatch;       /* most tokens per forward pass               */
+    uint32_t n_seq_max;      /* sequences; 1..UBD_MAX_SEQ                  */
+    ubd_type type_k;         /* K cache type: F32 or F16                   */
+    ubd_type type_v;         /* V cache type: F32 or F16                   */
+    bool kv_unified;         /* false: one stream of n_ctx/n_seq_max cells
+                                per sequence; true: one shared stream      */
+    ubd_abort_fn abort_callback;
+    void *abort_user_data;
+    void *stream;            /* hipStream_t for all work; NULL = null stream */
+} ubd_context_params;
+
+/* n_ctx 0, n_batch 2048, n_ubatch 512, n_seq_max 1, F16/F16, not unified. */
+ubd_context_params ubd_context_default_params(void);
+
+typedef struct ubd_context ubd_context;
+
+/* Create a context: KV cache for all cells and worst-case per-ubatch
+ * buffers are allocated here ([ENG] Step 7; [ARCH] Example 10).
+ * n_batch is clamped to n_ctx and n_ubatch to n_batch.  Status: 0 ok,
+ * -1 invalid parameters, -2 allocation failure.  NULL on failure. */
+ubd_context *ubd_init_from_model(ubd_model *model,
+                                 const ubd_context_params *params,
+                                 int32_t *status);
+void ubd_free(ubd_context *ctx);
+uint32_t ubd_n_ctx(const ubd_context *ctx);      /* padded total cells   */
+uint32_t ubd_n_batch(const ubd_context *ctx);
+uint32_t ubd_n_ubatch(const ubd_context *ctx);
+
+/* ------------------------------------------------------------------ batch */
+
+/* Mirror of llama_batch ([ENG] Step 10).  Arrays have n_tokens entries and
+ * belong to the caller; they are only read during ubd_decode.
+ *   token     token ids in [0, n_vocab)
+ *   embd      must be NULL (token input only)
+ *   pos       NULL = continue each sequence from seq_pos_max + 1
+ *   n_seq_id  NULL or all 1 (one sequence per token)
+ *   seq_id    NULL = sequence 0; else seq_id[i][0] in [0, n_seq_max)
+ *   logits    NULL = only the last token outputs; else nonzero = output */
+typedef struct ubd_batch {
+    int32_t n_tokens;
+    ubd_token *token;
+    float *embd;
+    ubd_pos *pos;
+    int32_t *n_seq_id;
+    ubd_seq_id **seq_id;
+    int8_t *logits;
+} ubd_batch;
+
+/* Allocate a batch with room for n_tokens_alloc tokens, one sequence id
+ * each (embd must be 0).  Free with ubd_batch_free. */
+ubd_batch ubd_batch_init(int32_t n_tokens_alloc, int32_t embd, int32_t n_seq_max);
+void ubd_batch_free(ubd_batch batch);
+/* Wrap existing token ids; pos, seq_id and logits stay NULL ([ENG] Step 10). */
+ubd_batch ubd_batch_get_one(ubd_token *tokens, int32_t n_tokens);
+
+/* ----------------------------------------------------------------- decode */
+
+/* Run one batch ([ENG] Steps 11-13; [DEC] "Batch pipeline" and
+ * "process_ubatch"): validate and autofill, split into ubatches (simple
+ * split with one KV stream, equal split with several), find KV cells for
+ * every ubatch before committing any, then per ubatch commit its cells and
+ * enqueue the forward pass.  Returns UBD_OK, UBD_NO_KV_SLOT (nothing
+ * changed), UBD_ABORTED (ubatches before the aborted one are kept),
+ * UBD_INVALID (nothing changed), UBD_ALLOC_FAILED or UBD_COMPUTE_FAILED
+ * (the failing ubatch is removed again with seq_rm(s, pos_min, -1)).
+ * Returns before the GPU finishes. */
+int32_t ubd_decode(ubd_context *ctx, ubd_batch batch);
+
+/* Number of output rows of the last successful decode (flagged tokens). */
+int32_t ubd_n_outputs(const ubd_context *ctx);
+
+/* Logits of the last decode as host f32 rows [n_outputs][n_vocab] in batch
+ * order of the flagged tokens ([ENG] Step 14).  Synchronises.  Valid until
+ * the next ubd_decode or ubd_free.  NULL if there are none. */
+float *ubd_get_logits(ubd_context *ctx);
+/* One row: i >= 0 is a batch index (NULL if that token was not flagged);
+ * i < 0 counts rows from the end ([ENG] Step 14, output row lookup). */
+float *ubd_get_logits_ith(ubd_context *ctx, int32_t i);
+/* Device pointer to the same rows (f32, row stride n_vocab), for callers
+ * that keep the data on the GPU.  Does not synchronise. */
+const float *ubd_get_logits_device(ubd_context *ctx);
+
+/* Greedy pick: the token with the largest logit, lowest id on ties
+ * ([ENG] Steps 14-16, sampling).  Runs on the GPU; i as in
+ * ubd_get_logits_ith.  Returns -1 for an invalid i. */
+ubd_token ubd_sample_greedy(ubd_context *ctx, int32_t i);
+/* Greedy pick for every output row at once: out[r] for r < n_outputs.
+ * Returns the number of rows written, or -1. */
+int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32_t cap);
+
+/* Wait for all work enqueued on the context's stream.  0 or -3. */
+int32_t ubd_synchronize(ubd_context *ctx);
+
+/* ----------------------------------------------------------------- memory */
+
+/* Smallest / largest position held for sequence s; -1 if none
+ * ([ENG] KV-cache section, seq_pos_max). */
+ubd_pos ubd_memory_seq_pos_min(ubd_context *ctx, ubd_seq_id s);
+ubd_pos ubd_memory_seq_pos_max(ubd_context *ctx, ubd_seq_id s);
+/* Remove the cells of sequence s (all sequences if s < 0) with
+ * p0 <= pos < p1; p0 < 0 means 0, p1 < 0 means infinity ([DEC] "Error
+ * recovery and state rollback").  Returns true. */
+bool ubd_memory_seq_rm(ubd_context *ctx, ubd_seq_id s, ubd_pos p0, ubd_pos p1);
+/* KV cell of each batch token of the last successful decode, in batch
+ * order ([DEC] "KV cache details": slot_info indices).  Returns the token
+ * count, or -1 if cap is too small. */
+int32_t ubd_get_kv_cells(ubd_context *ctx, int32_t *cells_out, int32_t cap);
+
+/* Fill positions 0..n_pos-1 of the empty sequence s with given K/V rows:
+ * k_layers[l] / v_layers[l] point to [n_pos][n_head_kv * head_dim] values of
+ * src_type (F16 or F32; converted to the cache types), host unless
+ * on_device.  Used to start from a long pre-filled context.  Returns 0,
+ * UBD_NO_KV_SLOT if the stream lacks room, UBD_INVALID otherwise. */
+int32_t ubd_kv_fill(ubd_context *ctx, ubd_seq_id s, int32_t n_pos,
+                    const void *const *k_layers, const void *const *v_layers,
+                    ubd_type src_type, int32_t on_device);
+/* Read back the K (which = 0) or V (which = 1) rows of cells
+ * [cell0, cell0 + n) of one layer and KV stream as f32
+ * [n][n_head_kv * head_dim] into host memory.  Synchronises.  0 or -1. */
+int32_t ubd_kv_read(ubd_context *ctx, int32_t layer, int32_t stream,
+                    int32_t which, int32_t cell0, int32_t n, float *out);
+
+/* ------------------------------------------------------- diagnostics/perf */
+
+/* Keep the residual stream entering every layer (and after the last) for
+ * the most recent ubatch, like the pages' per-node eval callback
+ * ([ARCH] Example 4).  enable = 0 frees it.  0 or -2. */
+int32_t ubd_debug_keep_residuals(ubd_context *ctx, int32_t enable);
+/* Copy the kept residual entering layer `layer` (layer == n_layer: after
+ * the last layer) for the n_tokens tokens of the last ubatch, in ubatch
+ * order, as f32 [n_tokens][n_embd].  Synchronises.  Returns the token count
+ * or -1. */
+int32_t ubd_debug_get_residual(ubd_context *ctx, int32_t layer, float *out,
+                               int32_t cap_tokens);
+/* Batch index of every token of the last ubatch, in ubatch order. */
+int32_t ubd_debug_last_ubatch(ubd_context *ctx, int32_t *batch_idx,
+                              int32_t cap);
+
+/* Counters in the spirit of llama_perf_context_print ([ARCH] Example 15). */
+typedef struct ubd_perf {
+    double t_load_ms;       /* ubd_model_load wall time                    */
+    double t_p_eval_ms;     /* host time in ubd_decode, batches > 1 token  */
+    double t_eval_ms;       /* host time in ubd_decode, 1-token batches    */
+    int32_t n_p_eval;       /* tokens in batches > 1 token                 */
+    int32_t n_eval;         /* 1-token batches                             */
+    int32_t n_ubatch;       /* forward passes enqueued                     */
+    int32_t n_decode;       /* ubd_decode calls returning UBD_OK           */
+} ubd_perf;
+void ubd_perf_get(const ubd_context *ctx, ubd_perf *out);
+void ubd_perf_reset(ubd_context *ctx);
+
+/* Log sink for info and error lines; NULL restores stderr for errors. */
+typedef void (*ubd_log_fn)(int32_t level, const char *text, void *user_data);
+void ubd_log_set(ubd_log_fn fn, void *user_data);
+/* Message of the last failure on this thread ("" if none). */
+const char *ubd_last_error(void);
+
+/* ---------------------------------------------------- host-only planner */
+
+/* The batch/ubatch/KV-cell bookkeeping of ubd_decode without a GPU: the
+ * same code ubd_decode runs, with the forward pass replaced by a stub that
+ * succeeds, or returns fail_code (UBD_ABORTED or UBD_COMPUTE_FAILED) at
+ * ubatch fail_at (fail_at < 0: never).  n_ctx, n_batch, n_ubatch,
+ * n_seq_max and kv_unified as in ubd_context_params. */
+typedef struct ubd_planner ubd_planner;
+ubd_planner *ubd_planner_new(uint32_t n_ctx, uint32_t n_batch,
+                             uint32_t n_ubatch, uint32_t n_seq_max,
+                             bool kv_unified, int32_t n_vocab);
+void ubd_planner_free(ubd_planner *p);
+int32_t ubd_planner_decode(ubd_planner *p, ubd_batch batch, int32_t fail_at,
+                           int32_t fail_code);
+/* Ubatches of the last decode and, for ubatch k, its tokens' batch
+ * indices, cells and streams (arrays of at least its token count). */
+int32_t ubd_planner_n_ubatches(const ubd_planner *p);
+int32_t ubd_planner_ubatch(const ubd_planner *p, int32_t k, int32_t *batch_idx,
+                           int32_t *cells, int32_t *streams, int32_t cap);
+/* Output row of batch index i (-1 if none) and the row count. */
+int32_t ubd_planner_output_row(const ubd_planner *p, int32_t i);
+int32_t ubd_planner_n_outputs(const ubd_planner *p);
+ubd_pos ubd_planner_seq_pos_min(const ubd_planner *p, ubd_seq_id s);
+ubd_pos ubd_planner_seq_pos_max(const ubd_planner *p, ubd_seq_id s);
+bool ubd_planner_seq_rm(ubd_planner *p, ubd_seq_id s, ubd_pos p0, ubd_pos p1);
+/* Cells scanned by attention in a stream: highest used cell + 1. */
+int32_t ubd_planner_n_kv(const ubd_planner *p, int32_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UBD_H */

@@ -1,0 +1,426 @@
+"""ctypes binding of libubd (include/ubd.h): argument marshalling only.
+
+Every step of the decode path runs inside libubd's HIP kernels; this module
+builds the C structs, hands PyTorch's device allocator and current stream to
+the library, and converts results to NumPy.  If libubd.so is missing it
+raises instead of falling back to anything else.
+"""
+import ctypes as C
+import os
+import weakref
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libubd.so")
+
+UBD_TYPE_F32, UBD_TYPE_F16, UBD_TYPE_BF16, UBD_TYPE_Q8_0 = 0, 1, 2, 3
+UBD_OK, UBD_NO_KV_SLOT, UBD_ABORTED = 0, 1, 2
+UBD_INVALID, UBD_ALLOC_FAILED, UBD_COMPUTE_FAILED = -1, -2, -3
+UBD_MAX_SEQ = 256
+TYPE_IDS = {"f32": UBD_TYPE_F32, "f16": UBD_TYPE_F16, "bf16": UBD_TYPE_BF16, "q8_0": UBD_TYPE_Q8_0}
+
+
+class Hparams(C.Structure):
+    _fields_ = [("n_layer", C.c_int32), ("n_embd", C.c_int32), ("n_head", C.c_int32),
+                ("n_head_kv", C.c_int32), ("n_ff", C.c_int32), ("n_vocab", C.c_int32),
+                ("n_ctx_train", C.c_int32), ("rms_eps", C.c_float), ("rope_freq_base", C.c_float),
+                ("rope_type", C.c_int32)]
+
+
+class TensorSrc(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("type", C.c_int), ("ne", C.c_int64 * 2),
+                ("data", C.c_void_p), ("scales", C.c_void_p), ("on_device", C.c_int32)]
+
+
+ALLOC_FN = C.CFUNCTYPE(C.c_void_p, C.c_size_t, C.c_void_p)
+FREE_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p)
+ABORT_FN = C.CFUNCTYPE(C.c_bool, C.c_void_p)
+LOG_FN = C.CFUNCTYPE(None, C.c_int32, C.c_char_p, C.c_void_p)
+
+
+class ModelParams(C.Structure):
+    _fields_ = [("device", C.c_int32), ("alloc", ALLOC_FN), ("free", FREE_FN),
+                ("alloc_user_data", C.c_void_p), ("stream", C.c_void_p)]
+
+
+class ContextParams(C.Structure):
+    _fields_ = [("n_ctx", C.c_uint32), ("n_batch", C.c_uint32), ("n_ubatch", C.c_uint32),
+                ("n_seq_max", C.c_uint32), ("type_k", C.c_int), ("type_v", C.c_int),
+                ("kv_unified", C.c_bool), ("abort_callback", ABORT_FN),
+                ("abort_user_data", C.c_void_p), ("stream", C.c_void_p)]
+
+
+class CBatch(C.Structure):
+    _fields_ = [("n_tokens", C.c_int32), ("token", C.POINTER(C.c_int32)),
+                ("embd", C.POINTER(C.c_float)), ("pos", C.POINTER(C.c_int32)),
+                ("n_seq_id", C.POINTER(C.c_int32)),
+                ("seq_id", C.POINTER(C.POINTER(C.c_int32))), ("logits", C.POINTER(C.c_int8))]
+
+
+class Perf(C.Structure):
+    _fields_ = [("t_load_ms", C.c_double), ("t_p_eval_ms", C.c_double), ("t_eval_ms", C.c_double),
+                ("n_p_eval", C.c_int32), ("n_eval", C.c_int32), ("n_ubatch", C.c_int32),
+                ("n_decode", C.c_int32)]
+
+
+# name -> (restype, argtypes); also the list of symbols include/ubd.h declares
+_P = C.c_void_p
+SIGNATURES = {
+    "ubd_model_load": (_P, [C.POINTER(Hparams), C.POINTER(TensorSrc), C.c_int32,
+                            C.POINTER(ModelParams), C.POINTER(C.c_int32)]),
+    "ubd_model_free": (None, [_P]),
+    "ubd_model_size": (C.c_size_t, [_P]),
+    "ubd_context_default_params": (ContextParams, []),
+    "ubd_init_from_model": (_P, [_P, C.POINTER(ContextParams), C.POINTER(C.c_int32)]),
+    "ubd_free": (None, [_P]),
+    "ubd_n_ctx": (C.c_uint32, [_P]),
+    "ubd_n_batch": (C.c_uint32, [_P]),
+    "ubd_n_ubatch": (C.c_uint32, [_P]),
+    "ubd_batch_init": (CBatch, [C.c_int32, C.c_int32, C.c_int32]),
+    "ubd_batch_free": (None, [CBatch]),
+    "ubd_batch_get_one": (CBatch, [C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_decode": (C.c_int32, [_P, CBatch]),
+    "ubd_n_outputs": (C.c_int32, [_P]),
+    "ubd_get_logits": (C.POINTER(C.c_float), [_P]),
+    "ubd_get_logits_ith": (C.POINTER(C.c_float), [_P, C.c_int32]),
+    "ubd_get_logits_device": (C.c_void_p, [_P]),
+    "ubd_sample_greedy": (C.c_int32, [_P, C.c_int32]),
+    "ubd_sample_greedy_all": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_synchronize": (C.c_int32, [_P]),
+    "ubd_memory_seq_pos_min": (C.c_int32, [_P, C.c_int32]),
+    "ubd_memory_seq_pos_max": (C.c_int32, [_P, C.c_int32]),
+    "ubd_memory_seq_rm": (C.c_bool, [_P, C.c_int32, C.c_int32, C.c_int32]),
+    "ubd_get_kv_cells": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_kv_fill": (C.c_int32, [_P, C.c_int32, C.c_int32, C.POINTER(C.c_void_p),
+                                C.POINTER(C.c_void_p), C.c_int, C.c_int32]),
+    "ubd_kv_read": (C.c_int32, [_P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                C.POINTER(C.c_float)]),
+    "ubd_debug_keep_residuals": (C.c_int32, [_P, C.c_int32]),
+    "ubd_debug_get_residual": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_float), C.c_int32]),
+    "ubd_debug_last_ubatch": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_perf_get": (None, [_P, C.POINTER(Perf)]),
+    "ubd_perf_reset": (None, [_P]),
+    "ubd_log_set": (None, [LOG_FN, C.c_void_p]),
+    "ubd_last_error": (C.c_char_p, []),
+    "ubd_planner_new": (_P, [C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32, C.c_bool, C.c_int32]),
+    "ubd_planner_free": (None, [_P]),
+    "ubd_planner_decode": (C.c_int32, [_P, CBatch, C.c_int32, C.c_int32]),
+    "ubd_planner_n_ubatches": (C.c_int32, [_P]),
+    "ubd_planner_ubatch": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                       C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_planner_output_row": (C.c_int32, [_P, C.c_int32]),
+    "ubd_planner_n_outputs": (C.c_int32, [_P]),
+    "ubd_planner_seq_pos_min": (C.c_int32, [_P, C.c_int32]),
+    "ubd_planner_seq_pos_max": (C.c_int32, [_P, C.c_int32]),
+    "ubd_planner_seq_rm": (C.c_bool, [_P, C.c_int32, C.c_int32, C.c_int32]),
+    "ubd_planner_n_kv": (C.c_int32, [_P, C.c_int32]),
+}
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libubd.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m llama_decode_ubatch_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    lib = C.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def last_error():
+    return load_library().ubd_last_error().decode()
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+
+
+class _BatchHolder:
+    """Keeps the arrays a CBatch points into alive."""
+
+    def __init__(self, tokens, pos=None, seq_id=None, logits=None):
+        self.token = _i32(tokens)
+        n = self.token.size
+        self.b = CBatch()
+        self.b.n_tokens = n
+        self.b.token = self.token.ctypes.data_as(C.POINTER(C.c_int32))
+        if pos is not None:
+            self.pos = _i32(pos)
+            self.b.pos = self.pos.ctypes.data_as(C.POINTER(C.c_int32))
+        if seq_id is not None:
+            self.seq = _i32(seq_id)
+            self.n_seq = np.ones(n, np.int32)
+            base = self.seq.ctypes.data
+            self.rows = (C.POINTER(C.c_int32) * n)(
+                *[C.cast(base + 4 * i, C.POINTER(C.c_int32)) for i in range(n)])
+            self.b.seq_id = C.cast(self.rows, C.POINTER(C.POINTER(C.c_int32)))
+            self.b.n_seq_id = self.n_seq.ctypes.data_as(C.POINTER(C.c_int32))
+        if logits is not None:
+            self.logits = np.ascontiguousarray(np.asarray(logits).reshape(-1) != 0, dtype=np.int8)
+            self.b.logits = self.logits.ctypes.data_as(C.POINTER(C.c_int8))
+
+
+class TorchAllocator:
+    """Device memory for libubd from PyTorch's caching allocator."""
+
+    def __init__(self, torch, device):
+        self.torch = torch
+        self.device = device
+        self.live = {}
+        self.alloc_fn = ALLOC_FN(self._alloc)
+        self.free_fn = FREE_FN(self._free)
+
+    def _alloc(self, n, ud):
+        try:
+            t = self.torch.empty(int(n), dtype=self.torch.uint8, device=self.device)
+        except Exception:  # out of memory -> NULL, reported by libubd as -2
+            return None
+        p = t.data_ptr()
+        self.live[p] = t
+        return p
+
+    def _free(self, p, ud):
+        self.live.pop(p, None)
+
+
+def _stream_ptr(torch, device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Model:
+    """A loaded model.  ``tensors`` maps GGUF names to dicts as produced by
+    workloads.gen.gen_tensor (NumPy host arrays) or workloads.device
+    (torch CUDA tensors, passed as device pointers)."""
+
+    def __init__(self, shape, tensors, device=0, torch_alloc=True):
+        import torch
+        self.lib = load_library()
+        self.torch = torch
+        self.shape = shape
+        self.device = device
+        torch.cuda.set_device(device)
+        self.alloc = TorchAllocator(torch, f"cuda:{device}") if torch_alloc else None
+        hp = Hparams(shape.n_layer, shape.n_embd, shape.n_head, shape.n_head_kv, shape.n_ff,
+                     shape.n_vocab, shape.n_ctx_train, shape.rms_eps, shape.rope_base, 0)
+        keep = []
+        arr = (TensorSrc * len(tensors))()
+        for i, (name, t) in enumerate(tensors.items()):
+            s = arr[i]
+            s.name = name.encode()
+            keep.append(s.name)
+            s.type = TYPE_IDS[t["type"]]
+            data = t["q"] if t["type"] == "q8_0" else t["data"]
+            if data.ndim == 1:
+                s.ne[0], s.ne[1] = data.shape[0], 1
+            else:
+                s.ne[0], s.ne[1] = data.shape[1], data.shape[0]
+            if isinstance(data, np.ndarray):
+                data = np.ascontiguousarray(data)
+                keep.append(data)
+                s.data = data.ctypes.data
+                s.on_device = 0
+                if t["type"] == "q8_0":
+                    sc = np.ascontiguousarray(t["scale"])
+                    keep.append(sc)
+                    s.scales = sc.ctypes.data
+            else:
+                s.data = data.data_ptr()
+                s.on_device = 1
+                if t["type"] == "q8_0":
+                    s.scales = t["scale"].data_ptr()
+        mp = ModelParams()
+        mp.device = device
+        if self.alloc:
+            mp.alloc = self.alloc.alloc_fn
+            mp.free = self.alloc.free_fn
+        mp.stream = _stream_ptr(torch, device)
+        st = C.c_int32(0)
+        self.ptr = self.lib.ubd_model_load(C.byref(hp), arr, len(tensors), C.byref(mp), C.byref(st))
+        if not self.ptr:
+            raise RuntimeError(f"ubd_model_load failed ({st.value}): {last_error()}")
+        self._finalizer = weakref.finalize(self, self.lib.ubd_model_free, self.ptr)
+
+    def size(self):
+        return self.lib.ubd_model_size(self.ptr)
+
+    def free(self):
+        self._finalizer()
+
+
+class Context:
+    def __init__(self, model, n_ctx, n_batch=2048, n_ubatch=512, n_seq_max=1, type_k="f16",
+                 type_v="f16", kv_unified=False, abort_callback=None):
+        self.lib = model.lib
+        self.model = model
+        torch = model.torch
+        p = self.lib.ubd_context_default_params()
+        p.n_ctx, p.n_batch, p.n_ubatch, p.n_seq_max = n_ctx, n_batch, n_ubatch, n_seq_max
+        p.type_k, p.type_v = TYPE_IDS[type_k], TYPE_IDS[type_v]
+        p.kv_unified = kv_unified
+        self._abort = None
+        if abort_callback is not None:
+            self._abort = ABORT_FN(lambda ud: bool(abort_callback()))
+            p.abort_callback = self._abort
+        p.stream = _stream_ptr(torch, model.device)
+        st = C.c_int32(0)
+        self.ptr = self.lib.ubd_init_from_model(model.ptr, C.byref(p), C.byref(st))
+        if not self.ptr:
+            raise RuntimeError(f"ubd_init_from_model failed ({st.value}): {last_error()}")
+        self.n_vocab = model.shape.n_vocab
+        self._finalizer = weakref.finalize(self, self.lib.ubd_free, self.ptr)
+
+    def free(self):
+        self._finalizer()
+
+    @property
+    def n_ctx(self):
+        return self.lib.ubd_n_ctx(self.ptr)
+
+    def decode(self, tokens, pos=None, seq_id=None, logits=None):
+        h = _BatchHolder(tokens, pos, seq_id, logits)
+        return self.lib.ubd_decode(self.ptr, h.b)
+
+    def n_outputs(self):
+        return self.lib.ubd_n_outputs(self.ptr)
+
+    def logits(self):
+        n = self.n_outputs()
+        p = self.lib.ubd_get_logits(self.ptr)
+        if not p or n == 0:
+            return None
+        return np.ctypeslib.as_array(p, shape=(n, self.n_vocab)).copy()
+
+    def logits_ith(self, i):
+        p = self.lib.ubd_get_logits_ith(self.ptr, i)
+        return None if not p else np.ctypeslib.as_array(p, shape=(self.n_vocab,)).copy()
+
+    def greedy(self, i=-1):
+        return self.lib.ubd_sample_greedy(self.ptr, i)
+
+    def greedy_all(self):
+        n = self.n_outputs()
+        out = np.zeros(max(n, 1), np.int32)
+        r = self.lib.ubd_sample_greedy_all(self.ptr, out.ctypes.data_as(C.POINTER(C.c_int32)), out.size)
+        if r < 0:
+            raise RuntimeError(f"ubd_sample_greedy_all failed: {last_error()}")
+        return out[:r]
+
+    def synchronize(self):
+        return self.lib.ubd_synchronize(self.ptr)
+
+    def seq_pos_min(self, s):
+        return self.lib.ubd_memory_seq_pos_min(self.ptr, s)
+
+    def seq_pos_max(self, s):
+        return self.lib.ubd_memory_seq_pos_max(self.ptr, s)
+
+    def seq_rm(self, s, p0, p1):
+        return self.lib.ubd_memory_seq_rm(self.ptr, s, p0, p1)
+
+    def kv_cells(self, n_tokens):
+        out = np.zeros(n_tokens, np.int32)
+        r = self.lib.ubd_get_kv_cells(self.ptr, out.ctypes.data_as(C.POINTER(C.c_int32)), n_tokens)
+        return None if r < 0 else out[:r]
+
+    def kv_fill(self, seq, n_pos, k_layers, v_layers, src_type="f16"):
+        """k_layers / v_layers: per-layer arrays [n_pos][n_head_kv*head_dim]
+        (NumPy host arrays or torch CUDA tensors; f16 passed as uint16 /
+        int16 bit patterns)."""
+        on_device = not isinstance(k_layers[0], np.ndarray)
+        keep = []
+
+        def ptrs(layers):
+            a = (C.c_void_p * len(layers))()
+            for i, t in enumerate(layers):
+                if on_device:
+                    a[i] = t.data_ptr()
+                else:
+                    t = np.ascontiguousarray(t)
+                    keep.append(t)
+                    a[i] = t.ctypes.data
+            return a
+        ka, va = ptrs(k_layers), ptrs(v_layers)
+        return self.lib.ubd_kv_fill(self.ptr, seq, n_pos, ka, va, TYPE_IDS[src_type], int(on_device))
+
+    def kv_read(self, layer, stream, which, cell0, n):
+        hp = self.model.shape
+        out = np.zeros((n, hp.n_embd_kv), np.float32)
+        rc = self.lib.ubd_kv_read(self.ptr, layer, stream, which, cell0, n,
+                                  out.ctypes.data_as(C.POINTER(C.c_float)))
+        if rc != 0:
+            raise RuntimeError(f"ubd_kv_read failed: {last_error()}")
+        return out
+
+    def keep_residuals(self, enable=True):
+        return self.lib.ubd_debug_keep_residuals(self.ptr, int(enable))
+
+    def residual(self, layer, max_tokens):
+        out = np.zeros((max_tokens, self.model.shape.n_embd), np.float32)
+        r = self.lib.ubd_debug_get_residual(self.ptr, layer, out.ctypes.data_as(C.POINTER(C.c_float)),
+                                            max_tokens)
+        if r < 0:
+            raise RuntimeError(f"ubd_debug_get_residual failed: {last_error()}")
+        return out[:r]
+
+    def last_ubatch(self, max_tokens):
+        out = np.zeros(max_tokens, np.int32)
+        r = self.lib.ubd_debug_last_ubatch(self.ptr, out.ctypes.data_as(C.POINTER(C.c_int32)), max_tokens)
+        return out[:r]
+
+    def perf(self):
+        p = Perf()
+        self.lib.ubd_perf_get(self.ptr, C.byref(p))
+        return {f: getattr(p, f) for f, _ in Perf._fields_}
+
+
+class Planner:
+    """The host-only planner entry points (no GPU needed)."""
+
+    def __init__(self, n_ctx, n_batch, n_ubatch, n_seq_max, kv_unified, n_vocab):
+        self.lib = load_library()
+        self.ptr = self.lib.ubd_planner_new(n_ctx, n_batch, n_ubatch, n_seq_max, kv_unified, n_vocab)
+        if not self.ptr:
+            raise RuntimeError(f"ubd_planner_new failed: {last_error()}")
+        self._finalizer = weakref.finalize(self, self.lib.ubd_planner_free, self.ptr)
+
+    def decode(self, tokens, pos=None, seq_id=None, logits=None, fail_at=-1, fail_code=0):
+        h = _BatchHolder(tokens, pos, seq_id, logits)
+        return self.lib.ubd_planner_decode(self.ptr, h.b, fail_at, fail_code)
+
+    def ubatches(self, cap=1 << 16):
+        out = []
+        for k in range(self.lib.ubd_planner_n_ubatches(self.ptr)):
+            idx, cells, st = (np.zeros(cap, np.int32) for _ in range(3))
+            n = self.lib.ubd_planner_ubatch(self.ptr, k, idx.ctypes.data_as(C.POINTER(C.c_int32)),
+                                            cells.ctypes.data_as(C.POINTER(C.c_int32)),
+                                            st.ctypes.data_as(C.POINTER(C.c_int32)), cap)
+            out.append((idx[:n].copy(), cells[:n].copy(), st[:n].copy()))
+        return out
+
+    def output_row(self, i):
+        return self.lib.ubd_planner_output_row(self.ptr, i)
+
+    def n_outputs(self):
+        return self.lib.ubd_planner_n_outputs(self.ptr)
+
+    def seq_pos_min(self, s):
+        return self.lib.ubd_planner_seq_pos_min(self.ptr, s)
+
+    def seq_pos_max(self, s):
+        return self.lib.ubd_planner_seq_pos_max(self.ptr, s)
+
+    def seq_rm(self, s, p0, p1):
+        return self.lib.ubd_planner_seq_rm(self.ptr, s, p0, p1)
+
+    def n_kv(self, stream):
+        return self.lib.ubd_planner_n_kv(self.ptr, stream)

@@ -1,0 +1,132 @@
+// Host-callable launchers of the gfx950 kernels (kernels.hip).
+//
+// Layouts shared by the kernels and the runtime:
+//  * Activations are row-major [tokens][features].  An activation given to
+//    a matrix product is either F32 (f32 weights) or HILO: two bf16 planes
+//    with x ~= hi + lo (hi = bf16(x), lo = bf16(x - hi)), which keeps about
+//    16 significand bits when the weights are bf16 or q8_0.
+//  * Weight matrices [rows][cols] are stored pre-tiled in MFMA fragment
+//    order: one 1 KB tile per 16-row block and k-step, lane l = 16*g + r
+//    holding 16 bytes of row r:
+//      f32 : k-step 16 values, lane bytes = cols 16*s + 4g .. +4
+//      bf16: k-step 32 values, lane bytes = cols 32*s + 8g .. +8
+//      q8_0: k-step 64 values, lane bytes = cols 64*s + 8g .. +8 then
+//            cols 64*s + 32 + 8g .. +8 (codes), scales as
+//            [row block][cols/32][16 rows] f16.
+//    Tile (rb, s) starts at byte (rb * steps + s) * 1024.
+//  * KV cache per layer: K [stream][kv head][cell][head_dim] and V
+//    transposed [stream][kv head][head_dim][cell], each of type_k / type_v.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ubd {
+
+enum WType : int { W_F32 = 0, W_BF16 = 2, W_Q8 = 3 };
+enum KVType : int { KV_F32 = 0, KV_F16 = 1 };
+
+struct Act {
+    float *f32 = nullptr;      // F32 format
+    uint16_t *hi = nullptr;    // HILO format
+    uint16_t *lo = nullptr;
+    int ld = 0;                // elements per row
+};
+
+// Per-ubatch token table on the device (int32 planes of capacity `cap`).
+struct TokInfo {
+    const int32_t *token, *pos, *seq, *stream, *cell, *out_row, *tile_of;
+    const int32_t *out_tok;    // ubatch indices of output tokens
+    const int32_t *tiles;      // [n_tiles][4] = t0, n_tokens, stream, n_kv
+};
+
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_LOGITS = 4 };
+
+struct QKVEpi {
+    int n_q_rows = 0, n_k_rows = 0;   // H*hd, Hk*hd
+    int head_dim = 0, n_head_kv = 0, n_cells = 0;
+    const double *inv_freq = nullptr; // [head_dim / 2]
+    float *q_out = nullptr;           // [T][H*hd] f32, RoPE applied
+    void *k_cache = nullptr;          // layer base
+    void *v_cache = nullptr;
+    int type_k = KV_F16, type_v = KV_F16;
+};
+
+struct LinearArgs {
+    int wtype = W_BF16;
+    const void *w = nullptr;          // tiled weights
+    const uint16_t *wscale = nullptr; // q8_0 scales (tiled)
+    int N = 0, K = 0;                 // rows (outputs), cols (inputs)
+    Act x;                            // input [T][K] in F32 or HILO
+    int T = 0;                        // tokens
+    int epi = EPI_STORE;
+    float *y = nullptr;               // STORE / RESID target [T][ldy]
+    int ldy = 0;
+    Act out;                          // SWIGLU output [T][N/2]
+    const int32_t *row_map = nullptr; // LOGITS: output row of each token
+    float *logits = nullptr;          // LOGITS: [rows][N]
+    TokInfo tok;                      // QKV: pos / stream / cell per token
+    QKVEpi qkv;
+};
+
+void launch_linear(const LinearArgs &a, hipStream_t s);
+
+// x[t] = dequant(table[token[t]]); also records (pos, seq) of each token's
+// cell in the device cell tables [stream][n_cells].
+void launch_embed(int wtype, const void *table, const uint16_t *scales,
+                  int d, const TokInfo &ti, int T, float *x,
+                  int32_t *cell_pos, int32_t *cell_seq, int n_cells,
+                  hipStream_t s);
+
+// out[r] = rmsnorm(x[src_row(r)]) * gain, src_row = row_map ? row_map[r] : r
+void launch_rmsnorm(const float *x, int ldx, const int32_t *row_map, int rows,
+                    const float *gain, int d, float eps, const Act &out,
+                    hipStream_t s);
+
+struct AttnArgs {
+    const float *q = nullptr;         // [T][H*hd] f32 (RoPE applied)
+    const void *k_cache = nullptr;    // layer base
+    const void *v_cache = nullptr;
+    int type_k = KV_F16, type_v = KV_F16;
+    const int32_t *cell_pos = nullptr, *cell_seq = nullptr; // [stream][n_cells]
+    int n_cells = 0, n_head = 0, n_head_kv = 0, head_dim = 0;
+    TokInfo tok;
+    int T = 0, n_tiles = 0, max_chunks = 0;
+    float *part_o = nullptr;          // [T][H][max_chunks][hd]
+    float *part_ml = nullptr;         // [T][H][max_chunks][2]
+    Act out;                          // [T][H*hd]
+};
+constexpr int ATTN_CHUNK = 256;       // cells per split-K chunk
+constexpr int ATTN_TILE_ROWS = 64;    // query rows (tokens x n_gqa) per tile
+
+void launch_attention(const AttnArgs &a, hipStream_t s);
+// Query rows (tokens x n_gqa) one attention tile holds for a head size.
+int attn_tile_rows(int head_dim);
+
+// out[r] = argmax over n of logits[row(r)][n] (lowest index on ties)
+void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows,
+                   int n, int32_t *out, hipStream_t s);
+
+// Weight relayout: row-major source matrices -> tiled layout.  Up to three
+// sources are concatenated by rows (mode 0) or two are interleaved by
+// 16-row blocks, block 2j from src[0], block 2j+1 from src[1] (mode 1).
+struct RelayoutSrc {
+    const void *data = nullptr;        // row-major [rows][K]
+    const uint16_t *scales = nullptr;  // q8_0: [rows][K/32]
+    int rows = 0;
+};
+void launch_relayout(int wtype, const RelayoutSrc *src, int n_src, int mode,
+                     int K, void *dst, uint16_t *dst_scales, hipStream_t s);
+
+// KV rows [n][n_head_kv*hd] of src_type (KV_F32 / KV_F16) into the cache
+// cells cells[0..n) of one stream (K natural, V transposed).
+void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
+                     void *cache, int type, bool transposed, int stream,
+                     int n_head_kv, int hd, int n_cells, hipStream_t s);
+// Cache rows of cells [cell0, cell0+n) of one stream as f32 [n][n_head_kv*hd].
+void launch_kv_load(const void *cache, int type, bool transposed, int stream,
+                    int cell0, int n, int n_head_kv, int hd, int n_cells,
+                    float *out, hipStream_t s);
+
+}  // namespace ubd

@@ -1,0 +1,1077 @@
+// libubd runtime: model loading, contexts, the per-ubatch kernel schedule
+// and the C ABI declared in include/ubd.h.
+//
+// One forward pass per ubatch follows the per-layer outline of the engine
+// page ("llama.cpp AI LLM Engine - how it works", Step 13b) and the decode
+// node list of the architecture page ("llama.cpp Architecture", Example 4):
+//   embed -> per layer [RMSNorm -> QKV product (+RoPE, +K/V append into the
+//   ubatch's cells) -> attention over the stream's cells -> O product
+//   (+residual) -> RMSNorm -> gate|up product (+SwiGLU) -> down product
+//   (+residual)] -> output rows -> RMSNorm -> logits product.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "planner.h"
+#include "ubd.h"
+
+using namespace ubd;
+
+namespace {
+
+thread_local std::string g_err;
+ubd_log_fn g_log = nullptr;
+void *g_log_ud = nullptr;
+
+void log_line(int level, const char *fmt, ...) {
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (g_log)
+        g_log(level, buf, g_log_ud);
+    else if (level >= 2)
+        fprintf(stderr, "ubd: %s\n", buf);
+}
+
+void set_err(const std::string &m) {
+    g_err = m;
+    log_line(2, "%s", m.c_str());
+}
+
+bool hip_ok(hipError_t e, const char *what) {
+    if (e == hipSuccess) return true;
+    set_err(std::string(what) + ": " + hipGetErrorString(e));
+    return false;
+}
+
+double now_ms() {
+    using namespace std::chrono;
+    return duration<double, std::milli>(steady_clock::now().time_since_epoch()).count();
+}
+
+int wtype_of(ubd_type t) {
+    switch (t) {
+    case UBD_TYPE_F32: return W_F32;
+    case UBD_TYPE_BF16: return W_BF16;
+    case UBD_TYPE_Q8_0: return W_Q8;
+    default: return -1;
+    }
+}
+
+size_t elem_bytes(int wtype) { return wtype == W_F32 ? 4 : wtype == W_BF16 ? 2 : 1; }
+
+int kstep_of(int wtype) { return wtype == W_F32 ? 16 : wtype == W_BF16 ? 32 : 64; }
+
+// Device memory owner that goes through the caller's hooks (or hipMalloc).
+struct DevAlloc {
+    ubd_alloc_fn alloc = nullptr;
+    ubd_free_fn free = nullptr;
+    void *ud = nullptr;
+    std::vector<void *> blocks;
+    size_t bytes = 0;
+
+    void *get(size_t n) {
+        n = (n + 255) / 256 * 256;
+        if (n == 0) n = 256;
+        void *p = nullptr;
+        if (alloc) {
+            p = alloc(n, ud);
+        } else if (hipMalloc(&p, n) != hipSuccess) {
+            p = nullptr;
+        }
+        if (p) {
+            blocks.push_back(p);
+            bytes += n;
+        }
+        return p;
+    }
+    void release() {
+        for (void *p : blocks) {
+            if (free)
+                free(p, ud);
+            else
+                (void)hipFree(p);
+        }
+        blocks.clear();
+        bytes = 0;
+    }
+};
+
+}  // namespace
+
+struct DevMat {
+    int wtype = W_F32;
+    int rows = 0, cols = 0;
+    void *w = nullptr;
+    uint16_t *scales = nullptr;
+};
+
+struct ubd_model {
+    ubd_hparams hp{};
+    int device = 0;
+    hipStream_t stream = nullptr;
+    DevAlloc mem;
+    int wtype = W_F32;
+    int head_dim = 0;
+    void *embd = nullptr;
+    uint16_t *embd_scales = nullptr;
+    struct Layer {
+        float *attn_norm = nullptr, *ffn_norm = nullptr;
+        DevMat qkv, o, gu, down;
+    };
+    std::vector<Layer> layers;
+    float *out_norm = nullptr;
+    DevMat out;
+    double t_load_ms = 0;
+};
+
+// -------------------------------------------------------------- model load
+namespace {
+
+struct Expect {
+    int64_t ne0, ne1;
+    bool gain;
+};
+
+std::map<std::string, Expect> expected_tensors(const ubd_hparams &hp) {
+    const int64_t d = hp.n_embd, hd = hp.n_embd / hp.n_head;
+    const int64_t nq = hd * hp.n_head, nk = hd * hp.n_head_kv;
+    std::map<std::string, Expect> m;
+    m["token_embd.weight"] = {d, hp.n_vocab, false};
+    m["output_norm.weight"] = {d, 1, true};
+    m["output.weight"] = {d, hp.n_vocab, false};
+    for (int il = 0; il < hp.n_layer; ++il) {
+        const std::string p = "blk." + std::to_string(il) + ".";
+        m[p + "attn_norm.weight"] = {d, 1, true};
+        m[p + "attn_q.weight"] = {d, nq, false};
+        m[p + "attn_k.weight"] = {d, nk, false};
+        m[p + "attn_v.weight"] = {d, nk, false};
+        m[p + "attn_output.weight"] = {nq, d, false};
+        m[p + "ffn_norm.weight"] = {d, 1, true};
+        m[p + "ffn_gate.weight"] = {d, hp.n_ff, false};
+        m[p + "ffn_up.weight"] = {d, hp.n_ff, false};
+        m[p + "ffn_down.weight"] = {hp.n_ff, d, false};
+    }
+    return m;
+}
+
+// Copies a source tensor to device memory if it lives on the host.
+struct Staged {
+    Staged() = default;
+    Staged(const Staged &) = delete;
+    Staged &operator=(const Staged &) = delete;
+    const void *data = nullptr;
+    const uint16_t *scales = nullptr;
+    std::vector<void *> tmp;
+    ~Staged() {
+        for (void *p : tmp) (void)hipFree(p);
+    }
+};
+
+bool stage(const ubd_tensor_src &s, int wtype, hipStream_t st, Staged *out) {
+    const size_t n = (size_t)s.ne[0] * s.ne[1];
+    const size_t bytes = n * (wtype < 0 ? 4 : elem_bytes(wtype));
+    const size_t sbytes = wtype == W_Q8 ? (n / 32) * 2 : 0;
+    if (s.on_device) {
+        out->data = s.data;
+        out->scales = (const uint16_t *)s.scales;
+        return true;
+    }
+    void *d = nullptr;
+    if (!hip_ok(hipMalloc(&d, bytes), "staging allocation")) return false;
+    out->tmp.push_back(d);
+    if (!hip_ok(hipMemcpyAsync(d, s.data, bytes, hipMemcpyHostToDevice, st), "weight upload")) return false;
+    out->data = d;
+    if (sbytes) {
+        void *sd = nullptr;
+        if (!hip_ok(hipMalloc(&sd, sbytes), "staging allocation")) return false;
+        out->tmp.push_back(sd);
+        if (!hip_ok(hipMemcpyAsync(sd, s.scales, sbytes, hipMemcpyHostToDevice, st), "scale upload")) return false;
+        out->scales = (const uint16_t *)sd;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" ubd_model *ubd_model_load(const ubd_hparams *hparams, const ubd_tensor_src *tensors, int32_t n_tensors,
+                                     const ubd_model_params *params, int32_t *status) {
+    auto fail = [&](int32_t code, const std::string &msg) -> ubd_model * {
+        set_err(msg);
+        if (status) *status = code;
+        return nullptr;
+    };
+    g_err.clear();
+    const double t0 = now_ms();
+    if (!hparams || !tensors || n_tensors <= 0) return fail(-1, "ubd_model_load: missing arguments");
+    const ubd_hparams hp = *hparams;
+    if (hp.n_layer <= 0 || hp.n_embd <= 0 || hp.n_head <= 0 || hp.n_head_kv <= 0 || hp.n_ff <= 0 || hp.n_vocab <= 0)
+        return fail(-1, "ubd_model_load: sizes must be positive");
+    if (hp.n_embd % hp.n_head || hp.n_head % hp.n_head_kv) return fail(-1, "ubd_model_load: head counts do not divide");
+    const int hd = hp.n_embd / hp.n_head;
+    if (hd != 32 && hd != 64 && hd != 128) return fail(-1, "ubd_model_load: head_dim must be 32, 64 or 128");
+    if (hp.n_head / hp.n_head_kv > 32) return fail(-1, "ubd_model_load: at most 32 query heads per KV head");
+    if (hp.n_embd % 16 || hp.n_ff % 16 || hp.n_vocab % 16)
+        return fail(-1, "ubd_model_load: n_embd, n_ff and n_vocab must be multiples of 16");
+    if (hp.rope_type != 0) return fail(-1, "ubd_model_load: only rope type 0 is supported");
+
+    const auto expect = expected_tensors(hp);
+    std::map<std::string, const ubd_tensor_src *> got;
+    int wtype = -1;
+    for (int32_t i = 0; i < n_tensors; ++i) {
+        const ubd_tensor_src &t = tensors[i];
+        if (!t.name || !t.data) return fail(-1, "ubd_model_load: tensor without name or data");
+        auto it = expect.find(t.name);
+        if (it == expect.end()) return fail(-1, std::string("ubd_model_load: unknown tensor ") + t.name);
+        if (got.count(t.name)) return fail(-1, std::string("ubd_model_load: duplicate tensor ") + t.name);
+        if (t.ne[0] != it->second.ne0 || t.ne[1] != it->second.ne1)
+            return fail(-1, std::string("ubd_model_load: wrong shape for ") + t.name);
+        if (it->second.gain) {
+            if (t.type != UBD_TYPE_F32) return fail(-1, std::string("ubd_model_load: norm must be F32: ") + t.name);
+        } else {
+            const int wt = wtype_of(t.type);
+            if (wt < 0) return fail(-1, std::string("ubd_model_load: unsupported matrix type for ") + t.name);
+            if (wtype >= 0 && wt != wtype) return fail(-1, "ubd_model_load: all matrices must share one type");
+            wtype = wt;
+            if (t.ne[0] % kstep_of(wt))
+                return fail(-1, std::string("ubd_model_load: row length not a multiple of the tile for ") + t.name);
+            if (wt == W_Q8 && !t.scales) return fail(-1, std::string("ubd_model_load: q8_0 without scales: ") + t.name);
+        }
+        got[t.name] = &t;
+    }
+    for (auto &kv : expect)
+        if (!got.count(kv.first)) return fail(-1, "ubd_model_load: missing tensor " + kv.first);
+
+    ubd_model *m = new ubd_model();
+    m->hp = hp;
+    m->head_dim = hd;
+    m->wtype = wtype;
+    if (params) {
+        m->device = params->device;
+        m->stream = (hipStream_t)params->stream;
+        m->mem.alloc = params->alloc;
+        m->mem.free = params->free;
+        m->mem.ud = params->alloc_user_data;
+    }
+    auto bail = [&](int32_t code, const std::string &msg) -> ubd_model * {
+        m->mem.release();
+        delete m;
+        return fail(code, msg);
+    };
+    if (!hip_ok(hipSetDevice(m->device), "hipSetDevice")) return bail(-2, g_err);
+    hipStream_t st = m->stream;
+
+    auto copy_gain = [&](const std::string &name, float **dst) -> bool {
+        const ubd_tensor_src &s = *got[name];
+        *dst = (float *)m->mem.get((size_t)hp.n_embd * 4);
+        if (!*dst) return false;
+        return hip_ok(hipMemcpyAsync(*dst, s.data, (size_t)hp.n_embd * 4,
+                                     s.on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, st),
+                      "norm upload");
+    };
+    auto make_mat = [&](DevMat &dm, const std::vector<std::string> &names, int mode) -> bool {
+        const ubd_tensor_src &s0 = *got[names[0]];
+        const int K = (int)s0.ne[0];
+        int rows = 0;
+        std::vector<Staged> stg(names.size());
+        RelayoutSrc src[3];
+        for (size_t i = 0; i < names.size(); ++i) {
+            const ubd_tensor_src &s = *got[names[i]];
+            if (!stage(s, wtype, st, &stg[i])) return false;
+            src[i].data = stg[i].data;
+            src[i].scales = stg[i].scales;
+            src[i].rows = (int)s.ne[1];
+            rows += (int)s.ne[1];
+        }
+        dm.wtype = wtype;
+        dm.rows = rows;
+        dm.cols = K;
+        dm.w = m->mem.get((size_t)rows * K * elem_bytes(wtype));
+        if (!dm.w) return false;
+        if (wtype == W_Q8) {
+            dm.scales = (uint16_t *)m->mem.get((size_t)rows * (K / 32) * 2);
+            if (!dm.scales) return false;
+        }
+        launch_relayout(wtype, src, (int)names.size(), mode, K, dm.w, dm.scales, st);
+        if (!hip_ok(hipGetLastError(), "relayout")) return false;
+        // staging buffers are freed when stg goes out of scope: finish first
+        return hip_ok(hipStreamSynchronize(st), "relayout sync");
+    };
+
+    m->layers.resize(hp.n_layer);
+    for (int il = 0; il < hp.n_layer; ++il) {
+        const std::string p = "blk." + std::to_string(il) + ".";
+        auto &L = m->layers[il];
+        if (!copy_gain(p + "attn_norm.weight", &L.attn_norm) || !copy_gain(p + "ffn_norm.weight", &L.ffn_norm))
+            return bail(-2, "ubd_model_load: norm upload failed: " + g_err);
+        if (!make_mat(L.qkv, {p + "attn_q.weight", p + "attn_k.weight", p + "attn_v.weight"}, 0) ||
+            !make_mat(L.o, {p + "attn_output.weight"}, 0) ||
+            !make_mat(L.gu, {p + "ffn_gate.weight", p + "ffn_up.weight"}, 1) ||
+            !make_mat(L.down, {p + "ffn_down.weight"}, 0))
+            return bail(-2, "ubd_model_load: weight upload failed: " + g_err);
+    }
+    if (!copy_gain("output_norm.weight", &m->out_norm) || !make_mat(m->out, {"output.weight"}, 0))
+        return bail(-2, "ubd_model_load: output upload failed: " + g_err);
+    {
+        const ubd_tensor_src &s = *got["token_embd.weight"];
+        const size_t n = (size_t)s.ne[0] * s.ne[1];
+        const hipMemcpyKind kind = s.on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+        m->embd = m->mem.get(n * elem_bytes(wtype));
+        if (!m->embd || !hip_ok(hipMemcpyAsync(m->embd, s.data, n * elem_bytes(wtype), kind, st), "embedding upload"))
+            return bail(-2, "ubd_model_load: embedding upload failed: " + g_err);
+        if (wtype == W_Q8) {
+            m->embd_scales = (uint16_t *)m->mem.get(n / 32 * 2);
+            if (!m->embd_scales || !hip_ok(hipMemcpyAsync(m->embd_scales, s.scales, n / 32 * 2, kind, st), "scales"))
+                return bail(-2, "ubd_model_load: embedding upload failed: " + g_err);
+        }
+    }
+    if (!hip_ok(hipStreamSynchronize(st), "load sync")) return bail(-2, "ubd_model_load: " + g_err);
+    m->t_load_ms = now_ms() - t0;
+    log_line(1, "model loaded: %d layers, %.1f MiB on device, %.1f ms", hp.n_layer, m->mem.bytes / 1048576.0,
+             m->t_load_ms);
+    if (status) *status = 0;
+    return m;
+}
+
+extern "C" void ubd_model_free(ubd_model *model) {
+    if (!model) return;
+    (void)hipSetDevice(model->device);
+    (void)hipStreamSynchronize(model->stream);
+    model->mem.release();
+    delete model;
+}
+
+extern "C" size_t ubd_model_size(const ubd_model *model) { return model ? model->mem.bytes : 0; }
+
+// ----------------------------------------------------------------- context
+struct ubd_context : public Executor {
+    ubd_model *model = nullptr;
+    ubd_context_params cp{};
+    hipStream_t stream = nullptr;
+    Planner planner;
+    DevAlloc mem;
+    int type_k = KV_F16, type_v = KV_F16;
+    size_t kv_layer_elems = 0;              // per layer, K or V
+    void *k_cache = nullptr, *v_cache = nullptr;
+    int32_t *cell_pos = nullptr, *cell_seq = nullptr;
+    float *x = nullptr, *q = nullptr;
+    Act actA, actB, actC;
+    float *part_o = nullptr, *part_ml = nullptr;
+    int max_chunks = 0;
+    double *inv_freq = nullptr;
+    int32_t *info_dev = nullptr;
+    int32_t *info_host[2] = {nullptr, nullptr};
+    hipEvent_t info_ev[2] = {nullptr, nullptr};
+    int info_i = 0;
+    int cap = 0;                            // n_ubatch
+    float *logits_dev = nullptr;
+    int32_t logits_cap = 0;
+    std::vector<float> logits_host;
+    bool logits_host_valid = false;
+    int32_t *argmax_dev = nullptr;
+    std::vector<int32_t> last_ub_idx;
+    float *dump = nullptr;
+    ubd_perf perf{};
+
+    TokInfo tok_info() const {
+        TokInfo t;
+        const int32_t *b = info_dev;
+        t.token = b;
+        t.pos = b + cap;
+        t.seq = b + 2 * cap;
+        t.stream = b + 3 * cap;
+        t.cell = b + 4 * cap;
+        t.out_row = b + 5 * cap;
+        t.tile_of = b + 6 * cap;
+        t.out_tok = b + 7 * cap;
+        t.tiles = b + 9 * cap;
+        return t;
+    }
+    const int32_t *out_lrow() const { return info_dev + 8 * cap; }
+    size_t info_ints() const { return (size_t)13 * cap; }
+
+    int32_t reserve_outputs(int32_t n) override;
+    int32_t run_ubatch(const UBatch &ub, int32_t k) override;
+    void cells_cleared(const std::vector<std::pair<int32_t, int32_t>> &cl) override;
+    bool sync_cell_tables(int32_t stream);
+};
+
+extern "C" ubd_context_params ubd_context_default_params(void) {
+    ubd_context_params p{};
+    p.n_ctx = 0;
+    p.n_batch = 2048;
+    p.n_ubatch = 512;
+    p.n_seq_max = 1;
+    p.type_k = UBD_TYPE_F16;
+    p.type_v = UBD_TYPE_F16;
+    p.kv_unified = false;
+    return p;
+}
+
+extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_params *params, int32_t *status) {
+    g_err.clear();
+    auto fail = [&](int32_t code, const std::string &msg) -> ubd_context * {
+        set_err(msg);
+        if (status) *status = code;
+        return nullptr;
+    };
+    if (!model || !params) return fail(-1, "ubd_init_from_model: missing arguments");
+    const ubd_context_params cp = *params;
+    auto kvt = [](ubd_type t) { return t == UBD_TYPE_F32 ? KV_F32 : t == UBD_TYPE_F16 ? KV_F16 : -1; };
+    if (kvt(cp.type_k) < 0 || kvt(cp.type_v) < 0) return fail(-1, "ubd_init_from_model: KV types must be F32 or F16");
+    ubd_context *c = new ubd_context();
+    c->model = model;
+    c->cp = cp;
+    c->stream = (hipStream_t)cp.stream;
+    c->type_k = kvt(cp.type_k);
+    c->type_v = kvt(cp.type_v);
+    c->mem.alloc = model->mem.alloc;
+    c->mem.free = model->mem.free;
+    c->mem.ud = model->mem.ud;
+    std::string err;
+    const ubd_hparams &hp = model->hp;
+    if (c->planner.init(cp.n_ctx ? cp.n_ctx : (uint32_t)hp.n_ctx_train, cp.n_batch, cp.n_ubatch, cp.n_seq_max,
+                        cp.kv_unified, hp.n_vocab, &err) != UBD_OK) {
+        delete c;
+        return fail(-1, "ubd_init_from_model: " + err);
+    }
+    auto bail = [&](const std::string &msg) -> ubd_context * {
+        c->mem.release();
+        for (int i = 0; i < 2; ++i) {
+            if (c->info_host[i]) (void)hipHostFree(c->info_host[i]);
+            if (c->info_ev[i]) (void)hipEventDestroy(c->info_ev[i]);
+        }
+        delete c;
+        return fail(-2, "ubd_init_from_model: " + msg + (g_err.empty() ? "" : ": " + g_err));
+    };
+    if (!hip_ok(hipSetDevice(model->device), "hipSetDevice")) return bail("device");
+    const Planner &P = c->planner;
+    const int hd = model->head_dim, H = hp.n_head, Hk = hp.n_head_kv, d = hp.n_embd, F = hp.n_ff;
+    c->cap = (int)P.n_ubatch;
+    const size_t cells = (size_t)P.n_stream * P.n_cells;
+    c->kv_layer_elems = cells * Hk * hd;
+    const size_t kb = c->type_k == KV_F32 ? 4 : 2, vb = c->type_v == KV_F32 ? 4 : 2;
+    c->k_cache = c->mem.get(c->kv_layer_elems * hp.n_layer * kb);
+    c->v_cache = c->mem.get(c->kv_layer_elems * hp.n_layer * vb);
+    c->cell_pos = (int32_t *)c->mem.get(cells * 4);
+    c->cell_seq = (int32_t *)c->mem.get(cells * 4);
+    if (!c->k_cache || !c->v_cache || !c->cell_pos || !c->cell_seq) return bail("KV cache allocation failed");
+    if (!hip_ok(hipMemsetAsync(c->cell_pos, 0xff, cells * 4, c->stream), "memset") ||
+        !hip_ok(hipMemsetAsync(c->cell_seq, 0xff, cells * 4, c->stream), "memset"))
+        return bail("KV cell table init failed");
+    const int cap = c->cap;
+    const bool f32w = model->wtype == W_F32;
+    auto make_act = [&](Act &a, int ld) -> bool {
+        a.ld = ld;
+        if (f32w) {
+            a.f32 = (float *)c->mem.get((size_t)cap * ld * 4);
+            return a.f32 != nullptr;
+        }
+        a.hi = (uint16_t *)c->mem.get((size_t)cap * ld * 2);
+        a.lo = (uint16_t *)c->mem.get((size_t)cap * ld * 2);
+        return a.hi && a.lo;
+    };
+    c->x = (float *)c->mem.get((size_t)cap * d * 4);
+    c->q = (float *)c->mem.get((size_t)cap * H * hd * 4);
+    if (!c->x || !c->q || !make_act(c->actA, d) || !make_act(c->actB, H * hd) || !make_act(c->actC, F))
+        return bail("activation allocation failed");
+    c->max_chunks = (int)((P.n_cells + ATTN_CHUNK - 1) / ATTN_CHUNK);
+    c->part_o = (float *)c->mem.get((size_t)cap * H * c->max_chunks * hd * 4);
+    c->part_ml = (float *)c->mem.get((size_t)cap * H * c->max_chunks * 2 * 4);
+    if (!c->part_o || !c->part_ml) return bail("attention scratch allocation failed");
+    std::vector<double> inv(hd / 2);
+    for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)hp.rope_freq_base, -2.0 * i / hd);
+    c->inv_freq = (double *)c->mem.get(inv.size() * sizeof(double));
+    c->info_dev = (int32_t *)c->mem.get(c->info_ints() * 4);
+    c->argmax_dev = (int32_t *)c->mem.get((size_t)std::max<uint32_t>(P.n_batch, 1) * 4);
+    if (!c->inv_freq || !c->info_dev || !c->argmax_dev) return bail("allocation failed");
+    if (!hip_ok(hipMemcpyAsync(c->inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice,
+                               c->stream), "upload"))
+        return bail("upload failed");
+    for (int i = 0; i < 2; ++i) {
+        if (!hip_ok(hipHostMalloc((void **)&c->info_host[i], c->info_ints() * 4, hipHostMallocDefault), "pinned") ||
+            !hip_ok(hipEventCreateWithFlags(&c->info_ev[i], hipEventDisableTiming), "event"))
+            return bail("pinned staging allocation failed");
+    }
+    if (!hip_ok(hipStreamSynchronize(c->stream), "init sync")) return bail("sync failed");
+    log_line(1, "context: n_ctx %u (%u streams x %u cells), n_batch %u, n_ubatch %u, KV %.1f MiB", P.n_ctx,
+             P.n_stream, P.n_cells, P.n_batch, P.n_ubatch,
+             (double)c->kv_layer_elems * hp.n_layer * (kb + vb) / 1048576.0);
+    if (status) *status = 0;
+    return c;
+}
+
+extern "C" void ubd_free(ubd_context *ctx) {
+    if (!ctx) return;
+    (void)hipSetDevice(ctx->model->device);
+    (void)hipStreamSynchronize(ctx->stream);
+    ctx->mem.release();
+    for (int i = 0; i < 2; ++i) {
+        if (ctx->info_host[i]) (void)hipHostFree(ctx->info_host[i]);
+        if (ctx->info_ev[i]) (void)hipEventDestroy(ctx->info_ev[i]);
+    }
+    delete ctx;
+}
+
+extern "C" uint32_t ubd_n_ctx(const ubd_context *ctx) { return ctx ? ctx->planner.n_ctx : 0; }
+extern "C" uint32_t ubd_n_batch(const ubd_context *ctx) { return ctx ? ctx->planner.n_batch : 0; }
+extern "C" uint32_t ubd_n_ubatch(const ubd_context *ctx) { return ctx ? ctx->planner.n_ubatch : 0; }
+
+int32_t ubd_context::reserve_outputs(int32_t n) {
+    logits_host_valid = false;
+    if (n <= logits_cap) return UBD_OK;
+    const ubd_hparams &hp = model->hp;
+    int32_t want = std::max<int32_t>(n, 1);
+    // logits rows live as long as the context; an outgrown block is kept
+    float *p = (float *)mem.get((size_t)want * hp.n_vocab * 4);
+    if (!p) {
+        set_err("cannot allocate the logits buffer");
+        return UBD_ALLOC_FAILED;
+    }
+    logits_dev = p;
+    logits_cap = want;
+    return UBD_OK;
+}
+
+bool ubd_context::sync_cell_tables(int32_t st) {
+    const Planner &P = planner;
+    const size_t off = (size_t)st * P.n_cells;
+    return hip_ok(hipMemcpyAsync(cell_pos + off, P.cells.pos_data(st), (size_t)P.n_cells * 4,
+                                 hipMemcpyHostToDevice, stream), "cell table upload") &&
+           hip_ok(hipMemcpyAsync(cell_seq + off, P.cells.seq_data(st), (size_t)P.n_cells * 4,
+                                 hipMemcpyHostToDevice, stream), "cell table upload") &&
+           hip_ok(hipStreamSynchronize(stream), "cell table sync");
+}
+
+void ubd_context::cells_cleared(const std::vector<std::pair<int32_t, int32_t>> &cl) {
+    std::vector<uint8_t> touched(planner.n_stream, 0);
+    for (auto &p : cl) touched[p.first] = 1;
+    for (uint32_t st = 0; st < planner.n_stream; ++st)
+        if (touched[st]) sync_cell_tables((int32_t)st);
+}
+
+int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
+    (void)k;
+    if (cp.abort_callback && cp.abort_callback(cp.abort_user_data)) {
+        set_err("decode aborted by the callback");
+        return UBD_ABORTED;
+    }
+    const ubd_model &M = *model;
+    const ubd_hparams &hp = M.hp;
+    const int T = ub.size();
+    const int hd = M.head_dim, H = hp.n_head, Hk = hp.n_head_kv, d = hp.n_embd;
+    const int G = H / Hk;
+
+    // ---- per-ubatch token table (one H2D copy from pinned staging)
+    const int bi = info_i;
+    info_i ^= 1;
+    if (!hip_ok(hipEventSynchronize(info_ev[bi]), "staging reuse")) return UBD_COMPUTE_FAILED;
+    int32_t *h = info_host[bi];
+    std::fill(h, h + info_ints(), 0);
+    int n_out = 0;
+    for (int t = 0; t < T; ++t) {
+        h[t] = ub.token[t];
+        h[cap + t] = ub.pos[t];
+        h[2 * cap + t] = ub.seq[t];
+        h[3 * cap + t] = ub.stream[t];
+        h[4 * cap + t] = ub.cell[t];
+        h[5 * cap + t] = ub.out_row[t];
+        if (ub.out_row[t] >= 0) {
+            h[7 * cap + n_out] = t;
+            h[8 * cap + n_out] = ub.out_row[t];
+            ++n_out;
+        }
+    }
+    const int qt = std::max(1, attn_tile_rows(hd) / G);
+    int n_tiles = 0;
+    for (int t = 0; t < T;) {
+        int e = t + 1;
+        while (e < T && e - t < qt && ub.stream[e] == ub.stream[t]) ++e;
+        int32_t *tl = h + 9 * cap + 4 * n_tiles;
+        tl[0] = t;
+        tl[1] = e - t;
+        tl[2] = ub.stream[t];
+        tl[3] = planner.cells.n_kv(ub.stream[t]);
+        for (int j = t; j < e; ++j) h[6 * cap + j] = n_tiles;
+        ++n_tiles;
+        t = e;
+    }
+    if (!hip_ok(hipMemcpyAsync(info_dev, h, info_ints() * 4, hipMemcpyHostToDevice, stream), "token table upload") ||
+        !hip_ok(hipEventRecord(info_ev[bi], stream), "event"))
+        return UBD_COMPUTE_FAILED;
+    last_ub_idx = ub.idx;
+
+    const TokInfo ti = tok_info();
+    const int n_cells = (int)planner.n_cells;
+    launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, stream);
+    if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, stream), "dump");
+
+    const size_t kb = type_k == KV_F32 ? 4 : 2, vb = type_v == KV_F32 ? 4 : 2;
+    for (int il = 0; il < hp.n_layer; ++il) {
+        const auto &L = M.layers[il];
+        launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, actA, stream);
+
+        LinearArgs la;
+        la.wtype = M.wtype;
+        la.T = T;
+        la.tok = ti;
+        // Q, K, V (+RoPE, +append into the KV cells)
+        la.w = L.qkv.w;
+        la.wscale = L.qkv.scales;
+        la.N = L.qkv.rows;
+        la.K = L.qkv.cols;
+        la.x = actA;
+        la.epi = EPI_QKV;
+        la.qkv.n_q_rows = H * hd;
+        la.qkv.n_k_rows = Hk * hd;
+        la.qkv.head_dim = hd;
+        la.qkv.n_head_kv = Hk;
+        la.qkv.n_cells = n_cells;
+        la.qkv.inv_freq = inv_freq;
+        la.qkv.q_out = q;
+        la.qkv.k_cache = (char *)k_cache + kv_layer_elems * il * kb;
+        la.qkv.v_cache = (char *)v_cache + kv_layer_elems * il * vb;
+        la.qkv.type_k = type_k;
+        la.qkv.type_v = type_v;
+        launch_linear(la, stream);
+
+        AttnArgs aa;
+        aa.q = q;
+        aa.k_cache = la.qkv.k_cache;
+        aa.v_cache = la.qkv.v_cache;
+        aa.type_k = type_k;
+        aa.type_v = type_v;
+        aa.cell_pos = cell_pos;
+        aa.cell_seq = cell_seq;
+        aa.n_cells = n_cells;
+        aa.n_head = H;
+        aa.n_head_kv = Hk;
+        aa.head_dim = hd;
+        aa.tok = ti;
+        aa.T = T;
+        aa.n_tiles = n_tiles;
+        aa.max_chunks = max_chunks;
+        aa.part_o = part_o;
+        aa.part_ml = part_ml;
+        aa.out = actB;
+        launch_attention(aa, stream);
+
+        LinearArgs lo;
+        lo.wtype = M.wtype;
+        lo.T = T;
+        lo.tok = ti;
+        lo.w = L.o.w;
+        lo.wscale = L.o.scales;
+        lo.N = L.o.rows;
+        lo.K = L.o.cols;
+        lo.x = actB;
+        lo.epi = EPI_RESID;
+        lo.y = x;
+        lo.ldy = d;
+        launch_linear(lo, stream);
+
+        launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, actA, stream);
+        LinearArgs lg = lo;
+        lg.w = L.gu.w;
+        lg.wscale = L.gu.scales;
+        lg.N = L.gu.rows;
+        lg.K = L.gu.cols;
+        lg.x = actA;
+        lg.epi = EPI_SWIGLU;
+        lg.out = actC;
+        launch_linear(lg, stream);
+
+        LinearArgs ld = lo;
+        ld.w = L.down.w;
+        ld.wscale = L.down.scales;
+        ld.N = L.down.rows;
+        ld.K = L.down.cols;
+        ld.x = actC;
+        launch_linear(ld, stream);
+        if (dump)
+            hip_ok(hipMemcpyAsync(dump + (size_t)(il + 1) * cap * d, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice,
+                                  stream), "dump");
+    }
+    if (n_out > 0) {
+        launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, actA, stream);
+        LinearArgs lz;
+        lz.wtype = M.wtype;
+        lz.w = M.out.w;
+        lz.wscale = M.out.scales;
+        lz.N = M.out.rows;
+        lz.K = M.out.cols;
+        lz.x = actA;
+        lz.T = n_out;
+        lz.epi = EPI_LOGITS;
+        lz.row_map = out_lrow();
+        lz.logits = logits_dev;
+        launch_linear(lz, stream);
+    }
+    if (!hip_ok(hipGetLastError(), "kernel launch")) return UBD_COMPUTE_FAILED;
+    perf.n_ubatch += 1;
+    return UBD_OK;
+}
+
+// ------------------------------------------------------------------ decode
+extern "C" int32_t ubd_decode(ubd_context *ctx, ubd_batch batch) {
+    if (!ctx) return UBD_INVALID;
+    g_err.clear();
+    const double t0 = now_ms();
+    if (!hip_ok(hipSetDevice(ctx->model->device), "hipSetDevice")) return UBD_ALLOC_FAILED;
+    std::string err;
+    const int32_t rc = ctx->planner.decode(batch, ctx, &err);
+    if (rc != UBD_OK) {
+        if (g_err.empty()) set_err(err);
+        if (rc != UBD_NO_KV_SLOT && rc != UBD_INVALID) log_line(2, "decode failed, ret = %d", rc);
+        return rc;
+    }
+    const double dt = now_ms() - t0;
+    if (batch.n_tokens > 1) {
+        ctx->perf.t_p_eval_ms += dt;
+        ctx->perf.n_p_eval += batch.n_tokens;
+    } else {
+        ctx->perf.t_eval_ms += dt;
+        ctx->perf.n_eval += 1;
+    }
+    ctx->perf.n_decode += 1;
+    return UBD_OK;
+}
+
+extern "C" int32_t ubd_n_outputs(const ubd_context *ctx) {
+    return ctx && ctx->planner.last_ok ? ctx->planner.n_outputs : 0;
+}
+
+extern "C" int32_t ubd_synchronize(ubd_context *ctx) {
+    if (!ctx) return UBD_INVALID;
+    (void)hipSetDevice(ctx->model->device);
+    return hip_ok(hipStreamSynchronize(ctx->stream), "synchronize") ? UBD_OK : UBD_COMPUTE_FAILED;
+}
+
+namespace {
+int32_t resolve_row(const ubd_context *ctx, int32_t i) {
+    const Planner &P = ctx->planner;
+    if (!P.last_ok || P.n_outputs == 0) return -1;
+    if (i < 0) {
+        const int32_t r = P.n_outputs + i;
+        return r >= 0 && r < P.n_outputs ? r : -1;
+    }
+    if (i >= (int32_t)P.out_row.size()) return -1;
+    return P.out_row[i];
+}
+}  // namespace
+
+extern "C" float *ubd_get_logits(ubd_context *ctx) {
+    if (!ctx || !ctx->planner.last_ok || ctx->planner.n_outputs == 0) return nullptr;
+    if (!ctx->logits_host_valid) {
+        if (ubd_synchronize(ctx) != UBD_OK) return nullptr;
+        const size_t n = (size_t)ctx->planner.n_outputs * ctx->model->hp.n_vocab;
+        ctx->logits_host.resize(n);
+        if (!hip_ok(hipMemcpy(ctx->logits_host.data(), ctx->logits_dev, n * 4, hipMemcpyDeviceToHost), "logits"))
+            return nullptr;
+        ctx->logits_host_valid = true;
+    }
+    return ctx->logits_host.data();
+}
+
+extern "C" float *ubd_get_logits_ith(ubd_context *ctx, int32_t i) {
+    if (!ctx) return nullptr;
+    const int32_t r = resolve_row(ctx, i);
+    if (r < 0) return nullptr;
+    float *all = ubd_get_logits(ctx);
+    return all ? all + (size_t)r * ctx->model->hp.n_vocab : nullptr;
+}
+
+extern "C" const float *ubd_get_logits_device(ubd_context *ctx) {
+    return ctx && ctx->planner.last_ok && ctx->planner.n_outputs > 0 ? ctx->logits_dev : nullptr;
+}
+
+extern "C" ubd_token ubd_sample_greedy(ubd_context *ctx, int32_t i) {
+    if (!ctx) return -1;
+    const int32_t r = resolve_row(ctx, i);
+    if (r < 0) return -1;
+    (void)hipSetDevice(ctx->model->device);
+    const int V = ctx->model->hp.n_vocab;
+    launch_argmax(ctx->logits_dev + (size_t)r * V, V, nullptr, 1, V, ctx->argmax_dev, ctx->stream);
+    int32_t out = -1;
+    if (!hip_ok(hipMemcpyAsync(&out, ctx->argmax_dev, 4, hipMemcpyDeviceToHost, ctx->stream), "argmax") ||
+        !hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync"))
+        return -1;
+    return out;
+}
+
+extern "C" int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32_t cap) {
+    if (!ctx || !out) return -1;
+    const Planner &P = ctx->planner;
+    if (!P.last_ok) return -1;
+    if (P.n_outputs > cap) return -1;
+    if (P.n_outputs == 0) return 0;
+    (void)hipSetDevice(ctx->model->device);
+    const int V = ctx->model->hp.n_vocab;
+    launch_argmax(ctx->logits_dev, V, nullptr, P.n_outputs, V, ctx->argmax_dev, ctx->stream);
+    if (!hip_ok(hipMemcpyAsync(out, ctx->argmax_dev, (size_t)P.n_outputs * 4, hipMemcpyDeviceToHost, ctx->stream),
+                "argmax") ||
+        !hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync"))
+        return -1;
+    return P.n_outputs;
+}
+
+// ------------------------------------------------------------------ memory
+extern "C" ubd_pos ubd_memory_seq_pos_min(ubd_context *ctx, ubd_seq_id s) {
+    return ctx ? ctx->planner.cells.seq_pos_min(s) : -1;
+}
+extern "C" ubd_pos ubd_memory_seq_pos_max(ubd_context *ctx, ubd_seq_id s) {
+    return ctx ? ctx->planner.cells.seq_pos_max(s) : -1;
+}
+extern "C" bool ubd_memory_seq_rm(ubd_context *ctx, ubd_seq_id s, ubd_pos p0, ubd_pos p1) {
+    if (!ctx) return false;
+    (void)hipSetDevice(ctx->model->device);
+    return ctx->planner.seq_rm(s, p0, p1, ctx);
+}
+
+extern "C" int32_t ubd_get_kv_cells(ubd_context *ctx, int32_t *cells_out, int32_t cap) {
+    if (!ctx || !ctx->planner.last_ok) return -1;
+    const auto &c = ctx->planner.cell_of;
+    if ((int32_t)c.size() > cap || !cells_out) return -1;
+    std::copy(c.begin(), c.end(), cells_out);
+    return (int32_t)c.size();
+}
+
+extern "C" int32_t ubd_kv_fill(ubd_context *ctx, ubd_seq_id s, int32_t n_pos, const void *const *k_layers,
+                               const void *const *v_layers, ubd_type src_type, int32_t on_device) {
+    if (!ctx || !k_layers || !v_layers || n_pos <= 0) return UBD_INVALID;
+    if (s < 0 || (uint32_t)s >= ctx->planner.n_seq_max) return UBD_INVALID;
+    if (src_type != UBD_TYPE_F16 && src_type != UBD_TYPE_F32) return UBD_INVALID;
+    (void)hipSetDevice(ctx->model->device);
+    const ubd_hparams &hp = ctx->model->hp;
+    const int hd = ctx->model->head_dim, Hk = hp.n_head_kv;
+    const int st = ctx->planner.cells.stream_of(s);
+    std::vector<int32_t> cells;
+    if (ctx->planner.cells.seq_pos_max(s) >= 0) return UBD_INVALID;
+    if (!ctx->planner.cells.fill_sequence(s, n_pos, &cells)) return UBD_NO_KV_SLOT;
+    const size_t rows_bytes = (size_t)n_pos * Hk * hd * (src_type == UBD_TYPE_F32 ? 4 : 2);
+    int32_t *dcells = nullptr;
+    void *stage = nullptr;
+    bool ok = hip_ok(hipMalloc(&dcells, cells.size() * 4), "kv_fill alloc") &&
+              hip_ok(hipMemcpy(dcells, cells.data(), cells.size() * 4, hipMemcpyHostToDevice), "kv_fill cells");
+    if (ok && !on_device) ok = hip_ok(hipMalloc(&stage, rows_bytes), "kv_fill staging");
+    const int srct = src_type == UBD_TYPE_F32 ? KV_F32 : KV_F16;
+    const size_t kb = ctx->type_k == KV_F32 ? 4 : 2, vb = ctx->type_v == KV_F32 ? 4 : 2;
+    for (int il = 0; ok && il < hp.n_layer; ++il) {
+        for (int which = 0; ok && which < 2; ++which) {
+            const void *src = which == 0 ? k_layers[il] : v_layers[il];
+            if (!src) {
+                ok = false;
+                set_err("kv_fill: missing layer array");
+                break;
+            }
+            if (!on_device) {
+                ok = hip_ok(hipMemcpyAsync(stage, src, rows_bytes, hipMemcpyHostToDevice, ctx->stream), "kv upload");
+                src = stage;
+            }
+            void *cache = which == 0 ? (char *)ctx->k_cache + ctx->kv_layer_elems * il * kb
+                                     : (char *)ctx->v_cache + ctx->kv_layer_elems * il * vb;
+            launch_kv_store(src, srct, n_pos, dcells, cache, which == 0 ? ctx->type_k : ctx->type_v, which == 1, st,
+                            Hk, hd, (int)ctx->planner.n_cells, ctx->stream);
+            ok = ok && hip_ok(hipGetLastError(), "kv_store");
+            if (!on_device) ok = ok && hip_ok(hipStreamSynchronize(ctx->stream), "kv sync");
+        }
+    }
+    ok = ok && hip_ok(hipStreamSynchronize(ctx->stream), "kv sync") && ctx->sync_cell_tables(st);
+    if (dcells) (void)hipFree(dcells);
+    if (stage) (void)hipFree(stage);
+    if (!ok) {
+        ctx->planner.seq_rm(s, -1, -1, ctx);
+        return UBD_INVALID;
+    }
+    return UBD_OK;
+}
+
+extern "C" int32_t ubd_kv_read(ubd_context *ctx, int32_t layer, int32_t stream, int32_t which, int32_t cell0,
+                               int32_t n, float *out) {
+    if (!ctx || !out || n <= 0) return UBD_INVALID;
+    const ubd_hparams &hp = ctx->model->hp;
+    const Planner &P = ctx->planner;
+    if (layer < 0 || layer >= hp.n_layer || stream < 0 || (uint32_t)stream >= P.n_stream || cell0 < 0 ||
+        (uint32_t)(cell0 + n) > P.n_cells || (which != 0 && which != 1))
+        return UBD_INVALID;
+    (void)hipSetDevice(ctx->model->device);
+    const int hd = ctx->model->head_dim, Hk = hp.n_head_kv;
+    const size_t bytes = (size_t)n * Hk * hd * 4;
+    float *tmp = nullptr;
+    if (!hip_ok(hipMalloc(&tmp, bytes), "kv_read alloc")) return UBD_ALLOC_FAILED;
+    const size_t kb = ctx->type_k == KV_F32 ? 4 : 2, vb = ctx->type_v == KV_F32 ? 4 : 2;
+    const void *cache = which == 0 ? (const char *)ctx->k_cache + ctx->kv_layer_elems * layer * kb
+                                   : (const char *)ctx->v_cache + ctx->kv_layer_elems * layer * vb;
+    launch_kv_load(cache, which == 0 ? ctx->type_k : ctx->type_v, which == 1, stream, cell0, n, Hk, hd,
+                   (int)P.n_cells, tmp, ctx->stream);
+    bool ok = hip_ok(hipGetLastError(), "kv_load") && hip_ok(hipStreamSynchronize(ctx->stream), "kv_read sync") &&
+              hip_ok(hipMemcpy(out, tmp, bytes, hipMemcpyDeviceToHost), "kv_read copy");
+    (void)hipFree(tmp);
+    return ok ? UBD_OK : UBD_COMPUTE_FAILED;
+}
+
+// ------------------------------------------------------------- diagnostics
+extern "C" int32_t ubd_debug_keep_residuals(ubd_context *ctx, int32_t enable) {
+    if (!ctx) return UBD_INVALID;
+    if (!enable) {
+        ctx->dump = nullptr;   // the block stays with the context's allocations
+        return UBD_OK;
+    }
+    if (ctx->dump) return UBD_OK;
+    const ubd_hparams &hp = ctx->model->hp;
+    (void)hipSetDevice(ctx->model->device);
+    ctx->dump = (float *)ctx->mem.get((size_t)(hp.n_layer + 1) * ctx->cap * hp.n_embd * 4);
+    return ctx->dump ? UBD_OK : UBD_ALLOC_FAILED;
+}
+
+extern "C" int32_t ubd_debug_get_residual(ubd_context *ctx, int32_t layer, float *out, int32_t cap_tokens) {
+    if (!ctx || !ctx->dump || !out) return -1;
+    const ubd_hparams &hp = ctx->model->hp;
+    if (layer < 0 || layer > hp.n_layer) return -1;
+    const int32_t T = (int32_t)ctx->last_ub_idx.size();
+    if (T > cap_tokens) return -1;
+    if (ubd_synchronize(ctx) != UBD_OK) return -1;
+    if (!hip_ok(hipMemcpy(out, ctx->dump + (size_t)layer * ctx->cap * hp.n_embd, (size_t)T * hp.n_embd * 4,
+                          hipMemcpyDeviceToHost), "residual copy"))
+        return -1;
+    return T;
+}
+
+extern "C" int32_t ubd_debug_last_ubatch(ubd_context *ctx, int32_t *batch_idx, int32_t cap) {
+    if (!ctx || !batch_idx) return -1;
+    const int32_t T = (int32_t)ctx->last_ub_idx.size();
+    if (T > cap) return -1;
+    std::copy(ctx->last_ub_idx.begin(), ctx->last_ub_idx.end(), batch_idx);
+    return T;
+}
+
+extern "C" void ubd_perf_get(const ubd_context *ctx, ubd_perf *out) {
+    if (!ctx || !out) return;
+    *out = ctx->perf;
+    out->t_load_ms = ctx->model->t_load_ms;
+}
+
+extern "C" void ubd_perf_reset(ubd_context *ctx) {
+    if (ctx) ctx->perf = ubd_perf{};
+}
+
+extern "C" void ubd_log_set(ubd_log_fn fn, void *user_data) {
+    g_log = fn;
+    g_log_ud = user_data;
+}
+
+extern "C" const char *ubd_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------- batch
+extern "C" ubd_batch ubd_batch_init(int32_t n_tokens_alloc, int32_t embd, int32_t n_seq_max) {
+    ubd_batch b{};
+    if (n_tokens_alloc <= 0 || embd != 0 || n_seq_max <= 0) return b;
+    const size_t n = (size_t)n_tokens_alloc;
+    b.token = (ubd_token *)calloc(n, sizeof(ubd_token));
+    b.pos = (ubd_pos *)calloc(n, sizeof(ubd_pos));
+    b.n_seq_id = (int32_t *)calloc(n, sizeof(int32_t));
+    b.seq_id = (ubd_seq_id **)calloc(n + 1, sizeof(ubd_seq_id *));
+    b.logits = (int8_t *)calloc(n, 1);
+    for (size_t i = 0; i < n; ++i) b.seq_id[i] = (ubd_seq_id *)calloc((size_t)n_seq_max, sizeof(ubd_seq_id));
+    return b;
+}
+
+extern "C" void ubd_batch_free(ubd_batch b) {
+    if (b.seq_id) {
+        for (size_t i = 0; b.seq_id[i]; ++i) free(b.seq_id[i]);
+        free(b.seq_id);
+    }
+    free(b.token);
+    free(b.pos);
+    free(b.n_seq_id);
+    free(b.logits);
+}
+
+extern "C" ubd_batch ubd_batch_get_one(ubd_token *tokens, int32_t n_tokens) {
+    ubd_batch b{};
+    b.n_tokens = n_tokens;
+    b.token = tokens;
+    return b;
+}
+
+// ------------------------------------------------------- host-only planner
+struct ubd_planner {
+    Planner p;
+};
+
+namespace {
+struct StubExecutor : Executor {
+    int32_t fail_at = -1, fail_code = UBD_OK;
+    int32_t run_ubatch(const UBatch &, int32_t k) override { return k == fail_at ? fail_code : UBD_OK; }
+};
+}  // namespace
+
+extern "C" ubd_planner *ubd_planner_new(uint32_t n_ctx, uint32_t n_batch, uint32_t n_ubatch, uint32_t n_seq_max,
+                                        bool kv_unified, int32_t n_vocab) {
+    ubd_planner *pl = new ubd_planner();
+    std::string err;
+    if (pl->p.init(n_ctx, n_batch, n_ubatch, n_seq_max, kv_unified, n_vocab, &err) != UBD_OK) {
+        set_err(err);
+        delete pl;
+        return nullptr;
+    }
+    return pl;
+}
+
+extern "C" void ubd_planner_free(ubd_planner *p) { delete p; }
+
+extern "C" int32_t ubd_planner_decode(ubd_planner *p, ubd_batch batch, int32_t fail_at, int32_t fail_code) {
+    if (!p) return UBD_INVALID;
+    StubExecutor ex;
+    ex.fail_at = fail_at;
+    ex.fail_code = fail_code;
+    std::string err;
+    return p->p.decode(batch, &ex, &err);
+}
+
+extern "C" int32_t ubd_planner_n_ubatches(const ubd_planner *p) { return p ? (int32_t)p->p.ubatches.size() : -1; }
+
+extern "C" int32_t ubd_planner_ubatch(const ubd_planner *p, int32_t k, int32_t *batch_idx, int32_t *cells,
+                                      int32_t *streams, int32_t cap) {
+    if (!p || k < 0 || k >= (int32_t)p->p.ubatches.size()) return -1;
+    const UBatch &ub = p->p.ubatches[k];
+    if (ub.size() > cap) return -1;
+    for (int32_t t = 0; t < ub.size(); ++t) {
+        if (batch_idx) batch_idx[t] = ub.idx[t];
+        if (cells) cells[t] = ub.cell[t];
+        if (streams) streams[t] = ub.stream[t];
+    }
+    return ub.size();
+}
+
+extern "C" int32_t ubd_planner_output_row(const ubd_planner *p, int32_t i) {
+    if (!p || i < 0 || i >= (int32_t)p->p.out_row.size()) return -1;
+    return p->p.out_row[i];
+}
+
+extern "C" int32_t ubd_planner_n_outputs(const ubd_planner *p) { return p && p->p.last_ok ? p->p.n_outputs : 0; }
+
+extern "C" ubd_pos ubd_planner_seq_pos_min(const ubd_planner *p, ubd_seq_id s) {
+    return p ? p->p.cells.seq_pos_min(s) : -1;
+}
+extern "C" ubd_pos ubd_planner_seq_pos_max(const ubd_planner *p, ubd_seq_id s) {
+    return p ? p->p.cells.seq_pos_max(s) : -1;
+}
+extern "C" bool ubd_planner_seq_rm(ubd_planner *p, ubd_seq_id s, ubd_pos p0, ubd_pos p1) {
+    return p ? p->p.seq_rm(s, p0, p1, nullptr) : false;
+}
+extern "C" int32_t ubd_planner_n_kv(const ubd_planner *p, int32_t stream) {
+    if (!p || stream < 0 || (uint32_t)stream >= p->p.n_stream) return -1;
+    return p->p.cells.n_kv(stream);
+}

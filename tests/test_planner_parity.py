@@ -1,0 +1,130 @@
+"""The C++ host planner (libubd's ubd_planner_* entry points, the code
+ubd_decode runs) against the oracle's planner: identical ubatch splits, KV
+cells, output rows, positions and return codes, bit for bit (CPU only)."""
+import numpy as np
+import pytest
+
+from llama_decode_ubatch_amd import Planner
+from oracle.planner import Batch, KVMemory, plan_batch, rollback_ubatch, context_geometry
+
+
+class OraclePlanner:
+    def __init__(self, n_ctx, n_batch, n_ubatch, n_seq_max, unified, n_vocab):
+        self.n_ctx, self.n_stream, self.n_cells = context_geometry(n_ctx, n_seq_max, unified)
+        self.n_batch = min(self.n_ctx, n_batch)
+        self.n_ubatch = min(self.n_batch, n_ubatch)
+        self.n_seq_max, self.n_vocab = n_seq_max, n_vocab
+        self.mem = KVMemory(self.n_stream, self.n_cells, unified)
+        self.plan = None
+
+    def decode(self, batch, fail_at=-1, fail_code=0):
+        p = plan_batch(batch, self.mem, self.n_vocab, self.n_seq_max, self.n_batch, self.n_ubatch)
+        self.plan = p
+        if p.rc != 0:
+            return p.rc
+        for k, (ub, c) in enumerate(zip(p.ubatches, p.cells)):
+            self.mem.apply(ub, c)
+            if k == fail_at:
+                rollback_ubatch(self.mem, ub)
+                return fail_code
+        return 0
+
+
+def both(**kw):
+    args = (kw["n_ctx"], kw["n_batch"], kw["n_ubatch"], kw["n_seq_max"], kw["unified"], kw["n_vocab"])
+    return Planner(*args), OraclePlanner(*args)
+
+
+def check_same(cp, op, n_seq_max, rc_c, rc_o):
+    assert rc_c == rc_o
+    if rc_o == 0:
+        ubs = cp.ubatches()
+        assert len(ubs) == len(op.plan.ubatches)
+        for (idx, cells, st), ub, c in zip(ubs, op.plan.ubatches, op.plan.cells):
+            assert idx.tolist() == ub.idx.tolist()
+            assert cells.tolist() == c.tolist()
+            assert st.tolist() == [op.mem.stream_of(int(s)) for s in ub.seq]
+        assert cp.n_outputs() == op.plan.n_outputs
+        for i in range(op.plan.out_row.size):
+            assert cp.output_row(i) == op.plan.out_row[i]
+    for s in range(n_seq_max):
+        assert cp.seq_pos_max(s) == op.mem.seq_pos_max(s)
+        assert cp.seq_pos_min(s) == op.mem.seq_pos_min(s)
+    for st in range(op.n_stream):
+        assert cp.n_kv(st) == op.mem.n_kv(st)
+
+
+def test_config2_prefill_and_decode():
+    cp, op = both(n_ctx=2048, n_batch=1024, n_ubatch=128, n_seq_max=8, unified=False, n_vocab=151936)
+    seq = np.repeat(np.arange(8), 128)
+    toks = np.arange(1024) % 1000
+    logits = np.zeros(1024, np.int8)
+    logits[127::128] = 1
+    check_same(cp, op, 8, cp.decode(toks, seq_id=seq, logits=logits),
+               op.decode(Batch(toks, seq_id=seq, logits=logits)))
+    assert len(cp.ubatches()) == 8
+    for step in range(3):
+        t = np.arange(8) + step
+        check_same(cp, op, 8, cp.decode(t, seq_id=np.arange(8), logits=np.ones(8)),
+                   op.decode(Batch(t, seq_id=np.arange(8), logits=np.ones(8))))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_scenarios(seed):
+    rng = np.random.default_rng(seed)
+    n_seq = int(rng.integers(1, 5))
+    unified = bool(rng.integers(0, 2))
+    n_ctx = int(rng.choice([256, 512]))
+    n_ubatch = int(rng.choice([1, 3, 7, 16, 64]))
+    cfg = dict(n_ctx=n_ctx, n_batch=96, n_ubatch=n_ubatch, n_seq_max=n_seq, unified=unified, n_vocab=500)
+    cp, op = both(**cfg)
+    for it in range(25):
+        r = rng.random()
+        if r < 0.12:
+            s = int(rng.integers(-1, n_seq))
+            p0 = int(rng.integers(-1, 40))
+            p1 = int(rng.integers(-1, 80))
+            assert cp.seq_rm(s, p0, p1) == op.mem.seq_rm(s, p0, p1)
+            for st in range(op.n_stream):
+                assert cp.n_kv(st) == op.mem.n_kv(st)
+            continue
+        n = int(rng.integers(1, 110))          # sometimes > n_batch -> -1
+        toks = rng.integers(-2 if rng.random() < 0.05 else 0, 500, n)
+        seq = rng.integers(0, n_seq + (1 if rng.random() < 0.05 else 0), n)
+        kw = {"seq_id": seq}
+        if rng.random() < 0.5:
+            kw["logits"] = rng.integers(0, 2, n)
+        fail_at, code = -1, 0
+        if rng.random() < 0.2:
+            fail_at, code = int(rng.integers(0, 4)), int(rng.choice([2, -3]))
+        rc_c = cp.decode(toks, fail_at=fail_at, fail_code=code, **kw)
+        rc_o = op.decode(Batch(toks, **kw), fail_at=fail_at, fail_code=code)
+        if fail_at >= 0 and rc_o == code:
+            assert rc_c == rc_o
+        else:
+            check_same(cp, op, n_seq, rc_c, rc_o)
+        for s in range(n_seq):
+            assert cp.seq_pos_max(s) == op.mem.seq_pos_max(s)
+
+
+def test_explicit_positions_and_errors():
+    cp, op = both(n_ctx=256, n_batch=64, n_ubatch=16, n_seq_max=2, unified=True, n_vocab=50)
+    cases = [
+        dict(tokens=[1, 2, 3], pos=[5, 6, 7], seq_id=[1, 1, 1]),
+        dict(tokens=[1, 2], pos=[8, 9], seq_id=[1, 1]),
+        dict(tokens=[1], pos=[11], seq_id=[1]),          # gap -> -1
+        dict(tokens=[4, 5], seq_id=[0, 1]),
+        dict(tokens=[60], seq_id=[0]),                   # bad token -> -1
+        dict(tokens=[1], seq_id=[2]),                    # bad seq -> -1
+    ]
+    for c in cases:
+        t = c.pop("tokens")
+        check_same(cp, op, 2, cp.decode(t, **c), op.decode(Batch(t, **c)))
+
+
+def test_no_slot_returns_1_and_keeps_state():
+    cp, op = both(n_ctx=256, n_batch=256, n_ubatch=64, n_seq_max=1, unified=False, n_vocab=50)
+    check_same(cp, op, 1, cp.decode(np.ones(200)), op.decode(Batch(np.ones(200, int))))
+    check_same(cp, op, 1, cp.decode(np.ones(57)), op.decode(Batch(np.ones(57, int))))
+    assert cp.seq_pos_max(0) == 199
+    check_same(cp, op, 1, cp.decode(np.ones(56)), op.decode(Batch(np.ones(56, int))))
