@@ -1,0 +1,236 @@
+"""Throughput of the decode step on one MI355X.
+
+Default workload: the 8B-shaped bf16 model, batch 1, a 512-token prompt
+prefilled as one ubatch, then 128 greedy decode steps (f16 KV cache, n_ctx
+4096).  One timed "step" is that whole job: clear the cache, prefill,
+decode 128 tokens with on-device greedy picks.  Weights, prompt and KV cache
+live in HBM before timing starts.
+
+Prints one JSON line on stdout: whole-job tokens/s plus prefill / decode
+rates, the roofline of the dominant decode kernel (bf16 gate|up matvec)
+timed with HIP events inside the library, the prefill GEMM's MFMA
+fraction, and the CPU oracle timed on a bounded sample of the same job.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_job(ctx, w, prompt, first_tokens=None):
+    """One pass of the workload.  Returns (t_prefill_s, t_decode_s, ids)."""
+    import numpy as np
+    ctx.seq_rm(-1, -1, -1)
+    ids = []
+    t0 = time.perf_counter()
+    if w.n_prompt:
+        assert ctx.decode(prompt) == 0
+        tok = ctx.greedy(-1)            # synchronises
+    else:
+        tok = first_tokens
+    t1 = time.perf_counter()
+    ids.append(tok)
+    for _ in range(w.n_decode):
+        if w.n_seqs == 1:
+            assert ctx.decode([tok]) == 0
+            tok = ctx.greedy(-1)
+        else:
+            assert ctx.decode(tok, seq_id=np.arange(w.n_seqs), logits=np.ones(w.n_seqs)) == 0
+            tok = ctx.greedy_all()
+        ids.append(tok)
+    t2 = time.perf_counter()
+    return t1 - t0, t2 - t1, ids
+
+
+def cpu_baseline(w, sample_layers=2, n_prefill=32, n_decode=2):
+    """The oracle as it stands on a bounded sample of the same job: a
+    `sample_layers`-layer model of the same shape (its own seeded weights),
+    prefill of n_prefill tokens and n_decode single-token decodes; layer
+    time is scaled to the full depth and the output head added once."""
+    import dataclasses
+    import numpy as np
+    from oracle import OracleModel, OracleContext, Batch
+    from workloads import gen_tensor, gen_tensor_rows, prompt_tokens
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count()
+    shape = dataclasses.replace(w.model, n_layer=sample_layers)
+    om = OracleModel(shape, lambda name: gen_tensor(shape, name), dtype=np.float32, cache=True,
+                     rows_fn=lambda name, rows: gen_tensor_rows(shape, name, rows))
+    ctx = OracleContext(om, w.n_ctx, w.n_batch, w.n_ubatch, 1, w.type_k, w.type_v)
+    # generate and upcast every weight before timing
+    for il in range(sample_layers):
+        for t in ("attn_norm", "attn_q", "attn_k", "attn_v", "attn_output", "ffn_norm",
+                  "ffn_gate", "ffn_up", "ffn_down"):
+            om.w(f"blk.{il}.{t}.weight")
+    om.w("output_norm.weight")
+    om.w("output.weight")
+    prompt = prompt_tokens(w, 0)[:n_prefill]
+    h = np.zeros((1, shape.n_embd), np.float32)
+    t0 = time.perf_counter()
+    ctx.head(h)
+    t_head = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    assert ctx.decode(Batch(prompt)) == 0
+    t_pp = time.perf_counter() - t0
+    tok = ctx.greedy(-1)
+    t0 = time.perf_counter()
+    for _ in range(n_decode):
+        assert ctx.decode(Batch([tok])) == 0
+        tok = ctx.greedy(-1)
+    t_tg = (time.perf_counter() - t0) / n_decode
+    L = w.model.n_layer
+    pp_full = (t_pp - t_head) * L / sample_layers + t_head
+    tg_full = (t_tg - t_head) * L / sample_layers + t_head
+    job_s = pp_full * w.n_prompt / n_prefill + tg_full * w.n_decode
+    return {
+        "value": (w.n_prompt + w.n_decode) / job_s,
+        "unit": "tokens/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "prefill_tok_s": n_prefill / pp_full,
+        "decode_tok_s": 1.0 / tg_full,
+        "sample": (f"oracle (NumPy float32) on a {sample_layers}-layer model of the same shape: "
+                   f"{n_prefill}-token prefill + {n_decode} decodes, layer time x{L}/{sample_layers} "
+                   f"plus the output head, job = {w.n_prompt}-token prefill + {w.n_decode} decodes"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from llama_decode_ubatch_amd import Model, Context
+    from workloads import WORKLOADS, prompt_tokens
+    from workloads import device as wdev
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.config]
+    shape = w.model
+    t0 = time.perf_counter()
+    if shape.wtype == "f32":
+        from workloads import gen_tensor, tensor_specs
+        tens = {s.name: gen_tensor(shape, s) for s in tensor_specs(shape)}
+    else:
+        tens = wdev.model_tensors(torch, shape, "cuda:0")
+        torch.cuda.synchronize()
+    model = Model(shape, tens, device=0)
+    del tens
+    torch.cuda.empty_cache()
+    log(f"model {shape.tag}: {model.size() / 2**30:.2f} GiB on device, built in {time.perf_counter() - t0:.1f}s")
+    ctx = Context(model, n_ctx=w.n_ctx, n_batch=w.n_batch, n_ubatch=w.n_ubatch, n_seq_max=w.n_seq_max,
+                  type_k=w.type_k, type_v=w.type_v, kv_unified=w.kv_unified)
+    prompt = prompt_tokens(w, 0) if w.n_prompt else None
+
+    for i in range(args.warmup):
+        tp, td, _ = run_job(ctx, w, prompt)
+        log(f"warmup {i}: prefill {tp * 1e3:.1f} ms, decode {td * 1e3:.1f} ms")
+
+    ctx.kernel_timing(None)
+    ctx.kernel_stats()                   # reset
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    tp_sum = td_sum = 0.0
+    for i in range(args.steps):
+        tp, td, ids = run_job(ctx, w, prompt)
+        tp_sum += tp
+        td_sum += td
+        log(f"step {i}: prefill {tp * 1e3:.1f} ms, decode {td * 1e3:.1f} ms")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    stats = ctx.kernel_stats()
+    ctx.kernel_timing([])
+
+    n_tok = (w.n_prompt + w.n_decode * w.n_seqs) * args.steps
+    value = n_tok / elapsed
+    prefill_tps = w.n_prompt * args.steps / tp_sum if w.n_prompt else None
+    decode_tps = w.n_decode * w.n_seqs * args.steps / td_sum
+
+    d, F, V = shape.n_embd, shape.n_ff, shape.n_vocab
+    wbytes = {"f32": 4, "bf16": 2, "q8_0": 34 / 32}[shape.wtype]
+    kernels = {k: {"launches": n, "avg_us": 1e3 * ms / n} for k, (n, ms) in stats.items()}
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["launches"]):
+        log(f"  {k:22s} {v['launches']:6d} launches  avg {v['avg_us']:9.2f} us  "
+            f"total {v['avg_us'] * v['launches'] / 1e3:9.2f} ms")
+    roofline = None
+    if "decode.ffn_gate_up" in kernels:
+        T = w.n_seqs
+        alg = 2 * F * d * wbytes + T * d * 4 + T * F * 4     # weights + input + output
+        avg_s = kernels["decode.ffn_gate_up"]["avg_us"] * 1e-6
+        ach = alg / avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "decode.ffn_gate_up (linear_small_kernel, SwiGLU epilogue)",
+                    "bytes_per_launch": int(alg)}
+    roofline_prefill = None
+    if "prefill.ffn_gate_up" in kernels and w.n_prompt:
+        flops = 2.0 * w.n_prompt * 2 * F * d
+        avg_s = kernels["prefill.ffn_gate_up"]["avg_us"] * 1e-6
+        ach = flops / avg_s / 1e12
+        roofline_prefill = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                            "kernel": "prefill.ffn_gate_up (gemm_kernel, SwiGLU epilogue)",
+                            "flops_per_launch": flops}
+
+    cpu = None
+    if not args.no_cpu_baseline and shape.wtype != "f32":
+        try:
+            cpu = cpu_baseline(w)
+            log(f"cpu baseline: {cpu}")
+        except Exception as e:  # report, do not fail the GPU measurement
+            log(f"cpu baseline failed: {e!r}")
+
+    out = {
+        "metric": "decode & prefill tokens/s, 8B-shape bf16, 1 MI355X; % of HBM / MFMA roofline",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.wtype,
+        "data": "synthetic (seeded counter-based generator; random weights, uniform token ids)",
+        "config": {"workload": w.name, "n_prompt": w.n_prompt, "n_decode": w.n_decode,
+                   "n_seqs": w.n_seqs, "n_ctx": w.n_ctx, "n_ubatch": w.n_ubatch,
+                   "kv_type": w.type_k, "parallelism": "single-gpu"},
+        "prefill_tok_s": None if prefill_tps is None else round(prefill_tps, 1),
+        "decode_tok_s": round(decode_tps, 2),
+        "roofline": roofline,
+        "roofline_prefill": roofline_prefill,
+        "cpu_baseline": cpu,
+        "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2)} for k, v in kernels.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -279,6 +279,21 @@ int32_t ubd_debug_get_residual(ubd_context *ctx, int32_t layer, float *out,
 int32_t ubd_debug_last_ubatch(ubd_context *ctx, int32_t *batch_idx,
                               int32_t cap);
 
+/* Kernel timing with HIP events on the context's stream.  Kernels fall in
+ * classes 2*kind + phase, phase 0 for ubatches of <= 16 tokens (decode) and
+ * 1 for larger ones (prefill), kind 0 embed, 1 rmsnorm, 2 qkv (+RoPE and
+ * K/V append), 3 attention (partial + combine), 4 attn_output (+residual),
+ * 5 ffn_gate_up (+SwiGLU), 6 ffn_down (+residual), 7 logits.  mask selects
+ * the timed classes (bit = class); 0 turns timing off.  0 or -1. */
+#define UBD_KERNEL_CLASSES 16
+int32_t ubd_debug_kernel_timing(ubd_context *ctx, uint32_t mask);
+/* Name of a class, e.g. "decode.ffn_gate_up"; "" for an invalid class. */
+const char *ubd_debug_kernel_class_name(int32_t cls);
+/* Synchronises, then writes the launches and summed milliseconds of the
+ * first n classes since the last call and resets them.  n or -1. */
+int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
+                               double *total_ms, int32_t n);
+
 /* Counters in the spirit of llama_perf_context_print ([ARCH] Example 15). */
 typedef struct ubd_perf {
     double t_load_ms;       /* ubd_model_load wall time                    */

@@ -99,6 +99,9 @@ SIGNATURES = {
     "ubd_debug_keep_residuals": (C.c_int32, [_P, C.c_int32]),
     "ubd_debug_get_residual": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_float), C.c_int32]),
     "ubd_debug_last_ubatch": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_debug_kernel_timing": (C.c_int32, [_P, C.c_uint32]),
+    "ubd_debug_kernel_class_name": (C.c_char_p, [C.c_int32]),
+    "ubd_debug_kernel_stats": (C.c_int32, [_P, C.POINTER(C.c_int32), C.POINTER(C.c_double), C.c_int32]),
     "ubd_perf_get": (None, [_P, C.POINTER(Perf)]),
     "ubd_perf_reset": (None, [_P]),
     "ubd_log_set": (None, [LOG_FN, C.c_void_p]),
@@ -376,6 +379,30 @@ class Context:
         out = np.zeros(max_tokens, np.int32)
         r = self.lib.ubd_debug_last_ubatch(self.ptr, out.ctypes.data_as(C.POINTER(C.c_int32)), max_tokens)
         return out[:r]
+
+    N_KERNEL_CLASSES = 16
+
+    def kernel_timing(self, classes=None):
+        """Time the named kernel classes (None: all, []: off)."""
+        if classes is None:
+            mask = (1 << self.N_KERNEL_CLASSES) - 1
+        else:
+            names = [self.lib.ubd_debug_kernel_class_name(i).decode() for i in range(self.N_KERNEL_CLASSES)]
+            mask = 0
+            for c in classes:
+                mask |= 1 << names.index(c)
+        return self.lib.ubd_debug_kernel_timing(self.ptr, mask)
+
+    def kernel_stats(self):
+        n = self.N_KERNEL_CLASSES
+        la = (C.c_int32 * n)()
+        ms = (C.c_double * n)()
+        self.lib.ubd_debug_kernel_stats(self.ptr, la, ms, n)
+        out = {}
+        for i in range(n):
+            if la[i]:
+                out[self.lib.ubd_debug_kernel_class_name(i).decode()] = (la[i], ms[i])
+        return out
 
     def perf(self):
         p = Perf()

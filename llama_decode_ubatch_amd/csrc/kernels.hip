@@ -160,6 +160,77 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
 
 __device__ __forceinline__ void store4(float *p, f32x4_t v) { *(f32x4_t *)p = v; }
 
+// Epilogue of one MFMA output fragment: token t and four consecutive output
+// rows n..n+3 (for SWIGLU: gate values v, up values u, output columns
+// n..n+3).  ATOMIC accumulates a split-K partial into the residual.
+template <int EPI, bool ATOMIC>
+__device__ __forceinline__ void epilogue4(const LinearArgs &a, int t, int n, f32x4_t v, f32x4_t u) {
+    if (EPI == EPI_STORE || EPI == EPI_RESID) {
+        float *p = a.y + (size_t)t * a.ldy + n;
+        if (EPI == EPI_RESID && ATOMIC) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) atomicAdd(p + i, v[i]);
+        } else if (EPI == EPI_RESID) {
+            f32x4_t o = *(f32x4_t *)p;
+            store4(p, o + v);
+        } else {
+            store4(p, v);
+        }
+    } else if (EPI == EPI_LOGITS) {
+        const int row = a.row_map[t];
+        store4(a.logits + (size_t)row * a.N + n, v);
+    } else if (EPI == EPI_SWIGLU) {
+        const size_t o = (size_t)t * a.out.ld + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float gt = v[i], up = u[i];
+            store_act(a.out, o + i, gt / (1.0f + expf(-gt)) * up);
+        }
+    } else if (EPI == EPI_QKV) {
+        const QKVEpi &q = a.qkv;
+        const int hd = q.head_dim;
+        if (n < q.n_q_rows + q.n_k_rows) {
+            const int pos = a.tok.pos[t];
+            const int base = n < q.n_q_rows ? 0 : q.n_q_rows;
+            const int d = (n - base) % hd;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const double ang = (double)pos * q.inv_freq[(d >> 1) + pr];
+                double sn, cs;
+                sincos(ang, &sn, &cs);
+                const float c = (float)cs, sf = (float)sn;
+                const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
+                v[2 * pr] = x0 * c - x1 * sf;
+                v[2 * pr + 1] = x0 * sf + x1 * c;
+            }
+        }
+        if (n < q.n_q_rows) {
+            store4(q.q_out + (size_t)t * q.n_q_rows + n, v);
+        } else if (n < q.n_q_rows + q.n_k_rows) {
+            const int o = n - q.n_q_rows, head = o / hd, d = o % hd;
+            const size_t idx = (((size_t)a.tok.stream[t] * q.n_head_kv + head) * q.n_cells + a.tok.cell[t]) * hd + d;
+            if (q.type_k == KV_F32) {
+                store4((float *)q.k_cache + idx, v);
+            } else {
+                u16x4_t h = {f2h(v[0]), f2h(v[1]), f2h(v[2]), f2h(v[3])};
+                *(u16x4_t *)((uint16_t *)q.k_cache + idx) = h;
+            }
+        } else {
+            const int o = n - q.n_q_rows - q.n_k_rows, head = o / hd, d = o % hd;
+            const size_t base = ((size_t)a.tok.stream[t] * q.n_head_kv + head) * hd + d;
+            const int cell = a.tok.cell[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const size_t idx = (base + i) * q.n_cells + cell;
+                if (q.type_v == KV_F32)
+                    ((float *)q.v_cache)[idx] = v[i];
+                else
+                    ((uint16_t *)q.v_cache)[idx] = f2h(v[i]);
+            }
+        }
+    }
+}
+
 template <int WT, int EPI, int NW>
 __global__ __launch_bounds__(64 * NW) void linear_small_kernel(LinearArgs a) {
     constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
@@ -206,78 +277,219 @@ __global__ __launch_bounds__(64 * NW) void linear_small_kernel(LinearArgs a) {
             for (int j = 0; j < RB; ++j) acc[j] += red[w][j][lane];
     }
     if (!tok_ok) return;
-
     const int t = t0 + r;
-    if (EPI == EPI_STORE || EPI == EPI_RESID) {
-        const int n = rb0 * 16 + 4 * g;
-        float *p = a.y + (size_t)t * a.ldy + n;
-        if (EPI == EPI_RESID) {
-            f32x4_t o = *(f32x4_t *)p;
-            store4(p, o + acc[0]);
-        } else {
-            store4(p, acc[0]);
+    if (EPI == EPI_SWIGLU)
+        epilogue4<EPI, false>(a, t, blockIdx.x * 16 + 4 * g, acc[0], acc[RB - 1]);
+    else
+        epilogue4<EPI, false>(a, t, rb0 * 16 + 4 * g, acc[0], acc[0]);
+}
+
+// ----------------------------------------------------------------- GEMM
+// Product for bf16 / q8_0 weights and many tokens (prefill).  Work-group
+// tile: 256 weight rows (4 waves x 4 row blocks of 16) x BT tokens; k
+// advances 64 values per stage.  A (weights) is read straight from HBM in
+// fragment order; B (the hi plane of the activations) goes through LDS in
+// fragment order, with the next stage prefetched into registers.  Tiles are
+// numbered so that the work-groups sharing a weight tile (all token tiles
+// and k-splits) run on the same XCD and reuse it from that XCD's L2.
+__device__ __forceinline__ bf16x8_t i8x8_scaled_bf16(uint32_t w0, uint32_t w1, float sc) {
+    u16x8_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = f2bf((float)(int8_t)(w0 >> (8 * i)) * sc);
+        r[4 + i] = f2bf((float)(int8_t)(w1 >> (8 * i)) * sc);
+    }
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+template <int WT, int EPI, int BT, int SPLITK>
+__global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, int n_ttiles) {
+    // q8_0: the codes enter the MFMA exactly (|code| <= 127 is exact in
+    // bf16), the activations as hi + lo planes, and each 32-value block's
+    // f16 scale multiplies that block's MFMA result, so only the f32
+    // accumulation rounds.  bf16 weights use the hi plane only.
+    constexpr bool Q8 = WT == W_Q8;
+    constexpr int TB = BT / 16;
+    constexpr int XCH = BT * 8 / 256;       // 16-byte activation chunks per thread per stage
+    constexpr int XS = TB * 2 * 64;         // one plane: [token block][k half][lane]
+    __shared__ u32x4_t xs[(Q8 ? 2 : 1) * XS];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int total = n_wtiles * n_ttiles * SPLITK;
+    const int b = blockIdx.x;
+    const int tile = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
+    const int ks = tile % SPLITK;
+    const int tt = (tile / SPLITK) % n_ttiles;
+    const int nt = tile / (SPLITK * n_ttiles);
+    const int nrb = a.N / 16;
+    const int rb0 = nt * 16 + wave * 4;
+    const int t0 = tt * BT;
+    const int nstage = a.K / 64;
+    const int st0 = ks * nstage / SPLITK, st1 = (ks + 1) * nstage / SPLITK;
+    const int steps = a.K / (WT == W_BF16 ? 32 : 64);
+    const int KB = a.K / 32;
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+
+    f32x4_t acc[4][TB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t xr[XCH], xrl[Q8 ? XCH : 1];
+    u32x4_t wr[4][2];
+    u32x2_t sc[4][2];
+
+    auto load_stage = [&](int st) {
+#pragma unroll
+        for (int q = 0; q < XCH; ++q) {
+            const int c = threadIdx.x + 256 * q;
+            const int row = c >> 3, ch = c & 7;
+            const int t = t0 + row;
+            const size_t o = (size_t)t * a.x.ld + st * 64 + ch * 8;
+            xr[q] = t < a.T ? *(const u32x4_t *)(a.x.hi + o) : z4;
+            if (Q8) xrl[q] = t < a.T ? *(const u32x4_t *)(a.x.lo + o) : z4;
         }
-    } else if (EPI == EPI_LOGITS) {
-        const int row = a.row_map[t];
-        store4(a.logits + (size_t)row * a.N + rb0 * 16 + 4 * g, acc[0]);
-    } else if (EPI == EPI_SWIGLU) {
-        const int col = blockIdx.x * 16 + 4 * g;
-        const size_t o = (size_t)t * a.out.ld + col;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float gt = acc[0][i], up = acc[1][i];
-            store_act(a.out, o + i, gt / (1.0f + expf(-gt)) * up);
-        }
-    } else if (EPI == EPI_QKV) {
-        const QKVEpi &q = a.qkv;
-        const int n = rb0 * 16 + 4 * g;
-        const int hd = q.head_dim;
-        const int pos = a.tok.pos[t];
-        f32x4_t v = acc[0];
-        if (n < q.n_q_rows + q.n_k_rows) {
-            const int base = n < q.n_q_rows ? 0 : q.n_q_rows;
-            const int d = (n - base) % hd;
+            const int rb = rb0 + i;
+            if (rb < nrb) {
+                if (!Q8) {
 #pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const double ang = (double)pos * q.inv_freq[(d >> 1) + pr];
-                double sn, cs;
-                sincos(ang, &sn, &cs);
-                const float c = (float)cs, sf = (float)sn;
-                const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
-                v[2 * pr] = x0 * c - x1 * sf;
-                v[2 * pr + 1] = x0 * sf + x1 * c;
-            }
-        }
-        if (n < q.n_q_rows) {
-            store4(q.q_out + (size_t)t * q.n_q_rows + n, v);
-        } else if (n < q.n_q_rows + q.n_k_rows) {
-            const int o = n - q.n_q_rows, head = o / hd, d = o % hd;
-            const size_t idx = (((size_t)a.tok.stream[t] * q.n_head_kv + head) * q.n_cells + a.tok.cell[t]) * hd + d;
-            if (q.type_k == KV_F32) {
-                store4((float *)q.k_cache + idx, v);
+                    for (int j = 0; j < 2; ++j)
+                        wr[i][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
+                                                           ((size_t)rb * steps + 2 * st + j) * 1024 + lane * 16));
+                } else {
+                    wr[i][0] = ldg_nt((const u32x4_t *)((const char *)a.w + ((size_t)rb * steps + st) * 1024 +
+                                                       lane * 16));
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        sc[i][j] = *(const u32x2_t *)(a.wscale + ((size_t)rb * KB + 2 * st + j) * 16 + 4 * g);
+                }
             } else {
-                u16x4_t h = {f2h(v[0]), f2h(v[1]), f2h(v[2]), f2h(v[3])};
-                *(u16x4_t *)((uint16_t *)q.k_cache + idx) = h;
-            }
-        } else {
-            const int o = n - q.n_q_rows - q.n_k_rows, head = o / hd, d = o % hd;
-            const size_t base = ((size_t)a.tok.stream[t] * q.n_head_kv + head) * hd + d;
-            const int cell = a.tok.cell[t];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t idx = (base + i) * q.n_cells + cell;
-                if (q.type_v == KV_F32)
-                    ((float *)q.v_cache)[idx] = v[i];
-                else
-                    ((uint16_t *)q.v_cache)[idx] = f2h(v[i]);
+                wr[i][0] = wr[i][1] = z4;
+                sc[i][0] = sc[i][1] = u32x2_t{0u, 0u};
             }
         }
+    };
+
+    if (st0 < st1) load_stage(st0);
+    for (int st = st0; st < st1; ++st) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < XCH; ++q) {
+            const int c = threadIdx.x + 256 * q;
+            const int row = c >> 3, ch = c & 7;
+            const int idx = ((row >> 4) * 2 + (ch >> 2)) * 64 + (ch & 3) * 16 + (row & 15);
+            xs[idx] = xr[q];
+            if (Q8) xs[XS + idx] = xrl[q];
+        }
+        __syncthreads();
+        bf16x8_t A[4][2];
+        f32x4_t S[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!Q8) {
+                A[i][0] = __builtin_bit_cast(bf16x8_t, wr[i][0]);
+                A[i][1] = __builtin_bit_cast(bf16x8_t, wr[i][1]);
+            } else {
+                A[i][0] = i8x8_to_bf16(wr[i][0][0], wr[i][0][1]);
+                A[i][1] = i8x8_to_bf16(wr[i][0][2], wr[i][0][3]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[i][j][e] = h2f((uint16_t)(sc[i][j][e >> 1] >> (16 * (e & 1))));
+            }
+        }
+        if (st + 1 < st1) load_stage(st + 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            bf16x8_t B[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) B[tb] = __builtin_bit_cast(bf16x8_t, xs[(tb * 2 + j) * 64 + lane]);
+            if (!Q8) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb)
+                        acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][j], B[tb], acc[i][tb], 0, 0, 0);
+            } else {
+                const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const bf16x8_t Bl = __builtin_bit_cast(bf16x8_t, xs[XS + (tb * 2 + j) * 64 + lane]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][j], B[tb], zf, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i][j], Bl, d, 0, 0, 0);
+                        acc[i][tb] += S[i][j] * d;
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rb = rb0 + i;
+        if (rb >= nrb) continue;
+        if (EPI == EPI_SWIGLU && (i & 1)) continue;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = t0 + tb * 16 + r;
+            if (t >= a.T) continue;
+            if (EPI == EPI_SWIGLU)
+                epilogue4<EPI, false>(a, t, (rb >> 1) * 16 + 4 * g, acc[i][tb], acc[i + 1][tb]);
+            else
+                epilogue4<EPI, (SPLITK > 1)>(a, t, rb * 16 + 4 * g, acc[i][tb], acc[i][tb]);
+        }
+    }
+}
+
+template <int WT, int EPI, int BT, int SPLITK>
+static void launch_gemm(const LinearArgs &a, hipStream_t s) {
+    const int n_wtiles = (a.N + 255) / 256;
+    const int n_ttiles = (a.T + BT - 1) / BT;
+    const int total = n_wtiles * n_ttiles * SPLITK;
+    hipLaunchKernelGGL((gemm_kernel<WT, EPI, BT, SPLITK>), dim3(total), dim3(256), 0, s, a, n_wtiles, n_ttiles);
+}
+
+// True if the product was issued as a GEMM (bf16 / q8_0 weights, >= 64
+// tokens, K a multiple of 64).
+template <int WT, int EPI>
+static bool try_gemm(const LinearArgs &a, hipStream_t s) {
+    if constexpr (WT == W_F32) {
+        return false;
+    } else {
+    if (a.T < 64 || a.K % 64) return false;
+    if (EPI == EPI_SWIGLU && a.N % 32) return false;
+    const int n_wtiles = (a.N + 255) / 256;
+    const bool big = (long)n_wtiles * ((a.T + 127) / 128) >= 256;
+    if (EPI == EPI_RESID) {
+        const long tiles = (long)n_wtiles * ((a.T + 63) / 64);
+        if (tiles >= 256 || a.K < 256) {
+            launch_gemm<WT, EPI, 64, 1>(a, s);
+        } else if (tiles * 2 >= 256 || a.K < 512) {
+            launch_gemm<WT, EPI, 64, 2>(a, s);
+        } else {
+            launch_gemm<WT, EPI, 64, 4>(a, s);
+        }
+        return true;
+    }
+    if (big && WT != W_Q8)
+        launch_gemm<WT, EPI, 128, 1>(a, s);
+    else
+        launch_gemm<WT, EPI, 64, 1>(a, s);
+    return true;
     }
 }
 
 template <int WT, int EPI>
 static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
     constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
+    if (try_gemm<WT, EPI>(a, s)) return;
     dim3 grid(a.N / 16 / RB, (a.T + 15) / 16);
     const long blocks = (long)grid.x * grid.y;
     if (blocks >= 2048)

@@ -383,6 +383,52 @@ struct ubd_context : public Executor {
     std::vector<int32_t> last_ub_idx;
     float *dump = nullptr;
     ubd_perf perf{};
+    // kernel timing
+    uint32_t time_mask = 0;
+    std::vector<hipEvent_t> ev_pool;
+    struct Pending {
+        int cls;
+        hipEvent_t a, b;
+    };
+    std::vector<Pending> pending;
+    int32_t t_launches[UBD_KERNEL_CLASSES] = {};
+    double t_ms[UBD_KERNEL_CLASSES] = {};
+
+    hipEvent_t take_event() {
+        if (!ev_pool.empty()) {
+            hipEvent_t e = ev_pool.back();
+            ev_pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        (void)hipEventCreate(&e);
+        return e;
+    }
+    template <typename F>
+    void timed(int cls, F &&launch) {
+        if (!(time_mask & (1u << cls))) {
+            launch();
+            return;
+        }
+        hipEvent_t a = take_event(), b = take_event();
+        (void)hipEventRecord(a, stream);
+        launch();
+        (void)hipEventRecord(b, stream);
+        pending.push_back({cls, a, b});
+    }
+    void collect_timing() {
+        (void)hipStreamSynchronize(stream);
+        for (auto &p : pending) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+                t_ms[p.cls] += ms;
+                t_launches[p.cls] += 1;
+            }
+            ev_pool.push_back(p.a);
+            ev_pool.push_back(p.b);
+        }
+        pending.clear();
+    }
 
     TokInfo tok_info() const {
         TokInfo t;
@@ -516,6 +562,8 @@ extern "C" void ubd_free(ubd_context *ctx) {
     if (!ctx) return;
     (void)hipSetDevice(ctx->model->device);
     (void)hipStreamSynchronize(ctx->stream);
+    ctx->collect_timing();
+    for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
     ctx->mem.release();
     for (int i = 0; i < 2; ++i) {
         if (ctx->info_host[i]) (void)hipHostFree(ctx->info_host[i]);
@@ -614,13 +662,14 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
 
     const TokInfo ti = tok_info();
     const int n_cells = (int)planner.n_cells;
-    launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, stream);
+    const int ph = T > 16 ? 1 : 0;
+    timed(0 + ph, [&] { launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, stream); });
     if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, stream), "dump");
 
     const size_t kb = type_k == KV_F32 ? 4 : 2, vb = type_v == KV_F32 ? 4 : 2;
     for (int il = 0; il < hp.n_layer; ++il) {
         const auto &L = M.layers[il];
-        launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, actA, stream);
+        timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, actA, stream); });
 
         LinearArgs la;
         la.wtype = M.wtype;
@@ -644,7 +693,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         la.qkv.v_cache = (char *)v_cache + kv_layer_elems * il * vb;
         la.qkv.type_k = type_k;
         la.qkv.type_v = type_v;
-        launch_linear(la, stream);
+        timed(4 + ph, [&] { launch_linear(la, stream); });
 
         AttnArgs aa;
         aa.q = q;
@@ -665,7 +714,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         aa.part_o = part_o;
         aa.part_ml = part_ml;
         aa.out = actB;
-        launch_attention(aa, stream);
+        timed(6 + ph, [&] { launch_attention(aa, stream); });
 
         LinearArgs lo;
         lo.wtype = M.wtype;
@@ -679,9 +728,9 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lo.epi = EPI_RESID;
         lo.y = x;
         lo.ldy = d;
-        launch_linear(lo, stream);
+        timed(8 + ph, [&] { launch_linear(lo, stream); });
 
-        launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, actA, stream);
+        timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, actA, stream); });
         LinearArgs lg = lo;
         lg.w = L.gu.w;
         lg.wscale = L.gu.scales;
@@ -690,7 +739,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lg.x = actA;
         lg.epi = EPI_SWIGLU;
         lg.out = actC;
-        launch_linear(lg, stream);
+        timed(10 + ph, [&] { launch_linear(lg, stream); });
 
         LinearArgs ld = lo;
         ld.w = L.down.w;
@@ -698,13 +747,13 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         ld.N = L.down.rows;
         ld.K = L.down.cols;
         ld.x = actC;
-        launch_linear(ld, stream);
+        timed(12 + ph, [&] { launch_linear(ld, stream); });
         if (dump)
             hip_ok(hipMemcpyAsync(dump + (size_t)(il + 1) * cap * d, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice,
                                   stream), "dump");
     }
     if (n_out > 0) {
-        launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, actA, stream);
+        timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, actA, stream); });
         LinearArgs lz;
         lz.wtype = M.wtype;
         lz.w = M.out.w;
@@ -716,7 +765,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lz.epi = EPI_LOGITS;
         lz.row_map = out_lrow();
         lz.logits = logits_dev;
-        launch_linear(lz, stream);
+        timed(14 + ph, [&] { launch_linear(lz, stream); });
     }
     if (!hip_ok(hipGetLastError(), "kernel launch")) return UBD_COMPUTE_FAILED;
     perf.n_ubatch += 1;
@@ -954,6 +1003,36 @@ extern "C" int32_t ubd_debug_last_ubatch(ubd_context *ctx, int32_t *batch_idx, i
     if (T > cap) return -1;
     std::copy(ctx->last_ub_idx.begin(), ctx->last_ub_idx.end(), batch_idx);
     return T;
+}
+
+static const char *kClassNames[UBD_KERNEL_CLASSES] = {
+    "decode.embed",       "prefill.embed",       "decode.rmsnorm",     "prefill.rmsnorm",
+    "decode.qkv",         "prefill.qkv",         "decode.attention",   "prefill.attention",
+    "decode.attn_output", "prefill.attn_output", "decode.ffn_gate_up", "prefill.ffn_gate_up",
+    "decode.ffn_down",    "prefill.ffn_down",    "decode.logits",      "prefill.logits"};
+
+extern "C" int32_t ubd_debug_kernel_timing(ubd_context *ctx, uint32_t mask) {
+    if (!ctx) return UBD_INVALID;
+    ctx->collect_timing();
+    ctx->time_mask = mask;
+    return UBD_OK;
+}
+
+extern "C" const char *ubd_debug_kernel_class_name(int32_t cls) {
+    return cls >= 0 && cls < UBD_KERNEL_CLASSES ? kClassNames[cls] : "";
+}
+
+extern "C" int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches, double *total_ms, int32_t n) {
+    if (!ctx || n < 0 || n > UBD_KERNEL_CLASSES) return UBD_INVALID;
+    (void)hipSetDevice(ctx->model->device);
+    ctx->collect_timing();
+    for (int32_t i = 0; i < n; ++i) {
+        if (launches) launches[i] = ctx->t_launches[i];
+        if (total_ms) total_ms[i] = ctx->t_ms[i];
+        ctx->t_launches[i] = 0;
+        ctx->t_ms[i] = 0;
+    }
+    return n;
 }
 
 extern "C" void ubd_perf_get(const ubd_context *ctx, ubd_perf *out) {

@@ -1,0 +1,103 @@
+"""8B-shaped parity at full size, in the launch configuration bench.py
+times (512-token prefill as one ubatch, then single-token decode), on
+sampled outputs the oracle computes one by one: the oracle re-runs sampled
+layers from the GPU's own input to that layer and the output head from the
+GPU's final residual.  Tolerance (bf16 / int8 configs): max |error| within
+3e-2 of the max-norm of the oracle's output."""
+import numpy as np
+import pytest
+
+from oracle import OracleModel, OracleContext, Batch
+from oracle.planner import plan_batch
+from workloads import WORKLOADS, gen_tensor, gen_tensor_rows, prompt_tokens
+
+pytestmark = pytest.mark.gpu
+TOL = 3e-2
+LAYERS = (0, 1, 17, 31)
+
+
+def rel(a, b):
+    return float(np.abs(np.asarray(a, np.float64) - b).max() / np.abs(b).max())
+
+
+def build(cfg):
+    import torch
+    from llama_decode_ubatch_amd import Model
+    from workloads import device as wdev
+    w = WORKLOADS[cfg]
+    tens = wdev.model_tensors(torch, w.model, "cuda:0")
+    torch.cuda.synchronize()
+    model = Model(w.model, tens, device=0)
+    del tens
+    torch.cuda.empty_cache()
+    om = OracleModel(w.model, lambda n: gen_tensor(w.model, n), dtype=np.float32, cache=True,
+                     rows_fn=lambda n, r: gen_tensor_rows(w.model, n, r))
+    return w, model, om
+
+
+def oracle_layer(om, w, il, x_in, tokens, pos0, kv_prefix=None):
+    """Oracle layer il on the GPU's input residual for one sequence's tokens
+    at positions pos0..; kv_prefix = (K, V) f32 rows of positions < pos0."""
+    ref = OracleContext(om, w.n_ctx, w.n_batch, w.n_ubatch, 1, w.type_k, w.type_v)
+    if pos0:
+        K, V = kv_prefix
+        zeros = [np.zeros_like(K)] * w.model.n_layer
+        ks, vs = list(zeros), list(zeros)
+        ks[il], vs[il] = K, V
+        assert ref.kv_fill(0, pos0, ks, vs)
+    plan = plan_batch(Batch(tokens), ref.mem, w.model.n_vocab, 1, ref.n_batch, len(tokens))
+    ub, cells = plan.ubatches[0], plan.cells[0]
+    ref.mem.apply(ub, cells)
+    y = ref.layer_forward(il, x_in.astype(np.float32), ub, cells)
+    for k in [k for k in om._cache if k.startswith("blk.")]:   # keep only the head cached
+        del om._cache[k]
+    return y, ref
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_prefill_and_decode_sampled_layers(cfg):
+    from llama_decode_ubatch_amd import Context
+    w, model, om = build(cfg)
+    ctx = Context(model, n_ctx=w.n_ctx, n_batch=w.n_batch, n_ubatch=w.n_ubatch, type_k=w.type_k,
+                  type_v=w.type_v)
+    assert ctx.keep_residuals(True) == 0
+    prompt = prompt_tokens(w, 0)
+    T = prompt.size
+    print(f"config {cfg}: prefill {T} tokens", flush=True)
+    assert ctx.decode(prompt) == 0
+    for il in LAYERS:
+        x_in, x_out = ctx.residual(il, T), ctx.residual(il + 1, T)
+        y, ref = oracle_layer(om, w, il, x_in, prompt, 0)
+        err = rel(x_out, y)
+        print(f"  prefill layer {il}: rel err {err:.2e}", flush=True)
+        assert err < TOL, il
+        # the K/V this layer appended, as stored (f16)
+        Kr, Vr = ref.kv(il, 0)
+        assert rel(ctx.kv_read(il, 0, 0, 0, T), Kr[:T].astype(np.float32)) < TOL
+        assert rel(ctx.kv_read(il, 0, 1, 0, T), Vr[:T].astype(np.float32)) < TOL
+    x_last = ctx.residual(w.model.n_layer, T)[-1:]
+    zr = OracleContext(om, w.n_ctx).head(x_last.astype(np.float32))[0]
+    z = ctx.logits_ith(-1)
+    print(f"  prefill logits: rel err {rel(z, zr):.2e}", flush=True)
+    assert rel(z, zr) < TOL and int(np.argmax(z)) == int(np.argmax(zr))
+    tok = ctx.greedy(-1)
+    assert tok == int(np.argmax(z))
+    # three decode steps, each checked at a sampled layer with the GPU's KV prefix
+    for step, il in enumerate((0, 31, 5)):
+        assert ctx.decode([tok]) == 0
+        p = T + step
+        x_in, x_out = ctx.residual(il, 1), ctx.residual(il + 1, 1)
+        K = ctx.kv_read(il, 0, 0, 0, p).astype(np.float16)
+        V = ctx.kv_read(il, 0, 1, 0, p).astype(np.float16)
+        y, _ = oracle_layer(om, w, il, x_in, np.array([tok]), p, (K, V))
+        err = rel(x_out, y)
+        print(f"  decode step {step} layer {il}: rel err {err:.2e}", flush=True)
+        assert err < TOL
+        x_last = ctx.residual(w.model.n_layer, 1)
+        zr = OracleContext(om, w.n_ctx).head(x_last.astype(np.float32))[0]
+        z = ctx.logits_ith(-1)
+        assert rel(z, zr) < TOL
+        tok = ctx.greedy(-1)
+        assert tok == int(np.argmax(z))
+    ctx.free()
+    model.free()

@@ -111,3 +111,8 @@ def fill_kv_block(torch, w: Workload, seq: int, layer: int, which: int, out, p0=
     _check(L.ubd_synth_table16(out.data_ptr(), out.numel(), gen.kv_key(w, seq, layer, which), p0 * ne,
                                _table(torch, "kv_f16", out.device).data_ptr(), stream))
     return out
+
+
+def model_tensors(torch, model: ModelShape, device="cuda", literal_gains=False):
+    """All tensors of a model generated on the device (name -> dict)."""
+    return {s.name: fill_tensor(torch, model, s, device, literal_gains) for s in tensor_specs(model)}
