@@ -96,13 +96,20 @@ struct AttnArgs {
     float *part_o = nullptr;          // [T][H][max_chunks][hd]
     float *part_ml = nullptr;         // [T][H][max_chunks][2]
     Act out;                          // [T][H*hd]
+    bool split = false;               // MFMA path: split cells into chunks + combine
 };
-constexpr int ATTN_CHUNK = 256;       // cells per split-K chunk
+constexpr int ATTN_CHUNK = 256;       // cells per split-K chunk (f32 path)
+constexpr int ATTN_DECODE_CHUNK = 64; // cells per wave in the split MFMA path
 constexpr int ATTN_TILE_ROWS = 64;    // query rows (tokens x n_gqa) per tile
 
 void launch_attention(const AttnArgs &a, hipStream_t s);
 // Query rows (tokens x n_gqa) one attention tile holds for a head size.
 int attn_tile_rows(int head_dim);
+// MFMA attention (f16 K/V): tiles are blocks of 16 / n_gqa tokens; with
+// split, tiles[3] cells are cut into ATTN_DECODE_CHUNK-cell chunks (one
+// wave each) and combined; otherwise one wave scans tiles[3] cells.
+bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa, int n_cells);
+void launch_attention_mfma(const AttnArgs &a, hipStream_t s);
 
 // out[r] = argmax over n of logits[row(r)][n] (lowest index on ties)
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows,

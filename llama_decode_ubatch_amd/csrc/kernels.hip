@@ -758,6 +758,197 @@ void launch_attention(const AttnArgs &a, hipStream_t s) {
     }
 }
 
+// MFMA attention for f16 K/V (decode and prefill).  One wave = one block of
+// 16 query rows (row = token x query head of a KV group; a decode token
+// gives n_gqa rows) against a range of cells.  Scores are computed as
+// S^T = K Q^T (A = 16 cells x 32 dims of K straight from the cache, B = the
+// rows' q as f16 hi + lo), so lane (row r, group g) holds S[r][cells 4g+i]
+// of each 16-cell block.  Two blocks give exactly the P fragment of P*V for
+// the cell order {4g..4g+3, 16+4g..16+4g+3}, which V^T [dim][cell] supplies
+// as two contiguous 8-byte runs.  Online softmax per row; SPLIT writes the
+// range's (m, l, O) for a combine pass, otherwise O / l is stored.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+template <int HD, bool SPLIT, int NC>
+__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
+    constexpr int KK = HD / 32, DB = HD / 16;
+    const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+    const int chunk = blockIdx.x, blk = blockIdx.y, grp = blockIdx.z;
+    const int t0 = a.tok.tiles[blk * 4 + 0], nt = a.tok.tiles[blk * 4 + 1];
+    const int st = a.tok.tiles[blk * 4 + 2], nscan = a.tok.tiles[blk * 4 + 3];
+    const int G = a.n_head / a.n_head_kv;
+    const int R = nt * G;
+    int cbeg = 0, cend = nscan;
+    if (SPLIT) {
+        cbeg = chunk * NC;
+        if (cbeg >= nscan) return;
+        cend = min(nscan, cbeg + NC);
+    }
+    const float scale = 1.0f / sqrtf((float)HD);
+    // this lane's query row (S^T layout: row = r)
+    const bool row_ok = r < R;
+    const int rt = t0 + (row_ok ? r / G : 0), rh = grp * G + (row_ok ? r % G : 0);
+    const int rpos = a.tok.pos[rt], rseq = a.tok.seq[rt];
+    f16x8_t qh[KK], ql[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = row_ok ? a.q[(size_t)rt * a.n_head * HD + rh * HD + 32 * kk + 8 * g + e] * scale : 0.f;
+            const _Float16 h = (_Float16)v;
+            qh[kk][e] = h;
+            ql[kk][e] = (_Float16)(v - (float)h);
+        }
+    }
+    const _Float16 *K = (const _Float16 *)a.k_cache + ((size_t)st * a.n_head_kv + grp) * a.n_cells * HD;
+    const _Float16 *Vt = (const _Float16 *)a.v_cache + ((size_t)st * a.n_head_kv + grp) * HD * a.n_cells;
+    const int32_t *cpos = a.cell_pos + (size_t)st * a.n_cells;
+    const int32_t *cseq = a.cell_seq + (size_t)st * a.n_cells;
+
+    float m = -INFINITY, l = 0.f;
+    f32x4_t O[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) O[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int c0 = cbeg; c0 < cend; c0 += 32) {
+        f32x4_t S[2];
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+            const int cb = c0 + 16 * b2;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const f16x8_t A = *(const f16x8_t *)(K + (size_t)(cb + r) * HD + 32 * kk + 8 * g);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql[kk], acc, 0, 0, 0);
+            }
+            const int cc = cb + 4 * g;
+            const int4 p4 = *(const int4 *)(cpos + cc);
+            const int4 s4 = *(const int4 *)(cseq + cc);
+            const int pp[4] = {p4.x, p4.y, p4.z, p4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool vis = row_ok && cc + i < cend && ss[i] == rseq && pp[i] >= 0 && pp[i] <= rpos;
+                acc[i] = vis ? acc[i] : -INFINITY;
+            }
+            S[b2] = acc;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : expf(m - m_new);
+        float ps = 0.f;
+        f16x8_t ph, pl;
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sv = S[b2][i];
+                const float p = sv == -INFINITY ? 0.f : expf(sv - m_new);
+                ps += p;
+                const _Float16 h = (_Float16)p;
+                ph[4 * b2 + i] = h;
+                pl[4 * b2 + i] = (_Float16)(p - (float)h);
+            }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l = l * alpha + ps;
+        m = m_new;
+        // O rows are 4g+i in this lane: fetch their rescale factors
+        f32x4_t al;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const _Float16 *vrow = Vt + (size_t)(16 * db + r) * a.n_cells;
+            const f16x4_t v0 = *(const f16x4_t *)(vrow + c0 + 4 * g);
+            const f16x4_t v1 = *(const f16x4_t *)(vrow + c0 + 16 + 4 * g);
+            const f16x8_t B = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            f32x4_t o = O[db] * al;
+            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, B, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, o, 0, 0, 0);
+            O[db] = o;
+        }
+    }
+    // O: lane (dim r of each 16-dim block, group g) holds rows 4g+i
+    f32x4_t lrow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l, 4 * g + i, 64);
+    if (SPLIT) {
+        if (g == 0 && row_ok) {
+            float *ml = a.part_ml + (((size_t)rt * a.n_head + rh) * a.max_chunks + chunk) * 2;
+            ml[0] = m;
+            ml[1] = l;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        if (row >= R) continue;
+        const int t = t0 + row / G, h = grp * G + row % G;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int d = 16 * db + r;
+            if (SPLIT)
+                a.part_o[(((size_t)t * a.n_head + h) * a.max_chunks + chunk) * HD + d] = O[db][i];
+            else
+                store_act(a.out, (size_t)t * a.out.ld + h * HD + d, lrow[i] > 0.f ? O[db][i] / lrow[i] : 0.f);
+        }
+    }
+}
+
+template <int HD, int NC>
+__global__ __launch_bounds__(128) void attn_combine_nc_kernel(AttnArgs a) {
+    const int t = blockIdx.x / a.n_head, h = blockIdx.x % a.n_head;
+    const int tile = a.tok.tile_of[t];
+    const int nscan = a.tok.tiles[tile * 4 + 3];
+    const int nch = (nscan + NC - 1) / NC;
+    const float *ml = a.part_ml + ((size_t)t * a.n_head + h) * a.max_chunks * 2;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * c]);
+    float L = 0.f;
+    for (int c = 0; c < nch; ++c)
+        if (ml[2 * c] != -INFINITY) L += ml[2 * c + 1] * expf(ml[2 * c] - M);
+    const float invL = L > 0.f ? 1.0f / L : 0.f;
+    for (int d = threadIdx.x; d < HD; d += blockDim.x) {
+        float o = 0.f;
+        for (int c = 0; c < nch; ++c)
+            if (ml[2 * c] != -INFINITY)
+                o += a.part_o[(((size_t)t * a.n_head + h) * a.max_chunks + c) * HD + d] * expf(ml[2 * c] - M);
+        store_act(a.out, (size_t)t * a.out.ld + h * HD + d, o * invL);
+    }
+}
+
+template <int HD>
+static void launch_attention_mfma_hd(const AttnArgs &a, hipStream_t s) {
+    if (a.split) {
+        dim3 grid(a.max_chunks, a.n_tiles, a.n_head_kv);
+        hipLaunchKernelGGL((attn_mfma_kernel<HD, true, ATTN_DECODE_CHUNK>), grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((attn_combine_nc_kernel<HD, ATTN_DECODE_CHUNK>), dim3(a.T * a.n_head), dim3(128), 0, s,
+                           a);
+    } else {
+        dim3 grid(1, a.n_tiles, a.n_head_kv);
+        hipLaunchKernelGGL((attn_mfma_kernel<HD, false, ATTN_DECODE_CHUNK>), grid, dim3(64), 0, s, a);
+    }
+}
+
+bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa, int n_cells) {
+    return type_k == KV_F16 && type_v == KV_F16 && n_gqa <= 16 && n_cells % 32 == 0 &&
+           (head_dim == 32 || head_dim == 64 || head_dim == 128);
+}
+
+void launch_attention_mfma(const AttnArgs &a, hipStream_t s) {
+    if (a.T <= 0) return;
+    switch (a.head_dim) {
+    case 32: launch_attention_mfma_hd<32>(a, s); break;
+    case 64: launch_attention_mfma_hd<64>(a, s); break;
+    case 128: launch_attention_mfma_hd<128>(a, s); break;
+    }
+}
+
 int attn_tile_rows(int head_dim) { return head_dim >= 128 ? AttnCfg<128>::ROWS : AttnCfg<64>::ROWS; }
 
 // --------------------------------------------------------------- argmax

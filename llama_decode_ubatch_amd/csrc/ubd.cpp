@@ -368,7 +368,9 @@ struct ubd_context : public Executor {
     float *x = nullptr, *q = nullptr;
     Act actA, actB, actC;
     float *part_o = nullptr, *part_ml = nullptr;
-    int max_chunks = 0;
+    int max_chunks = 0;                     // f32-path chunks (ATTN_CHUNK cells)
+    int max_chunks_mfma = 0;                // MFMA split-path chunks (ATTN_DECODE_CHUNK cells)
+    bool mfma_attn = false;
     double *inv_freq = nullptr;
     int32_t *info_dev = nullptr;
     int32_t *info_host[2] = {nullptr, nullptr};
@@ -513,6 +515,11 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     c->cell_pos = (int32_t *)c->mem.get(cells * 4);
     c->cell_seq = (int32_t *)c->mem.get(cells * 4);
     if (!c->k_cache || !c->v_cache || !c->cell_pos || !c->cell_seq) return bail("KV cache allocation failed");
+    // zero K/V: masked cells still enter P*V with weight 0, so never-written
+    // cells must hold finite values
+    if (!hip_ok(hipMemsetAsync(c->k_cache, 0, c->kv_layer_elems * hp.n_layer * kb, c->stream), "memset") ||
+        !hip_ok(hipMemsetAsync(c->v_cache, 0, c->kv_layer_elems * hp.n_layer * vb, c->stream), "memset"))
+        return bail("KV cache init failed");
     if (!hip_ok(hipMemsetAsync(c->cell_pos, 0xff, cells * 4, c->stream), "memset") ||
         !hip_ok(hipMemsetAsync(c->cell_seq, 0xff, cells * 4, c->stream), "memset"))
         return bail("KV cell table init failed");
@@ -533,8 +540,13 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     if (!c->x || !c->q || !make_act(c->actA, d) || !make_act(c->actB, H * hd) || !make_act(c->actC, F))
         return bail("activation allocation failed");
     c->max_chunks = (int)((P.n_cells + ATTN_CHUNK - 1) / ATTN_CHUNK);
-    c->part_o = (float *)c->mem.get((size_t)cap * H * c->max_chunks * hd * 4);
-    c->part_ml = (float *)c->mem.get((size_t)cap * H * c->max_chunks * 2 * 4);
+    c->max_chunks_mfma = (int)((P.n_cells + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK);
+    c->mfma_attn = attn_mfma_ok(c->type_k, c->type_v, hd, H / Hk, (int)P.n_cells);
+    // split partials: f32 path up to n_ubatch tokens; MFMA path only for <= 16 tokens
+    const size_t part_rows = c->mfma_attn ? (size_t)std::min(cap, 16) * H * c->max_chunks_mfma
+                                          : (size_t)cap * H * c->max_chunks;
+    c->part_o = (float *)c->mem.get(part_rows * hd * 4);
+    c->part_ml = (float *)c->mem.get(part_rows * 2 * 4);
     if (!c->part_o || !c->part_ml) return bail("attention scratch allocation failed");
     std::vector<double> inv(hd / 2);
     for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)hp.rope_freq_base, -2.0 * i / hd);
@@ -641,7 +653,8 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
             ++n_out;
         }
     }
-    const int qt = std::max(1, attn_tile_rows(hd) / G);
+    const bool split = T <= 16;
+    const int qt = mfma_attn ? std::max(1, 16 / G) : std::max(1, attn_tile_rows(hd) / G);
     int n_tiles = 0;
     for (int t = 0; t < T;) {
         int e = t + 1;
@@ -651,6 +664,18 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         tl[1] = e - t;
         tl[2] = ub.stream[t];
         tl[3] = planner.cells.n_kv(ub.stream[t]);
+        if (mfma_attn && !split && tl[3] <= 8192) {
+            // scan only up to the last cell some token of the tile can see
+            const int st = ub.stream[t];
+            int c = tl[3] - 1;
+            for (; c >= 0; --c) {
+                const int cs = planner.cells.seq_at(st, c), cpp = planner.cells.pos_at(st, c);
+                bool vis = false;
+                for (int j = t; j < e && !vis; ++j) vis = cs == ub.seq[j] && cpp >= 0 && cpp <= ub.pos[j];
+                if (vis) break;
+            }
+            tl[3] = c + 1;
+        }
         for (int j = t; j < e; ++j) h[6 * cap + j] = n_tiles;
         ++n_tiles;
         t = e;
@@ -710,11 +735,17 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         aa.tok = ti;
         aa.T = T;
         aa.n_tiles = n_tiles;
-        aa.max_chunks = max_chunks;
         aa.part_o = part_o;
         aa.part_ml = part_ml;
         aa.out = actB;
-        timed(6 + ph, [&] { launch_attention(aa, stream); });
+        if (mfma_attn) {
+            aa.split = split;
+            aa.max_chunks = max_chunks_mfma;
+            timed(6 + ph, [&] { launch_attention_mfma(aa, stream); });
+        } else {
+            aa.max_chunks = max_chunks;
+            timed(6 + ph, [&] { launch_attention(aa, stream); });
+        }
 
         LinearArgs lo;
         lo.wtype = M.wtype;
