@@ -102,6 +102,7 @@ SIGNATURES = {
     "ubd_debug_kernel_timing": (C.c_int32, [_P, C.c_uint32]),
     "ubd_debug_kernel_class_name": (C.c_char_p, [C.c_int32]),
     "ubd_debug_kernel_stats": (C.c_int32, [_P, C.POINTER(C.c_int32), C.POINTER(C.c_double), C.c_int32]),
+    "ubd_debug_set_tuning": (C.c_int32, [C.c_char_p, C.c_int32]),
     "ubd_perf_get": (None, [_P, C.POINTER(Perf)]),
     "ubd_perf_reset": (None, [_P]),
     "ubd_log_set": (None, [LOG_FN, C.c_void_p]),
@@ -142,6 +143,12 @@ def load_library(path=LIB_PATH):
 
 def last_error():
     return load_library().ubd_last_error().decode()
+
+
+def set_tuning(key, value):
+    """Process-wide launch-shape knob (see ubd_debug_set_tuning)."""
+    if load_library().ubd_debug_set_tuning(key.encode(), int(value)) != 0:
+        raise KeyError(key)
 
 
 def _i32(a):

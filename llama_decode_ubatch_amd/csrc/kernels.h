@@ -13,7 +13,9 @@
 //      q8_0: k-step 64 values, lane bytes = cols 64*s + 8g .. +8 then
 //            cols 64*s + 32 + 8g .. +8 (codes), scales as
 //            [row block][cols/32][16 rows] f16.
-//    Tile (rb, s) starts at byte (rb * steps + s) * 1024.
+//    Tiles are stored k-step-major: tile (rb, s) starts at byte
+//    (s * rows/16 + rb) * 1024, so that the work-groups of a product, which
+//    advance through k together, read one contiguous window of memory.
 //  * KV cache per layer: K [stream][kv head][cell][head_dim] and V
 //    transposed [stream][kv head][head_dim][cell], each of type_k / type_v.
 #pragma once
@@ -25,6 +27,18 @@
 namespace ubd {
 
 enum WType : int { W_F32 = 0, W_BF16 = 2, W_Q8 = 3 };
+
+// Launch-shape knobs (process-wide; 0 = built-in choice).  Set through
+// ubd_debug_set_tuning for measurements.
+struct Tuning {
+    int skinny_nw = 0;        // waves per work-group of the small-T product
+    int fuse_norm = -1;       // -1: fuse RMSNorm into the QKV product only, 0: never, 1: QKV+gate|up+logits
+    int attn_chunk_min = 0;   // smallest cells per wave of split attention
+    int ldsx = 1;             // stage few-token activations in LDS (decode products)
+};
+// LDS bytes the activation copy of the LDS-staged few-token product may use
+constexpr size_t LDSX_MAX_BYTES = 64 * 1024;
+extern Tuning g_tuning;
 enum KVType : int { KV_F32 = 0, KV_F16 = 1 };
 
 struct Act {
@@ -53,6 +67,18 @@ struct QKVEpi {
     int type_k = KV_F16, type_v = KV_F16;
 };
 
+// Fused RMSNorm of the product's input (at most NORM_TMAX rows): x row of
+// token t is rows ? rows[t] : t, row stride ld; output = x / sqrt(mean(x^2)
+// + eps) * gain, formed per work-group in LDS.
+constexpr int NORM_TMAX = 2;
+struct NormIn {
+    const float *x = nullptr;
+    const int32_t *rows = nullptr;
+    const float *gain = nullptr;
+    float eps = 0.f;
+    int ld = 0;
+};
+
 struct LinearArgs {
     int wtype = W_BF16;
     const void *w = nullptr;          // tiled weights
@@ -68,6 +94,7 @@ struct LinearArgs {
     float *logits = nullptr;          // LOGITS: [rows][N]
     TokInfo tok;                      // QKV: pos / stream / cell per token
     QKVEpi qkv;
+    NormIn norm;                      // set: input is x normalised on the fly (T <= NORM_TMAX)
 };
 
 void launch_linear(const LinearArgs &a, hipStream_t s);
@@ -97,23 +124,35 @@ struct AttnArgs {
     float *part_ml = nullptr;         // [T][H][max_chunks][2]
     Act out;                          // [T][H*hd]
     bool split = false;               // MFMA path: split cells into chunks + combine
+    int chunk_cells = 32;             // MFMA split: cells per wave (multiple of 32)
+    int n_chunks_launch = 0;          // MFMA split: chunks launched per tile
 };
 constexpr int ATTN_CHUNK = 256;       // cells per split-K chunk (f32 path)
-constexpr int ATTN_DECODE_CHUNK = 64; // cells per wave in the split MFMA path
+constexpr int ATTN_DECODE_CHUNK = 32; // smallest cells-per-wave chunk of the split MFMA path
 constexpr int ATTN_TILE_ROWS = 64;    // query rows (tokens x n_gqa) per tile
 
 void launch_attention(const AttnArgs &a, hipStream_t s);
 // Query rows (tokens x n_gqa) one attention tile holds for a head size.
 int attn_tile_rows(int head_dim);
 // MFMA attention (f16 K/V): tiles are blocks of 16 / n_gqa tokens; with
-// split, tiles[3] cells are cut into ATTN_DECODE_CHUNK-cell chunks (one
-// wave each) and combined; otherwise one wave scans tiles[3] cells.
+// split (at most 16 tokens), tiles[3] cells are cut into chunk_cells-cell
+// chunks, one wave each, merged by a combine pass; otherwise one wave scans
+// tiles[3] cells.  Partials are indexed with max_chunks = ceil(n_cells /
+// ATTN_DECODE_CHUNK).
 bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa, int n_cells);
 void launch_attention_mfma(const AttnArgs &a, hipStream_t s);
 
-// out[r] = argmax over n of logits[row(r)][n] (lowest index on ties)
+// out[r] = argmax over n of logits[row(r)][n] (lowest index on ties).
+// Workspace: pv / pi [n_rows][ARGMAX_BLOCKS] and counter [n_rows], the
+// counters zero before the first call (each call leaves them zero).
+constexpr int ARGMAX_BLOCKS = 64;
+struct ArgmaxWork {
+    float *pv = nullptr;
+    int32_t *pi = nullptr;
+    int32_t *counter = nullptr;
+};
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows,
-                   int n, int32_t *out, hipStream_t s);
+                   int n, int32_t *out, const ArgmaxWork &w, hipStream_t s);
 
 // Weight relayout: row-major source matrices -> tiled layout.  Up to three
 // sources are concatenated by rows (mode 0) or two are interleaved by

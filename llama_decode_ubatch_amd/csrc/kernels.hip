@@ -5,10 +5,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
 namespace ubd {
+
+Tuning g_tuning;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -46,6 +49,12 @@ __device__ __forceinline__ void store_act(const Act &o, size_t idx, float v) {
     }
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
 template <typename T>
 __device__ __forceinline__ T ldg_nt(const T *p) {
     return __builtin_nontemporal_load(p);
@@ -61,7 +70,7 @@ __device__ __forceinline__ T ldg_nt(const T *p) {
 template <int WT> struct WT_;
 template <> struct WT_<W_F32> { static constexpr int KSTEP = 16, U = 8; };
 template <> struct WT_<W_BF16> { static constexpr int KSTEP = 32, U = 8; };
-template <> struct WT_<W_Q8> { static constexpr int KSTEP = 64, U = 4; };
+template <> struct WT_<W_Q8> { static constexpr int KSTEP = 64, U = 2; };
 
 __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t w0, uint32_t w1) {
     // |code| <= 127 has at most 7 significant bits: exact in bf16, so the
@@ -82,34 +91,43 @@ struct StepIn {
     u32x2_t sc[RB][2];                  // q8 scales of rows 4g..4g+3, blocks 2s, 2s+1
 };
 
-template <int WT, int RB>
-__device__ __forceinline__ void load_step(const LinearArgs &a, int rb0, int s, int steps,
+// One k-step's operands: the weight tile(s) from HBM and the activations of
+// this lane's token, from global memory or (LDSB) from the normalised copy
+// the fused-RMSNorm prologue left in LDS ([T][K] f32, or hi then lo planes).
+template <int WT, int RB, bool LDSB>
+__device__ __forceinline__ void load_step(const LinearArgs &a, const unsigned char *lds, int rb0, int s, int steps,
                                           int lane, int tok, bool tok_ok, StepIn<WT, RB> &in) {
     const int g = lane >> 4;
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
-        const size_t tile = (size_t)(rb0 + j) * steps + s;
+        const size_t tile = (size_t)s * (a.N / 16) + rb0 + j;      // k-step-major tiles
         in.w[j] = ldg_nt((const u32x4_t *)((const char *)a.w + tile * 1024 + lane * 16));
     }
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const size_t plane = (size_t)a.T * a.K;
     if (WT == W_F32) {
-        in.xh = tok_ok ? *(const u32x4_t *)(a.x.f32 + (size_t)tok * a.x.ld + 16 * s + 4 * g)
-                       : u32x4_t{0, 0, 0, 0};
-    } else if (WT == W_BF16) {
-        const size_t o = (size_t)tok * a.x.ld + 32 * s + 8 * g;
-        in.xh = tok_ok ? *(const u32x4_t *)(a.x.hi + o) : u32x4_t{0, 0, 0, 0};
-        in.xl = tok_ok ? *(const u32x4_t *)(a.x.lo + o) : u32x4_t{0, 0, 0, 0};
+        const size_t o = (size_t)tok * (LDSB ? a.K : a.x.ld) + 16 * s + 4 * g;
+        if (LDSB)
+            in.xh = tok_ok ? *(const u32x4_t *)(lds + o * 4) : z;
+        else
+            in.xh = tok_ok ? *(const u32x4_t *)(a.x.f32 + o) : z;
     } else {
-        const size_t o = (size_t)tok * a.x.ld + 64 * s + 8 * g;
-        in.xh = tok_ok ? *(const u32x4_t *)(a.x.hi + o) : u32x4_t{0, 0, 0, 0};
-        in.xl = tok_ok ? *(const u32x4_t *)(a.x.lo + o) : u32x4_t{0, 0, 0, 0};
-        in.xh2 = tok_ok ? *(const u32x4_t *)(a.x.hi + o + 32) : u32x4_t{0, 0, 0, 0};
-        in.xl2 = tok_ok ? *(const u32x4_t *)(a.x.lo + o + 32) : u32x4_t{0, 0, 0, 0};
-        const int KB = a.K / 32;
+        const int kofs = (WT == W_BF16 ? 32 : 64) * s + 8 * g;
+        const size_t o = (size_t)tok * (LDSB ? a.K : a.x.ld) + kofs;
+        const uint16_t *hi = LDSB ? (const uint16_t *)lds : a.x.hi;
+        const uint16_t *lo = LDSB ? (const uint16_t *)lds + plane : a.x.lo;
+        in.xh = tok_ok ? *(const u32x4_t *)(hi + o) : z;
+        in.xl = tok_ok ? *(const u32x4_t *)(lo + o) : z;
+        if (WT == W_Q8) {
+            in.xh2 = tok_ok ? *(const u32x4_t *)(hi + o + 32) : z;
+            in.xl2 = tok_ok ? *(const u32x4_t *)(lo + o + 32) : z;
+            const int KB = a.K / 32;
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
-            const size_t b0 = ((size_t)(rb0 + j) * KB + 2 * s) * 16 + 4 * g;
-            in.sc[j][0] = *(const u32x2_t *)(a.wscale + b0);
-            in.sc[j][1] = *(const u32x2_t *)(a.wscale + b0 + 16);
+            for (int j = 0; j < RB; ++j) {
+                const size_t b0 = ((size_t)(rb0 + j) * KB + 2 * s) * 16 + 4 * g;
+                in.sc[j][0] = *(const u32x2_t *)(a.wscale + b0);
+                in.sc[j][1] = *(const u32x2_t *)(a.wscale + b0 + 16);
+            }
         }
     }
 }
@@ -231,10 +249,68 @@ __device__ __forceinline__ void epilogue4(const LinearArgs &a, int t, int n, f32
     }
 }
 
-template <int WT, int EPI, int NW>
-__global__ __launch_bounds__(64 * NW) void linear_small_kernel(LinearArgs a) {
+// Fused RMSNorm of the (at most NORM_TMAX) input rows: every work-group
+// reduces the rows' squares itself, then leaves x * rsqrt(mean(x^2) + eps)
+// * gain in LDS in the format the MFMA B operand wants.
+template <int WT, int NW>
+__device__ void norm_prologue(const LinearArgs &a, unsigned char *lds) {
+    // one pass: each thread keeps its slice of x in registers (K <= 8192
+    // with 256+ threads -> at most 8 float4), reduces, then normalises it
+    constexpr int TH = 64 * NW, MAXV = (8192 / 4 + TH - 1) / TH;
+    __shared__ float red_ss[NORM_TMAX][NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K, T = a.T;
+    f32x4_t v[NORM_TMAX][MAXV];
+    for (int t = 0; t < T; ++t) {
+        const float *xr = a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[t] : t) * a.norm.ld;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXV; ++i) {
+            const int e = (tid + TH * i) * 4;
+            v[t][i] = e < K ? *(const f32x4_t *)(xr + e) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ss += v[t][i][0] * v[t][i][0] + v[t][i][1] * v[t][i][1] + v[t][i][2] * v[t][i][2] +
+                  v[t][i][3] * v[t][i][3];
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red_ss[t][wave] = ss;
+    }
+    __syncthreads();
+    const size_t plane = (size_t)T * K;
+    for (int t = 0; t < T; ++t) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += red_ss[t][w];
+        const float inv = 1.0f / sqrtf(tot / (float)K + a.norm.eps);
+#pragma unroll
+        for (int i = 0; i < MAXV; ++i) {
+            const int e = (tid + TH * i) * 4;
+            if (e >= K) continue;
+            const f32x4_t y = v[t][i] * inv * *(const f32x4_t *)(a.norm.gain + e);
+            const size_t o = (size_t)t * K + e;
+            if (WT == W_F32) {
+                *(f32x4_t *)(lds + o * 4) = y;
+            } else {
+                u16x4_t hh, ll;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    hh[k] = f2bf(y[k]);
+                    ll[k] = f2bf(y[k] - bf2f(hh[k]));
+                }
+                *(u16x4_t *)((uint16_t *)lds + o) = hh;
+                *(u16x4_t *)((uint16_t *)lds + plane + o) = ll;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <int WT, int EPI, int NW, bool NORM>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void linear_small_kernel(LinearArgs a) {
     constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
-    constexpr int KSTEP = WT_<WT>::KSTEP, U = WT_<WT>::U;
+    // k-steps per batch: the same 16-byte weight loads in flight per lane
+    // for one or two row blocks
+    constexpr int KSTEP = WT_<WT>::KSTEP, U = WT_<WT>::U / RB;
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int rb0 = blockIdx.x * RB;
@@ -249,18 +325,35 @@ __global__ __launch_bounds__(64 * NW) void linear_small_kernel(LinearArgs a) {
 #pragma unroll
     for (int j = 0; j < RB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    int s = s0;
-    for (; s + U <= s1; s += U) {
+    // with the fused norm, the first U weight tiles are requested before the
+    // prologue so that HBM traffic overlaps the reduction
+    constexpr int HOIST = U;
+    u32x4_t w0[NORM ? HOIST : 1][RB];
+    if (NORM) {
+#pragma unroll
+        for (int u = 0; u < HOIST; ++u)
+#pragma unroll
+            for (int j = 0; j < RB; ++j)
+                if (s0 + u < s1)
+                    w0[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
+                                                       ((size_t)(s0 + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
+        norm_prologue<WT, NW>(a, dyn_lds);
+    }
+
+    for (int s = s0; s < s1; s += U) {
         StepIn<WT, RB> in[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_step<WT, RB>(a, rb0, s + u, steps, lane, tok, tok_ok, in[u]);
+        for (int u = 0; u < U; ++u)
+            if (s + u < s1) load_step<WT, RB, NORM>(a, dyn_lds, rb0, s + u, steps, lane, tok, tok_ok, in[u]);
+        if (NORM && s == s0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) mfma_step<WT, RB>(in[u], acc);
-    }
-    for (; s < s1; ++s) {
-        StepIn<WT, RB> in;
-        load_step<WT, RB>(a, rb0, s, steps, lane, tok, tok_ok, in);
-        mfma_step<WT, RB>(in, acc);
+            for (int u = 0; u < HOIST; ++u)
+#pragma unroll
+                for (int j = 0; j < RB; ++j) in[u].w[j] = w0[u][j];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s + u < s1) mfma_step<WT, RB>(in[u], acc);
     }
 
     if (NW > 1) {
@@ -275,6 +368,188 @@ __global__ __launch_bounds__(64 * NW) void linear_small_kernel(LinearArgs a) {
         for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
             for (int j = 0; j < RB; ++j) acc[j] += red[w][j][lane];
+    }
+    if (!tok_ok) return;
+    const int t = t0 + r;
+    if (EPI == EPI_SWIGLU)
+        epilogue4<EPI, false>(a, t, blockIdx.x * 16 + 4 * g, acc[0], acc[RB - 1]);
+    else
+        epilogue4<EPI, false>(a, t, rb0 * 16 + 4 * g, acc[0], acc[0]);
+}
+
+// Few-token product with the activations in LDS (decode).  The work-group
+// first requests its first batch of weight tiles, then copies (NORM:
+// RMS-normalises) its <= 16 activation rows into LDS in the B-operand
+// format, then streams weight tiles through two register buffers so the
+// next batch is in flight while the current one is multiplied; B fragments
+// are read from LDS right before use.  k-steps are split over NW waves and
+// reduced through LDS (aliasing the activation copy).
+template <int WT, int RB, int UB>
+struct WBatch {
+    u32x4_t w[UB][RB];
+    u32x2_t sc[WT == W_Q8 ? UB : 1][RB][2];
+};
+
+template <int WT, int RB, int UB>
+__device__ __forceinline__ void load_wbatch(const LinearArgs &a, int rb0, int s, int s1, int steps, int lane,
+                                            WBatch<WT, RB, UB> &b) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+        if (s + u >= s1) break;
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
+                                                ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
+            if (WT == W_Q8) {
+                const size_t b0 = ((size_t)(rb0 + j) * (a.K / 32) + 2 * (s + u)) * 16 + 4 * g;
+                b.sc[u][j][0] = *(const u32x2_t *)(a.wscale + b0);
+                b.sc[u][j][1] = *(const u32x2_t *)(a.wscale + b0 + 16);
+            }
+        }
+    }
+}
+
+template <int WT, int RB, int UB>
+__device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const unsigned char *lds, int Tb, int K,
+                                           int s, int s1, int lane, int tok, bool tok_ok, f32x4_t *acc) {
+    const int g = lane >> 4;
+    const size_t plane = (size_t)Tb * K;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+        if (s + u >= s1) break;
+        StepIn<WT, RB> in;
+#pragma unroll
+        for (int j = 0; j < RB; ++j) in.w[j] = b.w[u][j];
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        if (WT == W_F32) {
+            const u32x4_t v = *(const u32x4_t *)(lds + ((size_t)tok * K + 16 * (s + u) + 4 * g) * 4);
+            in.xh = tok_ok ? v : z;
+        } else {
+            const size_t o = (size_t)tok * K + (WT == W_BF16 ? 32 : 64) * (s + u) + 8 * g;
+            const uint16_t *hi = (const uint16_t *)lds, *lo = (const uint16_t *)lds + plane;
+            const u32x4_t h0 = *(const u32x4_t *)(hi + o), l0 = *(const u32x4_t *)(lo + o);
+            in.xh = tok_ok ? h0 : z;
+            in.xl = tok_ok ? l0 : z;
+            if (WT == W_Q8) {
+                const u32x4_t h1 = *(const u32x4_t *)(hi + o + 32), l1 = *(const u32x4_t *)(lo + o + 32);
+                in.xh2 = tok_ok ? h1 : z;
+                in.xl2 = tok_ok ? l1 : z;
+#pragma unroll
+                for (int j = 0; j < RB; ++j) {
+                    in.sc[j][0] = b.sc[u][j][0];
+                    in.sc[j][1] = b.sc[u][j][1];
+                }
+            }
+        }
+        mfma_step<WT, RB>(in, acc);
+    }
+}
+
+template <int WT, int NW, bool NORM>
+__device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, int Tb) {
+    constexpr int TH = 64 * NW;
+    __shared__ float red_ss[16][NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K;
+    const size_t plane = (size_t)Tb * K;
+    float inv[16];
+    if (NORM) {
+        for (int t = 0; t < Tb; ++t) {
+            const float *xr = a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[t0 + t] : t0 + t) * a.norm.ld;
+            float ss = 0.f;
+            for (int e = tid * 4; e < K; e += TH * 4) {
+                const f32x4_t v = *(const f32x4_t *)(xr + e);
+                ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+            }
+            ss = wave_sum(ss);
+            if (lane == 0) red_ss[t][wave] = ss;
+        }
+        __syncthreads();
+        for (int t = 0; t < Tb; ++t) {
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) tot += red_ss[t][w];
+            inv[t] = 1.0f / sqrtf(tot / (float)K + a.norm.eps);
+        }
+    }
+    for (int t = 0; t < Tb; ++t) {
+        const float *xr = NORM ? a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[t0 + t] : t0 + t) * a.norm.ld
+                               : nullptr;
+        for (int e = tid * 4; e < K; e += TH * 4) {
+            const size_t o = (size_t)t * K + e;
+            if (NORM) {
+                const f32x4_t y = *(const f32x4_t *)(xr + e) * inv[t] * *(const f32x4_t *)(a.norm.gain + e);
+                if (WT == W_F32) {
+                    *(f32x4_t *)(lds + o * 4) = y;
+                } else {
+                    u16x4_t hh, ll;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        hh[k] = f2bf(y[k]);
+                        ll[k] = f2bf(y[k] - bf2f(hh[k]));
+                    }
+                    *(u16x4_t *)((uint16_t *)lds + o) = hh;
+                    *(u16x4_t *)((uint16_t *)lds + plane + o) = ll;
+                }
+            } else {
+                const size_t src = (size_t)(t0 + t) * a.x.ld + e;
+                if (WT == W_F32) {
+                    *(f32x4_t *)(lds + o * 4) = *(const f32x4_t *)(a.x.f32 + src);
+                } else {
+                    *(u16x4_t *)((uint16_t *)lds + o) = *(const u16x4_t *)(a.x.hi + src);
+                    *(u16x4_t *)((uint16_t *)lds + plane + o) = *(const u16x4_t *)(a.x.lo + src);
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <int WT, int EPI, int NW, bool NORM>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void linear_ldsx_kernel(LinearArgs a) {
+    constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
+    constexpr int KSTEP = WT_<WT>::KSTEP;
+    constexpr int UB = (WT == W_Q8 ? 2 : 8) / RB;
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int rb0 = blockIdx.x * RB;
+    const int t0 = blockIdx.y * 16;
+    const int Tb = min(16, a.T - t0);
+    const bool tok_ok = r < Tb;
+    const int tok = tok_ok ? r : 0;                 // row within the LDS copy
+    const int steps = a.K / KSTEP;
+    const int s0 = wave * steps / NW, s1 = (wave + 1) * steps / NW;
+
+    f32x4_t acc[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    WBatch<WT, RB, UB> bufA, bufB;
+    if (s0 < s1) load_wbatch<WT, RB, UB>(a, rb0, s0, s1, steps, lane, bufA);
+    ldsx_prologue<WT, NW, NORM>(a, dyn_lds, t0, Tb);
+    for (int s = s0; s < s1; s += 2 * UB) {
+        if (s + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s + UB, s1, steps, lane, bufB);
+        mul_wbatch<WT, RB, UB>(bufA, dyn_lds, Tb, a.K, s, s1, lane, tok, tok_ok, acc);
+        if (s + UB >= s1) break;
+        if (s + 2 * UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s + 2 * UB, s1, steps, lane, bufA);
+        mul_wbatch<WT, RB, UB>(bufB, dyn_lds, Tb, a.K, s + UB, s1, lane, tok, tok_ok, acc);
+    }
+
+    if (NW > 1) {
+        __syncthreads();                            // everyone is done with the activation copy
+        f32x4_t *red = (f32x4_t *)dyn_lds;          // [NW-1][RB][64]
+        if (wave > 0) {
+#pragma unroll
+            for (int j = 0; j < RB; ++j) red[((wave - 1) * RB + j) * 64 + lane] = acc[j];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+            for (int j = 0; j < RB; ++j) acc[j] += red[(w * RB + j) * 64 + lane];
     }
     if (!tok_ok) return;
     const int t = t0 + r;
@@ -327,7 +602,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, i
     const int t0 = tt * BT;
     const int nstage = a.K / 64;
     const int st0 = ks * nstage / SPLITK, st1 = (ks + 1) * nstage / SPLITK;
-    const int steps = a.K / (WT == W_BF16 ? 32 : 64);
     const int KB = a.K / 32;
     const u32x4_t z4 = {0u, 0u, 0u, 0u};
 
@@ -359,9 +633,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, i
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         wr[i][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
-                                                           ((size_t)rb * steps + 2 * st + j) * 1024 + lane * 16));
+                                                           ((size_t)(2 * st + j) * nrb + rb) * 1024 + lane * 16));
                 } else {
-                    wr[i][0] = ldg_nt((const u32x4_t *)((const char *)a.w + ((size_t)rb * steps + st) * 1024 +
+                    wr[i][0] = ldg_nt((const u32x4_t *)((const char *)a.w + ((size_t)st * nrb + rb) * 1024 +
                                                        lane * 16));
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
@@ -492,10 +766,45 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
     if (try_gemm<WT, EPI>(a, s)) return;
     dim3 grid(a.N / 16 / RB, (a.T + 15) / 16);
     const long blocks = (long)grid.x * grid.y;
-    if (blocks >= 2048)
-        hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 4>), grid, dim3(256), 0, s, a);
+    // k-split waves per work-group: about 4096 waves in flight, all resident
+    int nw = blocks >= 768 ? 4 : blocks >= 384 ? 8 : 16;
+    if (g_tuning.skinny_nw == 4 || g_tuning.skinny_nw == 8 || g_tuning.skinny_nw == 16) nw = g_tuning.skinny_nw;
+    const bool norm = a.norm.x != nullptr;
+    // activations of a 16-token block fit in LDS: the LDS-staged kernel
+    const size_t ldsx = (size_t)4 * std::min(16, a.T) * a.K;
+    if (ldsx <= LDSX_MAX_BYTES && g_tuning.ldsx != 0) {
+        const size_t bytes = std::max(ldsx, (size_t)16 * 64 * 16 * 2);   // also holds the wave reduction
+#define UBD_LAUNCH_LDSX(NW_)                                                                               \
+    do {                                                                                                   \
+        if (norm)                                                                                          \
+            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, true>), grid, dim3(64 * NW_), bytes, s, a); \
+        else                                                                                               \
+            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), bytes, s, a); \
+    } while (0)
+        if (nw == 4)
+            UBD_LAUNCH_LDSX(4);
+        else if (nw == 8)
+            UBD_LAUNCH_LDSX(8);
+        else
+            UBD_LAUNCH_LDSX(16);
+#undef UBD_LAUNCH_LDSX
+        return;
+    }
+    const size_t lds = norm ? (size_t)4 * a.T * a.K : 0;
+#define UBD_LAUNCH_SMALL(NW_)                                                                            \
+    do {                                                                                                 \
+        if (norm)                                                                                        \
+            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, true>), grid, dim3(64 * NW_), lds, s, a); \
+        else                                                                                             \
+            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), 0, s, a); \
+    } while (0)
+    if (nw == 4)
+        UBD_LAUNCH_SMALL(4);
+    else if (nw == 8)
+        UBD_LAUNCH_SMALL(8);
     else
-        hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 8>), grid, dim3(512), 0, s, a);
+        UBD_LAUNCH_SMALL(16);
+#undef UBD_LAUNCH_SMALL
 }
 
 template <int WT>
@@ -511,6 +820,8 @@ static void launch_linear_wt(const LinearArgs &a, hipStream_t s) {
 
 void launch_linear(const LinearArgs &a, hipStream_t s) {
     if (a.T <= 0 || a.N <= 0) return;
+    if (a.norm.x && a.T > NORM_TMAX) return;   // caller contract: fused norm only for few rows
+    if (a.norm.x && (size_t)4 * a.T * a.K > LDSX_MAX_BYTES) return;
     switch (a.wtype) {
     case W_F32: launch_linear_wt<W_F32>(a, s); break;
     case W_BF16: launch_linear_wt<W_BF16>(a, s); break;
@@ -525,15 +836,20 @@ __global__ __launch_bounds__(256) void embed_kernel(int wtype, const void *table
     const int t = blockIdx.x;
     const size_t row = (size_t)ti.token[t];
     float *xo = x + (size_t)t * d;
-    for (int j = threadIdx.x; j < d; j += blockDim.x) {
-        float v;
-        if (wtype == W_F32)
-            v = ((const float *)table)[row * d + j];
-        else if (wtype == W_BF16)
-            v = bf2f(((const uint16_t *)table)[row * d + j]);
-        else
-            v = (float)((const int8_t *)table)[row * d + j] * h2f(scales[row * (d / 32) + j / 32]);
-        xo[j] = v;
+    for (int e = threadIdx.x * 4; e < d; e += 1024) {      // d is a multiple of 16
+        f32x4_t v;
+        if (wtype == W_F32) {
+            v = *(const f32x4_t *)((const float *)table + row * d + e);
+        } else if (wtype == W_BF16) {
+            const u16x4_t h = *(const u16x4_t *)((const uint16_t *)table + row * d + e);
+            v = f32x4_t{bf2f(h[0]), bf2f(h[1]), bf2f(h[2]), bf2f(h[3])};
+        } else {
+            const uint32_t q = *(const uint32_t *)((const int8_t *)table + row * d + e);
+            const float sc = h2f(scales[row * (d / 32) + e / 32]);
+            v = f32x4_t{(float)(int8_t)q, (float)(int8_t)(q >> 8), (float)(int8_t)(q >> 16),
+                        (float)(int8_t)(q >> 24)} * sc;
+        }
+        *(f32x4_t *)(xo + e) = v;
     }
     if (threadIdx.x == 0) {
         const size_t c = (size_t)ti.stream[t] * n_cells + ti.cell[t];
@@ -550,27 +866,46 @@ void launch_embed(int wtype, const void *table, const uint16_t *scales, int d, c
 }
 
 // -------------------------------------------------------------- RMSNorm
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int ldx, const int32_t *row_map,
                                                       const float *gain, int d, float eps, Act out) {
+    // d is a multiple of 16: every thread handles whole float4s, loads issued
+    // together before the reduction
     const int r = blockIdx.x;
     const int src = row_map ? row_map[r] : r;
     const float *xr = x + (size_t)src * ldx;
+    constexpr int MAXV = 8;                  // float4 per thread held in registers (d <= 8192)
+    f32x4_t v[MAXV];
     float ss = 0.f;
-    for (int j = threadIdx.x; j < d; j += blockDim.x) ss += xr[j] * xr[j];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 4;
+        v[i] = e < d ? *(const f32x4_t *)(xr + e) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    }
+    for (int e = (threadIdx.x + 256 * MAXV) * 4; e < d; e += 1024) {
+        const f32x4_t w = *(const f32x4_t *)(xr + e);
+        ss += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
+    }
     __shared__ float part[4];
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float tot = part[0] + part[1] + part[2] + part[3];
-    const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-    for (int j = threadIdx.x; j < d; j += blockDim.x)
-        store_act(out, (size_t)r * out.ld + j, xr[j] * inv * gain[j]);
+    const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+    const size_t ob = (size_t)r * out.ld;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 4;
+        if (e < d) {
+            const f32x4_t y = v[i] * inv * *(const f32x4_t *)(gain + e);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) store_act(out, ob + e + k, y[k]);
+        }
+    }
+    for (int e = (threadIdx.x + 256 * MAXV) * 4; e < d; e += 1024) {
+        const f32x4_t y = *(const f32x4_t *)(xr + e) * inv * *(const f32x4_t *)(gain + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) store_act(out, ob + e + k, y[k]);
+    }
 }
 
 void launch_rmsnorm(const float *x, int ldx, const int32_t *row_map, int rows, const float *gain, int d,
@@ -770,7 +1105,7 @@ void launch_attention(const AttnArgs &a, hipStream_t s) {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
-template <int HD, bool SPLIT, int NC>
+template <int HD, bool SPLIT>
 __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     constexpr int KK = HD / 32, DB = HD / 16;
     const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
@@ -779,6 +1114,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     const int st = a.tok.tiles[blk * 4 + 2], nscan = a.tok.tiles[blk * 4 + 3];
     const int G = a.n_head / a.n_head_kv;
     const int R = nt * G;
+    const int NC = a.chunk_cells;
     int cbeg = 0, cend = nscan;
     if (SPLIT) {
         cbeg = chunk * NC;
@@ -812,21 +1148,36 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) O[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int c0 = cbeg; c0 < cend; c0 += 32) {
-        f32x4_t S[2];
+        // issue every load of the 32-cell step first
+        f16x8_t Ka[2][KK];
+        f16x4_t Va[DB][2];
+        int4 p4[2], s4[2];
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
             const int cb = c0 + 16 * b2;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) Ka[b2][kk] = *(const f16x8_t *)(K + (size_t)(cb + r) * HD + 32 * kk + 8 * g);
+            p4[b2] = *(const int4 *)(cpos + cb + 4 * g);
+            s4[b2] = *(const int4 *)(cseq + cb + 4 * g);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const _Float16 *vrow = Vt + (size_t)(16 * db + r) * a.n_cells;
+            Va[db][0] = *(const f16x4_t *)(vrow + c0 + 4 * g);
+            Va[db][1] = *(const f16x4_t *)(vrow + c0 + 16 + 4 * g);
+        }
+        f32x4_t S[2];
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const f16x8_t A = *(const f16x8_t *)(K + (size_t)(cb + r) * HD + 32 * kk + 8 * g);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh[kk], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ka[b2][kk], qh[kk], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ka[b2][kk], ql[kk], acc, 0, 0, 0);
             }
-            const int cc = cb + 4 * g;
-            const int4 p4 = *(const int4 *)(cpos + cc);
-            const int4 s4 = *(const int4 *)(cseq + cc);
-            const int pp[4] = {p4.x, p4.y, p4.z, p4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+            const int cc = c0 + 16 * b2 + 4 * g;
+            const int pp[4] = {p4[b2].x, p4[b2].y, p4[b2].z, p4[b2].w};
+            const int ss[4] = {s4[b2].x, s4[b2].y, s4[b2].z, s4[b2].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool vis = row_ok && cc + i < cend && ss[i] == rseq && pp[i] >= 0 && pp[i] <= rpos;
@@ -863,10 +1214,8 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const _Float16 *vrow = Vt + (size_t)(16 * db + r) * a.n_cells;
-            const f16x4_t v0 = *(const f16x4_t *)(vrow + c0 + 4 * g);
-            const f16x4_t v1 = *(const f16x4_t *)(vrow + c0 + 16 + 4 * g);
-            const f16x8_t B = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            const f16x8_t B = {Va[db][0][0], Va[db][0][1], Va[db][0][2], Va[db][0][3],
+                               Va[db][1][0], Va[db][1][1], Va[db][1][2], Va[db][1][3]};
             f32x4_t o = O[db] * al;
             o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, B, o, 0, 0, 0);
             o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, o, 0, 0, 0);
@@ -874,15 +1223,26 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         }
     }
     // O: lane (dim r of each 16-dim block, group g) holds rows 4g+i
-    f32x4_t lrow;
+    if (!SPLIT) {
+        f32x4_t lrow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l, 4 * g + i, 64);
-    if (SPLIT) {
-        if (g == 0 && row_ok) {
-            float *ml = a.part_ml + (((size_t)rt * a.n_head + rh) * a.max_chunks + chunk) * 2;
-            ml[0] = m;
-            ml[1] = l;
+        for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l, 4 * g + i, 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * g + i;
+            if (row >= R) continue;
+            const int t = t0 + row / G, h = grp * G + row % G;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                store_act(a.out, (size_t)t * a.out.ld + h * HD + 16 * db + r, lrow[i] > 0.f ? O[db][i] / lrow[i] : 0.f);
         }
+        return;
+    }
+    // split: publish this chunk's (m, l, O) for the combine pass
+    if (g == 0 && row_ok) {
+        float *ml = a.part_ml + (((size_t)rt * a.n_head + rh) * a.max_chunks + chunk) * 2;
+        ml[0] = m;
+        ml[1] = l;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -890,48 +1250,75 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         if (row >= R) continue;
         const int t = t0 + row / G, h = grp * G + row % G;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int d = 16 * db + r;
-            if (SPLIT)
-                a.part_o[(((size_t)t * a.n_head + h) * a.max_chunks + chunk) * HD + d] = O[db][i];
-            else
-                store_act(a.out, (size_t)t * a.out.ld + h * HD + d, lrow[i] > 0.f ? O[db][i] / lrow[i] : 0.f);
-        }
+        for (int db = 0; db < DB; ++db)
+            a.part_o[(((size_t)t * a.n_head + h) * a.max_chunks + chunk) * HD + 16 * db + r] = O[db][i];
     }
 }
 
-template <int HD, int NC>
-__global__ __launch_bounds__(128) void attn_combine_nc_kernel(AttnArgs a) {
+// Merge the chunks of one (token, head): weights exp(m_c - M) computed
+// lane-parallel over chunks, then every dim sums its chunks with the loads
+// of a 64-chunk pass issued together.
+template <int HD>
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
     const int t = blockIdx.x / a.n_head, h = blockIdx.x % a.n_head;
-    const int tile = a.tok.tile_of[t];
-    const int nscan = a.tok.tiles[tile * 4 + 3];
-    const int nch = (nscan + NC - 1) / NC;
+    const int lane = threadIdx.x;
+    const int nscan = a.tok.tiles[a.tok.tile_of[t] * 4 + 3];
+    const int nch = (nscan + a.chunk_cells - 1) / a.chunk_cells;
     const float *ml = a.part_ml + ((size_t)t * a.n_head + h) * a.max_chunks * 2;
+    const float *po = a.part_o + ((size_t)t * a.n_head + h) * a.max_chunks * HD;
     float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * c]);
+    for (int c = lane; c < nch; c += 64) M = fmaxf(M, ml[2 * c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float L = 0.f;
-    for (int c = 0; c < nch; ++c)
-        if (ml[2 * c] != -INFINITY) L += ml[2 * c + 1] * expf(ml[2 * c] - M);
+    constexpr int DPL = (HD + 63) / 64;
+    float o[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[j] = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        float wgt = 0.f;
+        if (c < nch) {
+            const float mc = ml[2 * c];
+            wgt = mc == -INFINITY ? 0.f : expf(mc - M);
+            L += wgt * ml[2 * c + 1];
+        }
+        const int n = min(64, nch - c0);
+        for (int k = 0; k < n; k += 8) {
+            float w8[8], v8[8][DPL];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                w8[u] = __shfl(wgt, min(k + u, 63), 64);
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) {
+                    const int d = lane + 64 * j;
+                    v8[u][j] = (k + u < n && d < HD) ? po[(size_t)(c0 + k + u) * HD + d] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) o[j] += (k + u < n) ? w8[u] * v8[u][j] : 0.f;
+        }
+    }
+    L = wave_sum(L);
     const float invL = L > 0.f ? 1.0f / L : 0.f;
-    for (int d = threadIdx.x; d < HD; d += blockDim.x) {
-        float o = 0.f;
-        for (int c = 0; c < nch; ++c)
-            if (ml[2 * c] != -INFINITY)
-                o += a.part_o[(((size_t)t * a.n_head + h) * a.max_chunks + c) * HD + d] * expf(ml[2 * c] - M);
-        store_act(a.out, (size_t)t * a.out.ld + h * HD + d, o * invL);
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+        const int d = lane + 64 * j;
+        if (d < HD) store_act(a.out, (size_t)t * a.out.ld + h * HD + d, o[j] * invL);
     }
 }
 
 template <int HD>
 static void launch_attention_mfma_hd(const AttnArgs &a, hipStream_t s) {
     if (a.split) {
-        dim3 grid(a.max_chunks, a.n_tiles, a.n_head_kv);
-        hipLaunchKernelGGL((attn_mfma_kernel<HD, true, ATTN_DECODE_CHUNK>), grid, dim3(64), 0, s, a);
-        hipLaunchKernelGGL((attn_combine_nc_kernel<HD, ATTN_DECODE_CHUNK>), dim3(a.T * a.n_head), dim3(128), 0, s,
-                           a);
+        dim3 grid((unsigned)a.n_chunks_launch, a.n_tiles, a.n_head_kv);
+        hipLaunchKernelGGL((attn_mfma_kernel<HD, true>), grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(a.T * a.n_head), dim3(64), 0, s, a);
     } else {
         dim3 grid(1, a.n_tiles, a.n_head_kv);
-        hipLaunchKernelGGL((attn_mfma_kernel<HD, false, ATTN_DECODE_CHUNK>), grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL((attn_mfma_kernel<HD, false>), grid, dim3(64), 0, s, a);
     }
 }
 
@@ -952,49 +1339,76 @@ void launch_attention_mfma(const AttnArgs &a, hipStream_t s) {
 int attn_tile_rows(int head_dim) { return head_dim >= 128 ? AttnCfg<128>::ROWS : AttnCfg<64>::ROWS; }
 
 // --------------------------------------------------------------- argmax
-__global__ __launch_bounds__(1024) void argmax_kernel(const float *logits, int ld, const int32_t *rows,
-                                                      int n, int32_t *out) {
-    const int r = blockIdx.x;
-    const float *z = logits + (size_t)(rows ? rows[r] : r) * ld;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const float v = z[i];
-        if (v > bv || (v == bv && i < bi)) {
-            bv = v;
-            bi = i;
-        }
+// ARGMAX_BLOCKS work-groups per row each reduce a slice; the last one to
+// finish (counted with an atomic) reduces the slices' winners and re-arms
+// the counter.  Ties go to the lowest index.
+__device__ __forceinline__ void better(float &bv, int &bi, float v, int i) {
+    if (v > bv || (v == bv && i < bi)) {
+        bv = v;
+        bi = i;
     }
+}
+
+__device__ __forceinline__ void block_best(float &bv, int &bi) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(bv, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-            bv = ov;
-            bi = oi;
-        }
+        better(bv, bi, ov, oi);
     }
-    __shared__ float sv[16];
-    __shared__ int si[16];
+    __shared__ float sv[4];
+    __shared__ int si[4];
     if ((threadIdx.x & 63) == 0) {
         sv[threadIdx.x >> 6] = bv;
         si[threadIdx.x >> 6] = bi;
     }
     __syncthreads();
+    bv = sv[0];
+    bi = si[0];
+    for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
+}
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int ld, const int32_t *rows, int n,
+                                                     int32_t *out, float *pv, int32_t *pi, int32_t *counter) {
+    const int row = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
+    const float *z = logits + (size_t)(rows ? rows[row] : row) * ld;
+    const int chunk = ((n + nb - 1) / nb + 3) & ~3;
+    const int beg = b * chunk, end = min(n, beg + chunk);
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = beg + threadIdx.x * 4; i < end; i += 1024) {     // n is a multiple of 16
+        const f32x4_t v = *(const f32x4_t *)(z + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) better(bv, bi, v[k], i + k);
+    }
+    block_best(bv, bi);
+    __shared__ int last;
     if (threadIdx.x == 0) {
-        for (int w = 1; w < (int)(blockDim.x >> 6); ++w)
-            if (sv[w] > bv || (sv[w] == bv && si[w] < bi)) {
-                bv = sv[w];
-                bi = si[w];
-            }
-        out[r] = bi == 0x7fffffff ? 0 : bi;
+        pv[row * nb + b] = bv;
+        pi[row * nb + b] = bi;
+        __threadfence();
+        last = atomicAdd(counter + row, 1) == nb - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    bv = -INFINITY;
+    bi = 0x7fffffff;
+    for (int k = threadIdx.x; k < nb; k += blockDim.x)
+        better(bv, bi, __hip_atomic_load(pv + row * nb + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+               __hip_atomic_load(pi + row * nb + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    block_best(bv, bi);
+    if (threadIdx.x == 0) {
+        out[row] = bi == 0x7fffffff ? 0 : bi;
+        counter[row] = 0;
     }
 }
 
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows, int n, int32_t *out,
-                   hipStream_t s) {
+                   const ArgmaxWork &w, hipStream_t s) {
     if (n_rows <= 0) return;
-    hipLaunchKernelGGL(argmax_kernel, dim3(n_rows), dim3(1024), 0, s, logits, ld, rows, n, out);
+    hipLaunchKernelGGL(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld, rows, n, out, w.pv,
+                       w.pi, w.counter);
 }
 
 // ------------------------------------------------------------- relayout
@@ -1029,9 +1443,10 @@ __global__ __launch_bounds__(256) void relayout_kernel(RelayoutArgs a) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t total = (size_t)(a.N / 16) * a.steps * 64;
     if (idx >= total) return;
-    const size_t tile = idx >> 6;
+    const size_t tile = idx >> 6;                   // k-step-major: tile = s * (N/16) + rb
     const int lane = (int)(idx & 63);
-    const int rb = (int)(tile / a.steps), s = (int)(tile % a.steps);
+    const int NB = a.N / 16;
+    const int rb = (int)(tile % NB), s = (int)(tile / NB);
     const int r = lane & 15, g = lane >> 4;
     int si, sr;
     map_row(a, rb * 16 + r, &si, &sr);

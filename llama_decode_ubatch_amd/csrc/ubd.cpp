@@ -382,6 +382,7 @@ struct ubd_context : public Executor {
     std::vector<float> logits_host;
     bool logits_host_valid = false;
     int32_t *argmax_dev = nullptr;
+    ArgmaxWork argmax_work;
     std::vector<int32_t> last_ub_idx;
     float *dump = nullptr;
     ubd_perf perf{};
@@ -547,13 +548,22 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
                                           : (size_t)cap * H * c->max_chunks;
     c->part_o = (float *)c->mem.get(part_rows * hd * 4);
     c->part_ml = (float *)c->mem.get(part_rows * 2 * 4);
+
     if (!c->part_o || !c->part_ml) return bail("attention scratch allocation failed");
     std::vector<double> inv(hd / 2);
     for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)hp.rope_freq_base, -2.0 * i / hd);
     c->inv_freq = (double *)c->mem.get(inv.size() * sizeof(double));
     c->info_dev = (int32_t *)c->mem.get(c->info_ints() * 4);
     c->argmax_dev = (int32_t *)c->mem.get((size_t)std::max<uint32_t>(P.n_batch, 1) * 4);
-    if (!c->inv_freq || !c->info_dev || !c->argmax_dev) return bail("allocation failed");
+    const size_t amax_rows = std::max<uint32_t>(P.n_batch, 1);
+    c->argmax_work.pv = (float *)c->mem.get(amax_rows * ARGMAX_BLOCKS * 4);
+    c->argmax_work.pi = (int32_t *)c->mem.get(amax_rows * ARGMAX_BLOCKS * 4);
+    c->argmax_work.counter = (int32_t *)c->mem.get(amax_rows * 4);
+    if (!c->inv_freq || !c->info_dev || !c->argmax_dev || !c->argmax_work.pv || !c->argmax_work.pi ||
+        !c->argmax_work.counter)
+        return bail("allocation failed");
+    if (!hip_ok(hipMemsetAsync(c->argmax_work.counter, 0, amax_rows * 4, c->stream), "memset"))
+        return bail("counter init failed");
     if (!hip_ok(hipMemcpyAsync(c->inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice,
                                c->stream), "upload"))
         return bail("upload failed");
@@ -654,6 +664,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         }
     }
     const bool split = T <= 16;
+    int max_scan = 0;
     const int qt = mfma_attn ? std::max(1, 16 / G) : std::max(1, attn_tile_rows(hd) / G);
     int n_tiles = 0;
     for (int t = 0; t < T;) {
@@ -677,6 +688,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
             tl[3] = c + 1;
         }
         for (int j = t; j < e; ++j) h[6 * cap + j] = n_tiles;
+        max_scan = std::max(max_scan, (int)tl[3]);
         ++n_tiles;
         t = e;
     }
@@ -694,7 +706,10 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     const size_t kb = type_k == KV_F32 ? 4 : 2, vb = type_v == KV_F32 ? 4 : 2;
     for (int il = 0; il < hp.n_layer; ++il) {
         const auto &L = M.layers[il];
-        timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, actA, stream); });
+        const bool fuse_norm = T <= NORM_TMAX && g_tuning.fuse_norm != 0;
+        const bool fuse_norm_ffn = fuse_norm && g_tuning.fuse_norm == 1;
+        if (!fuse_norm)
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, actA, stream); });
 
         LinearArgs la;
         la.wtype = M.wtype;
@@ -718,6 +733,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         la.qkv.v_cache = (char *)v_cache + kv_layer_elems * il * vb;
         la.qkv.type_k = type_k;
         la.qkv.type_v = type_v;
+        if (fuse_norm) la.norm = NormIn{x, nullptr, L.attn_norm, hp.rms_eps, d};
         timed(4 + ph, [&] { launch_linear(la, stream); });
 
         AttnArgs aa;
@@ -741,6 +757,11 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         if (mfma_attn) {
             aa.split = split;
             aa.max_chunks = max_chunks_mfma;
+            // about 32 chunks per (tile, KV head), at least 32 cells each
+            const int want = (max_scan + 31) / 32;
+            const int cmin = std::max(ATTN_DECODE_CHUNK, g_tuning.attn_chunk_min / 32 * 32);
+            aa.chunk_cells = std::max(cmin, (want + 31) / 32 * 32);
+            aa.n_chunks_launch = std::max(1, (max_scan + aa.chunk_cells - 1) / aa.chunk_cells);
             timed(6 + ph, [&] { launch_attention_mfma(aa, stream); });
         } else {
             aa.max_chunks = max_chunks;
@@ -761,7 +782,8 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lo.ldy = d;
         timed(8 + ph, [&] { launch_linear(lo, stream); });
 
-        timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, actA, stream); });
+        if (!fuse_norm_ffn)
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, actA, stream); });
         LinearArgs lg = lo;
         lg.w = L.gu.w;
         lg.wscale = L.gu.scales;
@@ -770,9 +792,11 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lg.x = actA;
         lg.epi = EPI_SWIGLU;
         lg.out = actC;
+        if (fuse_norm_ffn) lg.norm = NormIn{x, nullptr, L.ffn_norm, hp.rms_eps, d};
         timed(10 + ph, [&] { launch_linear(lg, stream); });
 
         LinearArgs ld = lo;
+        ld.norm = NormIn{};
         ld.w = L.down.w;
         ld.wscale = L.down.scales;
         ld.N = L.down.rows;
@@ -784,7 +808,9 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
                                   stream), "dump");
     }
     if (n_out > 0) {
-        timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, actA, stream); });
+        const bool fuse_norm = n_out <= NORM_TMAX && g_tuning.fuse_norm == 1;
+        if (!fuse_norm)
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, actA, stream); });
         LinearArgs lz;
         lz.wtype = M.wtype;
         lz.w = M.out.w;
@@ -796,6 +822,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lz.epi = EPI_LOGITS;
         lz.row_map = out_lrow();
         lz.logits = logits_dev;
+        if (fuse_norm) lz.norm = NormIn{x, ti.out_tok, M.out_norm, hp.rms_eps, d};
         timed(14 + ph, [&] { launch_linear(lz, stream); });
     }
     if (!hip_ok(hipGetLastError(), "kernel launch")) return UBD_COMPUTE_FAILED;
@@ -882,7 +909,7 @@ extern "C" ubd_token ubd_sample_greedy(ubd_context *ctx, int32_t i) {
     if (r < 0) return -1;
     (void)hipSetDevice(ctx->model->device);
     const int V = ctx->model->hp.n_vocab;
-    launch_argmax(ctx->logits_dev + (size_t)r * V, V, nullptr, 1, V, ctx->argmax_dev, ctx->stream);
+    launch_argmax(ctx->logits_dev + (size_t)r * V, V, nullptr, 1, V, ctx->argmax_dev, ctx->argmax_work, ctx->stream);
     int32_t out = -1;
     if (!hip_ok(hipMemcpyAsync(&out, ctx->argmax_dev, 4, hipMemcpyDeviceToHost, ctx->stream), "argmax") ||
         !hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync"))
@@ -898,7 +925,7 @@ extern "C" int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32
     if (P.n_outputs == 0) return 0;
     (void)hipSetDevice(ctx->model->device);
     const int V = ctx->model->hp.n_vocab;
-    launch_argmax(ctx->logits_dev, V, nullptr, P.n_outputs, V, ctx->argmax_dev, ctx->stream);
+    launch_argmax(ctx->logits_dev, V, nullptr, P.n_outputs, V, ctx->argmax_dev, ctx->argmax_work, ctx->stream);
     if (!hip_ok(hipMemcpyAsync(out, ctx->argmax_dev, (size_t)P.n_outputs * 4, hipMemcpyDeviceToHost, ctx->stream),
                 "argmax") ||
         !hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync"))
@@ -1074,6 +1101,23 @@ extern "C" void ubd_perf_get(const ubd_context *ctx, ubd_perf *out) {
 
 extern "C" void ubd_perf_reset(ubd_context *ctx) {
     if (ctx) ctx->perf = ubd_perf{};
+}
+
+extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
+    if (!key) return UBD_INVALID;
+    const std::string k(key);
+    if (k == "skinny_nw") {
+        g_tuning.skinny_nw = value;
+    } else if (k == "fuse_norm") {
+        g_tuning.fuse_norm = value;
+    } else if (k == "attn_chunk_min") {
+        g_tuning.attn_chunk_min = value;
+    } else if (k == "ldsx") {
+        g_tuning.ldsx = value;
+    } else {
+        return UBD_INVALID;
+    }
+    return UBD_OK;
 }
 
 extern "C" void ubd_log_set(ubd_log_fn fn, void *user_data) {
