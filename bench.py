@@ -21,6 +21,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_ffn_gate_up_8b_bf16_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "llama_decode_ubatch_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode gate|up product from the committed
+    rocprofv3 counter summary, if kernels.hip is unchanged since then."""
+    import hashlib
+    try:
+        lines = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l)
+        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+        if lines.get("kernels_hip_sha256_16", "").strip() != src_hash:
+            return None
+        return int(float(lines["hbm_bytes_per_launch"].strip()))
+    except Exception:
+        return None
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
@@ -31,7 +47,11 @@ def log(*a):
 def run_job(ctx, w, prompt, first_tokens=None):
     """One pass of the workload.  Returns (t_prefill_s, t_decode_s, ids)."""
     import numpy as np
-    ctx.seq_rm(-1, -1, -1)
+    if w.kv_prefill:
+        for s in range(w.n_seqs):          # back to the pre-filled state
+            ctx.seq_rm(s, w.kv_prefill, -1)
+    else:
+        ctx.seq_rm(-1, -1, -1)
     ids = []
     t0 = time.perf_counter()
     if w.n_prompt:
@@ -53,6 +73,24 @@ def run_job(ctx, w, prompt, first_tokens=None):
     return t1 - t0, t2 - t1, ids
 
 
+def fill_kv(torch, ctx, w):
+    """Pre-fill every sequence's KV stream with the seeded f16 values,
+    generated on the device, before any timing."""
+    import numpy as np
+    from workloads import device as wdev
+    P, L, ne = w.kv_prefill, w.model.n_layer, w.model.n_embd_kv
+    t0 = time.perf_counter()
+    for s in range(w.n_seqs):
+        kv = [[wdev.fill_kv_block(torch, w, s, il, which,
+                                  torch.empty((P, ne), dtype=torch.int16, device="cuda:0"))
+               for il in range(L)] for which in (0, 1)]
+        torch.cuda.synchronize()
+        assert ctx.kv_fill(s, P, kv[0], kv[1], "f16") == 0
+        del kv
+    torch.cuda.empty_cache()
+    log(f"KV pre-filled: {w.n_seqs} x {P} positions in {time.perf_counter() - t0:.1f}s")
+
+
 def cpu_baseline(w, sample_layers=2, n_prefill=32, n_decode=2):
     """The oracle as it stands on a bounded sample of the same job: a
     `sample_layers`-layer model of the same shape (its own seeded weights),
@@ -70,7 +108,7 @@ def cpu_baseline(w, sample_layers=2, n_prefill=32, n_decode=2):
     shape = dataclasses.replace(w.model, n_layer=sample_layers)
     om = OracleModel(shape, lambda name: gen_tensor(shape, name), dtype=np.float32, cache=True,
                      rows_fn=lambda name, rows: gen_tensor_rows(shape, name, rows))
-    ctx = OracleContext(om, w.n_ctx, w.n_batch, w.n_ubatch, 1, w.type_k, w.type_v)
+    ctx = OracleContext(om, w.n_ctx, w.n_batch, w.n_ubatch, w.n_seq_max, w.type_k, w.type_v)
     # generate and upcast every weight before timing
     for il in range(sample_layers):
         for t in ("attn_norm", "attn_q", "attn_k", "attn_v", "attn_output", "ffn_norm",
@@ -78,6 +116,9 @@ def cpu_baseline(w, sample_layers=2, n_prefill=32, n_decode=2):
             om.w(f"blk.{il}.{t}.weight")
     om.w("output_norm.weight")
     om.w("output.weight")
+    L = w.model.n_layer
+    if w.kv_prefill:
+        return _cpu_baseline_prefilled(w, om, ctx, shape, sample_layers, n_decode, blas_threads)
     prompt = prompt_tokens(w, 0)[:n_prefill]
     h = np.zeros((1, shape.n_embd), np.float32)
     t0 = time.perf_counter()
@@ -92,7 +133,6 @@ def cpu_baseline(w, sample_layers=2, n_prefill=32, n_decode=2):
         assert ctx.decode(Batch([tok])) == 0
         tok = ctx.greedy(-1)
     t_tg = (time.perf_counter() - t0) / n_decode
-    L = w.model.n_layer
     pp_full = (t_pp - t_head) * L / sample_layers + t_head
     tg_full = (t_tg - t_head) * L / sample_layers + t_head
     job_s = pp_full * w.n_prompt / n_prefill + tg_full * w.n_decode
@@ -110,6 +150,41 @@ def cpu_baseline(w, sample_layers=2, n_prefill=32, n_decode=2):
     }
 
 
+def _cpu_baseline_prefilled(w, om, ctx, shape, sample_layers, n_decode, blas_threads):
+    """Pre-filled KV workload: the sample model's layers hold every
+    sequence's pre-filled KV; n_decode steps of one token per sequence."""
+    import numpy as np
+    from oracle import Batch
+    from workloads import kv_prefill_block, prompt_tokens
+    for s in range(w.n_seqs):
+        K = [kv_prefill_block(w, s, il, 0).view(np.float16) for il in range(sample_layers)]
+        V = [kv_prefill_block(w, s, il, 1).view(np.float16) for il in range(sample_layers)]
+        assert ctx.kv_fill(s, w.kv_prefill, K, V)
+    seqs = np.arange(w.n_seqs)
+    tok = np.array([prompt_tokens(w, s, 1)[0] for s in seqs])
+    t0 = time.perf_counter()
+    ctx.head(np.zeros((w.n_seqs, shape.n_embd), np.float32))
+    t_head = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _ in range(n_decode):
+        assert ctx.decode(Batch(tok, seq_id=seqs, logits=np.ones(w.n_seqs, np.int8))) == 0
+        tok = np.array([int(np.argmax(ctx.logits_ith(i))) for i in range(w.n_seqs)])
+    t_tg = (time.perf_counter() - t0) / n_decode
+    L = w.model.n_layer
+    step_full = (t_tg - t_head) * L / sample_layers + t_head
+    return {
+        "value": w.n_seqs / step_full,
+        "unit": "tokens/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "decode_tok_s": w.n_seqs / step_full,
+        "sample": (f"oracle (NumPy float32) on a {sample_layers}-layer model of the same shape with "
+                   f"{w.n_seqs} sequences x {w.kv_prefill} pre-filled f16 KV positions: {n_decode} "
+                   f"decode steps of {w.n_seqs} tokens, layer time x{L}/{sample_layers} plus the output head"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +192,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first copy 256 MiB device-to-device (reference dispatch for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -131,6 +208,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = WORKLOADS[args.config]
     shape = w.model
     t0 = time.perf_counter()
@@ -147,19 +230,26 @@ def main():
     ctx = Context(model, n_ctx=w.n_ctx, n_batch=w.n_batch, n_ubatch=w.n_ubatch, n_seq_max=w.n_seq_max,
                   type_k=w.type_k, type_v=w.type_v, kv_unified=w.kv_unified)
     prompt = prompt_tokens(w, 0) if w.n_prompt else None
+    first = None
+    if w.kv_prefill:
+        fill_kv(torch, ctx, w)
+        first = np.array([prompt_tokens(w, s, 1)[0] for s in range(w.n_seqs)], np.int32)
+    # the kernel whose roofline is reported: the FFN gate|up matvec when the
+    # weights dominate, the attention when the KV cache does
+    hot = "decode.attention" if w.kv_prefill else "decode.ffn_gate_up"
 
     for i in range(args.warmup):
-        tp, td, _ = run_job(ctx, w, prompt)
+        tp, td, _ = run_job(ctx, w, prompt, first)
         log(f"warmup {i}: prefill {tp * 1e3:.1f} ms, decode {td * 1e3:.1f} ms")
 
     # HIP events only around the two roofline kernels inside the timed region
-    ctx.kernel_timing(["decode.ffn_gate_up", "prefill.ffn_gate_up"])
+    ctx.kernel_timing([hot, "prefill.ffn_gate_up"])
     ctx.kernel_stats()                   # reset
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     tp_sum = td_sum = 0.0
     for i in range(args.steps):
-        tp, td, ids = run_job(ctx, w, prompt)
+        tp, td, ids = run_job(ctx, w, prompt, first)
         tp_sum += tp
         td_sum += td
         log(f"step {i}: prefill {tp * 1e3:.1f} ms, decode {td * 1e3:.1f} ms")
@@ -168,7 +258,7 @@ def main():
     stats = ctx.kernel_stats()
     # per-class breakdown from one more (untimed) job with events on every class
     ctx.kernel_timing(None)
-    run_job(ctx, w, prompt)
+    run_job(ctx, w, prompt, first)
     breakdown = ctx.kernel_stats()
     ctx.kernel_timing([])
 
@@ -186,13 +276,25 @@ def main():
         log(f"  {k:22s} {v['launches']:6d} launches  avg {v['avg_us']:9.2f} us  "
             f"total {v['avg_us'] * v['launches'] / 1e3:9.2f} ms")
     roofline = None
-    if "decode.ffn_gate_up" in kernels:
+    if hot == "decode.attention" and hot in kernels:
+        # every launch reads each sequence's K and V rows (f16) once; the
+        # cache grows by one cell per sequence per step
+        kvb = 2 if w.type_k == "f16" else 4
+        cells = w.n_seqs * (w.kv_prefill + (w.n_decode + 1) / 2.0)
+        alg = 2 * cells * shape.n_embd_kv * kvb + 2 * w.n_seqs * d * 4
+        avg_s = kernels[hot]["avg_us"] * 1e-6
+        ach = alg / avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "decode.attention (attn_mfma_kernel split-K + attn_merge_kernel)",
+                    "bytes_per_launch": int(alg)}
+    elif "decode.ffn_gate_up" in kernels:
         T = w.n_seqs
         alg = 2 * F * d * wbytes + T * d * 4 + T * F * 4     # weights + input + output
         avg_s = kernels["decode.ffn_gate_up"]["avg_us"] * 1e-6
         ach = alg / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                     "kernel": "decode.ffn_gate_up (linear_small_kernel, SwiGLU epilogue)",
                     "bytes_per_launch": int(alg)}
     roofline_prefill = None

@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 
 from oracle import OracleModel, OracleContext, Batch
-from oracle.planner import plan_batch
 from workloads import WORKLOADS, gen_tensor, gen_tensor_rows, prompt_tokens
+from tests.helpers import oracle_layer_check
 
 pytestmark = pytest.mark.gpu
 TOL = 3e-2
@@ -36,22 +36,7 @@ def build(cfg):
 
 
 def oracle_layer(om, w, il, x_in, tokens, pos0, kv_prefix=None):
-    """Oracle layer il on the GPU's input residual for one sequence's tokens
-    at positions pos0..; kv_prefix = (K, V) f32 rows of positions < pos0."""
-    ref = OracleContext(om, w.n_ctx, w.n_batch, w.n_ubatch, 1, w.type_k, w.type_v)
-    if pos0:
-        K, V = kv_prefix
-        zeros = [np.zeros_like(K)] * w.model.n_layer
-        ks, vs = list(zeros), list(zeros)
-        ks[il], vs[il] = K, V
-        assert ref.kv_fill(0, pos0, ks, vs)
-    plan = plan_batch(Batch(tokens), ref.mem, w.model.n_vocab, 1, ref.n_batch, len(tokens))
-    ub, cells = plan.ubatches[0], plan.cells[0]
-    ref.mem.apply(ub, cells)
-    y = ref.layer_forward(il, x_in.astype(np.float32), ub, cells)
-    for k in [k for k in om._cache if k.startswith("blk.")]:   # keep only the head cached
-        del om._cache[k]
-    return y, ref
+    return oracle_layer_check(om, w, il, x_in, tokens, pos0, kv_prefix)
 
 
 @pytest.mark.parametrize("cfg", [3, 5])
