@@ -16,8 +16,11 @@
 //    Tiles are stored k-step-major: tile (rb, s) starts at byte
 //    (s * rows/16 + rb) * 1024, so that the work-groups of a product, which
 //    advance through k together, read one contiguous window of memory.
-//  * KV cache per layer: K [stream][kv head][cell][head_dim] and V
-//    transposed [stream][kv head][head_dim][cell], each of type_k / type_v.
+//  * KV cache per layer: K [stream][kv head][cell][head_dim] and V in
+//    32-cell tiles [stream][kv head][cell / 32][head_dim][32], each of
+//    type_k / type_v.  n_cells given to the kernels is the per-stream cell
+//    stride, the context's cells per stream rounded up to 32; the device
+//    cell tables [stream][n_cells] hold pos = seq = -1 in the padding.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -139,7 +142,7 @@ int attn_tile_rows(int head_dim);
 // chunks, one wave each, merged by a combine pass; otherwise one wave scans
 // tiles[3] cells.  Partials are indexed with max_chunks = ceil(n_cells /
 // ATTN_DECODE_CHUNK).
-bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa, int n_cells);
+bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa);
 void launch_attention_mfma(const AttnArgs &a, hipStream_t s);
 
 // out[r] = argmax over n of logits[row(r)][n] (lowest index on ties).
@@ -166,7 +169,7 @@ void launch_relayout(int wtype, const RelayoutSrc *src, int n_src, int mode,
                      int K, void *dst, uint16_t *dst_scales, hipStream_t s);
 
 // KV rows [n][n_head_kv*hd] of src_type (KV_F32 / KV_F16) into the cache
-// cells cells[0..n) of one stream (K natural, V transposed).
+// cells cells[0..n) of one stream (K rows, V in 32-cell tiles).
 void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
                      void *cache, int type, bool transposed, int stream,
                      int n_head_kv, int hd, int n_cells, hipStream_t s);

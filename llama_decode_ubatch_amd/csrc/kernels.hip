@@ -181,6 +181,17 @@ __device__ __forceinline__ void store4(float *p, f32x4_t v) { *(f32x4_t *)p = v;
 // Epilogue of one MFMA output fragment: token t and four consecutive output
 // rows n..n+3 (for SWIGLU: gate values v, up values u, output columns
 // n..n+3).  ATOMIC accumulates a split-K partial into the residual.
+// V cache element (cell c, dim d) inside one (stream, KV head) block of
+// n_cells * hd elements: 32-cell tiles [c / 32][hd][32 slots], so a 32-cell
+// step of attention reads one contiguous hd * 32 run.  Inside a tile, cell
+// j sits in slot 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3): the eight
+// cells {4g..4g+3, 16+4g..16+4g+3} that one lane of the P*V product needs
+// (see attn_mfma_kernel) are one 16-byte run.
+__device__ __forceinline__ size_t v_off(int hd, int d, size_t c) {
+    const int j = (int)(c & 31);
+    return ((c >> 5) * hd + d) * 32 + 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3);
+}
+
 template <int EPI, bool ATOMIC>
 __device__ __forceinline__ void epilogue4(const LinearArgs &a, int t, int n, f32x4_t v, f32x4_t u) {
     if (EPI == EPI_STORE || EPI == EPI_RESID) {
@@ -235,11 +246,11 @@ __device__ __forceinline__ void epilogue4(const LinearArgs &a, int t, int n, f32
             }
         } else {
             const int o = n - q.n_q_rows - q.n_k_rows, head = o / hd, d = o % hd;
-            const size_t base = ((size_t)a.tok.stream[t] * q.n_head_kv + head) * hd + d;
+            const size_t base = ((size_t)a.tok.stream[t] * q.n_head_kv + head) * q.n_cells * hd;
             const int cell = a.tok.cell[t];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const size_t idx = (base + i) * q.n_cells + cell;
+                const size_t idx = base + v_off(hd, d + i, cell);
                 if (q.type_v == KV_F32)
                     ((float *)q.v_cache)[idx] = v[i];
                 else
@@ -971,7 +982,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     for (int j = 0; j < C::NACC; ++j) acc[j] = 0.f;
 
     const size_t kbase = ((size_t)st * a.n_head_kv + g) * a.n_cells * HD;  // [cell][hd]
-    const size_t vbase = ((size_t)st * a.n_head_kv + g) * HD * a.n_cells;  // [hd][cell]
+    const size_t vbase = ((size_t)st * a.n_head_kv + g) * HD * a.n_cells;  // 32-cell tiles
     const int32_t *cp = a.cell_pos + (size_t)st * a.n_cells;
     const int32_t *cs = a.cell_seq + (size_t)st * a.n_cells;
 
@@ -984,7 +995,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         }
         for (int e = tid; e < SUB * HD; e += 256) {
             const int d = e / SUB, c = e % SUB;
-            Vt[d][c] = c < ns ? load_kv(a.v_cache, a.type_v, vbase + (size_t)d * a.n_cells + sub + c) : 0.f;
+            Vt[d][c] = c < ns ? load_kv(a.v_cache, a.type_v, vbase + v_off(HD, d, (size_t)(sub + c))) : 0.f;
         }
         if (tid < SUB) {
             cpos[tid] = tid < ns ? cp[sub + tid] : -1;
@@ -1099,11 +1110,107 @@ void launch_attention(const AttnArgs &a, hipStream_t s) {
 // S^T = K Q^T (A = 16 cells x 32 dims of K straight from the cache, B = the
 // rows' q as f16 hi + lo), so lane (row r, group g) holds S[r][cells 4g+i]
 // of each 16-cell block.  Two blocks give exactly the P fragment of P*V for
-// the cell order {4g..4g+3, 16+4g..16+4g+3}, which V^T [dim][cell] supplies
-// as two contiguous 8-byte runs.  Online softmax per row; SPLIT writes the
+// the cell order {4g..4g+3, 16+4g..16+4g+3}, which the V tile supplies as
+// one contiguous 16-byte run per lane.  Online softmax per row; SPLIT writes the
 // range's (m, l, O) for a combine pass, otherwise O / l is stored.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+template <int HD> struct KVSrc {
+    const _Float16 *K, *Vt;
+    const int32_t *cpos, *cseq;
+    int n_cells, r, g;
+};
+
+// One 32-cell step of K (two 16-cell MFMA A blocks), V^T (the P*V B
+// fragments) and the cells' (pos, seq).
+template <int HD> struct KVStep {
+    static constexpr int KK = HD / 32, DB = HD / 16;
+    f16x8_t k[2][KK];
+    f16x8_t v[DB];
+    int4 p[2], s[2];
+};
+
+template <int HD>
+__device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src, int c0) {
+    constexpr int KK = HD / 32, DB = HD / 16;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+        const int cb = c0 + 16 * b2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            b.k[b2][kk] = *(const f16x8_t *)(src.K + (size_t)(cb + src.r) * HD + 32 * kk + 8 * src.g);
+        b.p[b2] = *(const int4 *)(src.cpos + cb + 4 * src.g);
+        b.s[b2] = *(const int4 *)(src.cseq + cb + 4 * src.g);
+    }
+    // c0 is a multiple of 32: the step's V is the contiguous tile c0 / 32,
+    // and this lane's B fragment of dims 16 db + r is slots 8g .. 8g+7
+    const _Float16 *vt = src.Vt + (size_t)(c0 >> 5) * HD * 32 + src.r * 32 + 8 * src.g;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) b.v[db] = *(const f16x8_t *)(vt + db * 16 * 32);
+}
+
+// Scores of the step's 32 cells for the wave's 16 rows, mask, online-softmax
+// update of (m, l) and O += P V.
+template <int HD>
+__device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int cend, const f16x8_t *qh,
+                                                const f16x8_t *ql, bool row_ok, int rseq, int rpos, int g,
+                                                float &m, float &l, f32x4_t *O) {
+    constexpr int KK = HD / 32, DB = HD / 16;
+    f32x4_t S[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.k[b2][kk], qh[kk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.k[b2][kk], ql[kk], acc, 0, 0, 0);
+        }
+        const int cc = c0 + 16 * b2 + 4 * g;
+        const int pp[4] = {b.p[b2].x, b.p[b2].y, b.p[b2].z, b.p[b2].w};
+        const int ss[4] = {b.s[b2].x, b.s[b2].y, b.s[b2].z, b.s[b2].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool vis = row_ok && cc + i < cend && ss[i] == rseq && pp[i] >= 0 && pp[i] <= rpos;
+            acc[i] = vis ? acc[i] : -INFINITY;
+        }
+        S[b2] = acc;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m - m_new);
+    float ps = 0.f;
+    f16x8_t ph, pl;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sv = S[b2][i];
+            const float p = sv == -INFINITY ? 0.f : expf(sv - m_new);
+            ps += p;
+            const _Float16 h = (_Float16)p;
+            ph[4 * b2 + i] = h;
+            pl[4 * b2 + i] = (_Float16)(p - (float)h);
+        }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = m_new;
+    // O rows are 4g+i in this lane: fetch their rescale factors
+    f32x4_t al;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        f32x4_t o = O[db] * al;
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, b.v[db], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, b.v[db], o, 0, 0, 0);
+        O[db] = o;
+    }
+}
 
 template <int HD, bool SPLIT>
 __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
@@ -1126,19 +1233,31 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     const bool row_ok = r < R;
     const int rt = t0 + (row_ok ? r / G : 0), rh = grp * G + (row_ok ? r % G : 0);
     const int rpos = a.tok.pos[rt], rseq = a.tok.seq[rt];
+    // every lane loads a valid row (rows past R read row 0) and zeroes it
+    // afterwards, so the loads are unconditional and issued together
     f16x8_t qh[KK], ql[KK];
+    const float *qrow = a.q + (size_t)rt * a.n_head * HD + rh * HD + 8 * g;
+    const float qs = row_ok ? scale : 0.f;
+    float4 qv[KK][2];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
+        qv[kk][0] = *(const float4 *)(qrow + 32 * kk);
+        qv[kk][1] = *(const float4 *)(qrow + 32 * kk + 4);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const float e8[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
+                             qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float v = row_ok ? a.q[(size_t)rt * a.n_head * HD + rh * HD + 32 * kk + 8 * g + e] * scale : 0.f;
+            const float v = e8[e] * qs;
             const _Float16 h = (_Float16)v;
             qh[kk][e] = h;
             ql[kk][e] = (_Float16)(v - (float)h);
         }
     }
     const _Float16 *K = (const _Float16 *)a.k_cache + ((size_t)st * a.n_head_kv + grp) * a.n_cells * HD;
-    const _Float16 *Vt = (const _Float16 *)a.v_cache + ((size_t)st * a.n_head_kv + grp) * HD * a.n_cells;
+    const _Float16 *Vt = (const _Float16 *)a.v_cache + ((size_t)st * a.n_head_kv + grp) * a.n_cells * HD;
     const int32_t *cpos = a.cell_pos + (size_t)st * a.n_cells;
     const int32_t *cseq = a.cell_seq + (size_t)st * a.n_cells;
 
@@ -1147,80 +1266,26 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = cbeg; c0 < cend; c0 += 32) {
-        // issue every load of the 32-cell step first
-        f16x8_t Ka[2][KK];
-        f16x4_t Va[DB][2];
-        int4 p4[2], s4[2];
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            const int cb = c0 + 16 * b2;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) Ka[b2][kk] = *(const f16x8_t *)(K + (size_t)(cb + r) * HD + 32 * kk + 8 * g);
-            p4[b2] = *(const int4 *)(cpos + cb + 4 * g);
-            s4[b2] = *(const int4 *)(cseq + cb + 4 * g);
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const _Float16 *vrow = Vt + (size_t)(16 * db + r) * a.n_cells;
-            Va[db][0] = *(const f16x4_t *)(vrow + c0 + 4 * g);
-            Va[db][1] = *(const f16x4_t *)(vrow + c0 + 16 + 4 * g);
-        }
-        f32x4_t S[2];
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ka[b2][kk], qh[kk], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ka[b2][kk], ql[kk], acc, 0, 0, 0);
-            }
-            const int cc = c0 + 16 * b2 + 4 * g;
-            const int pp[4] = {p4[b2].x, p4[b2].y, p4[b2].z, p4[b2].w};
-            const int ss[4] = {s4[b2].x, s4[b2].y, s4[b2].z, s4[b2].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool vis = row_ok && cc + i < cend && ss[i] == rseq && pp[i] >= 0 && pp[i] <= rpos;
-                acc[i] = vis ? acc[i] : -INFINITY;
-            }
-            S[b2] = acc;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m, mx);
-        const float alpha = (m_new == -INFINITY) ? 1.f : expf(m - m_new);
-        float ps = 0.f;
-        f16x8_t ph, pl;
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float sv = S[b2][i];
-                const float p = sv == -INFINITY ? 0.f : expf(sv - m_new);
-                ps += p;
-                const _Float16 h = (_Float16)p;
-                ph[4 * b2 + i] = h;
-                pl[4 * b2 + i] = (_Float16)(p - (float)h);
-            }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        l = l * alpha + ps;
-        m = m_new;
-        // O rows are 4g+i in this lane: fetch their rescale factors
-        f32x4_t al;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const f16x8_t B = {Va[db][0][0], Va[db][0][1], Va[db][0][2], Va[db][0][3],
-                               Va[db][1][0], Va[db][1][1], Va[db][1][2], Va[db][1][3]};
-            f32x4_t o = O[db] * al;
-            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, B, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, o, 0, 0, 0);
-            O[db] = o;
-        }
+    // Two register sets: the loads of the next 32-cell step are in flight
+    // while the current one is computed.  Past the range the load repeats
+    // the current step's cells (in bounds, served by the cache) and the
+    // compute masks every cell, so the loop has no data-dependent branch.
+    const KVSrc<HD> src{K, Vt, cpos, cseq, a.n_cells, r, g};
+    KVStep<HD> A, B;
+    if (cbeg < cend) kv_step_load(A, src, cbeg);
+    // (the scheduling fences keep the next step's score MFMAs, which do not
+    // depend on the softmax state, from being hoisted above the current
+    // step and forcing an early wait on loads just issued)
+    for (int c0 = cbeg; c0 < cend; c0 += 64) {
+        const int c1 = c0 + 32, c2 = c0 + 64;
+        kv_step_load(B, src, c1 < cend ? c1 : c0);
+        __builtin_amdgcn_sched_barrier(0);
+        kv_step_compute(A, c0, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+        __builtin_amdgcn_sched_barrier(0);
+        kv_step_load(A, src, c2 < cend ? c2 : c0);
+        __builtin_amdgcn_sched_barrier(0);
+        kv_step_compute(B, c1, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+        __builtin_amdgcn_sched_barrier(0);
     }
     // O: lane (dim r of each 16-dim block, group g) holds rows 4g+i
     if (!SPLIT) {
@@ -1322,8 +1387,8 @@ static void launch_attention_mfma_hd(const AttnArgs &a, hipStream_t s) {
     }
 }
 
-bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa, int n_cells) {
-    return type_k == KV_F16 && type_v == KV_F16 && n_gqa <= 16 && n_cells % 32 == 0 &&
+bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa) {
+    return type_k == KV_F16 && type_v == KV_F16 && n_gqa <= 16 &&
            (head_dim == 32 || head_dim == 64 || head_dim == 128);
 }
 
@@ -1534,7 +1599,7 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const void *src, int src_
         const size_t c = (size_t)cells[p];
         size_t idx;
         if (transposed)
-            idx = (((size_t)stream * n_head_kv + head) * hd + d) * n_cells + c;
+            idx = ((size_t)stream * n_head_kv + head) * n_cells * hd + v_off(hd, d, c);
         else
             idx = (((size_t)stream * n_head_kv + head) * n_cells + c) * hd + d;
         if (type == KV_F32)
@@ -1564,7 +1629,7 @@ __global__ __launch_bounds__(256) void kv_load_kernel(const void *cache, int typ
     const size_t c = (size_t)cell0 + p;
     size_t src;
     if (transposed)
-        src = (((size_t)stream * n_head_kv + head) * hd + d) * n_cells + c;
+        src = ((size_t)stream * n_head_kv + head) * n_cells * hd + v_off(hd, d, c);
     else
         src = (((size_t)stream * n_head_kv + head) * n_cells + c) * hd + d;
     out[idx] = load_kv(cache, type, src);

@@ -363,6 +363,7 @@ struct ubd_context : public Executor {
     DevAlloc mem;
     int type_k = KV_F16, type_v = KV_F16;
     size_t kv_layer_elems = 0;              // per layer, K or V
+    uint32_t cell_stride = 0;               // cells per stream rounded up to 32
     void *k_cache = nullptr, *v_cache = nullptr;
     int32_t *cell_pos = nullptr, *cell_seq = nullptr;
     float *x = nullptr, *q = nullptr;
@@ -508,7 +509,8 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     const Planner &P = c->planner;
     const int hd = model->head_dim, H = hp.n_head, Hk = hp.n_head_kv, d = hp.n_embd, F = hp.n_ff;
     c->cap = (int)P.n_ubatch;
-    const size_t cells = (size_t)P.n_stream * P.n_cells;
+    c->cell_stride = (P.n_cells + 31) / 32 * 32;
+    const size_t cells = (size_t)P.n_stream * c->cell_stride;
     c->kv_layer_elems = cells * Hk * hd;
     const size_t kb = c->type_k == KV_F32 ? 4 : 2, vb = c->type_v == KV_F32 ? 4 : 2;
     c->k_cache = c->mem.get(c->kv_layer_elems * hp.n_layer * kb);
@@ -542,7 +544,7 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
         return bail("activation allocation failed");
     c->max_chunks = (int)((P.n_cells + ATTN_CHUNK - 1) / ATTN_CHUNK);
     c->max_chunks_mfma = (int)((P.n_cells + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK);
-    c->mfma_attn = attn_mfma_ok(c->type_k, c->type_v, hd, H / Hk, (int)P.n_cells);
+    c->mfma_attn = attn_mfma_ok(c->type_k, c->type_v, hd, H / Hk);
     // split partials: f32 path up to n_ubatch tokens; MFMA path only for <= 16 tokens
     const size_t part_rows = c->mfma_attn ? (size_t)std::min(cap, 16) * H * c->max_chunks_mfma
                                           : (size_t)cap * H * c->max_chunks;
@@ -616,7 +618,7 @@ int32_t ubd_context::reserve_outputs(int32_t n) {
 
 bool ubd_context::sync_cell_tables(int32_t st) {
     const Planner &P = planner;
-    const size_t off = (size_t)st * P.n_cells;
+    const size_t off = (size_t)st * cell_stride;
     return hip_ok(hipMemcpyAsync(cell_pos + off, P.cells.pos_data(st), (size_t)P.n_cells * 4,
                                  hipMemcpyHostToDevice, stream), "cell table upload") &&
            hip_ok(hipMemcpyAsync(cell_seq + off, P.cells.seq_data(st), (size_t)P.n_cells * 4,
@@ -698,7 +700,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     last_ub_idx = ub.idx;
 
     const TokInfo ti = tok_info();
-    const int n_cells = (int)planner.n_cells;
+    const int n_cells = (int)cell_stride;   // per-stream stride of the device KV and cell tables
     const int ph = T > 16 ? 1 : 0;
     timed(0 + ph, [&] { launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, stream); });
     if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, stream), "dump");
@@ -989,7 +991,7 @@ extern "C" int32_t ubd_kv_fill(ubd_context *ctx, ubd_seq_id s, int32_t n_pos, co
             void *cache = which == 0 ? (char *)ctx->k_cache + ctx->kv_layer_elems * il * kb
                                      : (char *)ctx->v_cache + ctx->kv_layer_elems * il * vb;
             launch_kv_store(src, srct, n_pos, dcells, cache, which == 0 ? ctx->type_k : ctx->type_v, which == 1, st,
-                            Hk, hd, (int)ctx->planner.n_cells, ctx->stream);
+                            Hk, hd, (int)ctx->cell_stride, ctx->stream);
             ok = ok && hip_ok(hipGetLastError(), "kv_store");
             if (!on_device) ok = ok && hip_ok(hipStreamSynchronize(ctx->stream), "kv sync");
         }
@@ -1021,7 +1023,7 @@ extern "C" int32_t ubd_kv_read(ubd_context *ctx, int32_t layer, int32_t stream, 
     const void *cache = which == 0 ? (const char *)ctx->k_cache + ctx->kv_layer_elems * layer * kb
                                    : (const char *)ctx->v_cache + ctx->kv_layer_elems * layer * vb;
     launch_kv_load(cache, which == 0 ? ctx->type_k : ctx->type_v, which == 1, stream, cell0, n, Hk, hd,
-                   (int)P.n_cells, tmp, ctx->stream);
+                   (int)ctx->cell_stride, tmp, ctx->stream);
     bool ok = hip_ok(hipGetLastError(), "kv_load") && hip_ok(hipStreamSynchronize(ctx->stream), "kv_read sync") &&
               hip_ok(hipMemcpy(out, tmp, bytes, hipMemcpyDeviceToHost), "kv_read copy");
     (void)hipFree(tmp);
