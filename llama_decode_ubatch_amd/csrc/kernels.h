@@ -38,6 +38,8 @@ struct Tuning {
     int fuse_norm = -1;       // -1: fuse RMSNorm into the QKV product only, 0: never, 1: QKV+gate|up+logits
     int attn_chunk_min = 0;   // smallest cells per wave of split attention
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
+    int gemm = 1;             // prefill products: 0 = register-staged kernel, 1 = LDS-ring kernel except
+                              // residual products, 2 = LDS-ring kernel for all
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;

@@ -3,6 +3,8 @@
 // launchers derive grids from the same arguments.
 #include "kernels.h"
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -733,6 +735,263 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, i
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill product with an LDS ring of activation stages.  A work-group of 4
+// waves owns 64*RBW weight rows x 16*TB tokens; wave w owns row blocks
+// rb0 + w*RBW ...  The k range is walked in stages of KS values.  Weight
+// tiles (already in MFMA fragment order) stream into registers one stage
+// ahead; activation fragments are copied by every wave, a quarter each,
+// straight from global memory into a 3-deep LDS ring (buffer_load ... lds,
+// 16 bytes per lane, fragment order) two stages ahead.  One barrier per
+// stage, after each wave has waited for its own copies of that stage.
+
+// Raw buffer resource over `bytes` bytes at p (gfx9 descriptor: 32-bit
+// data format word; loads beyond num_records return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)min(bytes, (size_t)0x7fffffff), 0x00020000);
+}
+
+// s_waitcnt immediate (gfx9 encoding) that bounds only the vector-memory
+// counter: at most N vector loads of this wave still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Work-group barrier that leaves the memory counters to the caller; the
+// empty asm statements stop the compiler from moving memory accesses across.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int WT, int RBW, int TB, int KS> struct GemmCfg {
+    static constexpr bool Q8 = WT == W_Q8;
+    static constexpr int PL = Q8 ? 2 : 1;         // activation planes: hi (+ lo for q8_0)
+    static constexpr int KH = KS / 32;            // 32-wide k halves per stage
+    static constexpr int NA = Q8 ? KS / 64 : KH;  // weight tiles per row block per stage
+    static constexpr int XF = TB * KH * PL;       // activation fragments per stage
+    static_assert(KS % 64 == 0 && XF % 4 == 0, "stage shape");
+    static constexpr int XW = XF / 4;             // ... copied by each wave
+    static constexpr int NX = 3;                  // LDS ring depth
+};
+
+template <int WT, int EPI, int RBW, int TB, int SPLITK, int KS>
+__global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a, int n_wtiles, int n_ttiles) {
+    // (the host pass only needs the launch stub; the buffer-resource
+    // builtins below exist for the device pass alone)
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = GemmCfg<WT, RBW, TB, KS>;
+    constexpr bool Q8 = C::Q8;
+    constexpr int KH = C::KH, NA = C::NA;
+    __shared__ u32x4_t xs[C::NX * C::XF * 64];
+
+    const int lane = threadIdx.x & 63;
+    // wave-uniform (scalar) wave index: the LDS destination of the copies
+    // goes through M0 and must be uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int total = n_wtiles * n_ttiles * SPLITK;
+    const int b = blockIdx.x;
+    // consecutive tiles (same weight rows, next token block) on one XCD
+    const int tile = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
+    const int ks = tile % SPLITK;
+    const int tt = (tile / SPLITK) % n_ttiles;
+    const int nt = tile / (SPLITK * n_ttiles);
+    const int nrb = a.N / 16;
+    const int rb0 = nt * 4 * RBW + wave * RBW;
+    const int t0 = tt * 16 * TB;
+    const int nstage = a.K / KS;
+    const int st0 = ks * nstage / SPLITK, st1 = (ks + 1) * nstage / SPLITK;
+    const int KB = a.K / 32;
+
+    // Buffer resources (bounds-checked: offsets past num_records read 0, so
+    // token rows past T need no clamping).  Every load is a loop-invariant
+    // 32-bit lane offset plus a per-stage scalar offset.
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (size_t)a.N * a.K * (Q8 ? 1 : 2));
+    const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, (size_t)a.T * a.x.ld * 2);
+    const __amdgpu_buffer_rsrc_t rxl = make_rsrc(Q8 ? a.x.lo : a.x.hi, (size_t)a.T * a.x.ld * 2);
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.wscale, Q8 ? (size_t)a.N * KB * 2 : 0);
+    // this wave's activation fragments f = wave*XW + u = (plane, token block, k half)
+    int xoff[C::XW];
+#pragma unroll
+    for (int u = 0; u < C::XW; ++u) {
+        const int f = wave * C::XW + u;
+        const int tb = (f / KH) % TB, j = f % KH;
+        xoff[u] = ((t0 + 16 * tb + r) * a.x.ld + 32 * j + 8 * g) * 2;
+    }
+    // weight row blocks past N re-read the last one (never stored)
+    int woff[RBW], soff[RBW];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+        const int rbc = min(rb0 + i, nrb - 1);
+        woff[i] = rbc * 1024 + lane * 16;
+        soff[i] = (rbc * KB * 16 + 4 * g) * 2;
+    }
+    const int wstep = nrb * 1024;   // bytes between consecutive k-steps of the weight tiles
+
+    u32x4_t wn[RBW][NA];            // next stage's weight tiles (in flight)
+    u32x2_t sn[RBW][KH];            // ... and q8_0 scales
+    f32x4_t acc[RBW][TB];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto issue_w = [&](int s) {
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+            const int so = (NA * s + j) * wstep;
+#pragma unroll
+            for (int i = 0; i < RBW; ++i) wn[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i], so, 0);
+        }
+        if (Q8) {
+#pragma unroll
+            for (int i = 0; i < RBW; ++i)
+#pragma unroll
+                for (int j = 0; j < KH; ++j)
+                    sn[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rsc, soff[i], (KH * s + j) * 32, 0);
+        }
+    };
+    // stage s's activation copies into ring slot s % NX (stage clamped)
+    auto issue_x = [&](int s) {
+        const int sl = min(s, st1 - 1);
+        u32x4_t *dst = xs + (size_t)((s % C::NX) * C::XF + wave * C::XW) * 64;
+#pragma unroll
+        for (int u = 0; u < C::XW; ++u) {
+            const bool lo = (wave * C::XW + u) >= TB * KH;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(lo ? rxl : rxh,
+                                                     (__attribute__((address_space(3))) void *)(dst + u * 64), 16,
+                                                     xoff[u], sl * KS * 2, 0, 0);
+        }
+    };
+
+    if (st0 < st1) {
+        issue_w(st0);
+        issue_x(st0);
+        issue_x(st0 + 1);
+        for (int s = st0; s < st1; ++s) {
+            // everything but the newest activation copies (stage s+1) has landed
+            wait_vm<C::XW>();
+            wg_barrier();
+            u32x4_t wc[RBW][NA];
+            u32x2_t sc[RBW][KH];
+#pragma unroll
+            for (int i = 0; i < RBW; ++i) {
+#pragma unroll
+                for (int j = 0; j < NA; ++j) wc[i][j] = wn[i][j];
+#pragma unroll
+                for (int j = 0; j < KH; ++j) sc[i][j] = sn[i][j];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            issue_w(min(s + 1, st1 - 1));
+            issue_x(s + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4_t *xb = xs + (size_t)(s % C::NX) * C::XF * 64;
+#pragma unroll
+            for (int j = 0; j < KH; ++j) {
+                bf16x8_t Bh[TB];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) Bh[tb] = __builtin_bit_cast(bf16x8_t, xb[(tb * KH + j) * 64 + lane]);
+                if (!Q8) {
+#pragma unroll
+                    for (int i = 0; i < RBW; ++i) {
+                        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, wc[i][j]);
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb)
+                            acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh[tb], acc[i][tb], 0, 0, 0);
+                    }
+                } else {
+                    const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < RBW; ++i) {
+                        const u32x4_t w = wc[i][j >> 1];
+                        const bf16x8_t A = (j & 1) ? i8x8_to_bf16(w[2], w[3]) : i8x8_to_bf16(w[0], w[1]);
+                        f32x4_t S;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[e] = h2f((uint16_t)(sc[i][j][e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb) {
+                            const bf16x8_t Bl =
+                                __builtin_bit_cast(bf16x8_t, xb[((TB + tb) * KH + j) * 64 + lane]);
+                            f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh[tb], zf, 0, 0, 0);
+                            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, d, 0, 0, 0);
+                            acc[i][tb] += S * d;
+                        }
+                    }
+                }
+            }
+        }
+        // the ring's last copies must land before the work-group's LDS is released
+        wait_vm<0>();
+    }
+
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+        const int rb = rb0 + i;
+        if (rb >= nrb) continue;
+        if (EPI == EPI_SWIGLU && (i & 1)) continue;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = t0 + tb * 16 + r;
+            if (t >= a.T) continue;
+            if (EPI == EPI_SWIGLU)
+                epilogue4<EPI, false>(a, t, (rb >> 1) * 16 + 4 * g, acc[i][tb], acc[i + 1][tb]);
+            else
+                epilogue4<EPI, (SPLITK > 1)>(a, t, rb * 16 + 4 * g, acc[i][tb], acc[i][tb]);
+        }
+    }
+#endif
+}
+
+template <int WT, int EPI, int RBW, int TB, int SPLITK>
+static void launch_gemm_lds(const LinearArgs &a, hipStream_t s) {
+    // 128-wide stages for bf16 when K allows; q8_0 keeps two activation
+    // planes in the ring and uses 64-wide stages (K is a multiple of 64)
+    const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
+    const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
+    const int total = n_wtiles * n_ttiles * SPLITK;
+    constexpr int KW = WT == W_Q8 ? 64 : 128;   // the wide stage of this weight type
+    if (a.K % KW == 0)
+        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, KW>), dim3(total), dim3(256), 0, s, a,
+                           n_wtiles, n_ttiles);
+    else
+        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64>), dim3(total), dim3(256), 0, s, a,
+                           n_wtiles, n_ttiles);
+}
+
+// Shape choice for the LDS-ring product: the largest tile (256 rows x 128
+// tokens) when it yields enough work-groups for the 256 CUs, else narrower
+// tiles; residual products may also split k (partial sums added atomically).
+template <int WT, int EPI>
+static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
+    auto tiles = [&](int rbw, int tb) {
+        return (long)((a.N + 64 * rbw - 1) / (64 * rbw)) * ((a.T + 16 * tb - 1) / (16 * tb));
+    };
+    // q8_0 (two activation planes and the scale products) uses 2 row
+    // blocks per wave, bf16 up to 4
+    constexpr int RBW = WT == W_Q8 ? 2 : 4;
+    if (EPI == EPI_RESID) {
+        const long t = tiles(RBW, 8);
+        const int nst = a.K / 128;
+        if (t >= 192 || nst < 8)
+            launch_gemm_lds<WT, EPI, RBW, 8, 1>(a, s);
+        else if (t * 2 >= 192 || nst < 16)
+            launch_gemm_lds<WT, EPI, RBW, 8, 2>(a, s);
+        else
+            launch_gemm_lds<WT, EPI, RBW, 8, 4>(a, s);
+        return;
+    }
+    if (tiles(RBW, 8) >= 192)
+        launch_gemm_lds<WT, EPI, RBW, 8, 1>(a, s);
+    else if (tiles(2, 8) >= 192)
+        launch_gemm_lds<WT, EPI, 2, 8, 1>(a, s);
+    else
+        launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s);
+}
+
 template <int WT, int EPI, int BT, int SPLITK>
 static void launch_gemm(const LinearArgs &a, hipStream_t s) {
     const int n_wtiles = (a.N + 255) / 256;
@@ -750,6 +1009,12 @@ static bool try_gemm(const LinearArgs &a, hipStream_t s) {
     } else {
     if (a.T < 64 || a.K % 64) return false;
     if (EPI == EPI_SWIGLU && a.N % 32) return false;
+    // residual products (narrow N, split k) run faster on the register-
+    // staged kernel; the others on the LDS-ring kernel
+    if (g_tuning.gemm == 2 || (g_tuning.gemm == 1 && EPI != EPI_RESID)) {
+        launch_gemm_lds_shape<WT, EPI>(a, s);
+        return true;
+    }
     const int n_wtiles = (a.N + 255) / 256;
     const bool big = (long)n_wtiles * ((a.T + 127) / 128) >= 256;
     if (EPI == EPI_RESID) {

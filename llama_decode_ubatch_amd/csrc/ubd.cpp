@@ -1116,6 +1116,8 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.attn_chunk_min = value;
     } else if (k == "ldsx") {
         g_tuning.ldsx = value;
+    } else if (k == "gemm") {
+        g_tuning.gemm = value;
     } else {
         return UBD_INVALID;
     }

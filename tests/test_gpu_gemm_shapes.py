@@ -1,0 +1,72 @@
+"""Prefill products at small, ragged shapes, through the C ABI.
+
+Small Llama-architecture models with bf16 and q8_0 weights (the tiny
+workloads use f32 weights, which never take the MFMA GEMM path) prefill
+prompts of 64, 100 and 200 tokens with every token flagged for output, so
+the QKV, O, gate|up, down and logits products all run as GEMMs with a
+ragged token tail, weight-row tiles that overhang N, k both a multiple of 128
+and not (n_ff 704), and split-k residual products (n_ff 1408).  All logits
+are compared with the float64 oracle; the LDS-ring kernel is also compared
+with the register-staged one.
+"""
+import numpy as np
+import pytest
+
+from workloads import ModelShape, gen_tensor, tensor_specs
+from tests.helpers import oracle_ctx, rand_tokens
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "bf16-ff1408": ModelShape("small-bf16-a", 10, n_layer=2, n_embd=256, n_head=8, n_head_kv=2, n_ff=1408,
+                              n_vocab=1024, n_ctx_train=2048, rope_base=10000.0, wtype="bf16"),
+    "bf16-ff704": ModelShape("small-bf16-b", 11, n_layer=2, n_embd=256, n_head=8, n_head_kv=2, n_ff=704,
+                             n_vocab=1024, n_ctx_train=2048, rope_base=10000.0, wtype="bf16"),
+    "q8_0-ff1408": ModelShape("small-q8-a", 12, n_layer=2, n_embd=256, n_head=8, n_head_kv=2, n_ff=1408,
+                              n_vocab=1024, n_ctx_train=2048, rope_base=10000.0, wtype="q8_0"),
+}
+# bf16 products see bf16-rounded activations; q8_0 products see hi + lo
+TOL = {"bf16": 3e-2, "q8_0": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def built():
+    import torch  # noqa: F401
+    from llama_decode_ubatch_amd import Model
+    out = {}
+    for key, shape in SHAPES.items():
+        tens = {s.name: gen_tensor(shape, s) for s in tensor_specs(shape)}
+        out[key] = (shape, tens, Model(shape, tens, device=0))
+    return out
+
+
+def gpu_logits(model, tokens, gemm):
+    from llama_decode_ubatch_amd import Context
+    from llama_decode_ubatch_amd.binding import set_tuning
+    set_tuning("gemm", gemm)
+    try:
+        ctx = Context(model, n_ctx=512, n_batch=512, n_ubatch=512, n_seq_max=1, type_k="f16", type_v="f16")
+        assert ctx.decode(tokens, logits=np.ones(len(tokens))) == 0
+        return ctx.logits()
+    finally:
+        set_tuning("gemm", 1)
+
+
+@pytest.mark.parametrize("key", list(SHAPES))
+@pytest.mark.parametrize("n", [64, 100, 200])
+def test_prefill_gemm_matches_oracle(built, key, n):
+    shape, tens, model = built[key]
+    tokens = rand_tokens(n, shape.n_vocab, seed=1000 + n)
+    z = gpu_logits(model, tokens, 1)
+    ref = oracle_ctx(shape, tens, np.float64, n_ctx=512, n_batch=512, n_ubatch=512, type_k="f16", type_v="f16")
+    from oracle import Batch
+    assert ref.decode(Batch(tokens, logits=[1] * n)) == 0
+    zr = np.stack([ref.logits_ith(i) for i in range(n)])
+    err = float(np.abs(z - zr).max() / np.abs(zr).max())
+    print(f"{key} T={n}: logits rel err {err:.2e}", flush=True)
+    assert err < TOL[shape.wtype]
+    # the other kernel choices (register-staged for all products; LDS-ring
+    # for all, residual products included) must sit within the tolerance too
+    for choice in (0, 2):
+        zc = gpu_logits(model, tokens, choice)
+        assert float(np.abs(zc - zr).max() / np.abs(zr).max()) < TOL[shape.wtype], choice
