@@ -296,12 +296,14 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
 
 /* Process-wide launch-shape knobs for measurements: "skinny_nw" (waves
  * per work-group of the few-token products: 4, 8, 16; 0 = automatic),
- * "fuse_norm" (-1 = RMSNorm fused into the QKV product when a ubatch has
- * at most 2 tokens, 0 = never, 1 = also gate|up and logits),
+ * "fuse_norm" (ubatches of at most 2 tokens: 1 = RMSNorm fused into the
+ * QKV, gate|up and logits products, -1 = into QKV only, 0 = never),
  * "attn_chunk_min" (smallest cells per wave of split attention), "ldsx"
  * (0 = few-token products read activations from global memory), "gemm"
  * (prefill products: 0 = register-staged kernel, 1 = LDS-ring kernel except
- * for residual products, 2 = LDS-ring kernel for all).
+ * for residual products, 2 = LDS-ring kernel for all), "small_rb" (1 =
+ * products of 3..16 tokens share activation fragments over 4 row blocks
+ * or split k, 0 = one row block per work-group).
  * Results do not depend on them beyond rounding.  0, or -1 for an unknown
  * key. */
 int32_t ubd_debug_set_tuning(const char *key, int32_t value);

@@ -35,9 +35,11 @@ enum WType : int { W_F32 = 0, W_BF16 = 2, W_Q8 = 3 };
 // ubd_debug_set_tuning for measurements.
 struct Tuning {
     int skinny_nw = 0;        // waves per work-group of the small-T product
-    int fuse_norm = -1;       // -1: fuse RMSNorm into the QKV product only, 0: never, 1: QKV+gate|up+logits
+    int fuse_norm = 1;        // ubatches of <= 2 tokens: 1 = RMSNorm fused into the QKV, gate|up and
+                              // logits products, -1 = into QKV only, 0 = never
     int attn_chunk_min = 0;   // smallest cells per wave of split attention
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
+    int small_rb = 1;         // several-token products: 4 row blocks per work-group / split k (0 = off)
     int gemm = 1;             // prefill products: 0 = register-staged kernel, 1 = LDS-ring kernel except
                               // residual products, 2 = LDS-ring kernel for all
 };

@@ -317,12 +317,15 @@ __device__ void norm_prologue(const LinearArgs &a, unsigned char *lds) {
     __syncthreads();
 }
 
-template <int WT, int EPI, int NW, bool NORM>
+// RB row blocks per work-group share each k-step's activation fragment
+// (SWIGLU: RB/2 gate|up pairs); KSPLIT > 1 (residual products only) splits
+// k over grid.z and adds the partial sums atomically.
+template <int WT, int EPI, int NW, bool NORM, int RB, int KSPLIT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void linear_small_kernel(LinearArgs a) {
-    constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
+    static_assert(EPI != EPI_SWIGLU || RB % 2 == 0, "gate|up pairs");
+    static_assert(KSPLIT == 1 || EPI == EPI_RESID, "k split only for residual products");
     // k-steps per batch: the same 16-byte weight loads in flight per lane
-    // for one or two row blocks
-    constexpr int KSTEP = WT_<WT>::KSTEP, U = WT_<WT>::U / RB;
+    constexpr int KSTEP = WT_<WT>::KSTEP, U = WT_<WT>::U / RB > 0 ? WT_<WT>::U / RB : 1;
     extern __shared__ __align__(16) unsigned char dyn_lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -332,7 +335,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     const bool tok_ok = r < n_tok;
     const int tok = t0 + (tok_ok ? r : 0);
     const int steps = a.K / KSTEP;
-    const int s0 = wave * steps / NW, s1 = (wave + 1) * steps / NW;
+    const int kz0 = blockIdx.z * steps / KSPLIT, kz1 = (blockIdx.z + 1) * steps / KSPLIT;
+    const int s0 = kz0 + wave * (kz1 - kz0) / NW, s1 = kz0 + (wave + 1) * (kz1 - kz0) / NW;
 
     f32x4_t acc[RB];
 #pragma unroll
@@ -384,10 +388,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
     if (!tok_ok) return;
     const int t = t0 + r;
-    if (EPI == EPI_SWIGLU)
-        epilogue4<EPI, false>(a, t, blockIdx.x * 16 + 4 * g, acc[0], acc[RB - 1]);
-    else
-        epilogue4<EPI, false>(a, t, rb0 * 16 + 4 * g, acc[0], acc[0]);
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+        if (EPI == EPI_SWIGLU) {
+            if (j & 1) continue;
+            epilogue4<EPI, false>(a, t, (rb0 / 2 + j / 2) * 16 + 4 * g, acc[j], acc[j + 1]);
+        } else {
+            epilogue4<EPI, (KSPLIT > 1)>(a, t, (rb0 + j) * 16 + 4 * g, acc[j], acc[j]);
+        }
+    }
 }
 
 // Few-token product with the activations in LDS (decode).  The work-group
@@ -539,15 +548,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
     for (int j = 0; j < RB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // both weight batches go out before the prologue, and each is refilled
+    // right after it has been multiplied: two batches stay in flight
     WBatch<WT, RB, UB> bufA, bufB;
     if (s0 < s1) load_wbatch<WT, RB, UB>(a, rb0, s0, s1, steps, lane, bufA);
+    if (s0 + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s0 + UB, s1, steps, lane, bufB);
     ldsx_prologue<WT, NW, NORM>(a, dyn_lds, t0, Tb);
     for (int s = s0; s < s1; s += 2 * UB) {
-        if (s + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s + UB, s1, steps, lane, bufB);
         mul_wbatch<WT, RB, UB>(bufA, dyn_lds, Tb, a.K, s, s1, lane, tok, tok_ok, acc);
-        if (s + UB >= s1) break;
         if (s + 2 * UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s + 2 * UB, s1, steps, lane, bufA);
+        if (s + UB >= s1) break;
         mul_wbatch<WT, RB, UB>(bufB, dyn_lds, Tb, a.K, s + UB, s1, lane, tok, tok_ok, acc);
+        if (s + 3 * UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s + 3 * UB, s1, steps, lane, bufB);
     }
 
     if (NW > 1) {
@@ -1067,12 +1079,39 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
         return;
     }
     const size_t lds = norm ? (size_t)4 * a.T * a.K : 0;
+    if (!norm && a.T > 2 && g_tuning.small_rb != 0) {
+        // several tokens: 4 row blocks per work-group share each activation
+        // fragment when that still gives >= 256 work-groups per token block;
+        // narrower products use 2 row blocks or (residual products) split k
+        const int nrb = a.N / 16;
+        if (nrb % 4 == 0 && nrb / 4 >= 256) {
+            dim3 g4(nrb / 4, grid.y);
+            const int nw4 = nrb / 4 >= 768 ? 4 : 8;
+            if (nw4 == 4)
+                hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 4, false, 4, 1>), g4, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 8, false, 4, 1>), g4, dim3(512), 0, s, a);
+            return;
+        }
+        // narrower products that cannot split k (QKV): 2 row blocks, 16 waves
+        if (nrb % 2 == 0 && nrb / 2 >= 192) {
+            dim3 g2(nrb / 2, grid.y);
+            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 16, false, 2, 1>), g2, dim3(1024), 0, s, a);
+            return;
+        }
+        constexpr int KSPLIT = EPI == EPI_RESID ? 4 : 1;
+        if (KSPLIT > 1 && nrb % 4 == 0 && (a.K / WT_<WT>::KSTEP) % 32 == 0) {
+            dim3 g4(nrb / 4, grid.y, KSPLIT);
+            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 8, false, 4, KSPLIT>), g4, dim3(512), 0, s, a);
+            return;
+        }
+    }
 #define UBD_LAUNCH_SMALL(NW_)                                                                            \
     do {                                                                                                 \
         if (norm)                                                                                        \
-            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, true>), grid, dim3(64 * NW_), lds, s, a); \
+            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, true, RB, 1>), grid, dim3(64 * NW_), lds, s, a); \
         else                                                                                             \
-            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), 0, s, a); \
+            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, false, RB, 1>), grid, dim3(64 * NW_), 0, s, a); \
     } while (0)
     if (nw == 4)
         UBD_LAUNCH_SMALL(4);

@@ -86,3 +86,31 @@ def test_prefill_and_decode_sampled_layers(cfg):
         assert tok == int(np.argmax(z))
     ctx.free()
     model.free()
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_few_token_ubatch_sampled_layers(cfg):
+    """A 7-token prompt: below the GEMM threshold and above the fused-norm
+    one, so every product runs as a few-token product with several row
+    blocks per work-group (gate|up, logits) or k split over work-groups
+    (O, down), all 7 logits rows requested."""
+    from llama_decode_ubatch_amd import Context
+    w, model, om = build(cfg)
+    ctx = Context(model, n_ctx=w.n_ctx, n_batch=w.n_batch, n_ubatch=w.n_ubatch, type_k=w.type_k,
+                  type_v=w.type_v)
+    assert ctx.keep_residuals(True) == 0
+    prompt = prompt_tokens(w, 0)[:7]
+    T = prompt.size
+    assert ctx.decode(prompt, logits=np.ones(T)) == 0
+    for il in (0, 31):
+        x_in, x_out = ctx.residual(il, T), ctx.residual(il + 1, T)
+        y, _ = oracle_layer(om, w, il, x_in, prompt, 0)
+        err = rel(x_out, y)
+        print(f"  {T}-token ubatch layer {il}: rel err {err:.2e}", flush=True)
+        assert err < TOL, il
+    z = ctx.logits()
+    zr = OracleContext(om, 512).head(ctx.residual(w.model.n_layer, T).astype(np.float32))
+    err = rel(z, zr)
+    print(f"  {T}-token ubatch logits: rel err {err:.2e}", flush=True)
+    assert err < TOL
+    om.drop_cache()
