@@ -300,8 +300,9 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * QKV, gate|up and logits products, -1 = into QKV only, 0 = never),
  * "attn_chunk_min" (smallest cells per wave of split attention), "ldsx"
  * (0 = few-token products read activations from global memory), "gemm"
- * (prefill products: 0 = register-staged kernel, 1 = LDS-ring kernel except
- * for residual products, 2 = LDS-ring kernel for all), "small_rb" (1 =
+ * (prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel),
+ * "gemm_shape" (0 = automatic LDS-ring tile; 1, 2, 3, 4 force 2x4, 2x8,
+ * 4x4, 4x8 blocks of 16 weight rows per wave x 16 tokens), "small_rb" (1 =
  * products of 3..16 tokens share activation fragments over 4 row blocks
  * or split k, 0 = one row block per work-group).
  * Results do not depend on them beyond rounding.  0, or -1 for an unknown

@@ -40,8 +40,8 @@ struct Tuning {
     int attn_chunk_min = 0;   // smallest cells per wave of split attention
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
     int small_rb = 1;         // several-token products: 4 row blocks per work-group / split k (0 = off)
-    int gemm = 1;             // prefill products: 0 = register-staged kernel, 1 = LDS-ring kernel except
-                              // residual products, 2 = LDS-ring kernel for all
+    int gemm = 1;             // prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel
+    int gemm_shape = 0;       // LDS-ring tile (0 = automatic; 1..4 force 2x4, 2x8, 4x4, 4x8 row x token blocks)
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;

@@ -791,7 +791,9 @@ template <int WT, int RBW, int TB, int KS> struct GemmCfg {
 };
 
 template <int WT, int EPI, int RBW, int TB, int SPLITK, int KS>
-__global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a, int n_wtiles, int n_ttiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_lds_kernel(LinearArgs a,
+                                                                                             int n_wtiles,
+                                                                                             int n_ttiles) {
     // (the host pass only needs the launch stub; the buffer-resource
     // builtins below exist for the device pass alone)
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -960,18 +962,13 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(LinearArgs a, int n_wtile
 
 template <int WT, int EPI, int RBW, int TB, int SPLITK>
 static void launch_gemm_lds(const LinearArgs &a, hipStream_t s) {
-    // 128-wide stages for bf16 when K allows; q8_0 keeps two activation
-    // planes in the ring and uses 64-wide stages (K is a multiple of 64)
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
     const int total = n_wtiles * n_ttiles * SPLITK;
-    constexpr int KW = WT == W_Q8 ? 64 : 128;   // the wide stage of this weight type
-    if (a.K % KW == 0)
-        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, KW>), dim3(total), dim3(256), 0, s, a,
-                           n_wtiles, n_ttiles);
-    else
-        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64>), dim3(total), dim3(256), 0, s, a,
-                           n_wtiles, n_ttiles);
+    // 64-wide stages: the kernel then fits 2 waves per SIMD (two work-groups
+    // per CU), which hides the LDS reads and barriers of one behind the other
+    hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64>), dim3(total), dim3(256), 0, s, a, n_wtiles,
+                       n_ttiles);
 }
 
 // Shape choice for the LDS-ring product: the largest tile (256 rows x 128
@@ -982,24 +979,32 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     auto tiles = [&](int rbw, int tb) {
         return (long)((a.N + 64 * rbw - 1) / (64 * rbw)) * ((a.T + 16 * tb - 1) / (16 * tb));
     };
-    // q8_0 (two activation planes and the scale products) uses 2 row
-    // blocks per wave, bf16 up to 4
-    constexpr int RBW = WT == W_Q8 ? 2 : 4;
+    // forced shapes for measurements
+    switch (g_tuning.gemm_shape) {
+    case 1: launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s); return;
+    case 2: launch_gemm_lds<WT, EPI, 2, 8, 1>(a, s); return;
+    case 3: launch_gemm_lds<WT, EPI, 4, 4, 1>(a, s); return;
+    case 4: if (WT != W_Q8) { launch_gemm_lds<WT, EPI, WT == W_Q8 ? 2 : 4, 8, 1>(a, s); return; } break;
+    default: break;
+    }
+    // residual products: 128 x 64 tiles, splitting k (atomic partial sums)
+    // only when there are too few tiles for the CUs
     if (EPI == EPI_RESID) {
-        const long t = tiles(RBW, 8);
-        const int nst = a.K / 128;
-        if (t >= 192 || nst < 8)
-            launch_gemm_lds<WT, EPI, RBW, 8, 1>(a, s);
-        else if (t * 2 >= 192 || nst < 16)
-            launch_gemm_lds<WT, EPI, RBW, 8, 2>(a, s);
+        const long t = tiles(2, 4);
+        if (t >= 192 || a.K < 1024)
+            launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s);
+        else if (t * 2 >= 192 || a.K < 2048)
+            launch_gemm_lds<WT, EPI, 2, 4, 2>(a, s);
         else
-            launch_gemm_lds<WT, EPI, RBW, 8, 4>(a, s);
+            launch_gemm_lds<WT, EPI, 2, 4, 4>(a, s);
         return;
     }
-    if (tiles(RBW, 8) >= 192)
-        launch_gemm_lds<WT, EPI, RBW, 8, 1>(a, s);
-    else if (tiles(2, 8) >= 192)
-        launch_gemm_lds<WT, EPI, 2, 8, 1>(a, s);
+    // wide products: 256 x 128 tiles (bf16) / 256 x 64 (q8_0: two activation
+    // planes and the scale products); narrower ones 128 x 64
+    if (WT == W_Q8 && tiles(4, 4) >= 192)
+        launch_gemm_lds<WT, EPI, 4, 4, 1>(a, s);
+    else if (WT != W_Q8 && tiles(4, 8) >= 192)
+        launch_gemm_lds<WT, EPI, WT == W_Q8 ? 2 : 4, 8, 1>(a, s);
     else
         launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s);
 }
@@ -1021,9 +1026,7 @@ static bool try_gemm(const LinearArgs &a, hipStream_t s) {
     } else {
     if (a.T < 64 || a.K % 64) return false;
     if (EPI == EPI_SWIGLU && a.N % 32) return false;
-    // residual products (narrow N, split k) run faster on the register-
-    // staged kernel; the others on the LDS-ring kernel
-    if (g_tuning.gemm == 2 || (g_tuning.gemm == 1 && EPI != EPI_RESID)) {
+    if (g_tuning.gemm != 0) {
         launch_gemm_lds_shape<WT, EPI>(a, s);
         return true;
     }

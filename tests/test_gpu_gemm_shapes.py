@@ -40,16 +40,18 @@ def built():
     return out
 
 
-def gpu_logits(model, tokens, gemm):
+def gpu_logits(model, tokens, gemm, shape=0):
     from llama_decode_ubatch_amd import Context
     from llama_decode_ubatch_amd.binding import set_tuning
     set_tuning("gemm", gemm)
+    set_tuning("gemm_shape", shape)
     try:
         ctx = Context(model, n_ctx=512, n_batch=512, n_ubatch=512, n_seq_max=1, type_k="f16", type_v="f16")
         assert ctx.decode(tokens, logits=np.ones(len(tokens))) == 0
         return ctx.logits()
     finally:
         set_tuning("gemm", 1)
+        set_tuning("gemm_shape", 0)
 
 
 @pytest.mark.parametrize("key", list(SHAPES))
@@ -65,8 +67,8 @@ def test_prefill_gemm_matches_oracle(built, key, n):
     err = float(np.abs(z - zr).max() / np.abs(zr).max())
     print(f"{key} T={n}: logits rel err {err:.2e}", flush=True)
     assert err < TOL[shape.wtype]
-    # the other kernel choices (register-staged for all products; LDS-ring
-    # for all, residual products included) must sit within the tolerance too
-    for choice in (0, 2):
-        zc = gpu_logits(model, tokens, choice)
+    # the other kernel choices (register-staged kernel; LDS-ring kernel with
+    # each forced tile shape) must sit within the tolerance too
+    for choice in ((0, 0), (1, 1), (1, 2), (1, 3), (1, 4)):
+        zc = gpu_logits(model, tokens, *choice)
         assert float(np.abs(zc - zr).max() / np.abs(zr).max()) < TOL[shape.wtype], choice
