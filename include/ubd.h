@@ -302,7 +302,9 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * (0 = few-token products read activations from global memory), "gemm"
  * (prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel),
  * "gemm_shape" (0 = automatic LDS-ring tile; 1, 2, 3, 4 force 2x4, 2x8,
- * 4x4, 4x8 blocks of 16 weight rows per wave x 16 tokens), "small_rb" (1 =
+ * 4x4, 4x8 blocks of 16 weight rows per wave x 16 tokens), "gemm_split"
+ * (residual prefill products: 0 = automatic k split, 2 or 4 forced),
+ * "small_rb" (1 =
  * products of 3..16 tokens share activation fragments over 4 row blocks
  * or split k, 0 = one row block per work-group).
  * Results do not depend on them beyond rounding.  0, or -1 for an unknown

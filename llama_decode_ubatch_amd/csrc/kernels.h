@@ -41,6 +41,7 @@ struct Tuning {
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
     int small_rb = 1;         // several-token products: 4 row blocks per work-group / split k (0 = off)
     int gemm = 1;             // prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel
+    int gemm_split = 0;       // residual prefill products: forced k split (2, 4; 0 = automatic)
     int gemm_shape = 0;       // LDS-ring tile (0 = automatic; 1..4 force 2x4, 2x8, 4x4, 4x8 row x token blocks)
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use

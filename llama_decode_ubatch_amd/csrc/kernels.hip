@@ -991,7 +991,19 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     // only when there are too few tiles for the CUs
     if (EPI == EPI_RESID) {
         const long t = tiles(2, 4);
-        if (t >= 192 || a.K < 1024)
+        if (g_tuning.gemm_split == 2) {
+            launch_gemm_lds<WT, EPI, 2, 4, 2>(a, s);
+            return;
+        }
+        if (g_tuning.gemm_split == 4) {
+            launch_gemm_lds<WT, EPI, 2, 4, 4>(a, s);
+            return;
+        }
+        // (long k, e.g. the FFN down product: 2-way split even with enough
+        // tiles, which measured faster despite the atomic adds)
+        if (a.K >= 8192 && t >= 192)
+            launch_gemm_lds<WT, EPI, 2, 4, 2>(a, s);
+        else if (t >= 192 || a.K < 1024)
             launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s);
         else if (t * 2 >= 192 || a.K < 2048)
             launch_gemm_lds<WT, EPI, 2, 4, 2>(a, s);

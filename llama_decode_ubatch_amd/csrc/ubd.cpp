@@ -1118,6 +1118,8 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.ldsx = value;
     } else if (k == "gemm") {
         g_tuning.gemm = value;
+    } else if (k == "gemm_split") {
+        g_tuning.gemm_split = value;
     } else if (k == "gemm_shape") {
         g_tuning.gemm_shape = value;
     } else if (k == "small_rb") {
