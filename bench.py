@@ -21,16 +21,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_ffn_gate_up_8b_bf16_traffic.txt")
+TRAFFIC_FILES = {
+    "decode.ffn_gate_up": os.path.join(ROOT, "profiles", "decode_ffn_gate_up_8b_bf16_traffic.txt"),
+    "decode.attention": os.path.join(ROOT, "profiles", "decode_attention_8b_16seq_32k_traffic.txt"),
+}
 KERNEL_SRC = os.path.join(ROOT, "llama_decode_ubatch_amd", "csrc", "kernels.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the decode gate|up product from the committed
+def measured_traffic(kernel_class):
+    """HBM bytes per launch of the roofline kernel from the committed
     rocprofv3 counter summary, if kernels.hip is unchanged since then."""
     import hashlib
     try:
-        lines = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l)
+        lines = dict(l.split(":", 1) for l in open(TRAFFIC_FILES[kernel_class]).read().splitlines() if ":" in l)
         src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
         if lines.get("kernels_hip_sha256_16", "").strip() != src_hash:
             return None
@@ -285,7 +288,7 @@ def main():
         avg_s = kernels[hot]["avg_us"] * 1e-6
         ach = alg / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(hot),
                     "kernel": "decode.attention (attn_mfma_kernel split-K + attn_merge_kernel)",
                     "bytes_per_launch": int(alg)}
     elif "decode.ffn_gate_up" in kernels:
@@ -294,8 +297,8 @@ def main():
         avg_s = kernels["decode.ffn_gate_up"]["avg_us"] * 1e-6
         ach = alg / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                    "kernel": "decode.ffn_gate_up (linear_small_kernel, SwiGLU epilogue)",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(hot),
+                    "kernel": "decode.ffn_gate_up (linear_ldsx_kernel, fused RMSNorm, SwiGLU epilogue)",
                     "bytes_per_launch": int(alg)}
     roofline_prefill = None
     if "prefill.ffn_gate_up" in kernels and w.n_prompt:
@@ -304,7 +307,7 @@ def main():
         ach = flops / avg_s / 1e12
         roofline_prefill = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                            "kernel": "prefill.ffn_gate_up (gemm_kernel, SwiGLU epilogue)",
+                            "kernel": "prefill.ffn_gate_up (gemm_lds_kernel, SwiGLU epilogue)",
                             "flops_per_launch": flops}
 
     cpu = None
