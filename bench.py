@@ -194,6 +194,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--kv-type", choices=["f16", "q8_0"], default=None,
+                    help="override the workload's KV cache type (q8_0: 34 bytes per 32 values)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 256 MiB device-to-device (reference dispatch for HBM byte counters)")
@@ -218,6 +220,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = WORKLOADS[args.config]
+    if args.kv_type:
+        import dataclasses
+        w = dataclasses.replace(w, type_k=args.kv_type, type_v=args.kv_type)
     shape = w.model
     t0 = time.perf_counter()
     if shape.wtype == "f32":
@@ -282,13 +287,14 @@ def main():
     if hot == "decode.attention" and hot in kernels:
         # every launch reads each sequence's K and V rows (f16) once; the
         # cache grows by one cell per sequence per step
-        kvb = 2 if w.type_k == "f16" else 4
+        kvb = {"f16": 2.0, "f32": 4.0, "q8_0": 34 / 32}[w.type_k]
         cells = w.n_seqs * (w.kv_prefill + (w.n_decode + 1) / 2.0)
         alg = 2 * cells * shape.n_embd_kv * kvb + 2 * w.n_seqs * d * 4
         avg_s = kernels[hot]["avg_us"] * 1e-6
         ach = alg / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(hot),
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(hot) if w.type_k == "f16" else None,
                     "kernel": "decode.attention (attn_mfma_kernel split-K + attn_merge_kernel)",
                     "bytes_per_launch": int(alg)}
     elif "decode.ffn_gate_up" in kernels:

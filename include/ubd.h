@@ -143,8 +143,11 @@ typedef struct ubd_context_params {
     uint32_t n_batch;        /* most tokens per ubd_decode call            */
     uint32_t n_ubatch;       /* most tokens per forward pass               */
     uint32_t n_seq_max;      /* sequences; 1..UBD_MAX_SEQ                  */
-    ubd_type type_k;         /* K cache type: F32 or F16                   */
-    ubd_type type_v;         /* V cache type: F32 or F16                   */
+    ubd_type type_k;         /* K cache type: F32, F16 or Q8_0             */
+    ubd_type type_v;         /* V cache type: F32, F16 or Q8_0 (Q8_0 for
+                                both or neither; [ARCH] Ex. 10: 34 bytes
+                                per 32 values, blocks of 32 along each
+                                head's dims, scale = block max / 127)      */
     bool kv_unified;         /* false: one stream of n_ctx/n_seq_max cells
                                 per sequence; true: one shared stream      */
     ubd_abort_fn abort_callback;
@@ -251,15 +254,16 @@ int32_t ubd_get_kv_cells(ubd_context *ctx, int32_t *cells_out, int32_t cap);
 
 /* Fill positions 0..n_pos-1 of the empty sequence s with given K/V rows:
  * k_layers[l] / v_layers[l] point to [n_pos][n_head_kv * head_dim] values of
- * src_type (F16 or F32; converted to the cache types), host unless
- * on_device.  Used to start from a long pre-filled context.  Returns 0,
+ * src_type (F16 or F32; converted to the cache types, Q8_0 caches
+ * quantised block by block as at append), host unless on_device.  Used to start from a long pre-filled context.  Returns 0,
  * UBD_NO_KV_SLOT if the stream lacks room, UBD_INVALID otherwise. */
 int32_t ubd_kv_fill(ubd_context *ctx, ubd_seq_id s, int32_t n_pos,
                     const void *const *k_layers, const void *const *v_layers,
                     ubd_type src_type, int32_t on_device);
 /* Read back the K (which = 0) or V (which = 1) rows of cells
  * [cell0, cell0 + n) of one layer and KV stream as f32
- * [n][n_head_kv * head_dim] into host memory.  Synchronises.  0 or -1. */
+ * [n][n_head_kv * head_dim] into host memory (Q8_0: f16(scale) * code).
+ * Synchronises.  0 or -1. */
 int32_t ubd_kv_read(ubd_context *ctx, int32_t layer, int32_t stream,
                     int32_t which, int32_t cell0, int32_t n, float *out);
 

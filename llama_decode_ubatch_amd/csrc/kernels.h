@@ -18,7 +18,8 @@
 //    advance through k together, read one contiguous window of memory.
 //  * KV cache per layer: K [stream][kv head][cell][head_dim] and V in
 //    32-cell tiles [stream][kv head][cell / 32][head_dim][32], each of
-//    type_k / type_v.  n_cells given to the kernels is the per-stream cell
+//    type_k / type_v (q8_0: int8 codes in these layouts, then the f16 block
+//    scales, see kv_layer_bytes).  n_cells given to the kernels is the per-stream cell
 //    stride, the context's cells per stream rounded up to 32; the device
 //    cell tables [stream][n_cells] hold pos = seq = -1 in the padding.
 #pragma once
@@ -47,7 +48,13 @@ struct Tuning {
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;
 extern Tuning g_tuning;
-enum KVType : int { KV_F32 = 0, KV_F16 = 1 };
+enum KVType : int { KV_F32 = 0, KV_F16 = 1, KV_Q8 = 2 };
+// One layer of one cache (K or V) holding `elems` values: f32 / f16 values,
+// or for q8_0 the int8 codes (in the f16 layouts) followed by one f16 scale
+// per 32 values, ordered [stream][kv head][head_dim / 32][cell].
+inline size_t kv_layer_bytes(int type, size_t elems) {
+    return type == KV_F32 ? elems * 4 : type == KV_F16 ? elems * 2 : elems + elems / 32 * 2;
+}
 
 struct Act {
     float *f32 = nullptr;      // F32 format
@@ -73,6 +80,8 @@ struct QKVEpi {
     void *k_cache = nullptr;          // layer base
     void *v_cache = nullptr;
     int type_k = KV_F16, type_v = KV_F16;
+    float *kv_stage = nullptr;        // q8_0 caches: [T][2][Hk*hd] f32 K (after RoPE) and V rows,
+                                      // quantised into the cells by launch_kv_quant
 };
 
 // Fused RMSNorm of the product's input (at most NORM_TMAX rows): x row of
@@ -124,6 +133,7 @@ struct AttnArgs {
     const void *k_cache = nullptr;    // layer base
     const void *v_cache = nullptr;
     int type_k = KV_F16, type_v = KV_F16;
+    size_t layer_elems = 0;           // values per layer of each cache (q8_0 scale offset)
     const int32_t *cell_pos = nullptr, *cell_seq = nullptr; // [stream][n_cells]
     int n_cells = 0, n_head = 0, n_head_kv = 0, head_dim = 0;
     TokInfo tok;
@@ -173,6 +183,14 @@ struct RelayoutSrc {
 void launch_relayout(int wtype, const RelayoutSrc *src, int n_src, int mode,
                      int K, void *dst, uint16_t *dst_scales, hipStream_t s);
 
+// q8_0 caches: quantise KV rows [n][n_head_kv*hd] (row stride ld, src_type
+// KV_F32 / KV_F16) into the cells cells[r] of streams streams[r] (or of
+// `stream` when streams is null); is_v selects the V layout.  Per 32-value
+// block: d = amax / 127, codes = round-half-away(x / d), scale f16(d).
+void launch_kv_quant(const void *src, int src_type, int ld, int n, const int32_t *cells, const int32_t *streams,
+                     int stream, void *cache, bool is_v, int n_head_kv, int hd, int n_cells, size_t layer_elems,
+                     hipStream_t s);
+
 // KV rows [n][n_head_kv*hd] of src_type (KV_F32 / KV_F16) into the cache
 // cells cells[0..n) of one stream (K rows, V in 32-cell tiles).
 void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
@@ -181,6 +199,6 @@ void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
 // Cache rows of cells [cell0, cell0+n) of one stream as f32 [n][n_head_kv*hd].
 void launch_kv_load(const void *cache, int type, bool transposed, int stream,
                     int cell0, int n, int n_head_kv, int hd, int n_cells,
-                    float *out, hipStream_t s);
+                    size_t layer_elems, float *out, hipStream_t s);
 
 }  // namespace ubd

@@ -17,6 +17,7 @@ Tuning g_tuning;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
@@ -24,9 +25,7 @@ typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------- conversions
 __device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t b = __float_as_uint(f);
-    b += 0x7FFFu + ((b >> 16) & 1u);   // round to nearest even
-    return (uint16_t)(b >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: round to nearest even
 }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ float h2f(uint16_t h) {
@@ -75,15 +74,15 @@ template <> struct WT_<W_BF16> { static constexpr int KSTEP = 32, U = 8; };
 template <> struct WT_<W_Q8> { static constexpr int KSTEP = 64, U = 2; };
 
 __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t w0, uint32_t w1) {
-    // |code| <= 127 has at most 7 significant bits: exact in bf16, so the
-    // top half of the f32 value is the bf16 value.
-    u16x8_t r;
+    // |code| <= 127 has at most 7 significant bits: exact in bf16 (byte ->
+    // f32 conversions, then packed f32 -> bf16 conversions)
+    f32x8_t f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        r[i] = (uint16_t)(__float_as_uint((float)(int8_t)(w0 >> (8 * i))) >> 16);
-        r[4 + i] = (uint16_t)(__float_as_uint((float)(int8_t)(w1 >> (8 * i))) >> 16);
+        f[i] = (float)(int8_t)(w0 >> (8 * i));
+        f[4 + i] = (float)(int8_t)(w1 >> (8 * i));
     }
-    return __builtin_bit_cast(bf16x8_t, r);
+    return __builtin_convertvector(f, bf16x8_t);
 }
 
 template <int WT, int RB>
@@ -237,6 +236,10 @@ __device__ __forceinline__ void epilogue4(const LinearArgs &a, int t, int n, f32
         }
         if (n < q.n_q_rows) {
             store4(q.q_out + (size_t)t * q.n_q_rows + n, v);
+        } else if (n < q.n_q_rows + q.n_k_rows && q.type_k == KV_Q8) {
+            store4(q.kv_stage + (size_t)t * 2 * q.n_k_rows + (n - q.n_q_rows), v);
+        } else if (n >= q.n_q_rows + q.n_k_rows && q.type_v == KV_Q8) {
+            store4(q.kv_stage + (size_t)t * 2 * q.n_k_rows + (n - q.n_q_rows), v);
         } else if (n < q.n_q_rows + q.n_k_rows) {
             const int o = n - q.n_q_rows, head = o / hd, d = o % hd;
             const size_t idx = (((size_t)a.tok.stream[t] * q.n_head_kv + head) * q.n_cells + a.tok.cell[t]) * hd + d;
@@ -1531,7 +1534,131 @@ __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int
     }
 }
 
-template <int HD, bool SPLIT>
+// ----- q8_0 K/V: the int8 codes enter bf16 MFMAs exactly; q and P are
+// split hi + lo in bf16 (whose exponent range keeps small P * scale
+// products out of subnormals).  K scales (one per cell and 32-dim block)
+// multiply the score partial of each block; V scales are folded into P per
+// 32-dim block of V.
+template <int HD> struct KVSrcQ8 {
+    const int8_t *K, *Vt;
+    const uint16_t *ks, *vs;    // [HD/32][cells] f16 scales of this (stream, KV head)
+    const int32_t *cpos, *cseq;
+    int n_cells, r, g;
+};
+
+template <int HD> struct KVStepQ8 {
+    static constexpr int KK = HD / 32, DB = HD / 16;
+    u32x2_t k[2][KK];   // codes: cell cb + r, dims 32 kk + 8g .. + 8
+    u32x2_t ksc[2][KK]; // K scales of the D rows: cells cb + 4g .. + 4, block kk
+    u32x2_t v[DB];      // codes: dim 16 db + r, slots 8g .. 8g + 8
+    u32x2_t vsc[KK][2]; // V scales of the P columns: cells c0 + 4g .., c0 + 16 + 4g .., block b
+    int4 p[2], s[2];
+};
+
+template <int HD>
+__device__ __forceinline__ void kv_step_load_q8(KVStepQ8<HD> &b, const KVSrcQ8<HD> &src, int c0) {
+    constexpr int KK = HD / 32, DB = HD / 16;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+        const int cb = c0 + 16 * b2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            b.k[b2][kk] = *(const u32x2_t *)(src.K + (size_t)(cb + src.r) * HD + 32 * kk + 8 * src.g);
+            b.ksc[b2][kk] = *(const u32x2_t *)(src.ks + (size_t)kk * src.n_cells + cb + 4 * src.g);
+        }
+        b.p[b2] = *(const int4 *)(src.cpos + cb + 4 * src.g);
+        b.s[b2] = *(const int4 *)(src.cseq + cb + 4 * src.g);
+    }
+    const int8_t *vt = src.Vt + (size_t)(c0 >> 5) * HD * 32 + src.r * 32 + 8 * src.g;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) b.v[db] = *(const u32x2_t *)(vt + db * 16 * 32);
+#pragma unroll
+    for (int kb = 0; kb < KK; ++kb) {
+        b.vsc[kb][0] = *(const u32x2_t *)(src.vs + (size_t)kb * src.n_cells + c0 + 4 * src.g);
+        b.vsc[kb][1] = *(const u32x2_t *)(src.vs + (size_t)kb * src.n_cells + c0 + 16 + 4 * src.g);
+    }
+}
+
+__device__ __forceinline__ float h2f_lo(uint32_t w) { return h2f((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float h2f_hi(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+template <int HD>
+__device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0, int cend, const bf16x8_t *qh,
+                                                   const bf16x8_t *ql, bool row_ok, int rseq, int rpos, int g,
+                                                   float &m, float &l, f32x4_t *O) {
+    constexpr int KK = HD / 32, DB = HD / 16;
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t S[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+        f32x4_t acc = z;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8_t A = i8x8_to_bf16(b.k[b2][kk][0], b.k[b2][kk][1]);
+            f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qh[kk], z, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, ql[kk], d, 0, 0, 0);
+            const f32x4_t sc = {h2f_lo(b.ksc[b2][kk][0]), h2f_hi(b.ksc[b2][kk][0]), h2f_lo(b.ksc[b2][kk][1]),
+                                h2f_hi(b.ksc[b2][kk][1])};
+            acc += sc * d;
+        }
+        const int cc = c0 + 16 * b2 + 4 * g;
+        const int pp[4] = {b.p[b2].x, b.p[b2].y, b.p[b2].z, b.p[b2].w};
+        const int ss[4] = {b.s[b2].x, b.s[b2].y, b.s[b2].z, b.s[b2].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool vis = row_ok && cc + i < cend && ss[i] == rseq && pp[i] >= 0 && pp[i] <= rpos;
+            acc[i] = vis ? acc[i] : -INFINITY;
+        }
+        S[b2] = acc;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m - m_new);
+    float pv[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sv = S[b2][i];
+            const float p = sv == -INFINITY ? 0.f : expf(sv - m_new);
+            ps += p;
+            pv[4 * b2 + i] = p;
+        }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = m_new;
+    f32x4_t al;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+    for (int kb = 0; kb < KK; ++kb) {
+        // P of this lane's 8 cells times their V scales of dim block kb
+        f32x8_t x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t w = b.vsc[kb][e >> 2][(e & 3) >> 1];
+            x[e] = pv[e] * ((e & 1) ? h2f_hi(w) : h2f_lo(w));
+        }
+        const bf16x8_t Ph = __builtin_convertvector(x, bf16x8_t);
+        const bf16x8_t Pl = __builtin_convertvector(x - __builtin_convertvector(Ph, f32x8_t), bf16x8_t);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int db = 2 * kb + h2;
+            const bf16x8_t B = i8x8_to_bf16(b.v[db][0], b.v[db][1]);
+            f32x4_t o = O[db] * al;
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ph, B, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pl, B, o, 0, 0, 0);
+            O[db] = o;
+        }
+    }
+}
+
+template <int HD, bool SPLIT, bool KQ>
 __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     constexpr int KK = HD / 32, DB = HD / 16;
     const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
@@ -1554,7 +1681,6 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     const int rpos = a.tok.pos[rt], rseq = a.tok.seq[rt];
     // every lane loads a valid row (rows past R read row 0) and zeroes it
     // afterwards, so the loads are unconditional and issued together
-    f16x8_t qh[KK], ql[KK];
     const float *qrow = a.q + (size_t)rt * a.n_head * HD + rh * HD + 8 * g;
     const float qs = row_ok ? scale : 0.f;
     float4 qv[KK][2];
@@ -1563,48 +1689,81 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         qv[kk][0] = *(const float4 *)(qrow + 32 * kk);
         qv[kk][1] = *(const float4 *)(qrow + 32 * kk + 4);
     }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        const float e8[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
-                             qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = e8[e] * qs;
-            const _Float16 h = (_Float16)v;
-            qh[kk][e] = h;
-            ql[kk][e] = (_Float16)(v - (float)h);
-        }
-    }
-    const _Float16 *K = (const _Float16 *)a.k_cache + ((size_t)st * a.n_head_kv + grp) * a.n_cells * HD;
-    const _Float16 *Vt = (const _Float16 *)a.v_cache + ((size_t)st * a.n_head_kv + grp) * a.n_cells * HD;
-    const int32_t *cpos = a.cell_pos + (size_t)st * a.n_cells;
-    const int32_t *cseq = a.cell_seq + (size_t)st * a.n_cells;
-
     float m = -INFINITY, l = 0.f;
     f32x4_t O[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int32_t *cpos = a.cell_pos + (size_t)st * a.n_cells;
+    const int32_t *cseq = a.cell_seq + (size_t)st * a.n_cells;
+    const size_t hbase = (size_t)st * a.n_head_kv + grp;
 
     // Two register sets: the loads of the next 32-cell step are in flight
     // while the current one is computed.  Past the range the load repeats
     // the current step's cells (in bounds, served by the cache) and the
     // compute masks every cell, so the loop has no data-dependent branch.
-    const KVSrc<HD> src{K, Vt, cpos, cseq, a.n_cells, r, g};
-    KVStep<HD> A, B;
-    if (cbeg < cend) kv_step_load(A, src, cbeg);
-    // (the scheduling fences keep the next step's score MFMAs, which do not
+    // (The scheduling fences keep the next step's score MFMAs, which do not
     // depend on the softmax state, from being hoisted above the current
-    // step and forcing an early wait on loads just issued)
-    for (int c0 = cbeg; c0 < cend; c0 += 64) {
-        const int c1 = c0 + 32, c2 = c0 + 64;
-        kv_step_load(B, src, c1 < cend ? c1 : c0);
-        __builtin_amdgcn_sched_barrier(0);
-        kv_step_compute(A, c0, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
-        __builtin_amdgcn_sched_barrier(0);
-        kv_step_load(A, src, c2 < cend ? c2 : c0);
-        __builtin_amdgcn_sched_barrier(0);
-        kv_step_compute(B, c1, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
-        __builtin_amdgcn_sched_barrier(0);
+    // step and forcing an early wait on loads just issued.)
+    if constexpr (!KQ) {
+        f16x8_t qh[KK], ql[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const float e8[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
+                                 qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = e8[e] * qs;
+                const _Float16 h = (_Float16)v;
+                qh[kk][e] = h;
+                ql[kk][e] = (_Float16)(v - (float)h);
+            }
+        }
+        const _Float16 *K = (const _Float16 *)a.k_cache + hbase * a.n_cells * HD;
+        const _Float16 *Vt = (const _Float16 *)a.v_cache + hbase * a.n_cells * HD;
+        const KVSrc<HD> src{K, Vt, cpos, cseq, a.n_cells, r, g};
+        KVStep<HD> A, B;
+        if (cbeg < cend) kv_step_load(A, src, cbeg);
+        for (int c0 = cbeg; c0 < cend; c0 += 64) {
+            const int c1 = c0 + 32, c2 = c0 + 64;
+            kv_step_load(B, src, c1 < cend ? c1 : c0);
+            __builtin_amdgcn_sched_barrier(0);
+            kv_step_compute(A, c0, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            __builtin_amdgcn_sched_barrier(0);
+            kv_step_load(A, src, c2 < cend ? c2 : c0);
+            __builtin_amdgcn_sched_barrier(0);
+            kv_step_compute(B, c1, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        bf16x8_t qh[KK], ql[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const float e8[8] = {qv[kk][0].x, qv[kk][0].y, qv[kk][0].z, qv[kk][0].w,
+                                 qv[kk][1].x, qv[kk][1].y, qv[kk][1].z, qv[kk][1].w};
+            f32x8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = e8[e] * qs;
+            qh[kk] = __builtin_convertvector(v, bf16x8_t);
+            ql[kk] = __builtin_convertvector(v - __builtin_convertvector(qh[kk], f32x8_t), bf16x8_t);
+        }
+        const int8_t *K = (const int8_t *)a.k_cache + hbase * a.n_cells * HD;
+        const int8_t *Vt = (const int8_t *)a.v_cache + hbase * a.n_cells * HD;
+        const uint16_t *ks = (const uint16_t *)((const int8_t *)a.k_cache + a.layer_elems) + hbase * KK * a.n_cells;
+        const uint16_t *vs = (const uint16_t *)((const int8_t *)a.v_cache + a.layer_elems) + hbase * KK * a.n_cells;
+        const KVSrcQ8<HD> src{K, Vt, ks, vs, cpos, cseq, a.n_cells, r, g};
+        KVStepQ8<HD> A, B;
+        if (cbeg < cend) kv_step_load_q8(A, src, cbeg);
+        for (int c0 = cbeg; c0 < cend; c0 += 64) {
+            const int c1 = c0 + 32, c2 = c0 + 64;
+            kv_step_load_q8(B, src, c1 < cend ? c1 : c0);
+            __builtin_amdgcn_sched_barrier(0);
+            kv_step_compute_q8(A, c0, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            __builtin_amdgcn_sched_barrier(0);
+            kv_step_load_q8(A, src, c2 < cend ? c2 : c0);
+            __builtin_amdgcn_sched_barrier(0);
+            kv_step_compute_q8(B, c1, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     // O: lane (dim r of each 16-dim block, group g) holds rows 4g+i
     if (!SPLIT) {
@@ -1696,18 +1855,25 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 
 template <int HD>
 static void launch_attention_mfma_hd(const AttnArgs &a, hipStream_t s) {
+    const bool q8 = a.type_k == KV_Q8;
     if (a.split) {
         dim3 grid((unsigned)a.n_chunks_launch, a.n_tiles, a.n_head_kv);
-        hipLaunchKernelGGL((attn_mfma_kernel<HD, true>), grid, dim3(64), 0, s, a);
+        if (q8)
+            hipLaunchKernelGGL((attn_mfma_kernel<HD, true, true>), grid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_mfma_kernel<HD, true, false>), grid, dim3(64), 0, s, a);
         hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(a.T * a.n_head), dim3(64), 0, s, a);
     } else {
         dim3 grid(1, a.n_tiles, a.n_head_kv);
-        hipLaunchKernelGGL((attn_mfma_kernel<HD, false>), grid, dim3(64), 0, s, a);
+        if (q8)
+            hipLaunchKernelGGL((attn_mfma_kernel<HD, false, true>), grid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_mfma_kernel<HD, false, false>), grid, dim3(64), 0, s, a);
     }
 }
 
 bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa) {
-    return type_k == KV_F16 && type_v == KV_F16 && n_gqa <= 16 &&
+    return ((type_k == KV_F16 && type_v == KV_F16) || (type_k == KV_Q8 && type_v == KV_Q8)) && n_gqa <= 16 &&
            (head_dim == 32 || head_dim == 64 || head_dim == 128);
 }
 
@@ -1939,7 +2105,7 @@ void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
 
 __global__ __launch_bounds__(256) void kv_load_kernel(const void *cache, int type, int transposed, int stream,
                                                       int cell0, int n, int n_head_kv, int hd, int n_cells,
-                                                      float *out) {
+                                                      size_t layer_elems, float *out) {
     const int W = n_head_kv * hd;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)n * W) return;
@@ -1951,15 +2117,64 @@ __global__ __launch_bounds__(256) void kv_load_kernel(const void *cache, int typ
         src = ((size_t)stream * n_head_kv + head) * n_cells * hd + v_off(hd, d, c);
     else
         src = (((size_t)stream * n_head_kv + head) * n_cells + c) * hd + d;
+    if (type == KV_Q8) {
+        const uint16_t *sc = (const uint16_t *)((const int8_t *)cache + layer_elems);
+        const size_t si = (((size_t)stream * n_head_kv + head) * (hd / 32) + d / 32) * n_cells + c;
+        out[idx] = h2f(sc[si]) * (float)((const int8_t *)cache)[src];
+        return;
+    }
     out[idx] = load_kv(cache, type, src);
 }
 
 void launch_kv_load(const void *cache, int type, bool transposed, int stream, int cell0, int n, int n_head_kv,
-                    int hd, int n_cells, float *out, hipStream_t s) {
+                    int hd, int n_cells, size_t layer_elems, float *out, hipStream_t s) {
     if (n <= 0) return;
     const size_t total = (size_t)n * n_head_kv * hd;
     hipLaunchKernelGGL(kv_load_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, cache, type,
-                       (int)transposed, stream, cell0, n, n_head_kv, hd, n_cells, out);
+                       (int)transposed, stream, cell0, n, n_head_kv, hd, n_cells, layer_elems, out);
+}
+
+// q8_0 quantisation of KV rows into their cells: 32 lanes per 32-value
+// block (8 blocks per work-group).  All arithmetic is single float32
+// operations with IEEE rounding (amax / 127, 1 / d, x * (1 / d)), then
+// rounding to nearest with halves away from zero, so the codes follow from
+// the inputs alone.
+__global__ __launch_bounds__(256) void kv_quant_kernel(const void *src, int src_type, int ld, int n,
+                                                       const int32_t *cells, const int32_t *streams, int stream,
+                                                       void *cache, int is_v, int n_head_kv, int hd, int n_cells,
+                                                       size_t layer_elems) {
+    const int nb = n_head_kv * hd / 32;                  // blocks per row
+    const size_t blk = ((size_t)blockIdx.x * 256 + threadIdx.x) / 32;
+    const int j = threadIdx.x & 31;
+    if (blk >= (size_t)n * nb) return;                   // whole 32-lane groups leave together
+    const int r = (int)(blk / nb), b = (int)(blk % nb);
+    const int head = b / (hd / 32), hb = b % (hd / 32), d = hb * 32 + j;
+    const size_t si = (size_t)r * ld + head * hd + d;
+    const float x = src_type == KV_F32 ? ((const float *)src)[si] : h2f(((const uint16_t *)src)[si]);
+    float amax = fabsf(x);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    const float dsc = __fdiv_rn(amax, 127.0f);
+    const float inv = dsc > 0.f ? __fdiv_rn(1.0f, dsc) : 0.f;
+    const float q = roundf(__fmul_rn(x, inv));
+    const int st = streams ? streams[r] : stream;
+    const size_t c = (size_t)cells[r];
+    const size_t hb0 = (size_t)st * n_head_kv + head;
+    int8_t *codes = (int8_t *)cache;
+    if (is_v)
+        codes[hb0 * n_cells * hd + v_off(hd, d, c)] = (int8_t)q;
+    else
+        codes[(hb0 * n_cells + c) * hd + d] = (int8_t)q;
+    if (j == 0) ((uint16_t *)(codes + layer_elems))[(hb0 * (hd / 32) + hb) * n_cells + c] = f2h(dsc);
+}
+
+void launch_kv_quant(const void *src, int src_type, int ld, int n, const int32_t *cells, const int32_t *streams,
+                     int stream, void *cache, bool is_v, int n_head_kv, int hd, int n_cells, size_t layer_elems,
+                     hipStream_t s) {
+    if (n <= 0) return;
+    const size_t threads = (size_t)n * n_head_kv * hd;   // one lane per value
+    hipLaunchKernelGGL(kv_quant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, src, src_type, ld,
+                       n, cells, streams, stream, cache, (int)is_v, n_head_kv, hd, n_cells, layer_elems);
 }
 
 }  // namespace ubd

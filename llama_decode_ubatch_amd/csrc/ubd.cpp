@@ -363,6 +363,8 @@ struct ubd_context : public Executor {
     DevAlloc mem;
     int type_k = KV_F16, type_v = KV_F16;
     size_t kv_layer_elems = 0;              // per layer, K or V
+    size_t k_layer_bytes = 0, v_layer_bytes = 0;
+    float *kv_stage = nullptr;              // q8_0 caches: [cap][2][Hk*hd] rows awaiting quantisation
     uint32_t cell_stride = 0;               // cells per stream rounded up to 32
     void *k_cache = nullptr, *v_cache = nullptr;
     int32_t *cell_pos = nullptr, *cell_seq = nullptr;
@@ -478,8 +480,15 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     };
     if (!model || !params) return fail(-1, "ubd_init_from_model: missing arguments");
     const ubd_context_params cp = *params;
-    auto kvt = [](ubd_type t) { return t == UBD_TYPE_F32 ? KV_F32 : t == UBD_TYPE_F16 ? KV_F16 : -1; };
-    if (kvt(cp.type_k) < 0 || kvt(cp.type_v) < 0) return fail(-1, "ubd_init_from_model: KV types must be F32 or F16");
+    auto kvt = [](ubd_type t) {
+        return t == UBD_TYPE_F32 ? KV_F32 : t == UBD_TYPE_F16 ? KV_F16 : t == UBD_TYPE_Q8_0 ? KV_Q8 : -1;
+    };
+    if (kvt(cp.type_k) < 0 || kvt(cp.type_v) < 0)
+        return fail(-1, "ubd_init_from_model: KV types must be F32, F16 or Q8_0");
+    if ((kvt(cp.type_k) == KV_Q8) != (kvt(cp.type_v) == KV_Q8))
+        return fail(-1, "ubd_init_from_model: a Q8_0 KV cache needs type_k == type_v == Q8_0");
+    if (kvt(cp.type_k) == KV_Q8 && !attn_mfma_ok(KV_Q8, KV_Q8, model->head_dim, model->hp.n_head / model->hp.n_head_kv))
+        return fail(-1, "ubd_init_from_model: a Q8_0 KV cache needs head_dim 32, 64 or 128 and n_head / n_head_kv <= 16");
     ubd_context *c = new ubd_context();
     c->model = model;
     c->cp = cp;
@@ -512,16 +521,17 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     c->cell_stride = (P.n_cells + 31) / 32 * 32;
     const size_t cells = (size_t)P.n_stream * c->cell_stride;
     c->kv_layer_elems = cells * Hk * hd;
-    const size_t kb = c->type_k == KV_F32 ? 4 : 2, vb = c->type_v == KV_F32 ? 4 : 2;
-    c->k_cache = c->mem.get(c->kv_layer_elems * hp.n_layer * kb);
-    c->v_cache = c->mem.get(c->kv_layer_elems * hp.n_layer * vb);
+    c->k_layer_bytes = kv_layer_bytes(c->type_k, c->kv_layer_elems);
+    c->v_layer_bytes = kv_layer_bytes(c->type_v, c->kv_layer_elems);
+    c->k_cache = c->mem.get(c->k_layer_bytes * hp.n_layer);
+    c->v_cache = c->mem.get(c->v_layer_bytes * hp.n_layer);
     c->cell_pos = (int32_t *)c->mem.get(cells * 4);
     c->cell_seq = (int32_t *)c->mem.get(cells * 4);
     if (!c->k_cache || !c->v_cache || !c->cell_pos || !c->cell_seq) return bail("KV cache allocation failed");
     // zero K/V: masked cells still enter P*V with weight 0, so never-written
     // cells must hold finite values
-    if (!hip_ok(hipMemsetAsync(c->k_cache, 0, c->kv_layer_elems * hp.n_layer * kb, c->stream), "memset") ||
-        !hip_ok(hipMemsetAsync(c->v_cache, 0, c->kv_layer_elems * hp.n_layer * vb, c->stream), "memset"))
+    if (!hip_ok(hipMemsetAsync(c->k_cache, 0, c->k_layer_bytes * hp.n_layer, c->stream), "memset") ||
+        !hip_ok(hipMemsetAsync(c->v_cache, 0, c->v_layer_bytes * hp.n_layer, c->stream), "memset"))
         return bail("KV cache init failed");
     if (!hip_ok(hipMemsetAsync(c->cell_pos, 0xff, cells * 4, c->stream), "memset") ||
         !hip_ok(hipMemsetAsync(c->cell_seq, 0xff, cells * 4, c->stream), "memset"))
@@ -540,6 +550,10 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     };
     c->x = (float *)c->mem.get((size_t)cap * d * 4);
     c->q = (float *)c->mem.get((size_t)cap * H * hd * 4);
+    if (c->type_k == KV_Q8) {
+        c->kv_stage = (float *)c->mem.get((size_t)cap * 2 * Hk * hd * 4);
+        if (!c->kv_stage) return bail("KV staging allocation failed");
+    }
     if (!c->x || !c->q || !make_act(c->actA, d) || !make_act(c->actB, H * hd) || !make_act(c->actC, F))
         return bail("activation allocation failed");
     c->max_chunks = (int)((P.n_cells + ATTN_CHUNK - 1) / ATTN_CHUNK);
@@ -577,7 +591,7 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     if (!hip_ok(hipStreamSynchronize(c->stream), "init sync")) return bail("sync failed");
     log_line(1, "context: n_ctx %u (%u streams x %u cells), n_batch %u, n_ubatch %u, KV %.1f MiB", P.n_ctx,
              P.n_stream, P.n_cells, P.n_batch, P.n_ubatch,
-             (double)c->kv_layer_elems * hp.n_layer * (kb + vb) / 1048576.0);
+             (double)(c->k_layer_bytes + c->v_layer_bytes) * hp.n_layer / 1048576.0);
     if (status) *status = 0;
     return c;
 }
@@ -705,7 +719,6 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     timed(0 + ph, [&] { launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, stream); });
     if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, stream), "dump");
 
-    const size_t kb = type_k == KV_F32 ? 4 : 2, vb = type_v == KV_F32 ? 4 : 2;
     for (int il = 0; il < hp.n_layer; ++il) {
         const auto &L = M.layers[il];
         const bool fuse_norm = T <= NORM_TMAX && g_tuning.fuse_norm != 0;
@@ -731,12 +744,23 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         la.qkv.n_cells = n_cells;
         la.qkv.inv_freq = inv_freq;
         la.qkv.q_out = q;
-        la.qkv.k_cache = (char *)k_cache + kv_layer_elems * il * kb;
-        la.qkv.v_cache = (char *)v_cache + kv_layer_elems * il * vb;
+        la.qkv.k_cache = (char *)k_cache + k_layer_bytes * il;
+        la.qkv.v_cache = (char *)v_cache + v_layer_bytes * il;
+        la.qkv.kv_stage = kv_stage;
         la.qkv.type_k = type_k;
         la.qkv.type_v = type_v;
         if (fuse_norm) la.norm = NormIn{x, nullptr, L.attn_norm, hp.rms_eps, d};
-        timed(4 + ph, [&] { launch_linear(la, stream); });
+        timed(4 + ph, [&] {
+            launch_linear(la, stream);
+            if (type_k == KV_Q8) {
+                // the epilogue staged the f32 K / V rows: quantise them into their cells
+                const int ne = Hk * hd;
+                launch_kv_quant(kv_stage, KV_F32, 2 * ne, T, ti.cell, ti.stream, 0, la.qkv.k_cache, false, Hk, hd,
+                                n_cells, kv_layer_elems, stream);
+                launch_kv_quant(kv_stage + ne, KV_F32, 2 * ne, T, ti.cell, ti.stream, 0, la.qkv.v_cache, true, Hk, hd,
+                                n_cells, kv_layer_elems, stream);
+            }
+        });
 
         AttnArgs aa;
         aa.q = q;
@@ -744,6 +768,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         aa.v_cache = la.qkv.v_cache;
         aa.type_k = type_k;
         aa.type_v = type_v;
+        aa.layer_elems = kv_layer_elems;
         aa.cell_pos = cell_pos;
         aa.cell_seq = cell_seq;
         aa.n_cells = n_cells;
@@ -975,7 +1000,6 @@ extern "C" int32_t ubd_kv_fill(ubd_context *ctx, ubd_seq_id s, int32_t n_pos, co
               hip_ok(hipMemcpy(dcells, cells.data(), cells.size() * 4, hipMemcpyHostToDevice), "kv_fill cells");
     if (ok && !on_device) ok = hip_ok(hipMalloc(&stage, rows_bytes), "kv_fill staging");
     const int srct = src_type == UBD_TYPE_F32 ? KV_F32 : KV_F16;
-    const size_t kb = ctx->type_k == KV_F32 ? 4 : 2, vb = ctx->type_v == KV_F32 ? 4 : 2;
     for (int il = 0; ok && il < hp.n_layer; ++il) {
         for (int which = 0; ok && which < 2; ++which) {
             const void *src = which == 0 ? k_layers[il] : v_layers[il];
@@ -988,10 +1012,15 @@ extern "C" int32_t ubd_kv_fill(ubd_context *ctx, ubd_seq_id s, int32_t n_pos, co
                 ok = hip_ok(hipMemcpyAsync(stage, src, rows_bytes, hipMemcpyHostToDevice, ctx->stream), "kv upload");
                 src = stage;
             }
-            void *cache = which == 0 ? (char *)ctx->k_cache + ctx->kv_layer_elems * il * kb
-                                     : (char *)ctx->v_cache + ctx->kv_layer_elems * il * vb;
-            launch_kv_store(src, srct, n_pos, dcells, cache, which == 0 ? ctx->type_k : ctx->type_v, which == 1, st,
-                            Hk, hd, (int)ctx->cell_stride, ctx->stream);
+            void *cache = which == 0 ? (char *)ctx->k_cache + ctx->k_layer_bytes * il
+                                     : (char *)ctx->v_cache + ctx->v_layer_bytes * il;
+            const int ct = which == 0 ? ctx->type_k : ctx->type_v;
+            if (ct == KV_Q8)
+                launch_kv_quant(src, srct, Hk * hd, n_pos, dcells, nullptr, st, cache, which == 1, Hk, hd,
+                                (int)ctx->cell_stride, ctx->kv_layer_elems, ctx->stream);
+            else
+                launch_kv_store(src, srct, n_pos, dcells, cache, ct, which == 1, st, Hk, hd, (int)ctx->cell_stride,
+                                ctx->stream);
             ok = ok && hip_ok(hipGetLastError(), "kv_store");
             if (!on_device) ok = ok && hip_ok(hipStreamSynchronize(ctx->stream), "kv sync");
         }
@@ -1019,11 +1048,10 @@ extern "C" int32_t ubd_kv_read(ubd_context *ctx, int32_t layer, int32_t stream, 
     const size_t bytes = (size_t)n * Hk * hd * 4;
     float *tmp = nullptr;
     if (!hip_ok(hipMalloc(&tmp, bytes), "kv_read alloc")) return UBD_ALLOC_FAILED;
-    const size_t kb = ctx->type_k == KV_F32 ? 4 : 2, vb = ctx->type_v == KV_F32 ? 4 : 2;
-    const void *cache = which == 0 ? (const char *)ctx->k_cache + ctx->kv_layer_elems * layer * kb
-                                   : (const char *)ctx->v_cache + ctx->kv_layer_elems * layer * vb;
+    const void *cache = which == 0 ? (const char *)ctx->k_cache + ctx->k_layer_bytes * layer
+                                   : (const char *)ctx->v_cache + ctx->v_layer_bytes * layer;
     launch_kv_load(cache, which == 0 ? ctx->type_k : ctx->type_v, which == 1, stream, cell0, n, Hk, hd,
-                   (int)ctx->cell_stride, tmp, ctx->stream);
+                   (int)ctx->cell_stride, ctx->kv_layer_elems, tmp, ctx->stream);
     bool ok = hip_ok(hipGetLastError(), "kv_load") && hip_ok(hipStreamSynchronize(ctx->stream), "kv_read sync") &&
               hip_ok(hipMemcpy(out, tmp, bytes, hipMemcpyDeviceToHost), "kv_read copy");
     (void)hipFree(tmp);

@@ -106,19 +106,60 @@ def q8_0_dequant(q: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
             * s[:, :, None]).reshape(rows, cols)
 
 
+def q8_0_quantize(x: np.ndarray):
+    """Blocks of 32 consecutive values of each row to (int8 codes, f16 scale).
+
+    The pages fix the block (architecture page, Example 2: 32 one-byte
+    integers and a 2-byte scale; Example 10: a q8_0 KV cache stores 34 bytes
+    per 32 values) but not how the codes are chosen.  Reading: symmetric,
+    the block's largest magnitude maps to 127.  In float32: d = amax / 127,
+    codes = x * (1 / d) rounded to nearest with halves away from zero (all
+    codes 0 when d = 0); the scale kept is f16(d) (round to nearest even).
+
+    x: float32 [..., n], n a multiple of 32 -> (int8 [..., n], uint16 [..., n / 32]).
+    """
+    x = np.asarray(x, np.float32)
+    n = x.shape[-1]
+    assert n % Q8_0_BLOCK == 0
+    b = x.reshape(x.shape[:-1] + (n // Q8_0_BLOCK, Q8_0_BLOCK))
+    amax = np.abs(b).max(axis=-1)
+    d = (amax / np.float32(127)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(d > 0, np.float32(1) / d, np.float32(0)).astype(np.float32)
+    v = (b * inv[..., None]).astype(np.float32)
+    q = np.sign(v) * np.floor(np.abs(v) + np.float32(0.5))
+    codes = q.astype(np.int8).reshape(x.shape)
+    return codes, d.astype(np.float16).view(np.uint16)
+
+
 def round_to_kv_type(x: np.ndarray, kv_type: str) -> np.ndarray:
     """Value as stored in a KV cell of type_k / type_v.
 
     "llama.cpp Architecture" page, Example 4: SET_ROWS writes the f32 key into
     an F16 cache tensor; "-ctk/-ctv" choose the cache types (engine page,
-    KV-cache section).  f16 uses IEEE round-to-nearest-even (NumPy's cast).
+    KV-cache section; decode-loop page, context parameters: F16, Q8_0, ...).
+    f16 uses IEEE round-to-nearest-even (NumPy's cast); q8_0 quantises each
+    32-value block of the row (q8_0_quantize) and stores what dequantises
+    back, f16(d) * code.
     """
     if kv_type == "f32":
         return x.astype(np.float32)
     if kv_type == "f16":
         return x.astype(np.float16)
+    if kv_type == "q8_0":
+        x = np.asarray(x, np.float32)
+        codes, sc = q8_0_quantize(x.reshape(-1, x.shape[-1]))
+        return q8_0_dequant(codes, sc).reshape(x.shape)
     raise ValueError(kv_type)
 
 
 def kv_storage_dtype(kv_type: str):
-    return {"f32": np.float32, "f16": np.float16}[kv_type]
+    return {"f32": np.float32, "f16": np.float16, "q8_0": np.float32}[kv_type]
+
+
+def kv_cache_bytes(n_layer: int, n_embd_kv: int, n_cells: int, kv_type: str) -> int:
+    """Bytes of one of the K or V caches: n_layer x n_cells rows of n_embd_kv
+    values (architecture page, Example 10: 2 bytes per value for f16, 34
+    bytes per 32 values for q8_0)."""
+    per_row = {"f32": 4 * n_embd_kv, "f16": 2 * n_embd_kv, "q8_0": 34 * n_embd_kv // Q8_0_BLOCK}[kv_type]
+    return n_layer * n_cells * per_row

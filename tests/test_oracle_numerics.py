@@ -163,3 +163,45 @@ def test_bf16_upcast_exact():
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x7F7F], np.uint16)
     np.testing.assert_array_equal(nm.bf16_bits_to_f32(bits),
                                   np.array([1.0, -1.0, 3.140625, 0.0, 3.3895313892515355e38], np.float32))
+
+
+# ------------------------------------------------------------ q8_0 KV blocks
+def test_q8_0_quantize_exact_scale_block():
+    # amax 127 gives d = 1 and 1/d = 1 exactly: codes are x rounded to
+    # nearest with halves away from zero
+    x = np.zeros(32, np.float32)
+    x[:8] = [127.0, -127.0, 2.5, -2.5, 0.49, -0.51, 63.5, -0.5]
+    codes, sc = nm.q8_0_quantize(x[None, :])
+    assert codes[0, :8].tolist() == [127, -127, 3, -3, 0, -1, 64, -1]
+    assert np.all(codes[0, 8:] == 0)
+    assert nm.f16_bits_to_f32(sc)[0, 0] == 1.0
+
+
+def test_q8_0_quantize_error_bound_and_range():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((64, 128)) * rng.uniform(1e-3, 10, (64, 1))).astype(np.float32)
+    codes, sc = nm.q8_0_quantize(x)
+    assert codes.min() >= -127 and codes.max() <= 127
+    # every block reaches +-127 at its largest magnitude
+    assert np.all(np.abs(codes.reshape(64, 4, 32)).max(-1) == 127)
+    d = np.abs(x.reshape(64, 4, 32)).max(-1) / 127
+    y = nm.q8_0_dequant(codes, sc)
+    # rounding to the code grid (half a step) plus the f16 rounding of the scale
+    err = np.abs(y - x).reshape(64, 4, 32).max(-1)
+    assert np.all(err <= d * (0.5 + 127 * 2.0 ** -11) * (1 + 1e-6))
+    # stored value = round_to_kv_type
+    assert np.array_equal(nm.round_to_kv_type(x, "q8_0"), y)
+
+
+def test_q8_0_quantize_zero_block():
+    codes, sc = nm.q8_0_quantize(np.zeros((2, 64), np.float32))
+    assert not codes.any() and not sc.any()
+    assert not nm.round_to_kv_type(np.zeros((2, 64), np.float32), "q8_0").any()
+
+
+def test_q8_0_quantize_rejects_planted_offset():
+    # a quantiser that forgot the sign of the halves would fail the tie case
+    x = np.zeros(32, np.float32)
+    x[0], x[1] = 127.0, -2.5
+    codes, _ = nm.q8_0_quantize(x[None, :])
+    assert codes[0, 1] == -3 and np.trunc(-2.5 + 0.5) != -3

@@ -61,6 +61,9 @@ def test_kv_and_output_buffer_sizes():
     k_f16 = TINY.n_layer * TINY.n_embd_kv * cells * 2
     assert round(k_f16 / MIB, 2) == G["ex10_k_f16_MiB"] == G["ex10_v_f16_MiB"]
     assert round(TINY.n_layer * q8_0_bytes(TINY.n_embd_kv * cells) / MIB, 2) == G["ex10_k_q8_0_MiB"]
+    from oracle.numerics import kv_cache_bytes
+    assert kv_cache_bytes(TINY.n_layer, TINY.n_embd_kv, cells, "f16") == k_f16
+    assert round(kv_cache_bytes(TINY.n_layer, TINY.n_embd_kv, cells, "q8_0") / MIB, 2) == G["ex10_k_q8_0_MiB"]
     assert round(TINY.n_vocab * 4 / MIB, 2) == G["ex10_output_row_MiB"]
     for ub, mib in G["ex10_logits_full_ubatch_MiB"].items():
         assert round(int(ub) * TINY.n_vocab * 4 / MIB, 2) == mib
