@@ -234,6 +234,56 @@ ubd_token ubd_sample_greedy(ubd_context *ctx, int32_t i);
  * Returns the number of rows written, or -1. */
 int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32_t cap);
 
+/* Sampler chain ([ENG] Steps 14-16, "Sampler chain"): penalties of the
+ * tokens already chosen, then the top-k, top-p and min-p cut-offs, then
+ * temperature, then one random token.  Readings where the page gives no
+ * formula:
+ *   - penalties act on the distinct tokens of the last penalty_last_n
+ *     history entries, count c: logit / repeat if logit > 0 else logit *
+ *     repeat, then minus c * freq and minus present;
+ *   - candidates are ordered by logit descending, ties by lower id;
+ *   - top_k (1 .. 1024) keeps the first top_k;
+ *   - top_p < 1 keeps the shortest prefix whose softmax mass (temperature
+ *     1) reaches top_p;
+ *   - min_p > 0 keeps probabilities >= min_p times the largest;
+ *   - temperature > 0 divides the logits (<= 0: the first candidate);
+ *   - the draw takes u in [0, 1) and returns the first candidate whose
+ *     accumulated probability exceeds u.
+ * The sampler keeps its own history, like the pages' chain: every sampled
+ * token is appended, and ubd_sampler_accept appends others (a prompt). */
+typedef struct ubd_sampler_params {
+    int32_t top_k;           /* 1 .. 1024                                   */
+    float top_p;             /* (0, 1]; 1 = off                             */
+    float min_p;             /* [0, 1); 0 = off                             */
+    float temperature;       /* > 0; <= 0 picks the largest logit           */
+    int32_t penalty_last_n;  /* 0 .. 256 history entries penalised; 0 = off */
+    float penalty_repeat;    /* 1 = off                                     */
+    float penalty_freq;      /* 0 = off                                     */
+    float penalty_present;   /* 0 = off                                     */
+} ubd_sampler_params;
+typedef struct ubd_sampler ubd_sampler;
+
+/* top_k 40, top_p 1, min_p 0, temperature 1, no penalties. */
+ubd_sampler_params ubd_sampler_default_params(void);
+/* A sampler for rows of ctx's logits; device buffers on ctx's device.
+ * NULL (see ubd_last_error) for parameters out of range. */
+ubd_sampler *ubd_sampler_init(ubd_context *ctx, ubd_sampler_params params);
+/* Frees the sampler's buffers; valid before or after its context is freed. */
+void ubd_sampler_free(ubd_sampler *smpl);
+/* Append a token to the sampler's history. */
+void ubd_sampler_accept(ubd_sampler *smpl, ubd_token token);
+/* Run the chain on logits row i (as in ubd_get_logits_ith) of the
+ * sampler's context, draw with u in [0, 1), append the token to the
+ * history and return it; -1 for an invalid i or u.  Synchronises. */
+ubd_token ubd_sampler_sample(ubd_sampler *smpl, int32_t i, float u);
+/* The same chain on a caller's row of n_vocab float logits in device
+ * memory of the sampler's device (ordered on the context's stream, read
+ * only).  Appends the token to the history; -1 for invalid arguments. */
+ubd_token ubd_sampler_sample_logits(ubd_sampler *smpl, const float *logits, int32_t n_vocab, float u);
+/* The candidates the last sample drew from, in order, with their
+ * probabilities: writes min(n, cap) and returns n, the count. */
+int32_t ubd_sampler_candidates(ubd_sampler *smpl, ubd_token *ids, float *probs, int32_t cap);
+
 /* Wait for all work enqueued on the context's stream.  0 or -3. */
 int32_t ubd_synchronize(ubd_context *ctx);
 

@@ -58,6 +58,13 @@ class CBatch(C.Structure):
                 ("seq_id", C.POINTER(C.POINTER(C.c_int32))), ("logits", C.POINTER(C.c_int8))]
 
 
+class SamplerParams(C.Structure):
+    _fields_ = [("top_k", C.c_int32), ("top_p", C.c_float), ("min_p", C.c_float),
+                ("temperature", C.c_float), ("penalty_last_n", C.c_int32),
+                ("penalty_repeat", C.c_float), ("penalty_freq", C.c_float),
+                ("penalty_present", C.c_float)]
+
+
 class Perf(C.Structure):
     _fields_ = [("t_load_ms", C.c_double), ("t_p_eval_ms", C.c_double), ("t_eval_ms", C.c_double),
                 ("n_p_eval", C.c_int32), ("n_eval", C.c_int32), ("n_ubatch", C.c_int32),
@@ -87,6 +94,13 @@ SIGNATURES = {
     "ubd_get_logits_device": (C.c_void_p, [_P]),
     "ubd_sample_greedy": (C.c_int32, [_P, C.c_int32]),
     "ubd_sample_greedy_all": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_sampler_default_params": (SamplerParams, []),
+    "ubd_sampler_init": (_P, [_P, SamplerParams]),
+    "ubd_sampler_free": (None, [_P]),
+    "ubd_sampler_accept": (None, [_P, C.c_int32]),
+    "ubd_sampler_sample": (C.c_int32, [_P, C.c_int32, C.c_float]),
+    "ubd_sampler_sample_logits": (C.c_int32, [_P, C.c_void_p, C.c_int32, C.c_float]),
+    "ubd_sampler_candidates": (C.c_int32, [_P, C.POINTER(C.c_int32), C.POINTER(C.c_float), C.c_int32]),
     "ubd_synchronize": (C.c_int32, [_P]),
     "ubd_memory_seq_pos_min": (C.c_int32, [_P, C.c_int32]),
     "ubd_memory_seq_pos_max": (C.c_int32, [_P, C.c_int32]),
@@ -415,6 +429,56 @@ class Context:
         p = Perf()
         self.lib.ubd_perf_get(self.ptr, C.byref(p))
         return {f: getattr(p, f) for f, _ in Perf._fields_}
+
+
+class Sampler:
+    """The sampler chain on rows of a context's logits (ubd_sampler_*);
+    keyword arguments override ubd_sampler_default_params()."""
+
+    def __init__(self, ctx, **params):
+        self.lib = load_library()
+        self.ctx = ctx
+        p = self.lib.ubd_sampler_default_params()
+        for k, v in params.items():
+            if not hasattr(p, k):
+                raise KeyError(k)
+            setattr(p, k, v)
+        self.ptr = self.lib.ubd_sampler_init(ctx.ptr, p)
+        if not self.ptr:
+            raise ValueError(f"ubd_sampler_init failed: {last_error()}")
+
+    def free(self):
+        if self.ptr:
+            self.lib.ubd_sampler_free(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def accept(self, tokens):
+        for t in np.atleast_1d(tokens):
+            self.lib.ubd_sampler_accept(self.ptr, int(t))
+
+    def sample(self, i, u):
+        return self.lib.ubd_sampler_sample(self.ptr, i, u)
+
+    def sample_logits(self, logits, u):
+        """logits: a float32 CUDA tensor of one row, on the context's device."""
+        assert logits.dtype.itemsize == 4 and logits.is_cuda and logits.is_contiguous()
+        return self.lib.ubd_sampler_sample_logits(self.ptr, logits.data_ptr(), logits.numel(), u)
+
+    def candidates(self, cap=1024):
+        ids = np.zeros(cap, np.int32)
+        probs = np.zeros(cap, np.float32)
+        n = self.lib.ubd_sampler_candidates(self.ptr, ids.ctypes.data_as(C.POINTER(C.c_int32)),
+                                            probs.ctypes.data_as(C.POINTER(C.c_float)), cap)
+        if n < 0:
+            raise RuntimeError(f"ubd_sampler_candidates failed: {last_error()}")
+        n = min(n, cap)
+        return ids[:n], probs[:n]
 
 
 class Planner:

@@ -172,6 +172,28 @@ struct ArgmaxWork {
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows,
                    int n, int32_t *out, const ArgmaxWork &w, hipStream_t s);
 
+// Sampler chain on one logits row (one work-group): penalties of the
+// history tokens, top-k (1..SAMPLER_KMAX), top-p, min-p, temperature, then
+// the draw with u; out_token = {chosen id, number of candidates left},
+// out_ids / out_probs = those candidates in order with their final
+// probabilities.
+constexpr int SAMPLER_KMAX = 1024;
+constexpr int SAMPLER_HMAX = 256;
+struct SamplerArgs {
+    const float *logits = nullptr;
+    int n_vocab = 0;
+    const int32_t *hist = nullptr;    // last penalty_last_n chosen tokens (<= SAMPLER_HMAX)
+    int n_hist = 0;
+    int top_k = 40;
+    float top_p = 1.f, min_p = 0.f, temperature = 1.f;
+    float pen_repeat = 1.f, pen_freq = 0.f, pen_present = 0.f;
+    float u = 0.f;
+    int32_t *out_token = nullptr;     // [2]
+    int32_t *out_ids = nullptr;       // [SAMPLER_KMAX]
+    float *out_probs = nullptr;       // [SAMPLER_KMAX]
+};
+void launch_sampler(const SamplerArgs &a, hipStream_t s);
+
 // Weight relayout: row-major source matrices -> tiled layout.  Up to three
 // sources are concatenated by rows (mode 0) or two are interleaved by
 // 16-row blocks, block 2j from src[0], block 2j+1 from src[1] (mode 1).

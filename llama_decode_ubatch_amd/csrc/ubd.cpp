@@ -960,6 +960,144 @@ extern "C" int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32
     return P.n_outputs;
 }
 
+// ----------------------------------------------------------------- sampler
+struct ubd_sampler {
+    ubd_context *ctx = nullptr;
+    int device = 0;
+    ubd_sampler_params p{};
+    std::vector<int32_t> history;
+    int32_t *d_hist = nullptr, *d_out = nullptr, *d_ids = nullptr;
+    float *d_probs = nullptr;
+    int32_t *h_stage = nullptr;     // pinned: history upload, then {token, n}
+    int32_t n_last = 0;
+};
+
+extern "C" ubd_sampler_params ubd_sampler_default_params(void) {
+    ubd_sampler_params p;
+    p.top_k = 40;
+    p.top_p = 1.f;
+    p.min_p = 0.f;
+    p.temperature = 1.f;
+    p.penalty_last_n = 0;
+    p.penalty_repeat = 1.f;
+    p.penalty_freq = 0.f;
+    p.penalty_present = 0.f;
+    return p;
+}
+
+extern "C" void ubd_sampler_free(ubd_sampler *s) {
+    if (!s) return;
+    (void)hipSetDevice(s->device);
+    if (s->d_hist) (void)hipFree(s->d_hist);
+    if (s->d_out) (void)hipFree(s->d_out);
+    if (s->d_ids) (void)hipFree(s->d_ids);
+    if (s->d_probs) (void)hipFree(s->d_probs);
+    if (s->h_stage) (void)hipHostFree(s->h_stage);
+    delete s;
+}
+
+extern "C" ubd_sampler *ubd_sampler_init(ubd_context *ctx, ubd_sampler_params p) {
+    if (!ctx) {
+        set_err("ubd_sampler_init: no context");
+        return nullptr;
+    }
+    if (p.top_k < 1 || p.top_k > SAMPLER_KMAX || !(p.top_p > 0.f && p.top_p <= 1.f) ||
+        !(p.min_p >= 0.f && p.min_p < 1.f) || p.penalty_last_n < 0 || p.penalty_last_n > SAMPLER_HMAX ||
+        !(p.penalty_repeat > 0.f) || !std::isfinite(p.temperature) || !std::isfinite(p.penalty_freq) ||
+        !std::isfinite(p.penalty_present)) {
+        set_err("ubd_sampler_init: parameter out of range");
+        return nullptr;
+    }
+    (void)hipSetDevice(ctx->model->device);
+    ubd_sampler *s = new ubd_sampler();
+    s->ctx = ctx;
+    s->device = ctx->model->device;
+    s->p = p;
+    const bool ok = hip_ok(hipMalloc(&s->d_hist, SAMPLER_HMAX * 4), "sampler alloc") &&
+                    hip_ok(hipMalloc(&s->d_out, 2 * 4), "sampler alloc") &&
+                    hip_ok(hipMalloc(&s->d_ids, SAMPLER_KMAX * 4), "sampler alloc") &&
+                    hip_ok(hipMalloc(&s->d_probs, SAMPLER_KMAX * 4), "sampler alloc") &&
+                    hip_ok(hipHostMalloc((void **)&s->h_stage, (SAMPLER_HMAX + 2) * 4, hipHostMallocDefault),
+                           "sampler pinned");
+    if (!ok) {
+        ubd_sampler_free(s);
+        return nullptr;
+    }
+    return s;
+}
+
+namespace {
+// only the last SAMPLER_HMAX entries are ever read
+void remember(ubd_sampler *s, int32_t t) {
+    if (s->history.size() >= 16 * SAMPLER_HMAX)
+        s->history.erase(s->history.begin(), s->history.end() - SAMPLER_HMAX);
+    s->history.push_back(t);
+}
+}  // namespace
+
+extern "C" void ubd_sampler_accept(ubd_sampler *s, ubd_token t) {
+    if (s) remember(s, t);
+}
+
+namespace {
+ubd_token sampler_run(ubd_sampler *s, const float *logits, int V, float u) {
+    ubd_context *ctx = s->ctx;
+    (void)hipSetDevice(ctx->model->device);
+    const int nh = (int)std::min<size_t>(s->history.size(), (size_t)s->p.penalty_last_n);
+    std::copy(s->history.end() - nh, s->history.end(), s->h_stage);
+    SamplerArgs a;
+    a.logits = logits;
+    a.n_vocab = V;
+    a.hist = s->d_hist;
+    a.n_hist = nh;
+    a.top_k = s->p.top_k;
+    a.top_p = s->p.top_p;
+    a.min_p = s->p.min_p;
+    a.temperature = s->p.temperature;
+    a.pen_repeat = s->p.penalty_repeat;
+    a.pen_freq = s->p.penalty_freq;
+    a.pen_present = s->p.penalty_present;
+    a.u = u;
+    a.out_token = s->d_out;
+    a.out_ids = s->d_ids;
+    a.out_probs = s->d_probs;
+    if ((nh && !hip_ok(hipMemcpyAsync(s->d_hist, s->h_stage, (size_t)nh * 4, hipMemcpyHostToDevice, ctx->stream),
+                       "history upload")))
+        return -1;
+    launch_sampler(a, ctx->stream);
+    if (!hip_ok(hipGetLastError(), "sampler") ||
+        !hip_ok(hipMemcpyAsync(s->h_stage + SAMPLER_HMAX, s->d_out, 8, hipMemcpyDeviceToHost, ctx->stream), "sample") ||
+        !hip_ok(hipStreamSynchronize(ctx->stream), "sample sync"))
+        return -1;
+    const int32_t tok = s->h_stage[SAMPLER_HMAX];
+    s->n_last = s->h_stage[SAMPLER_HMAX + 1];
+    remember(s, tok);
+    return tok;
+}
+}  // namespace
+
+extern "C" ubd_token ubd_sampler_sample(ubd_sampler *s, int32_t i, float u) {
+    if (!s || !(u >= 0.f && u < 1.f)) return -1;
+    const int32_t r = resolve_row(s->ctx, i);
+    if (r < 0) return -1;
+    const int V = s->ctx->model->hp.n_vocab;
+    return sampler_run(s, s->ctx->logits_dev + (size_t)r * V, V, u);
+}
+
+extern "C" ubd_token ubd_sampler_sample_logits(ubd_sampler *s, const float *logits, int32_t n_vocab, float u) {
+    if (!s || !logits || n_vocab < 1 || !(u >= 0.f && u < 1.f)) return -1;
+    return sampler_run(s, logits, n_vocab, u);
+}
+
+extern "C" int32_t ubd_sampler_candidates(ubd_sampler *s, ubd_token *ids, float *probs, int32_t cap) {
+    if (!s || cap < 0) return -1;
+    const int n = std::min(s->n_last, cap);
+    if (n > 0 && ((ids && !hip_ok(hipMemcpy(ids, s->d_ids, (size_t)n * 4, hipMemcpyDeviceToHost), "candidates")) ||
+                  (probs && !hip_ok(hipMemcpy(probs, s->d_probs, (size_t)n * 4, hipMemcpyDeviceToHost), "candidates"))))
+        return -1;
+    return s->n_last;
+}
+
 // ------------------------------------------------------------------ memory
 extern "C" ubd_pos ubd_memory_seq_pos_min(ubd_context *ctx, ubd_seq_id s) {
     return ctx ? ctx->planner.cells.seq_pos_min(s) : -1;
