@@ -178,9 +178,16 @@ uint32_t ubd_n_ubatch(const ubd_context *ctx);
  * belong to the caller; they are only read during ubd_decode.
  *   token     token ids in [0, n_vocab)
  *   embd      must be NULL (token input only)
- *   pos       NULL = continue each sequence from seq_pos_max + 1
- *   n_seq_id  NULL or all 1 (one sequence per token)
- *   seq_id    NULL = sequence 0; else seq_id[i][0] in [0, n_seq_max)
+ *   pos       NULL = continue the token's first sequence from its
+ *             seq_pos_max + 1; given positions must continue every
+ *             sequence of the token (an empty sequence may start anywhere)
+ *   n_seq_id  NULL = one sequence per token; else n_seq_id[i] >= 1
+ *             distinct sequences seq_id[i][0 .. n_seq_id[i]) per token
+ *             ([ENG] Step 10: a token can belong to several sequences).
+ *             More than one needs a unified KV cache: the token is stored
+ *             once, in one cell shared by all its sequences, and its query
+ *             attends to the cells of its first sequence
+ *   seq_id    NULL = sequence 0; else ids in [0, n_seq_max)
  *   logits    NULL = only the last token outputs; else nonzero = output */
 typedef struct ubd_batch {
     int32_t n_tokens;
@@ -192,8 +199,8 @@ typedef struct ubd_batch {
     int8_t *logits;
 } ubd_batch;
 
-/* Allocate a batch with room for n_tokens_alloc tokens, one sequence id
- * each (embd must be 0).  Free with ubd_batch_free. */
+/* Allocate a batch with room for n_tokens_alloc tokens and n_seq_max
+ * sequence ids per token (embd must be 0).  Free with ubd_batch_free. */
 ubd_batch ubd_batch_init(int32_t n_tokens_alloc, int32_t embd, int32_t n_seq_max);
 void ubd_batch_free(ubd_batch batch);
 /* Wrap existing token ids; pos, seq_id and logits stay NULL ([ENG] Step 10). */
@@ -293,10 +300,36 @@ int32_t ubd_synchronize(ubd_context *ctx);
  * ([ENG] KV-cache section, seq_pos_max). */
 ubd_pos ubd_memory_seq_pos_min(ubd_context *ctx, ubd_seq_id s);
 ubd_pos ubd_memory_seq_pos_max(ubd_context *ctx, ubd_seq_id s);
-/* Remove the cells of sequence s (all sequences if s < 0) with
+/* Take sequence s (all sequences if s < 0) out of the cells with
  * p0 <= pos < p1; p0 < 0 means 0, p1 < 0 means infinity ([DEC] "Error
- * recovery and state rollback").  Returns true. */
+ * recovery and state rollback").  A cell that no sequence holds any more
+ * is free ([DEC] "KV cache details": cells hold a set of sequences).
+ * Returns false for s >= n_seq_max, else true. */
 bool ubd_memory_seq_rm(ubd_context *ctx, ubd_seq_id s, ubd_pos p0, ubd_pos p1);
+/* Give sequence dst the cells of src with p0 <= pos < p1 (same ranges as
+ * seq_rm).  In a unified cache the cells become shared: no K/V moves.
+ * With one stream per sequence only the whole sequence can be copied
+ * (p0 < 0 and p1 < 0): dst's stream is replaced by a copy of src's, K/V
+ * rows included.  The caller normally empties dst first; cells dst already
+ * holds stay.  False for invalid ids or a partial range across streams. */
+bool ubd_memory_seq_cp(ubd_context *ctx, ubd_seq_id src, ubd_seq_id dst, ubd_pos p0, ubd_pos p1);
+/* Drop every sequence but s from every cell.  False for an invalid s. */
+bool ubd_memory_seq_keep(ubd_context *ctx, ubd_seq_id s);
+/* Defrag ([DEC] "KV cache details", defrag and its figure): in every
+ * stream the occupied cells move to the lowest indices, ordered by (lowest
+ * sequence of the cell, position, old index), K/V rows with them (stored
+ * values unchanged), so attention scans fewer cells.  ubd_decode does the
+ * same once by itself when a batch finds no free cells, then searches
+ * again.  Returns the number of cells that moved, or a negative error
+ * code (then the cache is unchanged).  Cells reported by ubd_get_kv_cells
+ * for an earlier decode no longer apply. */
+int32_t ubd_memory_defrag(ubd_context *ctx);
+/* Cell table of a stream: pos[c] (-1 = empty) for its cells and, if
+ * seq_words is not NULL, the sequence bits: bit (s % 32) of
+ * seq_words[(s / 32) * n_cells + c] is set when cell c holds sequence s
+ * (n_cells * ceil(n_seq_max / 32) words).  Returns n_cells, -1 if cap (in
+ * entries of each array) is too small or the stream is invalid. */
+int32_t ubd_memory_cells(ubd_context *ctx, int32_t stream, int32_t *pos, uint32_t *seq_words, int32_t cap);
 /* KV cell of each batch token of the last successful decode, in batch
  * order ([DEC] "KV cache details": slot_info indices).  Returns the token
  * count, or -1 if cap is too small. */
@@ -409,6 +442,10 @@ int32_t ubd_planner_n_outputs(const ubd_planner *p);
 ubd_pos ubd_planner_seq_pos_min(const ubd_planner *p, ubd_seq_id s);
 ubd_pos ubd_planner_seq_pos_max(const ubd_planner *p, ubd_seq_id s);
 bool ubd_planner_seq_rm(ubd_planner *p, ubd_seq_id s, ubd_pos p0, ubd_pos p1);
+bool ubd_planner_seq_cp(ubd_planner *p, ubd_seq_id src, ubd_seq_id dst, ubd_pos p0, ubd_pos p1);
+bool ubd_planner_seq_keep(ubd_planner *p, ubd_seq_id s);
+int32_t ubd_planner_defrag(ubd_planner *p);
+int32_t ubd_planner_cells(const ubd_planner *p, int32_t stream, int32_t *pos, uint32_t *seq_words, int32_t cap);
 /* Cells scanned by attention in a stream: highest used cell + 1. */
 int32_t ubd_planner_n_kv(const ubd_planner *p, int32_t stream);
 

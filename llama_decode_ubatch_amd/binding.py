@@ -105,6 +105,10 @@ SIGNATURES = {
     "ubd_memory_seq_pos_min": (C.c_int32, [_P, C.c_int32]),
     "ubd_memory_seq_pos_max": (C.c_int32, [_P, C.c_int32]),
     "ubd_memory_seq_rm": (C.c_bool, [_P, C.c_int32, C.c_int32, C.c_int32]),
+    "ubd_memory_seq_cp": (C.c_bool, [_P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "ubd_memory_seq_keep": (C.c_bool, [_P, C.c_int32]),
+    "ubd_memory_defrag": (C.c_int32, [_P]),
+    "ubd_memory_cells": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_uint32), C.c_int32]),
     "ubd_get_kv_cells": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
     "ubd_kv_fill": (C.c_int32, [_P, C.c_int32, C.c_int32, C.POINTER(C.c_void_p),
                                 C.POINTER(C.c_void_p), C.c_int, C.c_int32]),
@@ -132,6 +136,10 @@ SIGNATURES = {
     "ubd_planner_seq_pos_min": (C.c_int32, [_P, C.c_int32]),
     "ubd_planner_seq_pos_max": (C.c_int32, [_P, C.c_int32]),
     "ubd_planner_seq_rm": (C.c_bool, [_P, C.c_int32, C.c_int32, C.c_int32]),
+    "ubd_planner_seq_cp": (C.c_bool, [_P, C.c_int32, C.c_int32, C.c_int32, C.c_int32]),
+    "ubd_planner_seq_keep": (C.c_bool, [_P, C.c_int32]),
+    "ubd_planner_defrag": (C.c_int32, [_P]),
+    "ubd_planner_cells": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_uint32), C.c_int32]),
     "ubd_planner_n_kv": (C.c_int32, [_P, C.c_int32]),
 }
 
@@ -169,6 +177,21 @@ def _i32(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
 
 
+def _cell_table(fn, ptr, stream, n_cells, n_seq_max):
+    """(pos [n_cells], has [n_cells][n_seq_max] bool) of one stream."""
+    W = (n_seq_max + 31) // 32
+    pos = np.zeros(n_cells, np.int32)
+    words = np.zeros(n_cells * W, np.uint32)
+    n = fn(ptr, stream, pos.ctypes.data_as(C.POINTER(C.c_int32)), words.ctypes.data_as(C.POINTER(C.c_uint32)),
+           n_cells * W)
+    if n != n_cells:
+        raise RuntimeError(f"cell table read failed: {last_error()}")
+    w = words.reshape(W, n_cells)
+    s = np.arange(n_seq_max)
+    has = ((w[s // 32] >> (s % 32)[:, None].astype(np.uint32)) & 1).T.astype(bool)
+    return pos, has
+
+
 class _BatchHolder:
     """Keeps the arrays a CBatch points into alive."""
 
@@ -182,11 +205,14 @@ class _BatchHolder:
             self.pos = _i32(pos)
             self.b.pos = self.pos.ctypes.data_as(C.POINTER(C.c_int32))
         if seq_id is not None:
-            self.seq = _i32(seq_id)
-            self.n_seq = np.ones(n, np.int32)
+            # one id per token, or a list of ids per token (several sequences)
+            rows = [np.atleast_1d(np.asarray(v, np.int32)) for v in seq_id]
+            self.n_seq = np.asarray([r.size for r in rows], np.int32)
+            self.seq = np.ascontiguousarray(np.concatenate(rows) if rows else np.zeros(0, np.int32))
+            offs = np.concatenate([[0], np.cumsum(self.n_seq)[:-1]]).astype(np.int64)
             base = self.seq.ctypes.data
             self.rows = (C.POINTER(C.c_int32) * n)(
-                *[C.cast(base + 4 * i, C.POINTER(C.c_int32)) for i in range(n)])
+                *[C.cast(base + 4 * int(o), C.POINTER(C.c_int32)) for o in offs])
             self.b.seq_id = C.cast(self.rows, C.POINTER(C.POINTER(C.c_int32)))
             self.b.n_seq_id = self.n_seq.ctypes.data_as(C.POINTER(C.c_int32))
         if logits is not None:
@@ -301,6 +327,9 @@ class Context:
         if not self.ptr:
             raise RuntimeError(f"ubd_init_from_model failed ({st.value}): {last_error()}")
         self.n_vocab = model.shape.n_vocab
+        self.n_seq_max = max(1, n_seq_max)
+        self.n_stream = 1 if kv_unified else self.n_seq_max
+        self.n_cells = self.lib.ubd_n_ctx(self.ptr) // self.n_stream
         self._finalizer = weakref.finalize(self, self.lib.ubd_free, self.ptr)
 
     def free(self):
@@ -350,6 +379,18 @@ class Context:
 
     def seq_rm(self, s, p0, p1):
         return self.lib.ubd_memory_seq_rm(self.ptr, s, p0, p1)
+
+    def seq_cp(self, src, dst, p0, p1):
+        return self.lib.ubd_memory_seq_cp(self.ptr, src, dst, p0, p1)
+
+    def seq_keep(self, s):
+        return self.lib.ubd_memory_seq_keep(self.ptr, s)
+
+    def defrag(self):
+        return self.lib.ubd_memory_defrag(self.ptr)
+
+    def cells(self, stream):
+        return _cell_table(self.lib.ubd_memory_cells, self.ptr, stream, self.n_cells, self.n_seq_max)
 
     def kv_cells(self, n_tokens):
         out = np.zeros(n_tokens, np.int32)
@@ -519,6 +560,18 @@ class Planner:
 
     def seq_rm(self, s, p0, p1):
         return self.lib.ubd_planner_seq_rm(self.ptr, s, p0, p1)
+
+    def seq_cp(self, src, dst, p0, p1):
+        return self.lib.ubd_planner_seq_cp(self.ptr, src, dst, p0, p1)
+
+    def seq_keep(self, s):
+        return self.lib.ubd_planner_seq_keep(self.ptr, s)
+
+    def defrag(self):
+        return self.lib.ubd_planner_defrag(self.ptr)
+
+    def cells(self, stream, n_cells, n_seq_max):
+        return _cell_table(self.lib.ubd_planner_cells, self.ptr, stream, n_cells, n_seq_max)
 
     def n_kv(self, stream):
         return self.lib.ubd_planner_n_kv(self.ptr, stream)

@@ -64,10 +64,14 @@ struct Act {
 };
 
 // Per-ubatch token table on the device (int32 planes of capacity `cap`).
+constexpr int MAX_SEQ_WORDS = 8;   // sequence-mask words per cell: 256 sequences
+
 struct TokInfo {
     const int32_t *token, *pos, *seq, *stream, *cell, *out_row, *tile_of;
     const int32_t *out_tok;    // ubatch indices of output tokens
     const int32_t *tiles;      // [n_tiles][4] = t0, n_tokens, stream, n_kv
+    const uint32_t *seqw;      // [token][n_seq_words] every sequence of the token
+    int n_seq_words = 1;       // seq is the first of them: attention follows it
 };
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_LOGITS = 4 };
@@ -116,11 +120,12 @@ struct LinearArgs {
 
 void launch_linear(const LinearArgs &a, hipStream_t s);
 
-// x[t] = dequant(table[token[t]]); also records (pos, seq) of each token's
-// cell in the device cell tables [stream][n_cells].
+// x[t] = dequant(table[token[t]]); also records the position and the
+// sequence mask of each token's cell in the device cell tables
+// (cell_pos [stream][n_cells], cell_seq [stream][n_seq_words][n_cells]).
 void launch_embed(int wtype, const void *table, const uint16_t *scales,
                   int d, const TokInfo &ti, int T, float *x,
-                  int32_t *cell_pos, int32_t *cell_seq, int n_cells,
+                  int32_t *cell_pos, uint32_t *cell_seq, int n_cells,
                   hipStream_t s);
 
 // out[r] = rmsnorm(x[src_row(r)]) * gain, src_row = row_map ? row_map[r] : r
@@ -134,7 +139,9 @@ struct AttnArgs {
     const void *v_cache = nullptr;
     int type_k = KV_F16, type_v = KV_F16;
     size_t layer_elems = 0;           // values per layer of each cache (q8_0 scale offset)
-    const int32_t *cell_pos = nullptr, *cell_seq = nullptr; // [stream][n_cells]
+    const int32_t *cell_pos = nullptr;    // [stream][n_cells]; -1 = empty
+    const uint32_t *cell_seq = nullptr;   // [stream][n_seq_words][n_cells] sequence bits
+    int n_seq_words = 1;
     int n_cells = 0, n_head = 0, n_head_kv = 0, head_dim = 0;
     TokInfo tok;
     int T = 0, n_tiles = 0, max_chunks = 0;
@@ -222,5 +229,13 @@ void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
 void launch_kv_load(const void *cache, int type, bool transposed, int stream,
                     int cell0, int n, int n_head_kv, int hd, int n_cells,
                     size_t layer_elems, float *out, hipStream_t s);
+// Bytes of tmp that kv_move needs for n cells.
+size_t kv_move_tmp_bytes(int type, int n, int n_head_kv, int hd);
+// Cell moves of one layer's K or V cache, stored values unchanged (q8_0
+// scales included): to_tmp copies the rows of cells[m] of the stream into
+// tmp row m, otherwise tmp row m into cells[m].
+void launch_kv_move(void *cache, int type, bool transposed, int stream, const int32_t *cells, int n,
+                    int n_head_kv, int hd, int n_cells, size_t layer_elems, void *tmp, bool to_tmp,
+                    hipStream_t s);
 
 }  // namespace ubd

@@ -1165,7 +1165,7 @@ void launch_linear(const LinearArgs &a, hipStream_t s) {
 // ------------------------------------------------------------ embedding
 __global__ __launch_bounds__(256) void embed_kernel(int wtype, const void *table, const uint16_t *scales,
                                                     int d, TokInfo ti, float *x, int32_t *cell_pos,
-                                                    int32_t *cell_seq, int n_cells) {
+                                                    uint32_t *cell_seq, int n_cells) {
     const int t = blockIdx.x;
     const size_t row = (size_t)ti.token[t];
     float *xo = x + (size_t)t * d;
@@ -1184,15 +1184,16 @@ __global__ __launch_bounds__(256) void embed_kernel(int wtype, const void *table
         }
         *(f32x4_t *)(xo + e) = v;
     }
-    if (threadIdx.x == 0) {
-        const size_t c = (size_t)ti.stream[t] * n_cells + ti.cell[t];
-        cell_pos[c] = ti.pos[t];
-        cell_seq[c] = ti.seq[t];
+    if (threadIdx.x == 0) cell_pos[(size_t)ti.stream[t] * n_cells + ti.cell[t]] = ti.pos[t];
+    if (threadIdx.x < ti.n_seq_words) {
+        const int w = threadIdx.x;
+        cell_seq[((size_t)ti.stream[t] * ti.n_seq_words + w) * n_cells + ti.cell[t]] =
+            ti.seqw[(size_t)t * ti.n_seq_words + w];
     }
 }
 
 void launch_embed(int wtype, const void *table, const uint16_t *scales, int d, const TokInfo &ti, int T,
-                  float *x, int32_t *cell_pos, int32_t *cell_seq, int n_cells, hipStream_t s) {
+                  float *x, int32_t *cell_pos, uint32_t *cell_seq, int n_cells, hipStream_t s) {
     if (T <= 0) return;
     hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, s, wtype, table, scales, d, ti, x, cell_pos,
                        cell_seq, n_cells);
@@ -1282,7 +1283,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     __shared__ float Kt[HD][SUB + 1];
     __shared__ float Vt[HD][SUB + 1];
     __shared__ float ps[ROWS][SUB + 1];
-    __shared__ int cpos[SUB], cseq[SUB];
+    __shared__ int cpos[SUB];
+    __shared__ uint32_t cseq[MAX_SEQ_WORDS][SUB];
     __shared__ float m_s[ROWS], l_s[ROWS], sc_s[ROWS];
     __shared__ int rpos[ROWS], rseq[ROWS];
 
@@ -1306,7 +1308,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const size_t kbase = ((size_t)st * a.n_head_kv + g) * a.n_cells * HD;  // [cell][hd]
     const size_t vbase = ((size_t)st * a.n_head_kv + g) * HD * a.n_cells;  // 32-cell tiles
     const int32_t *cp = a.cell_pos + (size_t)st * a.n_cells;
-    const int32_t *cs = a.cell_seq + (size_t)st * a.n_cells;
+    const uint32_t *cs = a.cell_seq + (size_t)st * a.n_seq_words * a.n_cells;
 
     for (int sub = cbeg; sub < cend; sub += SUB) {
         const int ns = min(SUB, cend - sub);
@@ -1319,15 +1321,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             const int d = e / SUB, c = e % SUB;
             Vt[d][c] = c < ns ? load_kv(a.v_cache, a.type_v, vbase + v_off(HD, d, (size_t)(sub + c))) : 0.f;
         }
-        if (tid < SUB) {
-            cpos[tid] = tid < ns ? cp[sub + tid] : -1;
-            cseq[tid] = tid < ns ? cs[sub + tid] : -1;
+        if (tid < SUB) cpos[tid] = tid < ns ? cp[sub + tid] : -1;
+        for (int e = tid; e < a.n_seq_words * SUB; e += 256) {
+            const int w = e / SUB, c = e % SUB;
+            cseq[w][c] = c < ns ? cs[(size_t)w * a.n_cells + sub + c] : 0u;
         }
         __syncthreads();
         for (int e = tid; e < R * SUB; e += 256) {
             const int row = e / SUB, c = e % SUB;
             float sv = -INFINITY;
-            if (c < ns && cseq[c] == rseq[row] && cpos[c] >= 0 && cpos[c] <= rpos[row]) {
+            const int rs = rseq[row];
+            if (c < ns && ((cseq[rs >> 5][c] >> (rs & 31)) & 1u) && cpos[c] >= 0 && cpos[c] <= rpos[row]) {
                 float dot = 0.f;
 #pragma unroll 8
                 for (int d = 0; d < HD; ++d) dot += qs[row][d] * Kt[d][c];
@@ -1440,7 +1444,8 @@ typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 template <int HD> struct KVSrc {
     const _Float16 *K, *Vt;
-    const int32_t *cpos, *cseq;
+    const int32_t *cpos;
+    const uint32_t *cseq;       // the sequence-mask word of this lane's row
     int n_cells, r, g;
 };
 
@@ -1476,7 +1481,7 @@ __device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src
 // update of (m, l) and O += P V.
 template <int HD>
 __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int cend, const f16x8_t *qh,
-                                                const f16x8_t *ql, bool row_ok, int rseq, int rpos, int g,
+                                                const f16x8_t *ql, bool row_ok, int rbit, int rpos, int g,
                                                 float &m, float &l, f32x4_t *O) {
     constexpr int KK = HD / 32, DB = HD / 16;
     f32x4_t S[2];
@@ -1493,7 +1498,8 @@ __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int
         const int ss[4] = {b.s[b2].x, b.s[b2].y, b.s[b2].z, b.s[b2].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool vis = row_ok && cc + i < cend && ss[i] == rseq && pp[i] >= 0 && pp[i] <= rpos;
+            const bool vis = row_ok && cc + i < cend && (((uint32_t)ss[i] >> rbit) & 1u) && pp[i] >= 0 &&
+                             pp[i] <= rpos;
             acc[i] = vis ? acc[i] : -INFINITY;
         }
         S[b2] = acc;
@@ -1542,7 +1548,8 @@ __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int
 template <int HD> struct KVSrcQ8 {
     const int8_t *K, *Vt;
     const uint16_t *ks, *vs;    // [HD/32][cells] f16 scales of this (stream, KV head)
-    const int32_t *cpos, *cseq;
+    const int32_t *cpos;
+    const uint32_t *cseq;       // the sequence-mask word of this lane's row
     int n_cells, r, g;
 };
 
@@ -1584,7 +1591,7 @@ __device__ __forceinline__ float h2f_hi(uint32_t w) { return h2f((uint16_t)(w >>
 
 template <int HD>
 __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0, int cend, const bf16x8_t *qh,
-                                                   const bf16x8_t *ql, bool row_ok, int rseq, int rpos, int g,
+                                                   const bf16x8_t *ql, bool row_ok, int rbit, int rpos, int g,
                                                    float &m, float &l, f32x4_t *O) {
     constexpr int KK = HD / 32, DB = HD / 16;
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -1606,7 +1613,8 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
         const int ss[4] = {b.s[b2].x, b.s[b2].y, b.s[b2].z, b.s[b2].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool vis = row_ok && cc + i < cend && ss[i] == rseq && pp[i] >= 0 && pp[i] <= rpos;
+            const bool vis = row_ok && cc + i < cend && (((uint32_t)ss[i] >> rbit) & 1u) && pp[i] >= 0 &&
+                             pp[i] <= rpos;
             acc[i] = vis ? acc[i] : -INFINITY;
         }
         S[b2] = acc;
@@ -1678,7 +1686,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     // this lane's query row (S^T layout: row = r)
     const bool row_ok = r < R;
     const int rt = t0 + (row_ok ? r / G : 0), rh = grp * G + (row_ok ? r % G : 0);
-    const int rpos = a.tok.pos[rt], rseq = a.tok.seq[rt];
+    const int rpos = a.tok.pos[rt], rseq = a.tok.seq[rt], rbit = rseq & 31;
     // every lane loads a valid row (rows past R read row 0) and zeroes it
     // afterwards, so the loads are unconditional and issued together
     const float *qrow = a.q + (size_t)rt * a.n_head * HD + rh * HD + 8 * g;
@@ -1694,7 +1702,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) O[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int32_t *cpos = a.cell_pos + (size_t)st * a.n_cells;
-    const int32_t *cseq = a.cell_seq + (size_t)st * a.n_cells;
+    const uint32_t *cseq = a.cell_seq + ((size_t)st * a.n_seq_words + (rseq >> 5)) * a.n_cells;
     const size_t hbase = (size_t)st * a.n_head_kv + grp;
 
     // Two register sets: the loads of the next 32-cell step are in flight
@@ -1727,11 +1735,11 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
             const int c1 = c0 + 32, c2 = c0 + 64;
             kv_step_load(B, src, c1 < cend ? c1 : c0);
             __builtin_amdgcn_sched_barrier(0);
-            kv_step_compute(A, c0, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            kv_step_compute(A, c0, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
             kv_step_load(A, src, c2 < cend ? c2 : c0);
             __builtin_amdgcn_sched_barrier(0);
-            kv_step_compute(B, c1, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            kv_step_compute(B, c1, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -1757,11 +1765,11 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
             const int c1 = c0 + 32, c2 = c0 + 64;
             kv_step_load_q8(B, src, c1 < cend ? c1 : c0);
             __builtin_amdgcn_sched_barrier(0);
-            kv_step_compute_q8(A, c0, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            kv_step_compute_q8(A, c0, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
             kv_step_load_q8(A, src, c2 < cend ? c2 : c0);
             __builtin_amdgcn_sched_barrier(0);
-            kv_step_compute_q8(B, c1, cend, qh, ql, row_ok, rseq, rpos, g, m, l, O);
+            kv_step_compute_q8(B, c1, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -2132,6 +2140,63 @@ void launch_kv_load(const void *cache, int type, bool transposed, int stream, in
     const size_t total = (size_t)n * n_head_kv * hd;
     hipLaunchKernelGGL(kv_load_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, cache, type,
                        (int)transposed, stream, cell0, n, n_head_kv, hd, n_cells, layer_elems, out);
+}
+
+// Defrag moves: one thread per stored value.  The tmp rows are [n][Hk*hd]
+// values of the cache's own type; q8_0 scales follow in a second plane
+// [n][Hk*hd/32] after the codes (256-byte aligned).
+template <typename E>
+__global__ __launch_bounds__(256) void kv_move_kernel(void *cache, int transposed, int stream,
+                                                      const int32_t *cells, int n, int n_head_kv, int hd,
+                                                      int n_cells, size_t layer_elems, int q8, void *tmp,
+                                                      int to_tmp) {
+    const int W = n_head_kv * hd;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)n * W) return;
+    const int m = (int)(idx / W), j = (int)(idx % W);
+    const int head = j / hd, d = j % hd;
+    const size_t c = (size_t)cells[m];
+    const size_t ci = transposed ? ((size_t)stream * n_head_kv + head) * n_cells * hd + v_off(hd, d, c)
+                                 : (((size_t)stream * n_head_kv + head) * n_cells + c) * hd + d;
+    E *cp = (E *)cache;
+    E *tp = (E *)tmp;
+    if (to_tmp)
+        tp[idx] = cp[ci];
+    else
+        cp[ci] = tp[idx];
+    if (q8 && d % 32 == 0) {
+        uint16_t *sc = (uint16_t *)((int8_t *)cache + layer_elems);
+        uint16_t *ts = (uint16_t *)((int8_t *)tmp + ((size_t)n * W + 255) / 256 * 256);
+        const size_t si = (((size_t)stream * n_head_kv + head) * (hd / 32) + d / 32) * n_cells + c;
+        const size_t ti = (size_t)m * (W / 32) + j / 32;
+        if (to_tmp)
+            ts[ti] = sc[si];
+        else
+            sc[si] = ts[ti];
+    }
+}
+
+size_t kv_move_tmp_bytes(int type, int n, int n_head_kv, int hd) {
+    const size_t vals = (size_t)n * n_head_kv * hd;
+    if (type == KV_Q8) return (vals + 255) / 256 * 256 + vals / 32 * 2;
+    return vals * (type == KV_F32 ? 4 : 2);
+}
+
+void launch_kv_move(void *cache, int type, bool transposed, int stream, const int32_t *cells, int n,
+                    int n_head_kv, int hd, int n_cells, size_t layer_elems, void *tmp, bool to_tmp,
+                    hipStream_t s) {
+    if (n <= 0) return;
+    const size_t total = (size_t)n * n_head_kv * hd;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (type == KV_F32)
+        hipLaunchKernelGGL(kv_move_kernel<uint32_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
+                           n, n_head_kv, hd, n_cells, layer_elems, 0, tmp, (int)to_tmp);
+    else if (type == KV_F16)
+        hipLaunchKernelGGL(kv_move_kernel<uint16_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
+                           n, n_head_kv, hd, n_cells, layer_elems, 0, tmp, (int)to_tmp);
+    else
+        hipLaunchKernelGGL(kv_move_kernel<uint8_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
+                           n, n_head_kv, hd, n_cells, layer_elems, 1, tmp, (int)to_tmp);
 }
 
 // q8_0 quantisation of KV rows into their cells: 32 lanes per 32-value

@@ -11,8 +11,10 @@ void KVCells::init(int32_t n_stream, int32_t n_cells, bool unified, int32_t n_se
     n_stream_ = n_stream;
     n_cells_ = n_cells;
     unified_ = unified;
+    n_seq_max_ = n_seq_max;
+    n_words_ = (n_seq_max + 31) / 32;
     pos_.assign(n_stream, std::vector<int32_t>(n_cells, -1));
-    seq_.assign(n_stream, std::vector<int32_t>(n_cells, -1));
+    seqw_.assign(n_stream, std::vector<uint32_t>((size_t)n_words_ * n_cells, 0u));
     free_.assign(n_stream, {});
     used_.assign(n_stream, {});
     for (int32_t st = 0; st < n_stream; ++st)
@@ -20,23 +22,38 @@ void KVCells::init(int32_t n_stream, int32_t n_cells, bool unified, int32_t n_se
     seq_pos_.assign(n_seq_max, {});
 }
 
-void KVCells::set_cell(int32_t st, int32_t c, int32_t p, int32_t s) {
+bool KVCells::empty_mask(int32_t st, int32_t c) const {
+    for (int32_t w = 0; w < n_words_; ++w)
+        if (seqw_[st][(size_t)w * n_cells_ + c]) return false;
+    return true;
+}
+
+void KVCells::set_cell(int32_t st, int32_t c, int32_t p, const uint32_t *mask) {
     pos_[st][c] = p;
-    seq_[st][c] = s;
     free_[st].erase(c);
     used_[st].insert(c);
-    seq_pos_[s][p] += 1;
+    for (int32_t w = 0; w < n_words_; ++w) {
+        seqw_[st][(size_t)w * n_cells_ + c] = mask[w];
+        for (uint32_t m = mask[w]; m; m &= m - 1) seq_pos_[32 * w + __builtin_ctz(m)][p] += 1;
+    }
+}
+
+void KVCells::drop_seq(int32_t st, int32_t c, int32_t s) {
+    if (!has(st, c, s)) return;
+    seqw_[st][(size_t)(s >> 5) * n_cells_ + c] &= ~(1u << (s & 31));
+    auto &m = seq_pos_[s];
+    auto it = m.find(pos_[st][c]);
+    if (it != m.end() && --it->second == 0) m.erase(it);
+    if (empty_mask(st, c)) {
+        pos_[st][c] = -1;
+        used_[st].erase(c);
+        free_[st].insert(c);
+    }
 }
 
 void KVCells::clear_cell(int32_t st, int32_t c) {
-    int32_t s = seq_[st][c], p = pos_[st][c];
-    auto &m = seq_pos_[s];
-    auto it = m.find(p);
-    if (it != m.end() && --it->second == 0) m.erase(it);
-    pos_[st][c] = -1;
-    seq_[st][c] = -1;
-    used_[st].erase(c);
-    free_[st].insert(c);
+    for (int32_t w = 0; w < n_words_; ++w)
+        for (uint32_t x = seqw_[st][(size_t)w * n_cells_ + c]; x; x &= x - 1) drop_seq(st, c, 32 * w + __builtin_ctz(x));
 }
 
 int32_t KVCells::seq_pos_max(int32_t s) const {
@@ -49,20 +66,103 @@ int32_t KVCells::seq_pos_min(int32_t s) const {
     return seq_pos_[s].begin()->first;
 }
 
-void KVCells::seq_rm(int32_t s, int32_t p0, int32_t p1,
-                     std::vector<std::pair<int32_t, int32_t>> *cleared) {
+void KVCells::seq_rm(int32_t s, int32_t p0, int32_t p1, std::vector<uint8_t> *touched) {
     const int32_t lo = p0 < 0 ? 0 : p0;
     const int32_t hi = p1 < 0 ? INT32_MAX : p1;
     for (int32_t st = 0; st < n_stream_; ++st) {
         if (s >= 0 && st != stream_of(s)) continue;
         std::vector<int32_t> victims;
         for (int32_t c : used_[st]) {
-            if (s >= 0 && seq_[st][c] != s) continue;
+            if (s >= 0 && !has(st, c, s)) continue;
             if (pos_[st][c] >= lo && pos_[st][c] < hi) victims.push_back(c);
         }
         for (int32_t c : victims) {
-            clear_cell(st, c);
-            if (cleared) cleared->emplace_back(st, c);
+            if (s >= 0)
+                drop_seq(st, c, s);
+            else
+                clear_cell(st, c);
+        }
+        if (touched && !victims.empty()) (*touched)[st] = 1;
+    }
+}
+
+bool KVCells::seq_cp(int32_t src, int32_t dst, int32_t p0, int32_t p1, bool *copied) {
+    *copied = false;
+    if (src < 0 || dst < 0 || src >= n_seq_max_ || dst >= n_seq_max_) return false;
+    if (src == dst) return true;
+    const int32_t ss = stream_of(src), sd = stream_of(dst);
+    if (ss == sd) {
+        const int32_t lo = p0 < 0 ? 0 : p0;
+        const int32_t hi = p1 < 0 ? INT32_MAX : p1;
+        for (int32_t c : used_[ss]) {
+            const int32_t p = pos_[ss][c];
+            if (has(ss, c, src) && !has(ss, c, dst) && p >= lo && p < hi) {
+                seqw_[ss][(size_t)(dst >> 5) * n_cells_ + c] |= 1u << (dst & 31);
+                seq_pos_[dst][p] += 1;
+            }
+        }
+        return true;
+    }
+    if (p0 >= 0 || p1 >= 0) return false;
+    std::vector<int32_t> old(used_[sd].begin(), used_[sd].end());
+    for (int32_t c : old) clear_cell(sd, c);
+    std::vector<uint32_t> mask(n_words_, 0u);
+    mask[dst >> 5] = 1u << (dst & 31);
+    std::vector<int32_t> take;
+    for (int32_t c : used_[ss])
+        if (has(ss, c, src)) take.push_back(c);
+    for (int32_t c : take) set_cell(sd, c, pos_[ss][c], mask.data());
+    *copied = true;
+    return true;
+}
+
+void KVCells::seq_keep(int32_t s) {
+    for (int32_t st = 0; st < n_stream_; ++st) {
+        std::vector<int32_t> cells(used_[st].begin(), used_[st].end());
+        for (int32_t c : cells)
+            for (int32_t w = 0; w < n_words_; ++w)
+                for (uint32_t x = seqw_[st][(size_t)w * n_cells_ + c]; x; x &= x - 1)
+                    if (32 * w + __builtin_ctz(x) != s) drop_seq(st, c, 32 * w + __builtin_ctz(x));
+    }
+}
+
+void KVCells::defrag_plan(std::vector<std::vector<int32_t>> *src) const {
+    src->assign(n_stream_, {});
+    for (int32_t st = 0; st < n_stream_; ++st) {
+        struct Key {
+            int32_t seq, pos, cell;
+        };
+        std::vector<Key> keys;
+        for (int32_t c : used_[st]) {
+            int32_t first = 0;
+            while (!has(st, c, first)) ++first;
+            keys.push_back({first, pos_[st][c], c});
+        }
+        std::sort(keys.begin(), keys.end(), [](const Key &a, const Key &b) {
+            if (a.seq != b.seq) return a.seq < b.seq;
+            if (a.pos != b.pos) return a.pos < b.pos;
+            return a.cell < b.cell;
+        });
+        for (const Key &k : keys) (*src)[st].push_back(k.cell);
+    }
+}
+
+void KVCells::defrag_apply(const std::vector<std::vector<int32_t>> &src) {
+    for (int32_t st = 0; st < n_stream_; ++st) {
+        const auto &order = src[st];
+        std::vector<int32_t> pos(order.size());
+        std::vector<uint32_t> words((size_t)n_words_ * order.size());
+        for (size_t j = 0; j < order.size(); ++j) {
+            pos[j] = pos_[st][order[j]];
+            for (int32_t w = 0; w < n_words_; ++w)
+                words[(size_t)w * order.size() + j] = seqw_[st][(size_t)w * n_cells_ + order[j]];
+        }
+        std::vector<int32_t> old(used_[st].begin(), used_[st].end());
+        for (int32_t c : old) clear_cell(st, c);
+        std::vector<uint32_t> mask(n_words_);
+        for (size_t j = 0; j < order.size(); ++j) {
+            for (int32_t w = 0; w < n_words_; ++w) mask[w] = words[(size_t)w * order.size() + j];
+            set_cell(st, (int32_t)j, pos[j], mask.data());
         }
     }
 }
@@ -84,7 +184,8 @@ bool KVCells::find_slots(std::vector<UBatch> &ubs) const {
 }
 
 void KVCells::apply(const UBatch &ub) {
-    for (int32_t t = 0; t < ub.size(); ++t) set_cell(ub.stream[t], ub.cell[t], ub.pos[t], ub.seq[t]);
+    for (int32_t t = 0; t < ub.size(); ++t)
+        set_cell(ub.stream[t], ub.cell[t], ub.pos[t], ub.seqw.data() + (size_t)t * n_words_);
 }
 
 int32_t KVCells::n_kv(int32_t stream) const {
@@ -98,7 +199,9 @@ bool KVCells::fill_sequence(int32_t s, int32_t n, std::vector<int32_t> *cells) {
     take.reserve(n);
     auto it = free_[st].begin();
     for (int32_t i = 0; i < n; ++i) take.push_back(*it++);
-    for (int32_t i = 0; i < n; ++i) set_cell(st, take[i], i, s);
+    std::vector<uint32_t> mask(n_words_, 0u);
+    mask[s >> 5] = 1u << (s & 31);
+    for (int32_t i = 0; i < n; ++i) set_cell(st, take[i], i, mask.data());
     if (cells) *cells = std::move(take);
     return true;
 }
@@ -144,16 +247,27 @@ int32_t Planner::sanitize(const ubd_batch &b, Clean *c, std::string *err) const 
     c->token.assign(b.token, b.token + n);
     for (int32_t v : c->token)
         if (v < 0 || v >= n_vocab) return bad("token id out of range");
+    const int32_t W = cells.n_seq_words();
     c->seq.assign(n, 0);
-    if (b.seq_id) {
-        for (int32_t i = 0; i < n; ++i) {
-            if (b.n_seq_id && b.n_seq_id[i] != 1) return bad("n_seq_id must be 1");
-            if (!b.seq_id[i]) return bad("seq_id row is NULL");
-            c->seq[i] = b.seq_id[i][0];
+    c->seqw.assign((size_t)n * W, 0u);
+    for (int32_t i = 0; i < n; ++i) {
+        uint32_t *m = c->seqw.data() + (size_t)i * W;
+        if (!b.seq_id) {
+            m[0] = 1u;
+            continue;
         }
+        const int32_t k = b.n_seq_id ? b.n_seq_id[i] : 1;
+        if (k < 1) return bad("n_seq_id must be at least 1");
+        if (k > 1 && n_stream != 1) return bad("a token of several sequences needs a unified KV cache");
+        if (!b.seq_id[i]) return bad("seq_id row is NULL");
+        for (int32_t j = 0; j < k; ++j) {
+            const int32_t s = b.seq_id[i][j];
+            if (s < 0 || (uint32_t)s >= n_seq_max) return bad("seq_id out of range");
+            if ((m[s >> 5] >> (s & 31)) & 1u) return bad("a sequence listed twice for one token");
+            m[s >> 5] |= 1u << (s & 31);
+        }
+        c->seq[i] = b.seq_id[i][0];
     }
-    for (int32_t s : c->seq)
-        if (s < 0 || (uint32_t)s >= n_seq_max) return bad("seq_id out of range");
     c->seq_order.clear();
     std::vector<uint8_t> seen(n_seq_max, 0);
     for (int32_t s : c->seq)
@@ -161,27 +275,41 @@ int32_t Planner::sanitize(const ubd_batch &b, Clean *c, std::string *err) const 
             seen[s] = 1;
             c->seq_order.push_back(s);
         }
+    auto seqs_of = [&](int32_t i, auto &&fn) {
+        const uint32_t *m = c->seqw.data() + (size_t)i * W;
+        for (int32_t w = 0; w < W; ++w)
+            for (uint32_t x = m[w]; x; x &= x - 1) fn(32 * w + __builtin_ctz(x));
+    };
     std::vector<int64_t> next(n_seq_max, 0);
-    for (int32_t s : c->seq_order) next[s] = (int64_t)cells.seq_pos_max(s) + 1;
+    for (int32_t i = 0; i < n; ++i) seqs_of(i, [&](int32_t s) { next[s] = (int64_t)cells.seq_pos_max(s) + 1; });
     c->pos.resize(n);
     if (!b.pos) {
-        for (int32_t i = 0; i < n; ++i) c->pos[i] = (int32_t)next[c->seq[i]]++;
-    } else {
-        std::vector<uint8_t> started(n_seq_max, 0);
+        // autofill from the first sequence of each token
+        std::vector<int64_t> fill = next;
         for (int32_t i = 0; i < n; ++i) {
-            const int32_t s = c->seq[i];
-            const int32_t p = b.pos[i];
+            const int64_t p = fill[c->seq[i]];
+            c->pos[i] = (int32_t)p;
+            seqs_of(i, [&](int32_t s) { fill[s] = p + 1; });
+        }
+    } else {
+        for (int32_t i = 0; i < n; ++i) c->pos[i] = b.pos[i];
+    }
+    std::vector<uint8_t> started(n_seq_max, 0);
+    bool ok = true;
+    for (int32_t i = 0; i < n && ok; ++i) {
+        const int32_t p = c->pos[i];
+        seqs_of(i, [&](int32_t s) {
             if (!started[s] && next[s] == 0) {
                 // an empty sequence may start at any position >= 0
-                if (p < 0) return bad("negative position");
+                if (p < 0) ok = false;
                 next[s] = p;
             }
             started[s] = 1;
-            if (p != next[s]) return bad("positions must continue each sequence consecutively");
+            if (p != next[s]) ok = false;
             ++next[s];
-            c->pos[i] = p;
-        }
+        });
     }
+    if (!ok) return bad("positions must continue each sequence consecutively");
     c->out.assign(n, 0);
     if (!b.logits) {
         c->out[n - 1] = 1;
@@ -197,10 +325,12 @@ void Planner::push_ubatch(const Clean &c, const std::vector<int32_t> &idx,
     ub.idx = idx;
     ub.n_seq_tokens = n_seq_tokens;
     ub.n_seqs = n_seqs;
+    const int32_t W = cells.n_seq_words();
     for (int32_t i : idx) {
         ub.token.push_back(c.token[i]);
         ub.pos.push_back(c.pos[i]);
         ub.seq.push_back(c.seq[i]);
+        ub.seqw.insert(ub.seqw.end(), c.seqw.begin() + (size_t)i * W, c.seqw.begin() + (size_t)(i + 1) * W);
     }
     ubatches.push_back(std::move(ub));
 }
@@ -237,22 +367,71 @@ void Planner::split_equal(const Clean &c) {
 }
 
 void Planner::rollback(const UBatch &ub, Executor *ex) {
+    const int32_t W = cells.n_seq_words();
     std::map<int32_t, int32_t> pos_min;
-    for (int32_t t = 0; t < ub.size(); ++t) {
-        auto it = pos_min.find(ub.seq[t]);
-        if (it == pos_min.end() || ub.pos[t] < it->second) pos_min[ub.seq[t]] = ub.pos[t];
-    }
-    std::vector<std::pair<int32_t, int32_t>> cleared;
-    for (auto &kv : pos_min) cells.seq_rm(kv.first, kv.second, -1, &cleared);
-    if (ex && !cleared.empty()) ex->cells_cleared(cleared);
+    for (int32_t t = 0; t < ub.size(); ++t)
+        for (int32_t w = 0; w < W; ++w)
+            for (uint32_t x = ub.seqw[(size_t)t * W + w]; x; x &= x - 1) {
+                const int32_t s = 32 * w + __builtin_ctz(x);
+                auto it = pos_min.find(s);
+                if (it == pos_min.end() || ub.pos[t] < it->second) pos_min[s] = ub.pos[t];
+            }
+    std::vector<uint8_t> touched(n_stream, 0);
+    for (auto &kv : pos_min) cells.seq_rm(kv.first, kv.second, -1, &touched);
+    if (ex) ex->cells_changed(touched);
 }
 
 bool Planner::seq_rm(int32_t s, int32_t p0, int32_t p1, Executor *ex) {
     if (s >= (int32_t)n_seq_max) return false;
-    std::vector<std::pair<int32_t, int32_t>> cleared;
-    cells.seq_rm(s, p0, p1, &cleared);
-    if (ex && !cleared.empty()) ex->cells_cleared(cleared);
+    std::vector<uint8_t> touched(n_stream, 0);
+    cells.seq_rm(s, p0, p1, &touched);
+    if (ex) ex->cells_changed(touched);
     return true;
+}
+
+bool Planner::seq_cp(int32_t src, int32_t dst, int32_t p0, int32_t p1, Executor *ex) {
+    if (src < 0 || dst < 0 || src >= (int32_t)n_seq_max || dst >= (int32_t)n_seq_max) return false;
+    if (src == dst) return true;
+    const int32_t ss = cells.stream_of(src), sd = cells.stream_of(dst);
+    if (ss != sd) {
+        if (p0 >= 0 || p1 >= 0) return false;
+        if (ex && ex->stream_copy(ss, sd) != UBD_OK) return false;
+    }
+    bool copied = false;
+    if (!cells.seq_cp(src, dst, p0, p1, &copied)) return false;
+    std::vector<uint8_t> touched(n_stream, 0);
+    touched[sd] = 1;
+    if (ex) ex->cells_changed(touched);
+    return true;
+}
+
+bool Planner::seq_keep(int32_t s, Executor *ex) {
+    if (s < 0 || s >= (int32_t)n_seq_max) return false;
+    cells.seq_keep(s);
+    std::vector<uint8_t> touched(n_stream, 1);
+    if (ex) ex->cells_changed(touched);
+    return true;
+}
+
+int32_t Planner::defrag(Executor *ex) {
+    std::vector<std::vector<int32_t>> src;
+    cells.defrag_plan(&src);
+    int32_t moved = 0;
+    std::vector<uint8_t> touched(n_stream, 0);
+    for (uint32_t st = 0; st < n_stream; ++st)
+        for (size_t j = 0; j < src[st].size(); ++j)
+            if (src[st][j] != (int32_t)j) {
+                ++moved;
+                touched[st] = 1;
+            }
+    if (moved == 0) return 0;
+    if (ex) {
+        const int32_t rc = ex->cells_move(src);
+        if (rc != UBD_OK) return rc;
+    }
+    cells.defrag_apply(src);
+    if (ex) ex->cells_changed(touched);
+    return moved;
 }
 
 int32_t Planner::decode(const ubd_batch &b, Executor *ex, std::string *err) {
@@ -269,9 +448,18 @@ int32_t Planner::decode(const ubd_batch &b, Executor *ex, std::string *err) {
     else
         split_equal(c);
     if (!cells.find_slots(ubatches)) {
-        if (err) *err = "no KV slot for the batch";
-        ubatches.clear();
-        return UBD_NO_KV_SLOT;
+        // compact the cache once and search again
+        rc = defrag(ex);
+        if (rc < 0) {
+            if (err) *err = "KV defrag failed";
+            ubatches.clear();
+            return rc;
+        }
+        if (!cells.find_slots(ubatches)) {
+            if (err) *err = "no KV slot for the batch";
+            ubatches.clear();
+            return UBD_NO_KV_SLOT;
+        }
     }
     const int32_t n = b.n_tokens;
     out_row.assign(n, -1);

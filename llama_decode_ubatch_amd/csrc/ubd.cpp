@@ -367,7 +367,9 @@ struct ubd_context : public Executor {
     float *kv_stage = nullptr;              // q8_0 caches: [cap][2][Hk*hd] rows awaiting quantisation
     uint32_t cell_stride = 0;               // cells per stream rounded up to 32
     void *k_cache = nullptr, *v_cache = nullptr;
-    int32_t *cell_pos = nullptr, *cell_seq = nullptr;
+    int32_t *cell_pos = nullptr;            // [stream][cell_stride]
+    uint32_t *cell_seq = nullptr;           // [stream][n_seq_words][cell_stride]
+    int n_seq_words = 1;
     float *x = nullptr, *q = nullptr;
     Act actA, actB, actC;
     float *part_o = nullptr, *part_ml = nullptr;
@@ -448,14 +450,18 @@ struct ubd_context : public Executor {
         t.tile_of = b + 6 * cap;
         t.out_tok = b + 7 * cap;
         t.tiles = b + 9 * cap;
+        t.seqw = (const uint32_t *)(b + 13 * cap);
+        t.n_seq_words = n_seq_words;
         return t;
     }
     const int32_t *out_lrow() const { return info_dev + 8 * cap; }
-    size_t info_ints() const { return (size_t)13 * cap; }
+    size_t info_ints() const { return (size_t)(13 + n_seq_words) * cap; }
 
     int32_t reserve_outputs(int32_t n) override;
     int32_t run_ubatch(const UBatch &ub, int32_t k) override;
-    void cells_cleared(const std::vector<std::pair<int32_t, int32_t>> &cl) override;
+    int32_t cells_changed(const std::vector<uint8_t> &touched) override;
+    int32_t stream_copy(int32_t src, int32_t dst) override;
+    int32_t cells_move(const std::vector<std::vector<int32_t>> &src) override;
     bool sync_cell_tables(int32_t stream);
 };
 
@@ -525,8 +531,9 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     c->v_layer_bytes = kv_layer_bytes(c->type_v, c->kv_layer_elems);
     c->k_cache = c->mem.get(c->k_layer_bytes * hp.n_layer);
     c->v_cache = c->mem.get(c->v_layer_bytes * hp.n_layer);
+    c->n_seq_words = P.cells.n_seq_words();
     c->cell_pos = (int32_t *)c->mem.get(cells * 4);
-    c->cell_seq = (int32_t *)c->mem.get(cells * 4);
+    c->cell_seq = (uint32_t *)c->mem.get(cells * c->n_seq_words * 4);
     if (!c->k_cache || !c->v_cache || !c->cell_pos || !c->cell_seq) return bail("KV cache allocation failed");
     // zero K/V: masked cells still enter P*V with weight 0, so never-written
     // cells must hold finite values
@@ -534,7 +541,7 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
         !hip_ok(hipMemsetAsync(c->v_cache, 0, c->v_layer_bytes * hp.n_layer, c->stream), "memset"))
         return bail("KV cache init failed");
     if (!hip_ok(hipMemsetAsync(c->cell_pos, 0xff, cells * 4, c->stream), "memset") ||
-        !hip_ok(hipMemsetAsync(c->cell_seq, 0xff, cells * 4, c->stream), "memset"))
+        !hip_ok(hipMemsetAsync(c->cell_seq, 0, cells * c->n_seq_words * 4, c->stream), "memset"))
         return bail("KV cell table init failed");
     const int cap = c->cap;
     const bool f32w = model->wtype == W_F32;
@@ -632,19 +639,89 @@ int32_t ubd_context::reserve_outputs(int32_t n) {
 
 bool ubd_context::sync_cell_tables(int32_t st) {
     const Planner &P = planner;
-    const size_t off = (size_t)st * cell_stride;
-    return hip_ok(hipMemcpyAsync(cell_pos + off, P.cells.pos_data(st), (size_t)P.n_cells * 4,
-                                 hipMemcpyHostToDevice, stream), "cell table upload") &&
-           hip_ok(hipMemcpyAsync(cell_seq + off, P.cells.seq_data(st), (size_t)P.n_cells * 4,
-                                 hipMemcpyHostToDevice, stream), "cell table upload") &&
-           hip_ok(hipStreamSynchronize(stream), "cell table sync");
+    bool ok = hip_ok(hipMemcpyAsync(cell_pos + (size_t)st * cell_stride, P.cells.pos_data(st),
+                                    (size_t)P.n_cells * 4, hipMemcpyHostToDevice, stream),
+                     "cell table upload");
+    for (int w = 0; ok && w < n_seq_words; ++w)
+        ok = hip_ok(hipMemcpyAsync(cell_seq + ((size_t)st * n_seq_words + w) * cell_stride,
+                                   P.cells.seq_words(st) + (size_t)w * P.n_cells, (size_t)P.n_cells * 4,
+                                   hipMemcpyHostToDevice, stream),
+                    "cell table upload");
+    return ok && hip_ok(hipStreamSynchronize(stream), "cell table sync");
 }
 
-void ubd_context::cells_cleared(const std::vector<std::pair<int32_t, int32_t>> &cl) {
-    std::vector<uint8_t> touched(planner.n_stream, 0);
-    for (auto &p : cl) touched[p.first] = 1;
+int32_t ubd_context::cells_changed(const std::vector<uint8_t> &touched) {
     for (uint32_t st = 0; st < planner.n_stream; ++st)
-        if (touched[st]) sync_cell_tables((int32_t)st);
+        if (touched[st] && !sync_cell_tables((int32_t)st)) return UBD_COMPUTE_FAILED;
+    return UBD_OK;
+}
+
+int32_t ubd_context::stream_copy(int32_t src, int32_t dst) {
+    const ubd_hparams &hp = model->hp;
+    const size_t per_stream = kv_layer_elems / planner.n_stream;     // values of one stream in one layer
+    auto copy = [&](void *base, size_t layer_bytes, int type) -> bool {
+        const size_t esz = type == KV_F32 ? 4 : type == KV_F16 ? 2 : 1;
+        for (int il = 0; il < hp.n_layer; ++il) {
+            char *l = (char *)base + layer_bytes * il;
+            if (!hip_ok(hipMemcpyAsync(l + dst * per_stream * esz, l + src * per_stream * esz, per_stream * esz,
+                                       hipMemcpyDeviceToDevice, stream),
+                        "stream copy"))
+                return false;
+            if (type == KV_Q8) {
+                char *sc = l + kv_layer_elems;
+                const size_t sb = per_stream / 32 * 2;
+                if (!hip_ok(hipMemcpyAsync(sc + dst * sb, sc + src * sb, sb, hipMemcpyDeviceToDevice, stream),
+                            "stream copy"))
+                    return false;
+            }
+        }
+        return true;
+    };
+    (void)hipSetDevice(model->device);
+    if (!copy(k_cache, k_layer_bytes, type_k) || !copy(v_cache, v_layer_bytes, type_v) ||
+        !hip_ok(hipStreamSynchronize(stream), "stream copy sync"))
+        return UBD_COMPUTE_FAILED;
+    return UBD_OK;
+}
+
+int32_t ubd_context::cells_move(const std::vector<std::vector<int32_t>> &src) {
+    const ubd_hparams &hp = model->hp;
+    const int hd = model->head_dim, Hk = hp.n_head_kv;
+    (void)hipSetDevice(model->device);
+    int32_t rc = UBD_OK;
+    for (uint32_t st = 0; st < planner.n_stream && rc == UBD_OK; ++st) {
+        // only the cells whose index changes
+        std::vector<int32_t> from, to;
+        for (size_t j = 0; j < src[st].size(); ++j)
+            if (src[st][j] != (int32_t)j) {
+                from.push_back(src[st][j]);
+                to.push_back((int32_t)j);
+            }
+        const int n = (int)from.size();
+        if (n == 0) continue;
+        int32_t *dcells = nullptr;
+        void *tmp = nullptr;
+        const size_t tb = std::max(kv_move_tmp_bytes(type_k, n, Hk, hd), kv_move_tmp_bytes(type_v, n, Hk, hd));
+        bool ok = hip_ok(hipMalloc(&dcells, (size_t)2 * n * 4), "defrag alloc") &&
+                  hip_ok(hipMalloc(&tmp, tb), "defrag alloc") &&
+                  hip_ok(hipMemcpy(dcells, from.data(), (size_t)n * 4, hipMemcpyHostToDevice), "defrag cells") &&
+                  hip_ok(hipMemcpy(dcells + n, to.data(), (size_t)n * 4, hipMemcpyHostToDevice), "defrag cells");
+        for (int il = 0; ok && il < hp.n_layer; ++il)
+            for (int which = 0; which < 2; ++which) {
+                void *cache = which == 0 ? (char *)k_cache + k_layer_bytes * il : (char *)v_cache + v_layer_bytes * il;
+                const int type = which == 0 ? type_k : type_v;
+                // every source row is in tmp before any destination is written
+                launch_kv_move(cache, type, which == 1, (int)st, dcells, n, Hk, hd, (int)cell_stride,
+                               kv_layer_elems, tmp, true, stream);
+                launch_kv_move(cache, type, which == 1, (int)st, dcells + n, n, Hk, hd, (int)cell_stride,
+                               kv_layer_elems, tmp, false, stream);
+            }
+        ok = ok && hip_ok(hipGetLastError(), "kv_move") && hip_ok(hipStreamSynchronize(stream), "defrag sync");
+        if (dcells) (void)hipFree(dcells);
+        if (tmp) (void)hipFree(tmp);
+        if (!ok) rc = UBD_COMPUTE_FAILED;
+    }
+    return rc;
 }
 
 int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
@@ -673,6 +750,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         h[3 * cap + t] = ub.stream[t];
         h[4 * cap + t] = ub.cell[t];
         h[5 * cap + t] = ub.out_row[t];
+        for (int w = 0; w < n_seq_words; ++w) h[13 * cap + t * n_seq_words + w] = (int32_t)ub.seqw[(size_t)t * n_seq_words + w];
         if (ub.out_row[t] >= 0) {
             h[7 * cap + n_out] = t;
             h[8 * cap + n_out] = ub.out_row[t];
@@ -696,9 +774,10 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
             const int st = ub.stream[t];
             int c = tl[3] - 1;
             for (; c >= 0; --c) {
-                const int cs = planner.cells.seq_at(st, c), cpp = planner.cells.pos_at(st, c);
+                const int cpp = planner.cells.pos_at(st, c);
                 bool vis = false;
-                for (int j = t; j < e && !vis; ++j) vis = cs == ub.seq[j] && cpp >= 0 && cpp <= ub.pos[j];
+                for (int j = t; j < e && !vis; ++j)
+                    vis = cpp >= 0 && cpp <= ub.pos[j] && planner.cells.has(st, c, ub.seq[j]);
                 if (vis) break;
             }
             tl[3] = c + 1;
@@ -771,6 +850,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         aa.layer_elems = kv_layer_elems;
         aa.cell_pos = cell_pos;
         aa.cell_seq = cell_seq;
+        aa.n_seq_words = n_seq_words;
         aa.n_cells = n_cells;
         aa.n_head = H;
         aa.n_head_kv = Hk;
@@ -1099,6 +1179,22 @@ extern "C" int32_t ubd_sampler_candidates(ubd_sampler *s, ubd_token *ids, float 
 }
 
 // ------------------------------------------------------------------ memory
+namespace {
+int32_t planner_cells(const Planner &P, int32_t stream, int32_t *pos, uint32_t *seq_words, int32_t cap) {
+    if (stream < 0 || (uint32_t)stream >= P.n_stream) return -1;
+    const int32_t n = (int32_t)P.n_cells, W = P.cells.n_seq_words();
+    if (pos) {
+        if (cap < n) return -1;
+        std::copy(P.cells.pos_data(stream), P.cells.pos_data(stream) + n, pos);
+    }
+    if (seq_words) {
+        if (cap < n * W) return -1;
+        std::copy(P.cells.seq_words(stream), P.cells.seq_words(stream) + (size_t)n * W, seq_words);
+    }
+    return n;
+}
+}  // namespace
+
 extern "C" ubd_pos ubd_memory_seq_pos_min(ubd_context *ctx, ubd_seq_id s) {
     return ctx ? ctx->planner.cells.seq_pos_min(s) : -1;
 }
@@ -1109,6 +1205,30 @@ extern "C" bool ubd_memory_seq_rm(ubd_context *ctx, ubd_seq_id s, ubd_pos p0, ub
     if (!ctx) return false;
     (void)hipSetDevice(ctx->model->device);
     return ctx->planner.seq_rm(s, p0, p1, ctx);
+}
+
+extern "C" bool ubd_memory_seq_cp(ubd_context *ctx, ubd_seq_id src, ubd_seq_id dst, ubd_pos p0, ubd_pos p1) {
+    if (!ctx) return false;
+    (void)hipSetDevice(ctx->model->device);
+    return ctx->planner.seq_cp(src, dst, p0, p1, ctx);
+}
+
+extern "C" bool ubd_memory_seq_keep(ubd_context *ctx, ubd_seq_id s) {
+    if (!ctx) return false;
+    (void)hipSetDevice(ctx->model->device);
+    return ctx->planner.seq_keep(s, ctx);
+}
+
+extern "C" int32_t ubd_memory_defrag(ubd_context *ctx) {
+    if (!ctx) return UBD_INVALID;
+    (void)hipSetDevice(ctx->model->device);
+    return ctx->planner.defrag(ctx);
+}
+
+extern "C" int32_t ubd_memory_cells(ubd_context *ctx, int32_t stream, int32_t *pos, uint32_t *seq_words,
+                                    int32_t cap) {
+    if (!ctx) return -1;
+    return planner_cells(ctx->planner, stream, pos, seq_words, cap);
 }
 
 extern "C" int32_t ubd_get_kv_cells(ubd_context *ctx, int32_t *cells_out, int32_t cap) {
@@ -1400,6 +1520,17 @@ extern "C" ubd_pos ubd_planner_seq_pos_max(const ubd_planner *p, ubd_seq_id s) {
 }
 extern "C" bool ubd_planner_seq_rm(ubd_planner *p, ubd_seq_id s, ubd_pos p0, ubd_pos p1) {
     return p ? p->p.seq_rm(s, p0, p1, nullptr) : false;
+}
+extern "C" bool ubd_planner_seq_cp(ubd_planner *p, ubd_seq_id src, ubd_seq_id dst, ubd_pos p0, ubd_pos p1) {
+    return p ? p->p.seq_cp(src, dst, p0, p1, nullptr) : false;
+}
+extern "C" bool ubd_planner_seq_keep(ubd_planner *p, ubd_seq_id s) { return p ? p->p.seq_keep(s, nullptr) : false; }
+extern "C" int32_t ubd_planner_defrag(ubd_planner *p) {
+    return p ? p->p.defrag(nullptr) : UBD_INVALID;
+}
+extern "C" int32_t ubd_planner_cells(const ubd_planner *p, int32_t stream, int32_t *pos, uint32_t *seq_words,
+                                     int32_t cap) {
+    return p ? planner_cells(p->p, stream, pos, seq_words, cap) : -1;
 }
 extern "C" int32_t ubd_planner_n_kv(const ubd_planner *p, int32_t stream) {
     if (!p || stream < 0 || (uint32_t)stream >= p->p.n_stream) return -1;

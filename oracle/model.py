@@ -11,7 +11,7 @@ matrix) and the node list of one decode step on the "llama.cpp Architecture"
 page (Example 4: GET_ROWS, RMS_NORM, MUL, MUL_MAT, ROPE, SET_ROWS,
 attention, ADD, SWIGLU).  KV handling follows the engine page's KV-cache
 section: the new token's K and V are appended first, then Q attends to every
-cached key of its sequence, its own included.
+cached key of its (first) sequence, its own included.
 
 Precision: the arrays are float64 for the tiny model and float32 for the
 8B shape (the pages' graph computes every node in f32).
@@ -100,12 +100,13 @@ class OracleContext:
         self.n_batch = min(self.n_ctx, n_batch)
         self.n_ubatch = min(self.n_batch, n_ubatch or self.n_batch)
         self.type_k, self.type_v = type_k, type_v
-        self.mem = KVMemory(self.n_stream, self.n_cells, kv_unified)
+        self.mem = KVMemory(self.n_stream, self.n_cells, kv_unified, self.n_seq_max)
         self._kv: Dict[tuple, tuple] = {}      # (layer, stream) -> (K, V)
         self.logits: Optional[np.ndarray] = None
         self.out_row: Optional[np.ndarray] = None
         self.n_outputs = 0
         self.last_plan: Optional[Plan] = None
+        self.last_defrag_src = None    # per stream: new cell j <- old cell src[j]
         self.record = None   # optional dict collecting per-layer residuals
 
     # ------------------------------------------------------------ storage
@@ -141,6 +142,36 @@ class OracleContext:
     def seq_rm(self, s, p0, p1):
         return self.mem.seq_rm(s, p0, p1)
 
+    def seq_cp(self, src, dst, p0, p1):
+        """Between streams the K/V rows of the whole stream go along."""
+        ss, sd = self.mem.stream_of(src), self.mem.stream_of(dst)
+        if not self.mem.seq_cp(src, dst, p0, p1):
+            return False
+        if ss != sd:
+            for il in range(self.model.hp.n_layer):
+                K, V = self.kv(il, ss)
+                self._kv[(il, sd)] = (K.copy(), V.copy())
+        return True
+
+    def seq_keep(self, s):
+        return self.mem.seq_keep(s)
+
+    def _move_cells(self, src):
+        self.last_defrag_src = src
+        for st, order in enumerate(src):
+            for il in range(self.model.hp.n_layer):
+                if (il, st) in self._kv:
+                    K, V = self._kv[(il, st)]
+                    K[:order.size] = K[order].copy()
+                    V[:order.size] = V[order].copy()
+
+    def defrag(self):
+        """Compact the cells of every stream and move their K/V rows along;
+        returns the number of cells whose index changed."""
+        src = self.mem.defrag()
+        self._move_cells(src)
+        return int(sum(int(np.count_nonzero(o != np.arange(o.size))) for o in src))
+
     def decode(self, batch: Batch, abort_at: Optional[int] = None,
                fail_at: Optional[int] = None) -> int:
         """One ``llama_decode`` call (engine page, Steps 11-12).  ``abort_at``
@@ -148,7 +179,7 @@ class OracleContext:
         index (test hooks)."""
         hp = self.model.hp
         plan = plan_batch(batch, self.mem, hp.n_vocab, self.n_seq_max,
-                          self.n_batch, self.n_ubatch)
+                          self.n_batch, self.n_ubatch, on_defrag=self._move_cells)
         self.last_plan = plan
         self.logits, self.out_row, self.n_outputs = None, None, 0
         if plan.rc != RC_OK:
@@ -230,7 +261,8 @@ class OracleContext:
                 K, V = self.kv(il, st)
                 cache[st] = (nkv, K[:nkv].astype(x.dtype), V[:nkv].astype(x.dtype))
             nkv, Kf, Vf = cache[st]
-            vis = (self.mem.seq[st, :nkv] == ub.seq[t]) & (self.mem.pos[st, :nkv] <= ub.pos[t])
+            # the cells of the token's first sequence, up to its position
+            vis = self.mem.has[st, :nkv, ub.seq[t]] & (self.mem.pos[st, :nkv] <= ub.pos[t])
             for gi in range(Hk):
                 hs = slice(gi * g, (gi + 1) * g)
                 cs = slice(gi * hd, (gi + 1) * hd)

@@ -13,18 +13,34 @@ Pages:
     slots for all ubatches before committing any; failure -> return code 1.
     Return codes 0 / 1 / 2 / -1 / -2 / -3.
   * decode-loop page ("Decode loop: batching, KV cache, memory management"),
-    "KV cache details": cells hold pos (-1 = empty) and their sequence;
-    "Error recovery and state rollback": ``apply`` is the only mutation, a
-    failed ubatch is undone with seq_rm(s, pos_min[s], -1).
+    "KV cache details": cells hold pos (-1 = empty) and the set of
+    sequences using them (a cell can be shared); defrag moves cells to
+    close the gaps (the section's before / after figure), and a failed
+    slot search is retried once after it; "Error recovery and state
+    rollback": ``apply`` is the only mutation, a failed ubatch is undone
+    with seq_rm(s, pos_min[s], -1).
+  * engine page, Step 10: a token may belong to several sequences
+    (n_seq_id > 1); positions are counted per sequence.
 
 Readings where the pages are silent (also listed in the design doc):
   * positions given by the caller must be consecutive per sequence in
     batch order and continue from seq_pos_max(s)+1 when the sequence
     already holds cells (an empty sequence may start at any p >= 0),
-    else -1;
-  * one sequence per token (n_seq_id == 1), else -1;
+    else -1; a token of several sequences must continue each of them,
+    and autofilled positions follow its first sequence;
+  * a token of several sequences is stored once, in one cell holding all
+    of them, which needs a unified cache (one stream), else -1; its
+    query attends to the cells of its first sequence;
   * slot search: in ubatch token order each token takes the lowest-index
     empty cell of its stream;
+  * seq_rm(s, ...) takes s out of the matching cells and frees a cell once
+    no sequence holds it; seq_cp(src, dst, p0, p1) adds dst to src's cells
+    with p0 <= pos < p1 in a unified cache, and between streams copies the
+    whole of src's stream (only for the full range: p0 < 0, p1 < 0)
+    replacing dst's; seq_keep(s) drops every other sequence;
+  * defrag packs each stream's occupied cells into its lowest indices,
+    ordered by (lowest sequence of the cell, position, old index), as in
+    the figure;
   * equal split: the sequences that still have tokens, in order of first
     appearance (at most n_ubatch of them), each give
     k = min(min remaining, n_ubatch // n_seqs) tokens; the ubatch lists
@@ -60,10 +76,11 @@ class UBatch:
     idx: np.ndarray          # batch index of each token, in ubatch order
     token: np.ndarray
     pos: np.ndarray
-    seq: np.ndarray
+    seq: np.ndarray          # first sequence of each token
     output: np.ndarray       # bool
     n_seq_tokens: int
     n_seqs: int
+    seqs: List[tuple] = field(default_factory=list)   # all sequences of each token
 
     @property
     def n_tokens(self) -> int:
@@ -77,6 +94,7 @@ class SanitizedBatch:
     seq: np.ndarray
     output: np.ndarray
     seq_order: List[int] = field(default_factory=list)  # first appearance
+    seqs: List[tuple] = field(default_factory=list)
 
 
 class KVMemory:
@@ -84,22 +102,35 @@ class KVMemory:
 
     One stream when the cache is unified, else one stream per sequence with
     n_ctx / n_seq_max cells each (engine page, Step 7; architecture page,
-    Example 10).  Each cell holds (pos, seq), -1 = empty.
+    Example 10).  Each cell holds a position (-1 = empty) and the set of
+    sequences using it, ``has[stream, cell, seq]``.
     """
 
-    def __init__(self, n_stream: int, n_cells: int, unified: bool):
+    def __init__(self, n_stream: int, n_cells: int, unified: bool,
+                 n_seq_max: Optional[int] = None):
         self.n_stream = n_stream
         self.n_cells = n_cells
         self.unified = unified
+        if n_seq_max is None:
+            n_seq_max = LLAMA_MAX_SEQ if unified or n_stream == 1 else n_stream
+        self.n_seq_max = n_seq_max
         self.pos = np.full((n_stream, n_cells), -1, np.int64)
-        self.seq = np.full((n_stream, n_cells), -1, np.int64)
+        self.has = np.zeros((n_stream, n_cells, n_seq_max), bool)
 
     def stream_of(self, s: int) -> int:
         return 0 if self.unified else int(s)
 
+    def occupy(self, st: int, cells, positions, seqs) -> None:
+        """Set cells of stream st to (position, sequence set); seqs holds
+        one sequence id or a tuple of them for all cells."""
+        cells = np.atleast_1d(cells)
+        self.pos[st, cells] = positions
+        self.has[st, cells] = False
+        self.has[st, cells[:, None], np.atleast_1d(seqs)[None, :]] = True
+
     def _cells_of(self, s: int):
         st = self.stream_of(s)
-        return st, np.flatnonzero(self.seq[st] == s)
+        return st, np.flatnonzero(self.has[st, :, s])
 
     def seq_pos_max(self, s: int) -> int:
         st, c = self._cells_of(s)
@@ -109,18 +140,79 @@ class KVMemory:
         st, c = self._cells_of(s)
         return int(self.pos[st, c].min()) if c.size else -1
 
+    def _free_unused(self, st: int) -> None:
+        self.pos[st, ~self.has[st].any(axis=1)] = -1
+
+    @staticmethod
+    def _range(p0: int, p1: int):
+        return (0 if p0 < 0 else p0), (np.iinfo(np.int64).max if p1 < 0 else p1)
+
     def seq_rm(self, s: int, p0: int, p1: int) -> bool:
-        """Empty the cells of sequence s (all sequences if s < 0) with
-        p0 <= pos < p1; p0 < 0 means 0, p1 < 0 means no upper bound."""
-        lo = 0 if p0 < 0 else p0
-        hi = np.iinfo(np.int64).max if p1 < 0 else p1
+        """Take sequence s (every sequence if s < 0) out of the cells with
+        p0 <= pos < p1; p0 < 0 means 0, p1 < 0 means no upper bound.  A cell
+        no sequence holds any more is empty."""
+        if s >= self.n_seq_max:
+            return False
+        lo, hi = self._range(p0, p1)
         for st in range(self.n_stream):
-            sel = (self.pos[st] >= lo) & (self.pos[st] < hi) & (self.seq[st] >= 0)
+            inr = (self.pos[st] >= lo) & (self.pos[st] < hi)
             if s >= 0:
-                sel &= self.seq[st] == s
-            self.pos[st, sel] = -1
-            self.seq[st, sel] = -1
+                self.has[st, inr, s] = False
+            else:
+                self.has[st, inr, :] = False
+            self._free_unused(st)
         return True
+
+    def seq_cp(self, src: int, dst: int, p0: int, p1: int) -> bool:
+        """Give dst the cells of src with p0 <= pos < p1.  Between streams
+        only the whole sequence can be copied: dst's stream becomes a copy
+        of src's (the caller copies the K/V rows of the stream too)."""
+        if not (0 <= src < self.n_seq_max and 0 <= dst < self.n_seq_max):
+            return False
+        if src == dst:
+            return True
+        ss, sd = self.stream_of(src), self.stream_of(dst)
+        if ss == sd:
+            lo, hi = self._range(p0, p1)
+            sel = self.has[ss, :, src] & (self.pos[ss] >= lo) & (self.pos[ss] < hi)
+            self.has[ss, sel, dst] = True
+            return True
+        if p0 >= 0 or p1 >= 0:
+            return False
+        self.has[sd] = False
+        self.pos[sd] = -1
+        sel = self.has[ss, :, src]
+        self.pos[sd, sel] = self.pos[ss, sel]
+        self.has[sd, sel, dst] = True
+        return True
+
+    def seq_keep(self, s: int) -> bool:
+        """Drop every sequence but s from every cell."""
+        if not 0 <= s < self.n_seq_max:
+            return False
+        for st in range(self.n_stream):
+            keep = self.has[st, :, s].copy()
+            self.has[st] = False
+            self.has[st, keep, s] = True
+            self._free_unused(st)
+        return True
+
+    def defrag(self) -> List[np.ndarray]:
+        """Pack each stream's occupied cells into its lowest indices, in
+        order of (lowest sequence, position, old index).  Returns per stream
+        ``src``: new cell j holds what was in cell src[j]."""
+        out = []
+        for st in range(self.n_stream):
+            used = np.flatnonzero(self.pos[st] >= 0)
+            first = np.argmax(self.has[st, used], axis=1)
+            src = used[np.lexsort((used, self.pos[st, used], first))]
+            pos, has = self.pos[st, src].copy(), self.has[st, src].copy()
+            self.pos[st] = -1
+            self.has[st] = False
+            self.pos[st, :src.size] = pos
+            self.has[st, :src.size] = has
+            out.append(src)
+        return out
 
     def n_kv(self, stream: int) -> int:
         """Cells an attention pass must scan: highest used index + 1."""
@@ -147,8 +239,8 @@ class KVMemory:
     def apply(self, ub: UBatch, cells: np.ndarray) -> None:
         for t in range(ub.n_tokens):
             st = self.stream_of(int(ub.seq[t]))
-            self.pos[st, cells[t]] = int(ub.pos[t])
-            self.seq[st, cells[t]] = int(ub.seq[t])
+            seqs = ub.seqs[t] if ub.seqs else (int(ub.seq[t]),)
+            self.occupy(st, int(cells[t]), int(ub.pos[t]), list(seqs))
 
     def fill_sequence(self, s: int, n_pos: int) -> Optional[np.ndarray]:
         """Occupy the n_pos lowest empty cells of s's stream with positions
@@ -161,8 +253,7 @@ class KVMemory:
         if free.size < n_pos:
             return None
         cells = free[:n_pos]
-        self.pos[st, cells] = np.arange(n_pos)
-        self.seq[st, cells] = s
+        self.occupy(st, cells, np.arange(n_pos), s)
         return cells
 
 
@@ -178,34 +269,45 @@ def sanitize(batch: Batch, n_vocab: int, n_seq_max: int, n_batch: int,
     if np.any(token < 0) or np.any(token >= n_vocab):
         return RC_INVALID, None
     if batch.seq_id is None:
-        seq = np.zeros(n, np.int64)
+        seqs = [(0,)] * n
     else:
-        if batch.n_seq_id is not None and any(int(v) != 1 for v in batch.n_seq_id):
+        if len(batch.seq_id) != n:
             return RC_INVALID, None
-        seq = np.asarray([v[0] if isinstance(v, (list, tuple, np.ndarray)) else v
-                          for v in batch.seq_id], dtype=np.int64)
-        if seq.size != n:
-            return RC_INVALID, None
-    if np.any(seq < 0) or np.any(seq >= n_seq_max):
+        seqs = []
+        for i, v in enumerate(batch.seq_id):
+            row = [int(x) for x in np.atleast_1d(v)]
+            if batch.n_seq_id is not None:
+                k = int(batch.n_seq_id[i])
+                if k < 1 or k > len(row):
+                    return RC_INVALID, None
+                row = row[:k]
+            if not row or len(set(row)) != len(row):
+                return RC_INVALID, None
+            seqs.append(tuple(row))
+    if any(s < 0 or s >= n_seq_max for row in seqs for s in row):
         return RC_INVALID, None
+    if any(len(row) > 1 for row in seqs) and mem.n_stream != 1:
+        return RC_INVALID, None            # shared cells need a unified cache
+    seq = np.asarray([row[0] for row in seqs], np.int64)
     order: List[int] = []
     for s in seq.tolist():
         if s not in order:
             order.append(s)
-    nxt = {s: mem.seq_pos_max(s) + 1 for s in order}
+    nxt = {s: mem.seq_pos_max(s) + 1 for row in seqs for s in row}
     if batch.pos is None:
         pos = np.empty(n, np.int64)
+        fill = dict(nxt)
         for i in range(n):
-            s = int(seq[i])
-            pos[i] = nxt[s]
-            nxt[s] += 1
+            pos[i] = fill[seqs[i][0]]
+            for s in seqs[i]:
+                fill[s] = pos[i] + 1
     else:
         pos = np.asarray(batch.pos, dtype=np.int64).reshape(-1)
         if pos.size != n:
             return RC_INVALID, None
-        started = set()
-        for i in range(n):
-            s = int(seq[i])
+    started = set()
+    for i in range(n):
+        for s in seqs[i]:
             if s not in started and nxt[s] == 0:
                 # an empty sequence may start at any position >= 0
                 if pos[i] < 0:
@@ -222,14 +324,14 @@ def sanitize(batch: Batch, n_vocab: int, n_seq_max: int, n_batch: int,
         out = np.asarray(batch.logits).reshape(-1) != 0
         if out.size != n:
             return RC_INVALID, None
-    return RC_OK, SanitizedBatch(token, pos, seq, out, order)
+    return RC_OK, SanitizedBatch(token, pos, seq, out, order, seqs)
 
 
 def _make_ubatch(sb: SanitizedBatch, idx: List[int], n_seq_tokens: int,
                  n_seqs: int) -> UBatch:
     ix = np.asarray(idx, dtype=np.int64)
     return UBatch(ix, sb.token[ix], sb.pos[ix], sb.seq[ix], sb.output[ix],
-                  n_seq_tokens, n_seqs)
+                  n_seq_tokens, n_seqs, [sb.seqs[i] for i in idx])
 
 
 def split_simple(sb: SanitizedBatch, n_ubatch: int) -> List[UBatch]:
@@ -269,14 +371,21 @@ class Plan:
 
 
 def plan_batch(batch: Batch, mem: KVMemory, n_vocab: int, n_seq_max: int,
-               n_batch: int, n_ubatch: int) -> Plan:
-    """Sanitise, split and find slots (no mutation of ``mem``)."""
+               n_batch: int, n_ubatch: int, on_defrag=None) -> Plan:
+    """Sanitise, split and find slots.  ``mem`` changes only when the slot
+    search fails: then the cache is defragmented (``on_defrag(src)`` sees
+    the moves) and the search runs once more."""
     rc, sb = sanitize(batch, n_vocab, n_seq_max, n_batch, mem)
     if rc != RC_OK:
         return Plan(rc)
     ubs = split_simple(sb, n_ubatch) if mem.n_stream == 1 else split_equal(sb, n_ubatch)
     assert sum(u.n_tokens for u in ubs) == sb.token.size
     cells = mem.find_slots(ubs)
+    if cells is None:
+        src = mem.defrag()
+        if on_defrag is not None:
+            on_defrag(src)
+        cells = mem.find_slots(ubs)
     if cells is None:
         return Plan(RC_NO_SLOT)
     out_row = np.full(sb.token.size, -1, np.int64)
@@ -289,8 +398,8 @@ def rollback_ubatch(mem: KVMemory, ub: UBatch) -> None:
     """Undo a committed ubatch: seq_rm(s, pos_min[s], -1) for its sequences."""
     pos_min = {}
     for t in range(ub.n_tokens):
-        s = int(ub.seq[t])
-        pos_min[s] = min(pos_min.get(s, int(ub.pos[t])), int(ub.pos[t]))
+        for s in (ub.seqs[t] if ub.seqs else (int(ub.seq[t]),)):
+            pos_min[s] = min(pos_min.get(s, int(ub.pos[t])), int(ub.pos[t]))
     for s, p in pos_min.items():
         mem.seq_rm(s, p, -1)
 

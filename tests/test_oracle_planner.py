@@ -30,7 +30,7 @@ def test_autofill_defaults():
 
 def test_autofill_positions_per_sequence():
     m = KVMemory(1, 32, unified=True)
-    m.pos[0, :3] = [0, 1, 2]; m.seq[0, :3] = 1
+    m.occupy(0, [0, 1, 2], [0, 1, 2], 1)
     rc, sb = sanitize(Batch([1, 2, 3, 4, 5], seq_id=[0, 1, 0, 1, 1]), 10, 2, 64, m)
     assert sb.pos.tolist() == [0, 3, 1, 4, 5]
 
@@ -42,7 +42,9 @@ def test_autofill_positions_per_sequence():
     Batch([-1]),                                   # token < 0
     Batch([1, 2], seq_id=[0, 4]),                  # seq id >= n_seq_max
     Batch([1, 2], seq_id=[0, -1]),
-    Batch([1], seq_id=[[0, 1]], n_seq_id=[2]),     # several seqs per token
+    Batch([1], seq_id=[[0, 0]], n_seq_id=[2]),     # a sequence twice
+    Batch([1], seq_id=[[0, 1]], n_seq_id=[0]),     # no sequence
+    Batch([1], seq_id=[[0, 1]], n_seq_id=[3]),     # fewer ids than n_seq_id
     Batch([1, 2], pos=[0, 2]),                     # non-consecutive
     Batch([1, 2], pos=[1, 0]),
     Batch([1], pos=[-3]),
@@ -55,7 +57,7 @@ def test_invalid_batches(batch):
 
 def test_positions_must_continue_sequence():
     m = mem1()
-    m.pos[0, :2] = [0, 1]; m.seq[0, :2] = 0
+    m.occupy(0, [0, 1], [0, 1], 0)
     assert plan_batch(Batch([1], pos=[3]), m, 100, 1, 64, 16).rc == RC_INVALID
     assert plan_batch(Batch([1], pos=[2]), m, 100, 1, 64, 16).rc == RC_OK
     # an empty sequence may start anywhere
@@ -102,14 +104,46 @@ def test_split_equal_uneven_and_order():
 
 def test_slots_lowest_free_and_prepare_all_or_nothing():
     m = mem1(8)
-    m.pos[0, [1, 4]] = [0, 1]; m.seq[0, [1, 4]] = 0
+    m.occupy(0, [1, 4], [0, 1], 0)
     p = plan_batch(Batch([1, 2, 3]), m, 10, 1, 64, 2)
     assert [c.tolist() for c in p.cells] == [[0, 2], [3]]
-    # 6 free cells; a 7-token batch needs 7 -> return 1 and nothing changes
-    before = (m.pos.copy(), m.seq.copy())
-    p = plan_batch(Batch([1] * 7), m, 10, 1, 64, 2)
+    # 6 free cells; a 7-token batch needs 7 -> the search fails, the cache is
+    # compacted and searched once more (decode-loop page, "KV cache
+    # details"), still 6 free -> return 1; positions and sequences survive,
+    # packed into the lowest cells
+    moves = []
+    p = plan_batch(Batch([1] * 7), m, 10, 1, 64, 2, on_defrag=moves.append)
     assert p.rc == RC_NO_SLOT
-    assert np.array_equal(m.pos, before[0]) and np.array_equal(m.seq, before[1])
+    assert m.pos[0].tolist() == [0, 1, -1, -1, -1, -1, -1, -1]
+    assert m.has[0, :2, 0].all() and not m.has[0, 2:].any()
+    assert len(moves) == 1 and [o.tolist() for o in moves[0]] == [[1, 4]]
+    assert (m.seq_pos_min(0), m.seq_pos_max(0)) == (0, 1)
+
+
+def test_shared_tokens_need_a_unified_cache():
+    assert plan_batch(Batch([1], seq_id=[[0, 1]], n_seq_id=[2]), KVMemory(2, 16, False),
+                      100, 2, 64, 16).rc == RC_INVALID
+    m = KVMemory(1, 16, True, 4)
+    p = plan_batch(Batch([1, 2, 3], seq_id=[[0, 1, 2], [0, 1, 2], [1]]), m, 100, 4, 64, 16)
+    assert p.rc == RC_OK
+    for ub, c in zip(p.ubatches, p.cells):
+        m.apply(ub, c)
+    # one cell per token; the shared ones hold all three sequences
+    assert m.pos[0, :3].tolist() == [0, 1, 2]
+    assert m.has[0, 0, :3].all() and m.has[0, 1, :3].all()
+    assert m.has[0, 2].tolist() == [False, True, False, False]
+    assert [m.seq_pos_max(s) for s in range(4)] == [1, 2, 1, -1]
+    # positions continue each sequence of a shared token
+    assert plan_batch(Batch([5], seq_id=[[0, 1]]), m, 100, 4, 64, 16).rc == RC_INVALID
+    assert plan_batch(Batch([5], seq_id=[[0, 2]]), m, 100, 4, 64, 16).rc == RC_OK
+    assert plan_batch(Batch([5], pos=[2], seq_id=[[0, 2]]), m, 100, 4, 64, 16).rc == RC_OK
+    assert plan_batch(Batch([5], pos=[2], seq_id=[[0, 1]]), m, 100, 4, 64, 16).rc == RC_INVALID
+    # a shared cell stays until its last sequence leaves it
+    m.seq_rm(0, -1, -1)
+    assert m.pos[0, :3].tolist() == [0, 1, 2] and not m.has[0, :, 0].any()
+    m.seq_rm(1, -1, -1)
+    m.seq_rm(2, 1, -1)
+    assert m.pos[0, :3].tolist() == [0, -1, -1] and m.has[0, 0].tolist() == [False, False, True, False]
 
 
 def test_seq_rm_and_reuse():

@@ -14,11 +14,12 @@ class OraclePlanner:
         self.n_batch = min(self.n_ctx, n_batch)
         self.n_ubatch = min(self.n_batch, n_ubatch)
         self.n_seq_max, self.n_vocab = n_seq_max, n_vocab
-        self.mem = KVMemory(self.n_stream, self.n_cells, unified)
+        self.mem = KVMemory(self.n_stream, self.n_cells, unified, n_seq_max)
         self.plan = None
 
     def decode(self, batch, fail_at=-1, fail_code=0):
-        p = plan_batch(batch, self.mem, self.n_vocab, self.n_seq_max, self.n_batch, self.n_ubatch)
+        p = plan_batch(batch, self.mem, self.n_vocab, self.n_seq_max, self.n_batch, self.n_ubatch,
+                       on_defrag=lambda src: None)
         self.plan = p
         if p.rc != 0:
             return p.rc
@@ -28,6 +29,10 @@ class OraclePlanner:
                 rollback_ubatch(self.mem, ub)
                 return fail_code
         return 0
+
+    def mem_defrag(self):
+        src = self.mem.defrag()
+        return int(sum(int(np.count_nonzero(o != np.arange(o.size))) for o in src))
 
 
 def both(**kw):
@@ -128,3 +133,69 @@ def test_no_slot_returns_1_and_keeps_state():
     check_same(cp, op, 1, cp.decode(np.ones(57)), op.decode(Batch(np.ones(57, int))))
     assert cp.seq_pos_max(0) == 199
     check_same(cp, op, 1, cp.decode(np.ones(56)), op.decode(Batch(np.ones(56, int))))
+
+
+def check_tables(cp, op):
+    for st in range(op.n_stream):
+        pos, has = cp.cells(st, op.n_cells, op.n_seq_max)
+        assert pos.tolist() == op.mem.pos[st].tolist()
+        assert np.array_equal(has, op.mem.has[st])
+        assert cp.n_kv(st) == op.mem.n_kv(st)
+    for s in range(op.n_seq_max):
+        assert (cp.seq_pos_min(s), cp.seq_pos_max(s)) == (op.mem.seq_pos_min(s), op.mem.seq_pos_max(s))
+
+
+def test_defrag_of_the_page_figure():
+    """The decode-loop page's defrag figure ("KV cache details"): the C++
+    planner reaches the figure's seven cells (a third sequence fills the two
+    gaps, then leaves) and compacts them as the figure shows."""
+    from tests.test_oracle_memory import read_figure
+    fig = read_figure()
+    cp, op = both(n_ctx=256, n_batch=64, n_ubatch=64, n_seq_max=3, unified=True, n_vocab=50)
+    toks, seq = [1] * 7, [0, 0, 2, 1, 0, 2, 1]
+    check_same(cp, op, 3, cp.decode(toks, seq_id=seq), op.decode(Batch(toks, seq_id=seq)))
+    assert cp.seq_rm(2, -1, -1) and op.mem.seq_rm(2, -1, -1)
+    for part in ("before", "after"):
+        pos, has = cp.cells(0, op.n_cells, 3)
+        for c, sq, p in fig[part]:
+            assert pos[c] == p and has[c].tolist() == [sq == 0, sq == 1, False]
+        check_tables(cp, op)
+        if part == "before":
+            assert cp.defrag() == op.mem_defrag() == 2     # cells 4 and 6 move
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_memory_ops(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n_seq = int(rng.integers(1, 6))
+    unified = bool(rng.integers(0, 2)) if seed % 4 else True
+    n_ubatch = int(rng.choice([1, 5, 16, 64]))
+    cfg = dict(n_ctx=256, n_batch=96, n_ubatch=n_ubatch, n_seq_max=n_seq, unified=unified, n_vocab=500)
+    cp, op = both(**cfg)
+    for it in range(40):
+        r = rng.random()
+        if r < 0.1:
+            s = int(rng.integers(-1, n_seq))
+            p0, p1 = int(rng.integers(-1, 40)), int(rng.integers(-1, 80))
+            assert cp.seq_rm(s, p0, p1) == op.mem.seq_rm(s, p0, p1)
+        elif r < 0.2:
+            a, b = (int(v) for v in rng.integers(0, n_seq, 2))
+            p0, p1 = (-1, -1) if rng.random() < 0.5 else (int(rng.integers(-1, 30)), int(rng.integers(-1, 60)))
+            assert cp.seq_cp(a, b, p0, p1) == op.mem.seq_cp(a, b, p0, p1)
+        elif r < 0.25:
+            s = int(rng.integers(0, n_seq))
+            assert cp.seq_keep(s) == op.mem.seq_keep(s)
+        elif r < 0.35:
+            assert cp.defrag() == op.mem_defrag()
+        else:
+            n = int(rng.integers(1, 50))
+            toks = rng.integers(0, 500, n)
+            if unified and n_seq > 1 and rng.random() < 0.5:
+                seq = [sorted(set(rng.integers(0, n_seq, int(rng.integers(1, n_seq + 1))).tolist()),
+                              key=lambda v: rng.random()) for _ in range(n)]
+            else:
+                seq = rng.integers(0, n_seq, n).tolist()
+            rc_c = cp.decode(toks, seq_id=seq)
+            rc_o = op.decode(Batch(toks, seq_id=seq))
+            check_same(cp, op, n_seq, rc_c, rc_o)
+        check_tables(cp, op)
