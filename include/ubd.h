@@ -83,10 +83,13 @@ typedef struct ubd_hparams {
  * Shapes use ggml's order ([ARCH] Example 4): ne[0] = values per row (the
  * input dimension), ne[1] = rows (the output dimension); norm gains have
  * ne = {n_embd, 1}.  Norm gains must be F32.  All 2-D matrices of a model
- * share one type: F32, BF16 or Q8_0.
- *   F32 / BF16: data = ne[1] rows of ne[0] values, row-major.
- *   Q8_0:       data = int8 codes [ne[1]][ne[0]]; scales = f16 bit patterns
- *               [ne[1]][ne[0] / 32]; ne[0] must be a multiple of 32.
+ * share one storage type: F32 (F16 sources are widened to it exactly), BF16
+ * or Q8_0.
+ *   F32 / F16 / BF16: data = ne[1] rows of ne[0] values, row-major.
+ *   Q8_0: data = int8 codes [ne[1]][ne[0]] and scales = f16 bit patterns
+ *         [ne[1]][ne[0] / 32]; or scales = NULL and data = the GGUF block
+ *         layout, [ne[1]][ne[0] / 32] blocks of 34 bytes (f16 scale, then
+ *         32 codes).  ne[0] must be a multiple of 32.
  * data / scales are host pointers unless on_device != 0.  They are copied
  * during ubd_model_load and may be freed afterwards. */
 typedef struct ubd_tensor_src {
@@ -129,6 +132,90 @@ ubd_model *ubd_model_load(const ubd_hparams *hparams,
 void ubd_model_free(ubd_model *model);
 /* Bytes of device memory held by the model's weights. */
 size_t ubd_model_size(const ubd_model *model);
+
+/* ------------------------------------------------------------------- GGUF */
+
+/* GGUF files ([ENG] "GGUF format" reference and Steps 2-4; loading page
+ * "Model loading": header parsed without tensor data, a name -> location
+ * map, data mapped or read, split files).  The layout is the pages': magic
+ * "GGUF", version (only 3 is read; others are rejected), tensor count, key
+ * count (u64 each); key/value pairs (key string, u32 value type, value;
+ * arrays: u32 element type, u64 count, elements); tensor records (name,
+ * u32 n_dims <= 4, u64 sizes innermost first, u32 tensor type, u64 offset
+ * from the data block); the data block.  The pages give no codes or
+ * alignment; these are the public GGUF specification's:
+ *   value types  0 u8, 1 i8, 2 u16, 3 i16, 4 u32, 5 i32, 6 f32, 7 bool,
+ *                8 string (u64 length + bytes), 9 array, 10 u64, 11 i64,
+ *                12 f64
+ *   tensor types 0 F32, 1 F16, 8 Q8_0 (34-byte blocks), 30 BF16; others
+ *                are rejected
+ *   alignment    general.alignment (u32) or 32: the data block starts at
+ *                the first multiple after the records; offsets are
+ *                multiples of it.
+ * Every size, count and offset is checked against the file: a malformed
+ * file gives status -1 and a message, never a read outside it. */
+typedef struct ubd_gguf ubd_gguf;
+ubd_gguf *ubd_gguf_open(const char *path, int32_t *status);
+void ubd_gguf_close(ubd_gguf *g);
+uint32_t ubd_gguf_version(const ubd_gguf *g);
+/* Absolute file offset of the data block. */
+int64_t ubd_gguf_data_offset(const ubd_gguf *g);
+/* Metadata, as the pages' gguf_get_n_kv / get_key / get_kv_type /
+ * find_key / get_val_*: index i in [0, n_kv); j = -1 reads a scalar, j >= 0
+ * element j of an array.  get_int covers the integer types and bool,
+ * get_float f32 / f64, get_str strings (*len gets the byte length; the
+ * bytes are also NUL-terminated).  Nested arrays report their type and
+ * count only.  Wrong type or index: -1 / NULL. */
+int64_t ubd_gguf_n_kv(const ubd_gguf *g);
+int64_t ubd_gguf_find_key(const ubd_gguf *g, const char *key);
+const char *ubd_gguf_key(const ubd_gguf *g, int64_t i);
+int32_t ubd_gguf_kv_type(const ubd_gguf *g, int64_t i);
+int32_t ubd_gguf_arr_type(const ubd_gguf *g, int64_t i);
+int64_t ubd_gguf_arr_n(const ubd_gguf *g, int64_t i);
+int32_t ubd_gguf_get_int(const ubd_gguf *g, int64_t i, int64_t j, int64_t *out);
+int32_t ubd_gguf_get_float(const ubd_gguf *g, int64_t i, int64_t j, double *out);
+const char *ubd_gguf_get_str(const ubd_gguf *g, int64_t i, int64_t j, uint64_t *len);
+/* Tensor records: dims writes ne[4] (unused = 1) and returns n_dims;
+ * offset is absolute in the file; nbytes from the type's block size. */
+int64_t ubd_gguf_n_tensors(const ubd_gguf *g);
+int64_t ubd_gguf_find_tensor(const ubd_gguf *g, const char *name);
+const char *ubd_gguf_tensor_name(const ubd_gguf *g, int64_t i);
+int32_t ubd_gguf_tensor_type(const ubd_gguf *g, int64_t i);
+int32_t ubd_gguf_tensor_dims(const ubd_gguf *g, int64_t i, int64_t *ne);
+int64_t ubd_gguf_tensor_offset(const ubd_gguf *g, int64_t i);
+int64_t ubd_gguf_tensor_nbytes(const ubd_gguf *g, int64_t i);
+
+/* Summary of a model file ([ARCH] Example 8 print_info): parameters from
+ * the tensor shapes, bits per weight = file bits / parameters, the most
+ * common tensor type (all_same = every tensor has it), the hyperparameters
+ * as ubd_model_load_gguf reads them. */
+typedef struct ubd_gguf_info {
+    uint32_t version;
+    int32_t n_files;
+    int64_t n_tensors;
+    double n_params;
+    double file_bytes;
+    double bpw;
+    int32_t file_type;
+    int32_t all_same;
+    ubd_hparams hparams;
+} ubd_gguf_info;
+int32_t ubd_gguf_model_info(const char *path, ubd_gguf_info *info);
+
+/* Load a llama model from a GGUF file ([ENG] Steps 2-6).  Architecture
+ * general.architecture = "llama"; hyperparameters from llama.block_count,
+ * .embedding_length, .feed_forward_length, .attention.head_count,
+ * .attention.head_count_kv (default head_count), .context_length,
+ * .attention.layer_norm_rms_epsilon, .rope.freq_base (default 10000);
+ * n_vocab from token_embd.weight.  A first part named
+ * <prefix>-00001-of-0000N.gguf with split.count = N pulls in the other
+ * parts by name (each must carry its split.no); all tensors go into one
+ * map, a name seen twice is an error.  use_mmap != 0 maps the files and
+ * uploads from the mapping; 0 reads each tensor with pread.  Tensors are
+ * then loaded as by ubd_model_load (same rules and status codes); the
+ * print_info summary goes to the log. */
+ubd_model *ubd_model_load_gguf(const char *path, const ubd_model_params *params, int32_t use_mmap,
+                               int32_t *status);
 
 /* ---------------------------------------------------------------- context */
 

@@ -7,6 +7,7 @@ raises instead of falling back to anything else.
 """
 import ctypes as C
 import os
+import types
 import weakref
 
 import numpy as np
@@ -65,6 +66,12 @@ class SamplerParams(C.Structure):
                 ("penalty_present", C.c_float)]
 
 
+class GgufInfo(C.Structure):
+    _fields_ = [("version", C.c_uint32), ("n_files", C.c_int32), ("n_tensors", C.c_int64),
+                ("n_params", C.c_double), ("file_bytes", C.c_double), ("bpw", C.c_double),
+                ("file_type", C.c_int32), ("all_same", C.c_int32), ("hparams", Hparams)]
+
+
 class Perf(C.Structure):
     _fields_ = [("t_load_ms", C.c_double), ("t_p_eval_ms", C.c_double), ("t_eval_ms", C.c_double),
                 ("n_p_eval", C.c_int32), ("n_eval", C.c_int32), ("n_ubatch", C.c_int32),
@@ -102,6 +109,28 @@ SIGNATURES = {
     "ubd_sampler_sample_logits": (C.c_int32, [_P, C.c_void_p, C.c_int32, C.c_float]),
     "ubd_sampler_candidates": (C.c_int32, [_P, C.POINTER(C.c_int32), C.POINTER(C.c_float), C.c_int32]),
     "ubd_synchronize": (C.c_int32, [_P]),
+    "ubd_gguf_open": (_P, [C.c_char_p, C.POINTER(C.c_int32)]),
+    "ubd_gguf_close": (None, [_P]),
+    "ubd_gguf_version": (C.c_uint32, [_P]),
+    "ubd_gguf_data_offset": (C.c_int64, [_P]),
+    "ubd_gguf_n_kv": (C.c_int64, [_P]),
+    "ubd_gguf_find_key": (C.c_int64, [_P, C.c_char_p]),
+    "ubd_gguf_key": (C.c_char_p, [_P, C.c_int64]),
+    "ubd_gguf_kv_type": (C.c_int32, [_P, C.c_int64]),
+    "ubd_gguf_arr_type": (C.c_int32, [_P, C.c_int64]),
+    "ubd_gguf_arr_n": (C.c_int64, [_P, C.c_int64]),
+    "ubd_gguf_get_int": (C.c_int32, [_P, C.c_int64, C.c_int64, C.POINTER(C.c_int64)]),
+    "ubd_gguf_get_float": (C.c_int32, [_P, C.c_int64, C.c_int64, C.POINTER(C.c_double)]),
+    "ubd_gguf_get_str": (C.c_void_p, [_P, C.c_int64, C.c_int64, C.POINTER(C.c_uint64)]),
+    "ubd_gguf_n_tensors": (C.c_int64, [_P]),
+    "ubd_gguf_find_tensor": (C.c_int64, [_P, C.c_char_p]),
+    "ubd_gguf_tensor_name": (C.c_char_p, [_P, C.c_int64]),
+    "ubd_gguf_tensor_type": (C.c_int32, [_P, C.c_int64]),
+    "ubd_gguf_tensor_dims": (C.c_int32, [_P, C.c_int64, C.POINTER(C.c_int64)]),
+    "ubd_gguf_tensor_offset": (C.c_int64, [_P, C.c_int64]),
+    "ubd_gguf_tensor_nbytes": (C.c_int64, [_P, C.c_int64]),
+    "ubd_gguf_model_info": (C.c_int32, [C.c_char_p, C.POINTER(GgufInfo)]),
+    "ubd_model_load_gguf": (_P, [C.c_char_p, C.POINTER(ModelParams), C.c_int32, C.POINTER(C.c_int32)]),
     "ubd_memory_seq_pos_min": (C.c_int32, [_P, C.c_int32]),
     "ubd_memory_seq_pos_max": (C.c_int32, [_P, C.c_int32]),
     "ubd_memory_seq_rm": (C.c_bool, [_P, C.c_int32, C.c_int32, C.c_int32]),
@@ -288,23 +317,120 @@ class Model:
                 s.on_device = 1
                 if t["type"] == "q8_0":
                     s.scales = t["scale"].data_ptr()
-        mp = ModelParams()
-        mp.device = device
-        if self.alloc:
-            mp.alloc = self.alloc.alloc_fn
-            mp.free = self.alloc.free_fn
-        mp.stream = _stream_ptr(torch, device)
+        mp = self._params()
         st = C.c_int32(0)
         self.ptr = self.lib.ubd_model_load(C.byref(hp), arr, len(tensors), C.byref(mp), C.byref(st))
         if not self.ptr:
             raise RuntimeError(f"ubd_model_load failed ({st.value}): {last_error()}")
         self._finalizer = weakref.finalize(self, self.lib.ubd_model_free, self.ptr)
 
+    def _params(self):
+        mp = ModelParams()
+        mp.device = self.device
+        if self.alloc:
+            mp.alloc = self.alloc.alloc_fn
+            mp.free = self.alloc.free_fn
+        mp.stream = _stream_ptr(self.torch, self.device)
+        return mp
+
+    @classmethod
+    def from_gguf(cls, path, device=0, use_mmap=True, torch_alloc=True):
+        """Load with ubd_model_load_gguf; ``shape`` then holds the
+        hyperparameters the file gives."""
+        import torch
+        self = cls.__new__(cls)
+        self.lib = load_library()
+        self.torch = torch
+        self.device = device
+        torch.cuda.set_device(device)
+        self.alloc = TorchAllocator(torch, f"cuda:{device}") if torch_alloc else None
+        hp = gguf_model_info(path).hparams
+        self.shape = types.SimpleNamespace(
+            n_layer=hp.n_layer, n_embd=hp.n_embd, n_head=hp.n_head, n_head_kv=hp.n_head_kv, n_ff=hp.n_ff,
+            n_vocab=hp.n_vocab, n_ctx_train=hp.n_ctx_train, rms_eps=hp.rms_eps, rope_base=hp.rope_freq_base)
+        mp = self._params()
+        st = C.c_int32(0)
+        self.ptr = self.lib.ubd_model_load_gguf(str(path).encode(), C.byref(mp), int(bool(use_mmap)), C.byref(st))
+        if not self.ptr:
+            raise RuntimeError(f"ubd_model_load_gguf failed ({st.value}): {last_error()}")
+        self._finalizer = weakref.finalize(self, self.lib.ubd_model_free, self.ptr)
+        return self
+
     def size(self):
         return self.lib.ubd_model_size(self.ptr)
 
     def free(self):
         self._finalizer()
+
+
+def gguf_model_info(path):
+    info = GgufInfo()
+    if load_library().ubd_gguf_model_info(str(path).encode(), C.byref(info)) != 0:
+        raise ValueError(f"ubd_gguf_model_info failed: {last_error()}")
+    return info
+
+
+class Gguf:
+    """Metadata and tensor records of one GGUF file (ubd_gguf_*)."""
+    INT_TYPES = {0, 1, 2, 3, 4, 5, 7, 10, 11}
+    FLOAT_TYPES = {6, 12}
+
+    def __init__(self, path):
+        self.lib = load_library()
+        st = C.c_int32(0)
+        self.ptr = self.lib.ubd_gguf_open(str(path).encode(), C.byref(st))
+        if not self.ptr:
+            raise ValueError(f"ubd_gguf_open failed ({st.value}): {last_error()}")
+        self._finalizer = weakref.finalize(self, self.lib.ubd_gguf_close, self.ptr)
+        self.version = self.lib.ubd_gguf_version(self.ptr)
+        self.data_offset = self.lib.ubd_gguf_data_offset(self.ptr)
+
+    def close(self):
+        self._finalizer()
+
+    def _elem(self, i, j, t):
+        if t in self.INT_TYPES:
+            v = C.c_int64()
+            assert self.lib.ubd_gguf_get_int(self.ptr, i, j, C.byref(v)) == 0
+            return v.value
+        if t in self.FLOAT_TYPES:
+            v = C.c_double()
+            assert self.lib.ubd_gguf_get_float(self.ptr, i, j, C.byref(v)) == 0
+            return v.value
+        n = C.c_uint64()
+        p = self.lib.ubd_gguf_get_str(self.ptr, i, j, C.byref(n))
+        assert p
+        return C.string_at(p, n.value)
+
+    def items(self):
+        """[(key, type, value)]: arrays as (element type, list), nested
+        arrays as (9, count); strings as bytes."""
+        out = []
+        for i in range(self.lib.ubd_gguf_n_kv(self.ptr)):
+            key = self.lib.ubd_gguf_key(self.ptr, i).decode("utf-8", errors="surrogateescape")
+            t = self.lib.ubd_gguf_kv_type(self.ptr, i)
+            if t == 9:
+                et, n = self.lib.ubd_gguf_arr_type(self.ptr, i), self.lib.ubd_gguf_arr_n(self.ptr, i)
+                v = (et, n) if et == 9 else (et, [self._elem(i, j, et) for j in range(n)])
+            else:
+                v = self._elem(i, -1, t)
+            out.append((key, t, v))
+        return out
+
+    def find_key(self, key):
+        return self.lib.ubd_gguf_find_key(self.ptr, key.encode())
+
+    def tensors(self):
+        out = []
+        ne = (C.c_int64 * 4)()
+        for i in range(self.lib.ubd_gguf_n_tensors(self.ptr)):
+            nd = self.lib.ubd_gguf_tensor_dims(self.ptr, i, ne)
+            name = self.lib.ubd_gguf_tensor_name(self.ptr, i).decode("utf-8", errors="surrogateescape")
+            out.append(dict(name=name, dims=list(ne[:nd]),
+                            type=self.lib.ubd_gguf_tensor_type(self.ptr, i),
+                            offset=self.lib.ubd_gguf_tensor_offset(self.ptr, i),
+                            nbytes=self.lib.ubd_gguf_tensor_nbytes(self.ptr, i)))
+        return out
 
 
 class Context:

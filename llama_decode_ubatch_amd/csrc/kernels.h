@@ -229,6 +229,13 @@ void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
 void launch_kv_load(const void *cache, int type, bool transposed, int stream,
                     int cell0, int n, int n_head_kv, int hd, int n_cells,
                     size_t layer_elems, float *out, hipStream_t s);
+// Load-time conversions: q8_0 blocks as GGUF stores them (f16 scale, then
+// 32 int8 codes: 34 bytes) into code and scale planes; f16 values widened
+// to f32 (exact).
+void launch_q8_blocks_split(const void *blocks, size_t n_blocks, int8_t *codes, uint16_t *scales,
+                            hipStream_t s);
+void launch_f16_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t s);
+
 // Bytes of tmp that kv_move needs for n cells.
 size_t kv_move_tmp_bytes(int type, int n, int n_head_kv, int hd);
 // Cell moves of one layer's K or V cache, stored values unchanged (q8_0

@@ -2199,6 +2199,35 @@ void launch_kv_move(void *cache, int type, bool transposed, int stream, const in
                            n, n_head_kv, hd, n_cells, layer_elems, 1, tmp, (int)to_tmp);
 }
 
+// One thread per 34-byte block; the block start is 2-byte aligned.
+__global__ __launch_bounds__(256) void q8_blocks_split_kernel(const uint16_t *blocks, size_t nb, int8_t *codes,
+                                                              uint16_t *scales) {
+    const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nb) return;
+    const uint16_t *p = blocks + b * 17;
+    scales[b] = p[0];
+    uint16_t *c = (uint16_t *)(codes + b * 32);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = p[1 + i];
+}
+
+void launch_q8_blocks_split(const void *blocks, size_t n_blocks, int8_t *codes, uint16_t *scales,
+                            hipStream_t s) {
+    if (n_blocks == 0) return;
+    hipLaunchKernelGGL(q8_blocks_split_kernel, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t *)blocks, n_blocks, codes, scales);
+}
+
+__global__ __launch_bounds__(256) void f16_to_f32_kernel(const uint16_t *src, size_t n, float *dst) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = h2f(src[i]);
+}
+
+void launch_f16_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t s) {
+    if (n == 0) return;
+    hipLaunchKernelGGL(f16_to_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, n, dst);
+}
+
 // q8_0 quantisation of KV rows into their cells: 32 lanes per 32-value
 // block (8 blocks per work-group).  All arithmetic is single float32
 // operations with IEEE rounding (amax / 127, 1 / d, x * (1 / d)), then

@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "common.h"
 #include "planner.h"
 #include "ubd.h"
 
@@ -49,6 +50,22 @@ void set_err(const std::string &m) {
     log_line(2, "%s", m.c_str());
 }
 
+}  // namespace
+
+namespace ubd {
+void set_error(const std::string &msg) { set_err(msg); }
+void log_msg(int level, const char *fmt, ...) {
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    log_line(level, "%s", buf);
+}
+}  // namespace ubd
+
+namespace {
+
 bool hip_ok(hipError_t e, const char *what) {
     if (e == hipSuccess) return true;
     set_err(std::string(what) + ": " + hipGetErrorString(e));
@@ -63,6 +80,7 @@ double now_ms() {
 int wtype_of(ubd_type t) {
     switch (t) {
     case UBD_TYPE_F32: return W_F32;
+    case UBD_TYPE_F16: return W_F32;      // widened exactly at load
     case UBD_TYPE_BF16: return W_BF16;
     case UBD_TYPE_Q8_0: return W_Q8;
     default: return -1;
@@ -181,6 +199,34 @@ struct Staged {
 
 bool stage(const ubd_tensor_src &s, int wtype, hipStream_t st, Staged *out) {
     const size_t n = (size_t)s.ne[0] * s.ne[1];
+    // sources that need a conversion pass on the device first
+    const bool q8_blocks = s.type == UBD_TYPE_Q8_0 && !s.scales;
+    if (q8_blocks || s.type == UBD_TYPE_F16) {
+        const size_t in_bytes = q8_blocks ? n / 32 * 34 : n * 2;
+        const void *in = s.data;
+        if (!s.on_device) {
+            void *d = nullptr;
+            if (!hip_ok(hipMalloc(&d, in_bytes), "staging allocation")) return false;
+            out->tmp.push_back(d);
+            if (!hip_ok(hipMemcpyAsync(d, s.data, in_bytes, hipMemcpyHostToDevice, st), "weight upload")) return false;
+            in = d;
+        }
+        void *a = nullptr, *b = nullptr;
+        if (q8_blocks) {
+            if (!hip_ok(hipMalloc(&a, n), "staging allocation")) return false;
+            out->tmp.push_back(a);
+            if (!hip_ok(hipMalloc(&b, n / 32 * 2), "staging allocation")) return false;
+            out->tmp.push_back(b);
+            launch_q8_blocks_split(in, n / 32, (int8_t *)a, (uint16_t *)b, st);
+            out->scales = (const uint16_t *)b;
+        } else {
+            if (!hip_ok(hipMalloc(&a, n * 4), "staging allocation")) return false;
+            out->tmp.push_back(a);
+            launch_f16_to_f32((const uint16_t *)in, n, (float *)a, st);
+        }
+        out->data = a;
+        return hip_ok(hipGetLastError(), "weight conversion");
+    }
     const size_t bytes = n * (wtype < 0 ? 4 : elem_bytes(wtype));
     const size_t sbytes = wtype == W_Q8 ? (n / 32) * 2 : 0;
     if (s.on_device) {
@@ -246,7 +292,6 @@ extern "C" ubd_model *ubd_model_load(const ubd_hparams *hparams, const ubd_tenso
             wtype = wt;
             if (t.ne[0] % kstep_of(wt))
                 return fail(-1, std::string("ubd_model_load: row length not a multiple of the tile for ") + t.name);
-            if (wt == W_Q8 && !t.scales) return fail(-1, std::string("ubd_model_load: q8_0 without scales: ") + t.name);
         }
         got[t.name] = &t;
     }
@@ -326,15 +371,20 @@ extern "C" ubd_model *ubd_model_load(const ubd_hparams *hparams, const ubd_tenso
     {
         const ubd_tensor_src &s = *got["token_embd.weight"];
         const size_t n = (size_t)s.ne[0] * s.ne[1];
-        const hipMemcpyKind kind = s.on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice;
+        Staged stg;
+        if (!stage(s, wtype, st, &stg)) return bail(-2, "ubd_model_load: embedding upload failed: " + g_err);
         m->embd = m->mem.get(n * elem_bytes(wtype));
-        if (!m->embd || !hip_ok(hipMemcpyAsync(m->embd, s.data, n * elem_bytes(wtype), kind, st), "embedding upload"))
+        if (!m->embd ||
+            !hip_ok(hipMemcpyAsync(m->embd, stg.data, n * elem_bytes(wtype), hipMemcpyDeviceToDevice, st), "embedding"))
             return bail(-2, "ubd_model_load: embedding upload failed: " + g_err);
         if (wtype == W_Q8) {
             m->embd_scales = (uint16_t *)m->mem.get(n / 32 * 2);
-            if (!m->embd_scales || !hip_ok(hipMemcpyAsync(m->embd_scales, s.scales, n / 32 * 2, kind, st), "scales"))
+            if (!m->embd_scales ||
+                !hip_ok(hipMemcpyAsync(m->embd_scales, stg.scales, n / 32 * 2, hipMemcpyDeviceToDevice, st), "scales"))
                 return bail(-2, "ubd_model_load: embedding upload failed: " + g_err);
         }
+        if (!hip_ok(hipStreamSynchronize(st), "embedding sync"))
+            return bail(-2, "ubd_model_load: embedding upload failed: " + g_err);
     }
     if (!hip_ok(hipStreamSynchronize(st), "load sync")) return bail(-2, "ubd_model_load: " + g_err);
     m->t_load_ms = now_ms() - t0;

@@ -17,6 +17,7 @@ specification, which the pages leave out:
   alignment    general.alignment (u32), default 32: the data block starts
                at the first multiple after the records; offsets are
                multiples of it.
+A dimension must be a positive size (reading: the pages give sizes only).
 
 ``model_info`` restates the architecture page's Example 8 summary: the
 parameter count from the tensor shapes, bits per weight = file bits over
@@ -110,6 +111,8 @@ class GGUF:
             if not 1 <= n_dims <= 4:
                 raise GGUFError(f"tensor {name}: {n_dims} dimensions")
             dims = [c.unpack("<Q", 8) for _ in range(n_dims)]
+            if min(dims) < 1 or max(dims) >= 2 ** 63:
+                raise GGUFError(f"tensor {name}: bad dimensions")
             ttype = c.unpack("<I", 4)
             offset = c.unpack("<Q", 8)
             if name in names:

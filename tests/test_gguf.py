@@ -131,3 +131,143 @@ def test_duplicate_across_parts(tmp_path):
     W.write_gguf(str(tmp_path / "p2.gguf"), [], [rec])
     with pytest.raises(GGUFError, match="duplicated"):
         open_model([str(tmp_path / "p1.gguf"), str(tmp_path / "p2.gguf")])
+
+
+# ------------------------------------------------- the library's reader
+def lib_reader(path):
+    from llama_decode_ubatch_amd.binding import Gguf
+    return Gguf(path)
+
+
+def oracle_items(g):
+    out = []
+    for k in g.keys:
+        t, v = g.kv[k]
+        if t == 8:
+            v = v.encode("utf-8", errors="surrogateescape")
+        elif t == 9:
+            et, items = v
+            if et == 9:
+                v = (9, len(items))
+            elif et == 8:
+                v = (8, [x.encode("utf-8", errors="surrogateescape") for x in items])
+            else:
+                v = (et, [int(x) if et not in (6, 12) else float(x) for x in items])
+        elif t in (6, 12):
+            v = float(v)
+        else:
+            v = int(v)
+        out.append((k, t, v))
+    return out
+
+
+def same_as_oracle(path):
+    g, c = GGUF(path), lib_reader(path)
+    assert c.version == g.version and c.data_offset == g.data_start
+    assert c.items() == oracle_items(g)
+    ct = c.tensors()
+    assert [t["name"] for t in ct] == [t["name"] for t in g.tensors]
+    for a, b in zip(ct, g.tensors):
+        assert (a["dims"], a["type"], a["nbytes"]) == (b["dims"], b["type"], b["nbytes"])
+        assert a["offset"] == g.data_start + b["offset"]
+    for t in g.tensors:
+        name = t["name"].encode("utf-8", errors="surrogateescape")
+        assert c.lib.ubd_gguf_find_tensor(c.ptr, name) == g.tensors.index(t)
+    assert c.find_key("no.such.key") == -1
+    c.close()
+
+
+def test_library_reader_matches_oracle_on_hand_file(tmp_path):
+    path, _ = hand_file(tmp_path)
+    same_as_oracle(path)
+
+
+def test_library_reader_matches_oracle_on_every_value_type(tmp_path):
+    kvs = [("u8", W.U8, 250), ("i8", W.I8, -5), ("u16", W.U16, 65000), ("i16", W.I16, -32000),
+           ("u32", W.U32, 4000000000), ("i32", W.I32, -2000000000), ("f32", W.F32, 1.5),
+           ("bool", W.BOOL, True), ("str", W.STR, "héllo 日本"), ("empty", W.STR, ""),
+           ("u64", W.U64, 2 ** 63 - 1), ("i64", W.I64, -(2 ** 62)), ("f64", W.F64, -2.5e300),
+           ("arr.i16", W.ARR, (W.I16, [-1, 2, -3])), ("arr.f64", W.ARR, (W.F64, [0.25, 1e-300])),
+           ("arr.str", W.ARR, (W.STR, ["a", "", "bc"])), ("arr.empty", W.ARR, (W.U8, [])),
+           ("arr.nested", W.ARR, (W.ARR, [(W.I32, [1, 2]), (W.STR, ["x"])])),
+           ("general.alignment", W.U32, 64)]
+    recs = [("m", W.T_BF16, [64, 3], np.arange(192, dtype=np.uint16).tobytes()),
+            ("v", W.T_F16, [7], np.ones(7, np.float16).tobytes()),
+            ("q", W.T_Q8_0, [64, 2], bytes(range(136)))]
+    p = str(tmp_path / "types.gguf")
+    W.write_gguf(p, kvs, recs, alignment=64)
+    same_as_oracle(p)
+    g = GGUF(p)
+    assert g.alignment == 64 and g.data_start % 64 == 0 and [t["offset"] % 64 for t in g.tensors] == [0, 0, 0]
+
+
+@pytest.mark.parametrize("kw", [dict(magic=b"GGUG"), dict(version=2), dict(version=4), dict(n_dims=5),
+                                dict(ttype=99), dict(offset=8), dict(offset=32), dict(dup=True)])
+def test_library_reader_rejects_what_the_oracle_rejects(tmp_path, kw):
+    from llama_decode_ubatch_amd.binding import Gguf
+    path, _ = hand_file(tmp_path, **kw)
+    with pytest.raises(ValueError):
+        Gguf(path)
+
+
+def test_library_reader_rejects_every_truncation(tmp_path):
+    from llama_decode_ubatch_amd.binding import Gguf
+    path, raw = hand_file(tmp_path)
+    for n in range(len(raw)):
+        open(path, "wb").write(raw[:n])
+        with pytest.raises(ValueError):
+            Gguf(path)
+
+
+def test_library_reader_survives_corrupted_counts(tmp_path):
+    """Random bytes written over the header and metadata: the reader either
+    accepts (then agrees with the oracle) or rejects, and never reads
+    outside the file."""
+    from llama_decode_ubatch_amd.binding import Gguf
+    path, raw = hand_file(tmp_path)
+    rng = np.random.default_rng(3)
+    for trial in range(300):
+        b = bytearray(raw)
+        for _ in range(int(rng.integers(1, 4))):
+            at = int(rng.integers(4, 200))
+            b[at] = int(rng.integers(0, 256))
+        open(path, "wb").write(bytes(b))
+        try:
+            g = GGUF(path)
+        except GGUFError:
+            g = None
+        try:
+            c = Gguf(path)
+        except ValueError:
+            c = None
+        assert (g is None) == (c is None), trial
+        if g is not None:
+            same_as_oracle(path)
+
+
+def test_library_model_info_matches_oracle(tiny_files):
+    from llama_decode_ubatch_amd.binding import gguf_model_info
+    m, one, three, q8, q8p = tiny_files
+    for paths in (one, three, q8p):
+        g, where = open_model(paths)
+        info = model_info([GGUF(p) for p in paths])
+        c = gguf_model_info(paths[0])
+        assert c.n_files == len(paths) and c.n_tensors == len(where)
+        assert c.n_params == info["n_params"] and c.file_bytes == info["file_bytes"]
+        assert abs(c.bpw - info["bpw"]) < 1e-12
+        assert ("all " if c.all_same else "mostly ") + {0: "F32", 8: "Q8_0"}[c.file_type] == info["file_type"]
+        hp = hparams(g, where)
+        for k in ("n_layer", "n_embd", "n_head", "n_head_kv", "n_ff", "n_vocab", "n_ctx_train"):
+            assert getattr(c.hparams, k) == hp[k], k
+        assert c.hparams.rms_eps == np.float32(hp["rms_eps"])
+        assert c.hparams.rope_freq_base == np.float32(hp["rope_freq_base"])
+    assert round(gguf_model_info(one[0]).n_params / 1e6, 2) == FIG["ex8_model_params_M"]
+
+
+def test_split_model_errors(tmp_path, tiny_files):
+    from llama_decode_ubatch_amd.binding import gguf_model_info
+    m = tiny_files[0]
+    paths = W.write_model_gguf(m, str(tmp_path / "s"), n_split=2)
+    os.remove(paths[1])
+    with pytest.raises(ValueError):
+        gguf_model_info(paths[0])
