@@ -79,7 +79,7 @@ enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_
 struct QKVEpi {
     int n_q_rows = 0, n_k_rows = 0;   // H*hd, Hk*hd
     int head_dim = 0, n_head_kv = 0, n_cells = 0;
-    const double *inv_freq = nullptr; // [head_dim / 2]
+    const float2 *rope_cs = nullptr;  // [T][head_dim / 2] (cos, sin) of each token's angles
     float *q_out = nullptr;           // [T][H*hd] f32, RoPE applied
     void *k_cache = nullptr;          // layer base
     void *v_cache = nullptr;
@@ -122,10 +122,14 @@ void launch_linear(const LinearArgs &a, hipStream_t s);
 
 // x[t] = dequant(table[token[t]]); also records the position and the
 // sequence mask of each token's cell in the device cell tables
-// (cell_pos [stream][n_cells], cell_seq [stream][n_seq_words][n_cells]).
+// (cell_pos [stream][n_cells], cell_seq [stream][n_seq_words][n_cells]),
+// and fills the ubatch's RoPE table: rope_cs[t][i] = (cos, sin) of
+// pos[t] * inv_freq[i], the angle and both functions in double precision,
+// rounded to f32 (i < head_dim / 2 <= 256).
 void launch_embed(int wtype, const void *table, const uint16_t *scales,
                   int d, const TokInfo &ti, int T, float *x,
                   int32_t *cell_pos, uint32_t *cell_seq, int n_cells,
+                  const double *inv_freq, int half_dim, float2 *rope_cs,
                   hipStream_t s);
 
 // out[r] = rmsnorm(x[src_row(r)]) * gain, src_row = row_map ? row_map[r] : r

@@ -220,18 +220,15 @@ __device__ __forceinline__ void epilogue4(const LinearArgs &a, int t, int n, f32
         const QKVEpi &q = a.qkv;
         const int hd = q.head_dim;
         if (n < q.n_q_rows + q.n_k_rows) {
-            const int pos = a.tok.pos[t];
             const int base = n < q.n_q_rows ? 0 : q.n_q_rows;
-            const int d = (n - base) % hd;
+            const int d = (n - base) % hd;       // a multiple of 4: two whole pairs, 16-byte aligned
+            const float4 cs = *(const float4 *)(q.rope_cs + (size_t)t * (hd >> 1) + (d >> 1));
+            const float c[2] = {cs.x, cs.z}, sf[2] = {cs.y, cs.w};
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
-                const double ang = (double)pos * q.inv_freq[(d >> 1) + pr];
-                double sn, cs;
-                sincos(ang, &sn, &cs);
-                const float c = (float)cs, sf = (float)sn;
                 const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
-                v[2 * pr] = x0 * c - x1 * sf;
-                v[2 * pr + 1] = x0 * sf + x1 * c;
+                v[2 * pr] = x0 * c[pr] - x1 * sf[pr];
+                v[2 * pr + 1] = x0 * sf[pr] + x1 * c[pr];
             }
         }
         if (n < q.n_q_rows) {
@@ -1165,8 +1162,14 @@ void launch_linear(const LinearArgs &a, hipStream_t s) {
 // ------------------------------------------------------------ embedding
 __global__ __launch_bounds__(256) void embed_kernel(int wtype, const void *table, const uint16_t *scales,
                                                     int d, TokInfo ti, float *x, int32_t *cell_pos,
-                                                    uint32_t *cell_seq, int n_cells) {
+                                                    uint32_t *cell_seq, int n_cells, const double *inv_freq,
+                                                    int half_dim, float2 *rope_cs) {
     const int t = blockIdx.x;
+    if (threadIdx.x < half_dim) {
+        double sn, cs;
+        sincos((double)ti.pos[t] * inv_freq[threadIdx.x], &sn, &cs);
+        rope_cs[(size_t)t * half_dim + threadIdx.x] = make_float2((float)cs, (float)sn);
+    }
     const size_t row = (size_t)ti.token[t];
     float *xo = x + (size_t)t * d;
     for (int e = threadIdx.x * 4; e < d; e += 1024) {      // d is a multiple of 16
@@ -1193,10 +1196,11 @@ __global__ __launch_bounds__(256) void embed_kernel(int wtype, const void *table
 }
 
 void launch_embed(int wtype, const void *table, const uint16_t *scales, int d, const TokInfo &ti, int T,
-                  float *x, int32_t *cell_pos, uint32_t *cell_seq, int n_cells, hipStream_t s) {
+                  float *x, int32_t *cell_pos, uint32_t *cell_seq, int n_cells, const double *inv_freq,
+                  int half_dim, float2 *rope_cs, hipStream_t s) {
     if (T <= 0) return;
     hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, s, wtype, table, scales, d, ti, x, cell_pos,
-                       cell_seq, n_cells);
+                       cell_seq, n_cells, inv_freq, half_dim, rope_cs);
 }
 
 // -------------------------------------------------------------- RMSNorm

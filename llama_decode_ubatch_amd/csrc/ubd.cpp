@@ -427,6 +427,7 @@ struct ubd_context : public Executor {
     int max_chunks_mfma = 0;                // MFMA split-path chunks (ATTN_DECODE_CHUNK cells)
     bool mfma_attn = false;
     double *inv_freq = nullptr;
+    float2 *rope_cs = nullptr;              // [cap][head_dim / 2] (cos, sin) of the ubatch's angles
     int32_t *info_dev = nullptr;
     int32_t *info_host[2] = {nullptr, nullptr};
     hipEvent_t info_ev[2] = {nullptr, nullptr};
@@ -626,13 +627,14 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     std::vector<double> inv(hd / 2);
     for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)hp.rope_freq_base, -2.0 * i / hd);
     c->inv_freq = (double *)c->mem.get(inv.size() * sizeof(double));
+    c->rope_cs = (float2 *)c->mem.get((size_t)cap * (hd / 2) * sizeof(float2));
     c->info_dev = (int32_t *)c->mem.get(c->info_ints() * 4);
     c->argmax_dev = (int32_t *)c->mem.get((size_t)std::max<uint32_t>(P.n_batch, 1) * 4);
     const size_t amax_rows = std::max<uint32_t>(P.n_batch, 1);
     c->argmax_work.pv = (float *)c->mem.get(amax_rows * ARGMAX_BLOCKS * 4);
     c->argmax_work.pi = (int32_t *)c->mem.get(amax_rows * ARGMAX_BLOCKS * 4);
     c->argmax_work.counter = (int32_t *)c->mem.get(amax_rows * 4);
-    if (!c->inv_freq || !c->info_dev || !c->argmax_dev || !c->argmax_work.pv || !c->argmax_work.pi ||
+    if (!c->inv_freq || !c->rope_cs || !c->info_dev || !c->argmax_dev || !c->argmax_work.pv || !c->argmax_work.pi ||
         !c->argmax_work.counter)
         return bail("allocation failed");
     if (!hip_ok(hipMemsetAsync(c->argmax_work.counter, 0, amax_rows * 4, c->stream), "memset"))
@@ -845,7 +847,8 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     const TokInfo ti = tok_info();
     const int n_cells = (int)cell_stride;   // per-stream stride of the device KV and cell tables
     const int ph = T > 16 ? 1 : 0;
-    timed(0 + ph, [&] { launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, stream); });
+    timed(0 + ph, [&] { launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, inv_freq,
+                                       hd / 2, rope_cs, stream); });
     if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, stream), "dump");
 
     for (int il = 0; il < hp.n_layer; ++il) {
@@ -871,7 +874,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         la.qkv.head_dim = hd;
         la.qkv.n_head_kv = Hk;
         la.qkv.n_cells = n_cells;
-        la.qkv.inv_freq = inv_freq;
+        la.qkv.rope_cs = rope_cs;
         la.qkv.q_out = q;
         la.qkv.k_cache = (char *)k_cache + k_layer_bytes * il;
         la.qkv.v_cache = (char *)v_cache + v_layer_bytes * il;
