@@ -44,6 +44,7 @@ struct Tuning {
     int gemm = 1;             // prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel
     int gemm_split = 0;       // residual prefill products: forced k split (2, 4; 0 = automatic)
     int gemm_shape = 0;       // LDS-ring tile (0 = automatic; 1..4 force 2x4, 2x8, 4x4, 4x8 row x token blocks)
+    int gemm_wpd = 0;         // LDS-ring product: stages of weight look-ahead (1 or 2; 0 = per shape)
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;

@@ -790,7 +790,7 @@ template <int WT, int RBW, int TB, int KS> struct GemmCfg {
     static constexpr int NX = 3;                  // LDS ring depth
 };
 
-template <int WT, int EPI, int RBW, int TB, int SPLITK, int KS>
+template <int WT, int EPI, int RBW, int TB, int SPLITK, int KS, int WPD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_lds_kernel(LinearArgs a,
                                                                                              int n_wtiles,
                                                                                              int n_ttiles) {
@@ -846,15 +846,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     }
     const int wstep = nrb * 1024;   // bytes between consecutive k-steps of the weight tiles
 
-    u32x4_t wn[RBW][NA];            // next stage's weight tiles (in flight)
-    u32x2_t sn[RBW][KH];            // ... and q8_0 scales
+    // weight tiles of the next WPD stages (in flight): one register set per
+    // stage of look-ahead, used in turn
+    u32x4_t wn0[RBW][NA], wn1[RBW][NA];
+    u32x2_t sn0[RBW][KH], sn1[RBW][KH];     // ... and q8_0 scales
+    constexpr int NWL = RBW * NA + (Q8 ? RBW * KH : 0);   // weight loads per stage
     f32x4_t acc[RBW][TB];
 #pragma unroll
     for (int i = 0; i < RBW; ++i)
 #pragma unroll
         for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto issue_w = [&](int s) {
+    auto issue_w = [&](int s, u32x4_t (&wn)[RBW][NA], u32x2_t (&sn)[RBW][KH]) {
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
             const int so = (NA * s + j) * wstep;
@@ -882,13 +885,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         }
     };
 
-    if (st0 < st1) {
-        issue_w(st0);
-        issue_x(st0);
-        issue_x(st0 + 1);
-        for (int s = st0; s < st1; ++s) {
-            // everything but the newest activation copies (stage s+1) has landed
-            wait_vm<C::XW>();
+    auto stage = [&](int s, u32x4_t (&wn)[RBW][NA], u32x2_t (&sn)[RBW][KH]) {
+            // landed: everything but the loads issued for the following
+            // stage (its activation copies, and with WPD 2 its weights)
+            wait_vm<WPD == 1 ? C::XW : C::XW + NWL>();
             wg_barrier();
             u32x4_t wc[RBW][NA];
             u32x2_t sc[RBW][KH];
@@ -900,7 +900,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
                 for (int j = 0; j < KH; ++j) sc[i][j] = sn[i][j];
             }
             __builtin_amdgcn_sched_barrier(0);
-            issue_w(min(s + 1, st1 - 1));
+            issue_w(min(s + WPD, st1 - 1), wn, sn);
             issue_x(s + 2);
             __builtin_amdgcn_sched_barrier(0);
             const u32x4_t *xb = xs + (size_t)(s % C::NX) * C::XF * 64;
@@ -937,6 +937,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
                     }
                 }
             }
+    };
+    if (st0 < st1) {
+        issue_w(st0, wn0, sn0);
+        issue_x(st0);
+        if (WPD == 2) issue_w(min(st0 + 1, st1 - 1), wn1, sn1);
+        issue_x(st0 + 1);
+        if (WPD == 2) {
+            for (int s = st0; s < st1; s += 2) {
+                stage(s, wn0, sn0);
+                if (s + 1 < st1) stage(s + 1, wn1, sn1);
+            }
+        } else {
+            for (int s = st0; s < st1; ++s) stage(s, wn0, sn0);
         }
         // the ring's last copies must land before the work-group's LDS is released
         wait_vm<0>();
@@ -960,15 +973,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #endif
 }
 
+// wpd: stages of weight look-ahead (the tuning knob overrides it)
 template <int WT, int EPI, int RBW, int TB, int SPLITK>
-static void launch_gemm_lds(const LinearArgs &a, hipStream_t s) {
+static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
     const int total = n_wtiles * n_ttiles * SPLITK;
+    if (g_tuning.gemm_wpd == 1 || g_tuning.gemm_wpd == 2) wpd = g_tuning.gemm_wpd;
     // 64-wide stages: the kernel then fits 2 waves per SIMD (two work-groups
     // per CU), which hides the LDS reads and barriers of one behind the other
-    hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64>), dim3(total), dim3(256), 0, s, a, n_wtiles,
-                       n_ttiles);
+    if (wpd == 2)
+        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 2>), dim3(total), dim3(256), 0, s, a,
+                           n_wtiles, n_ttiles);
+    else
+        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 1>), dim3(total), dim3(256), 0, s, a,
+                           n_wtiles, n_ttiles);
 }
 
 // Shape choice for the LDS-ring product: the largest tile (256 rows x 128
@@ -985,6 +1004,8 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     case 2: launch_gemm_lds<WT, EPI, 2, 8, 1>(a, s); return;
     case 3: launch_gemm_lds<WT, EPI, 4, 4, 1>(a, s); return;
     case 4: if (WT != W_Q8) { launch_gemm_lds<WT, EPI, WT == W_Q8 ? 2 : 4, 8, 1>(a, s); return; } break;
+    case 5: if (EPI != EPI_SWIGLU) { launch_gemm_lds<WT, EPI, 1, 4, 1>(a, s); return; } break;
+    case 6: if (EPI != EPI_SWIGLU) { launch_gemm_lds<WT, EPI, 1, 8, 1>(a, s); return; } break;
     default: break;
     }
     // residual products: 128 x 64 tiles, splitting k (atomic partial sums)
@@ -999,12 +1020,11 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
             launch_gemm_lds<WT, EPI, 2, 4, 4>(a, s);
             return;
         }
-        // (long k, e.g. the FFN down product: 2-way split even with enough
-        // tiles, which measured faster despite the atomic adds)
-        if (a.K >= 8192 && t >= 192)
-            launch_gemm_lds<WT, EPI, 2, 4, 2>(a, s);
-        else if (t >= 192 || a.K < 1024)
-            launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s);
+        // enough tiles: no split, weights two stages ahead (the narrow
+        // tile leaves the registers for it; measured O 50.6 -> 44.5 us and
+        // FFN down 143 -> 136 us at 512 tokens, 8B shape)
+        if (t >= 192 || a.K < 1024)
+            launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s, 2);
         else if (t * 2 >= 192 || a.K < 2048)
             launch_gemm_lds<WT, EPI, 2, 4, 2>(a, s);
         else
