@@ -1703,7 +1703,19 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
     int cbeg = 0, cend = nscan;
     if (SPLIT) {
         cbeg = chunk * NC;
-        if (cbeg >= nscan) return;
+        if (cbeg >= nscan) {
+            // past this tile's cells: an empty partial (m = -inf, l = 0), so
+            // the merge can take every launched chunk without looking up
+            // the tile's scan length
+            if ((lane >> 4) == 0 && (lane & 15) < R) {
+                const int row = lane & 15;
+                float *ml = a.part_ml +
+                            (((size_t)(t0 + row / G) * a.n_head + grp * G + row % G) * a.max_chunks + chunk) * 2;
+                ml[0] = -INFINITY;
+                ml[1] = 0.f;
+            }
+            return;
+        }
         cend = min(nscan, cbeg + NC);
     }
     const float scale = 1.0f / sqrtf((float)HD);
@@ -1832,13 +1844,13 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
 
 // Merge the chunks of one (token, head): weights exp(m_c - M) computed
 // lane-parallel over chunks, then every dim sums its chunks with the loads
-// of a 64-chunk pass issued together.
+// of a 64-chunk pass issued together.  Every launched chunk has a partial
+// (empty ones m = -inf, weight 0, their O never read into the sum).
 template <int HD>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
     const int t = blockIdx.x / a.n_head, h = blockIdx.x % a.n_head;
     const int lane = threadIdx.x;
-    const int nscan = a.tok.tiles[a.tok.tile_of[t] * 4 + 3];
-    const int nch = (nscan + a.chunk_cells - 1) / a.chunk_cells;
+    const int nch = a.n_chunks_launch;
     const float *ml = a.part_ml + ((size_t)t * a.n_head + h) * a.max_chunks * 2;
     const float *po = a.part_o + ((size_t)t * a.n_head + h) * a.max_chunks * HD;
     float M = -INFINITY;
@@ -1873,7 +1885,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int j = 0; j < DPL; ++j) o[j] += (k + u < n) ? w8[u] * v8[u][j] : 0.f;
+                for (int j = 0; j < DPL; ++j) o[j] += (k + u < n && w8[u] != 0.f) ? w8[u] * v8[u][j] : 0.f;
         }
     }
     L = wave_sum(L);
