@@ -85,8 +85,21 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t w0, uint32_t w1) {
     return __builtin_convertvector(f, bf16x8_t);
 }
 
+// Offset codes: q + 128 as an unsigned byte is an integer in [1, 255],
+// exact in bf16, and converts with one instruction per byte.
+__device__ __forceinline__ bf16x8_t u8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    f32x8_t f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = (float)((w0 >> (8 * i)) & 0xffu);
+        f[4 + i] = (float)((w1 >> (8 * i)) & 0xffu);
+    }
+    return __builtin_convertvector(f, bf16x8_t);
+}
+
 template <int WT, int RB>
 struct StepIn {
+    float xs[2];                        // q8 offset path: sums of this lane's token over blocks 2s, 2s+1
     u32x4_t w[RB];
     u32x4_t xh, xl, xh2, xl2;          // bf16: xh/xl; q8: block 0 (xh, xl), block 1 (xh2, xl2); f32: xh
     u32x2_t sc[RB][2];                  // q8 scales of rows 4g..4g+3, blocks 2s, 2s+1
@@ -133,7 +146,9 @@ __device__ __forceinline__ void load_step(const LinearArgs &a, const unsigned ch
     }
 }
 
-template <int WT, int RB>
+// OFS (q8_0): the products take the codes offset by 128 (cheaper to
+// convert), and 128 times the block's activation sum is taken off again.
+template <int WT, int RB, bool OFS = false>
 __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc) {
     if (WT == W_F32) {
 #pragma unroll
@@ -160,8 +175,10 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            const bf16x8_t A0 = i8x8_to_bf16(in.w[j][0], in.w[j][1]);
-            const bf16x8_t A1 = i8x8_to_bf16(in.w[j][2], in.w[j][3]);
+            const bf16x8_t A0 = OFS ? u8x8_to_bf16(in.w[j][0] ^ 0x80808080u, in.w[j][1] ^ 0x80808080u)
+                                    : i8x8_to_bf16(in.w[j][0], in.w[j][1]);
+            const bf16x8_t A1 = OFS ? u8x8_to_bf16(in.w[j][2] ^ 0x80808080u, in.w[j][3] ^ 0x80808080u)
+                                    : i8x8_to_bf16(in.w[j][2], in.w[j][3]);
             f32x4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, xh0, z, 0, 0, 0);
             d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, xl0, d0, 0, 0, 0);
             f32x4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, xh1, z, 0, 0, 0);
@@ -171,7 +188,10 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
                 const uint32_t s0w = in.sc[j][0][i >> 1], s1w = in.sc[j][1][i >> 1];
                 const float s0 = h2f((uint16_t)(s0w >> (16 * (i & 1))));
                 const float s1 = h2f((uint16_t)(s1w >> (16 * (i & 1))));
-                acc[j][i] += s0 * d0[i] + s1 * d1[i];
+                if (OFS)
+                    acc[j][i] += s0 * (d0[i] - 128.0f * in.xs[0]) + s1 * (d1[i] - 128.0f * in.xs[1]);
+                else
+                    acc[j][i] += s0 * d0[i] + s1 * d1[i];
             }
         }
     }
@@ -443,20 +463,22 @@ __device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const un
         StepIn<WT, RB> in;
 #pragma unroll
         for (int j = 0; j < RB; ++j) in.w[j] = b.w[u][j];
-        const u32x4_t z = {0u, 0u, 0u, 0u};
+        // lanes past the block's tokens read token 0: their output columns
+        // are never stored, so no masking
+        (void)tok_ok;
         if (WT == W_F32) {
-            const u32x4_t v = *(const u32x4_t *)(lds + ((size_t)tok * K + 16 * (s + u) + 4 * g) * 4);
-            in.xh = tok_ok ? v : z;
+            in.xh = *(const u32x4_t *)(lds + ((size_t)tok * K + 16 * (s + u) + 4 * g) * 4);
         } else {
             const size_t o = (size_t)tok * K + (WT == W_BF16 ? 32 : 64) * (s + u) + 8 * g;
             const uint16_t *hi = (const uint16_t *)lds, *lo = (const uint16_t *)lds + plane;
-            const u32x4_t h0 = *(const u32x4_t *)(hi + o), l0 = *(const u32x4_t *)(lo + o);
-            in.xh = tok_ok ? h0 : z;
-            in.xl = tok_ok ? l0 : z;
+            in.xh = *(const u32x4_t *)(hi + o);
+            in.xl = *(const u32x4_t *)(lo + o);
             if (WT == W_Q8) {
-                const u32x4_t h1 = *(const u32x4_t *)(hi + o + 32), l1 = *(const u32x4_t *)(lo + o + 32);
-                in.xh2 = tok_ok ? h1 : z;
-                in.xl2 = tok_ok ? l1 : z;
+                in.xh2 = *(const u32x4_t *)(hi + o + 32);
+                in.xl2 = *(const u32x4_t *)(lo + o + 32);
+                const float2 xs = *(const float2 *)((const float *)(lds + 4 * plane) + (size_t)tok * (K / 32) + 2 * (s + u));
+                in.xs[0] = xs.x;
+                in.xs[1] = xs.y;
 #pragma unroll
                 for (int j = 0; j < RB; ++j) {
                     in.sc[j][0] = b.sc[u][j][0];
@@ -464,25 +486,37 @@ __device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const un
                 }
             }
         }
-        mfma_step<WT, RB>(in, acc);
+        mfma_step<WT, RB, WT == W_Q8>(in, acc);
     }
 }
 
+// Activation copy of the LDS-staged product.  Every thread handles float4
+// slices e = (tid + TH * i) * 4 of a row, CH slices at a time: the CH loads
+// of a chunk are issued together and waited for once (a per-slice loop
+// waited for every load, and so for the weight batches issued before it).
 template <int WT, int NW, bool NORM>
 __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, int Tb) {
-    constexpr int TH = 64 * NW;
+    constexpr int TH = 64 * NW, CH = 4;
     __shared__ float red_ss[16][NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K;
     const size_t plane = (size_t)Tb * K;
+    const int nv = (K / 4 + TH - 1) / TH;     // float4 slices per thread per row
+    const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
     float inv[16];
     if (NORM) {
         for (int t = 0; t < Tb; ++t) {
             const float *xr = a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[t0 + t] : t0 + t) * a.norm.ld;
             float ss = 0.f;
-            for (int e = tid * 4; e < K; e += TH * 4) {
-                const f32x4_t v = *(const f32x4_t *)(xr + e);
-                ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+            for (int i0 = 0; i0 < nv; i0 += CH) {
+                f32x4_t v[CH];
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int e = (tid + TH * (i0 + i)) * 4;
+                    v[i] = (i0 + i < nv && e < K) ? *(const f32x4_t *)(xr + e) : z4;
+                }
+#pragma unroll
+                for (int i = 0; i < CH; ++i) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
             }
             ss = wave_sum(ss);
             if (lane == 0) red_ss[t][wave] = ss;
@@ -498,41 +532,102 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
     for (int t = 0; t < Tb; ++t) {
         const float *xr = NORM ? a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[t0 + t] : t0 + t) * a.norm.ld
                                : nullptr;
-        for (int e = tid * 4; e < K; e += TH * 4) {
-            const size_t o = (size_t)t * K + e;
+        for (int i0 = 0; i0 < nv; i0 += CH) {
             if (NORM) {
-                const f32x4_t y = *(const f32x4_t *)(xr + e) * inv[t] * *(const f32x4_t *)(a.norm.gain + e);
-                if (WT == W_F32) {
-                    *(f32x4_t *)(lds + o * 4) = y;
-                } else {
-                    u16x4_t hh, ll;
+                f32x4_t v[CH], gn[CH];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        hh[k] = f2bf(y[k]);
-                        ll[k] = f2bf(y[k] - bf2f(hh[k]));
+                for (int i = 0; i < CH; ++i) {
+                    const int e = (tid + TH * (i0 + i)) * 4;
+                    const bool ok = i0 + i < nv && e < K;
+                    v[i] = ok ? *(const f32x4_t *)(xr + e) : z4;
+                    gn[i] = ok ? *(const f32x4_t *)(a.norm.gain + e) : z4;
+                }
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int e = (tid + TH * (i0 + i)) * 4;
+                    if (i0 + i >= nv || e >= K) continue;
+                    const size_t o = (size_t)t * K + e;
+                    const f32x4_t y = v[i] * inv[t] * gn[i];
+                    if (WT == W_F32) {
+                        *(f32x4_t *)(lds + o * 4) = y;
+                    } else {
+                        u16x4_t hh, ll;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            hh[k] = f2bf(y[k]);
+                            ll[k] = f2bf(y[k] - bf2f(hh[k]));
+                        }
+                        *(u16x4_t *)((uint16_t *)lds + o) = hh;
+                        *(u16x4_t *)((uint16_t *)lds + plane + o) = ll;
                     }
-                    *(u16x4_t *)((uint16_t *)lds + o) = hh;
-                    *(u16x4_t *)((uint16_t *)lds + plane + o) = ll;
+                }
+            } else if (WT == W_F32) {
+                f32x4_t v[CH];
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int e = (tid + TH * (i0 + i)) * 4;
+                    v[i] = (i0 + i < nv && e < K) ? *(const f32x4_t *)(a.x.f32 + (size_t)(t0 + t) * a.x.ld + e) : z4;
+                }
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int e = (tid + TH * (i0 + i)) * 4;
+                    if (i0 + i < nv && e < K) *(f32x4_t *)(lds + ((size_t)t * K + e) * 4) = v[i];
                 }
             } else {
-                const size_t src = (size_t)(t0 + t) * a.x.ld + e;
-                if (WT == W_F32) {
-                    *(f32x4_t *)(lds + o * 4) = *(const f32x4_t *)(a.x.f32 + src);
-                } else {
-                    *(u16x4_t *)((uint16_t *)lds + o) = *(const u16x4_t *)(a.x.hi + src);
-                    *(u16x4_t *)((uint16_t *)lds + plane + o) = *(const u16x4_t *)(a.x.lo + src);
+                u16x4_t h[CH], l[CH];
+                const u16x4_t z = {0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int e = (tid + TH * (i0 + i)) * 4;
+                    const bool ok = i0 + i < nv && e < K;
+                    const size_t src = (size_t)(t0 + t) * a.x.ld + e;
+                    h[i] = ok ? *(const u16x4_t *)(a.x.hi + src) : z;
+                    l[i] = ok ? *(const u16x4_t *)(a.x.lo + src) : z;
+                }
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int e = (tid + TH * (i0 + i)) * 4;
+                    if (i0 + i >= nv || e >= K) continue;
+                    const size_t o = (size_t)t * K + e;
+                    *(u16x4_t *)((uint16_t *)lds + o) = h[i];
+                    *(u16x4_t *)((uint16_t *)lds + plane + o) = l[i];
                 }
             }
         }
     }
     __syncthreads();
+    if (WT == W_Q8) {
+        // per (token, 32-value block): sum of the staged hi + lo values, for
+        // the offset-code products; stored after the two planes
+        float *xsum = (float *)(lds + 4 * plane);
+        const uint16_t *hi = (const uint16_t *)lds, *lo = hi + plane;
+        for (int p = tid; p < Tb * (K / 32); p += TH) {
+            const size_t o = (size_t)p * 32;
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < 32; q += 8) {
+                const u16x8_t hh = *(const u16x8_t *)(hi + o + q), ll = *(const u16x8_t *)(lo + o + q);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += bf2f(hh[e]) + bf2f(ll[e]);
+            }
+            xsum[p] = acc;
+        }
+        __syncthreads();
+    }
 }
 
+// q8_0 with gate|up pairs (RB 2) needs more than 128 registers: 2 waves per
+// SIMD for it (at 4 it spilled ~60 registers to scratch, and the spill
+// reloads, counted with the weight loads, stalled every batch: 1.2 TB/s)
+template <int WT, int EPI>
+constexpr int ldsx_waves_per_eu() { return WT == W_Q8 && EPI == EPI_SWIGLU ? 2 : 4; }
+
 template <int WT, int EPI, int NW, bool NORM>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void linear_ldsx_kernel(LinearArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ldsx_waves_per_eu<WT, EPI>())))
+void linear_ldsx_kernel(LinearArgs a) {
     constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
     constexpr int KSTEP = WT_<WT>::KSTEP;
-    constexpr int UB = (WT == W_Q8 ? 2 : 8) / RB;
+    constexpr int UB = WT == W_Q8 ? (RB == 2 ? 4 : 2) : 8 / RB;   // k-steps per weight batch
     extern __shared__ __align__(16) unsigned char dyn_lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -1092,9 +1187,13 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
     // k-split waves per work-group: about 4096 waves in flight, all resident
     int nw = blocks >= 768 ? 4 : blocks >= 384 ? 8 : 16;
     if (g_tuning.skinny_nw == 4 || g_tuning.skinny_nw == 8 || g_tuning.skinny_nw == 16) nw = g_tuning.skinny_nw;
+    // 2 waves per SIMD: keep every wave of the launch resident at once (the
+    // second round of work-groups otherwise doubles the time)
+    if (ldsx_waves_per_eu<WT, EPI>() == 2) nw = blocks >= 768 ? 2 : blocks >= 384 ? 4 : 8;
     const bool norm = a.norm.x != nullptr;
     // activations of a 16-token block fit in LDS: the LDS-staged kernel
-    const size_t ldsx = (size_t)4 * std::min(16, a.T) * a.K;
+    // activation planes (+ q8_0 block sums)
+    const size_t ldsx = (size_t)4 * std::min(16, a.T) * a.K + (WT == W_Q8 ? (size_t)std::min(16, a.T) * a.K / 8 : 0);
     if (ldsx <= LDSX_MAX_BYTES && g_tuning.ldsx != 0) {
         const size_t bytes = std::max(ldsx, (size_t)16 * 64 * 16 * 2);   // also holds the wave reduction
 #define UBD_LAUNCH_LDSX(NW_)                                                                               \
@@ -1104,7 +1203,9 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
         else                                                                                               \
             hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), bytes, s, a); \
     } while (0)
-        if (nw == 4)
+        if (nw == 2)
+            UBD_LAUNCH_LDSX(2);
+        else if (nw == 4)
             UBD_LAUNCH_LDSX(4);
         else if (nw == 8)
             UBD_LAUNCH_LDSX(8);
