@@ -426,6 +426,7 @@ struct ubd_context : public Executor {
     int max_chunks = 0;                     // f32-path chunks (ATTN_CHUNK cells)
     int max_chunks_mfma = 0;                // MFMA split-path chunks (ATTN_DECODE_CHUNK cells)
     bool mfma_attn = false;
+    int attn_wave_slots = 1024;             // split-attention waves resident at once (CUs x SIMDs x waves)
     double *inv_freq = nullptr;
     float2 *rope_cs = nullptr;              // [cap][head_dim / 2] (cos, sin) of the ubatch's angles
     int32_t *info_dev = nullptr;
@@ -617,6 +618,15 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     c->max_chunks = (int)((P.n_cells + ATTN_CHUNK - 1) / ATTN_CHUNK);
     c->max_chunks_mfma = (int)((P.n_cells + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK);
     c->mfma_attn = attn_mfma_ok(c->type_k, c->type_v, hd, H / Hk);
+    {
+        // waves of the split attention kernel per SIMD (its registers:
+        // head size 128 fits one, 64 two, 32 four), 4 SIMDs per CU
+        int n_cu = 0;
+        if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, model->device) != hipSuccess ||
+            n_cu <= 0)
+            n_cu = 256;
+        c->attn_wave_slots = n_cu * 4 * (hd >= 128 ? 1 : hd >= 64 ? 2 : 4);
+    }
     // split partials: f32 path up to n_ubatch tokens; MFMA path only for <= 16 tokens
     const size_t part_rows = c->mfma_attn ? (size_t)std::min(cap, 16) * H * c->max_chunks_mfma
                                           : (size_t)cap * H * c->max_chunks;
@@ -917,8 +927,12 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         if (mfma_attn) {
             aa.split = split;
             aa.max_chunks = max_chunks_mfma;
-            // about 32 chunks per (tile, KV head), at least 32 cells each
-            const int want = (max_scan + 31) / 32;
+            // one round of waves: as many chunks as the GPU holds split-kernel
+            // waves at once (a second, partial round cost config 4 ~7 %),
+            // shared by the (tile, KV head) pairs; at least 32 cells each
+            const int pairs = std::max(1, n_tiles * Hk);
+            const int per_pair = std::max(1, attn_wave_slots / pairs);
+            const int want = (max_scan + per_pair - 1) / per_pair;
             const int cmin = std::max(ATTN_DECODE_CHUNK, g_tuning.attn_chunk_min / 32 * 32);
             aa.chunk_cells = std::max(cmin, (want + 31) / 32 * 32);
             aa.n_chunks_launch = std::max(1, (max_scan + aa.chunk_cells - 1) / aa.chunk_cells);
