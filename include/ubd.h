@@ -90,6 +90,9 @@ typedef struct ubd_hparams {
  *         [ne[1]][ne[0] / 32]; or scales = NULL and data = the GGUF block
  *         layout, [ne[1]][ne[0] / 32] blocks of 34 bytes (f16 scale, then
  *         32 codes).  ne[0] must be a multiple of 32.
+ * output.weight may be left out: the model is then tied and its logits
+ * use token_embd.weight as the output matrix ([ENG] Step 6: the output
+ * tensor is optional and duplicates the embedding when absent).
  * data / scales are host pointers unless on_device != 0.  They are copied
  * during ubd_model_load and may be freed afterwards. */
 typedef struct ubd_tensor_src {

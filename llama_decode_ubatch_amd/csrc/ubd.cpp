@@ -295,6 +295,13 @@ extern "C" ubd_model *ubd_model_load(const ubd_hparams *hparams, const ubd_tenso
         }
         got[t.name] = &t;
     }
+    // The output matrix is optional: without it the model is tied and the
+    // logits reuse the token embedding table, which has the same shape
+    // {n_embd, n_vocab} ("llama.cpp AI LLM Engine - how it works", Step 6:
+    // the output tensor is not required and is then a duplicate of
+    // token_embd).
+    const bool tied = !got.count("output.weight");
+    if (tied && got.count("token_embd.weight")) got["output.weight"] = got["token_embd.weight"];
     for (auto &kv : expect)
         if (!got.count(kv.first)) return fail(-1, "ubd_model_load: missing tensor " + kv.first);
 
@@ -388,8 +395,8 @@ extern "C" ubd_model *ubd_model_load(const ubd_hparams *hparams, const ubd_tenso
     }
     if (!hip_ok(hipStreamSynchronize(st), "load sync")) return bail(-2, "ubd_model_load: " + g_err);
     m->t_load_ms = now_ms() - t0;
-    log_line(1, "model loaded: %d layers, %.1f MiB on device, %.1f ms", hp.n_layer, m->mem.bytes / 1048576.0,
-             m->t_load_ms);
+    log_line(1, "model loaded: %d layers, %.1f MiB on device, %.1f ms%s", hp.n_layer, m->mem.bytes / 1048576.0,
+             m->t_load_ms, tied ? ", output tied to token_embd" : "");
     if (status) *status = 0;
     return m;
 }

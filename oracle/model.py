@@ -46,14 +46,21 @@ class OracleModel:
     "scale"}), or is a callable name -> stored tensor for lazy generation.
     ``rows_fn(name, rows)``, if given, returns selected rows of a stored
     matrix (used for the embedding gather so the table is never expanded).
+    A mapping without "output.weight" is a tied model (engine page, Step 6:
+    the output tensor is optional and then duplicates token_embd); for a
+    callable, ``tied`` says so.
     """
 
     def __init__(self, shape, tensors: Union[Mapping[str, dict], Callable],
                  dtype=np.float64, cache: bool = True,
-                 rows_fn: Optional[Callable] = None):
+                 rows_fn: Optional[Callable] = None, tied: Optional[bool] = None):
         self.hp = shape
         self.dtype = dtype
         self._get = tensors if callable(tensors) else tensors.__getitem__
+        if tied is None:
+            tied = not callable(tensors) and "output.weight" not in tensors
+        self.tied = bool(tied)
+        self.output_name = "token_embd.weight" if self.tied else "output.weight"
         self._rows = rows_fn
         self._cache_on = cache
         self._cache: Dict[str, np.ndarray] = {}
@@ -232,7 +239,7 @@ class OracleContext:
         """Final norm of the output rows, then the output matrix."""
         m, hp = self.model, self.model.hp
         h = nm.rms_norm(x_out, m.w("output_norm.weight"), hp.rms_eps)
-        return h @ m.w("output.weight").T
+        return h @ m.w(m.output_name).T
 
     def layer_forward(self, il: int, x: np.ndarray, ub: UBatch,
                       cells: np.ndarray) -> np.ndarray:

@@ -87,3 +87,34 @@ def test_split_gguf(tmp_path):
     paths = W.write_model_gguf(m, str(tmp_path / "tiny"), n_split=3, tensors=tens)
     toks = np.arange(1, 9, dtype=np.int32)
     assert np.array_equal(run(Model.from_gguf(paths[0], device=0), toks), run(Model(m, tens, device=0), toks))
+
+
+@pytest.mark.parametrize("kind", ["f32", "q8_0"])
+def test_tied_output(tmp_path, kind):
+    """A file without output.weight: the library uses token_embd as the
+    output matrix.  Bit-identical to an array model that passes the table
+    under both names (same kernels, same stored values); the f32 file also
+    against the oracle reading it as a tied model."""
+    import torch  # noqa: F401
+    from llama_decode_ubatch_amd import Model
+    m = variants()[kind]
+    tens = {s.name: gen_tensor(m, s) for s in tensor_specs(m)}
+    tied = {k: v for k, v in tens.items() if k != "output.weight"}
+    both = dict(tied, **{"output.weight": tens["token_embd.weight"]})
+    paths = W.write_model_gguf(m, str(tmp_path / f"tied-{kind}"), tensors=tens, tied=True)
+    toks = np.random.default_rng(8).integers(0, m.n_vocab, 12).astype(np.int32)
+    print(f"tied GGUF {kind}: {paths[0]}", flush=True)
+    z_both = run(Model(m, both, device=0), toks)
+    z_arr = run(Model(m, tied, device=0), toks)
+    assert np.array_equal(z_arr, z_both)
+    z_file = run(Model.from_gguf(paths[0], device=0), toks)
+    assert np.array_equal(z_file, z_both)
+    if kind == "f32":
+        g, where = open_model(paths)
+        assert "output.weight" not in where
+        om = OracleModel(m, lambda n: where[n].stored(n), dtype=np.float64, tied=True)
+        ref = OracleContext(om, n_ctx=256, n_batch=64, n_ubatch=16, type_k="f32", type_v="f32")
+        assert ref.decode(Batch(toks.tolist(), logits=[1] * len(toks))) == 0
+        zr = np.stack([ref.logits_ith(i) for i in range(len(toks))])
+        err = float(np.abs(z_file[:len(toks)] - zr).max() / np.abs(zr).max())
+        assert err < 1e-4, err

@@ -100,6 +100,22 @@ def test_bruteforce_no_cache_forward():
                                atol=1e-11 * np.abs(a).max())
 
 
+def test_tied_output_uses_the_embedding_table():
+    """A model without output.weight takes its logits from token_embd (the
+    engine page's Step 6: the output tensor is optional and duplicates the
+    embedding); the brute-force forward gets the table under both names."""
+    tied = {k: v for k, v in TENS.items() if k != "output.weight"}
+    both = dict(tied, **{"output.weight": TENS["token_embd.weight"]})
+    toks = rand_tokens(9, MICRO.n_vocab, 12)
+    ctx = oracle_ctx(tensors=tied, n_ubatch=4)
+    assert ctx.model.tied
+    a = _prefill_all(ctx, toks)
+    np.testing.assert_allclose(a, _brute_forward(MICRO, both, toks), rtol=0,
+                               atol=1e-11 * np.abs(a).max())
+    # and the untied model differs, so the test sees which table was used
+    assert np.abs(a - _prefill_all(oracle_ctx(tensors=TENS, n_ubatch=4), toks)).max() > 1e-3 * np.abs(a).max()
+
+
 def test_gqa_equals_replicated_heads():
     mha = ModelShape("micro-mha", 10, n_layer=MICRO.n_layer, n_embd=MICRO.n_embd,
                      n_head=MICRO.n_head, n_head_kv=MICRO.n_head,

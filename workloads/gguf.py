@@ -122,14 +122,17 @@ def model_kvs(m: ModelShape, extra=()) -> List[Tuple[str, int, object]]:
 
 
 def write_model_gguf(m: ModelShape, path_prefix: str, n_split: int = 1,
-                     tensors: dict = None) -> List[str]:
+                     tensors: dict = None, tied: bool = False) -> List[str]:
     """Write the synthetic model as one GGUF file (``<prefix>.gguf``) or as
     n_split files ``<prefix>-0000k-of-0000n.gguf`` (the loading page's
     split stage: every part is a whole GGUF file; the first holds the model
     keys, every part holds split.no / split.count / split.tensors.count).
-    Returns the paths, first part first."""
+    ``tied`` leaves output.weight out (a model whose output matrix is its
+    token embedding).  Returns the paths, first part first."""
     recs = []
     for s in tensor_specs(m):
+        if tied and s.name == "output.weight":
+            continue
         t = tensors[s.name] if tensors is not None else gen_tensor(m, s)
         recs.append(tensor_record(s.name, t))
     if n_split == 1:
