@@ -476,10 +476,21 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * "fuse_norm" (ubatches of at most 2 tokens: 1 = RMSNorm fused into the
  * QKV, gate|up and logits products, -1 = into QKV only, 0 = never),
  * "attn_chunk_min" (smallest cells per wave of split attention), "ldsx"
- * (0 = few-token products read activations from global memory), "gemm"
+ * (0 = few-token products read activations from global memory),
+ * "ldsx_early" (one-token products: 1 = activation loads issued before the
+ * weight loads, 0 = after; the results are identical), "gemm_wpd"
+ * (prefill product weight look-ahead stages, 1 or 2; 0 = per shape),
+ * "gemm_deep" (1 = bf16 residual and QKV prefill products use the kernel
+ * with weights three stages ahead where the shape allows, 0 = never), "gemm"
  * (prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel),
  * "gemm_shape" (0 = automatic LDS-ring tile; 1, 2, 3, 4 force 2x4, 2x8,
- * 4x4, 4x8 blocks of 16 weight rows per wave x 16 tokens), "gemm_split"
+ * 4x4, 4x8 blocks of 16 weight rows per wave x 16 tokens; 5, 6 force 1x4,
+ * 1x8 for products without SwiGLU; bf16 weights with the weights loaded
+ * further ahead in rotating register sets, where K / 64 is a multiple of
+ * the set count: 7 = 4x8 one stage ahead and 8 = 4x8 three stages ahead
+ * with one wave per SIMD, 9 = 2x8, 10 = 2x4, 11 = 4x4 three stages ahead,
+ * 12 = 4x16 one stage ahead with one wave per SIMD),
+ * "gemm_split"
  * (residual prefill products: 0 = automatic k split, 2 or 4 forced),
  * "small_rb" (1 =
  * products of 3..16 tokens share activation fragments over 4 row blocks

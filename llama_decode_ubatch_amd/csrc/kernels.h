@@ -40,11 +40,13 @@ struct Tuning {
                               // logits products, -1 = into QKV only, 0 = never
     int attn_chunk_min = 0;   // smallest cells per wave of split attention
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
+    int ldsx_early = 1;       // one-token LDS-staged products: activation loads ahead of the weights
     int small_rb = 1;         // several-token products: 4 row blocks per work-group / split k (0 = off)
     int gemm = 1;             // prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel
     int gemm_split = 0;       // residual prefill products: forced k split (2, 4; 0 = automatic)
     int gemm_shape = 0;       // LDS-ring tile (0 = automatic; 1..4 force 2x4, 2x8, 4x4, 4x8 row x token blocks)
     int gemm_wpd = 0;         // LDS-ring product: stages of weight look-ahead (1 or 2; 0 = per shape)
+    int gemm_deep = 1;        // bf16 residual / QKV prefill products: 1 = deep look-ahead kernel where it fits
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;
@@ -117,6 +119,7 @@ struct LinearArgs {
     TokInfo tok;                      // QKV: pos / stream / cell per token
     QKVEpi qkv;
     NormIn norm;                      // set: input is x normalised on the fly (T <= NORM_TMAX)
+    int early = 1;                    // LDS-staged product: one-token activation loads may go first
 };
 
 void launch_linear(const LinearArgs &a, hipStream_t s);

@@ -452,6 +452,27 @@ __device__ __forceinline__ void load_wbatch(const LinearArgs &a, int rb0, int s,
     }
 }
 
+// load_wbatch for a batch known to be whole: no per-step exits, so the
+// compiler sees a fixed count of loads after anything issued before them
+template <int WT, int RB, int UB>
+__device__ __forceinline__ void load_wbatch_whole(const LinearArgs &a, int rb0, int s, int lane,
+                                                  WBatch<WT, RB, UB> &b) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
+                                                ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
+            if (WT == W_Q8) {
+                const size_t b0 = ((size_t)(rb0 + j) * (a.K / 32) + 2 * (s + u)) * 16 + 4 * g;
+                b.sc[u][j][0] = *(const u32x2_t *)(a.wscale + b0);
+                b.sc[u][j][1] = *(const u32x2_t *)(a.wscale + b0 + 16);
+            }
+        }
+    }
+}
+
 template <int WT, int RB, int UB>
 __device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const unsigned char *lds, int Tb, int K,
                                            int s, int s1, int lane, int tok, bool tok_ok, f32x4_t *acc) {
@@ -616,6 +637,125 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
     }
 }
 
+// One-token variant of the activation copy, split in two so that the
+// activation loads go out before the weight batches.  A wave's vector loads
+// complete in issue order, so a copy issued after the weights (as above)
+// cannot start before every weight of the wave's first two batches has
+// arrived; issued first, it overlaps them.  Each thread keeps at most EVM
+// float4 slices (and the gain's) in registers; longer rows use the copy
+// above.
+constexpr int EVM = 4;
+
+template <int WT, bool NORM>
+struct EarlyX {
+    f32x4_t v[WT == W_F32 || NORM ? EVM : 1];
+    f32x4_t gn[NORM ? EVM : 1];
+    u16x4_t h[WT == W_F32 || NORM ? 1 : EVM], l[WT == W_F32 || NORM ? 1 : EVM];
+};
+
+// one token, a row short enough for the registers, and a whole first
+// weight batch for every wave
+template <int NW, int UB>
+__device__ __forceinline__ bool ldsx_early_fits(int K, int Tb, int steps) {
+    return Tb == 1 && (K / 4 + 64 * NW - 1) / (64 * NW) <= EVM && steps >= NW * UB;
+}
+
+template <int WT, int NW, bool NORM>
+__device__ __forceinline__ void ldsx_early_load(const LinearArgs &a, int t0, EarlyX<WT, NORM> &x) {
+    constexpr int TH = 64 * NW;
+    const int tid = threadIdx.x, K = a.K;
+    const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+    const u16x4_t z = {0, 0, 0, 0};
+    if (NORM) {
+        const float *xr = a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[t0] : t0) * a.norm.ld;
+#pragma unroll
+        for (int i = 0; i < EVM; ++i) {
+            const int e = (tid + TH * i) * 4;
+            x.v[i] = e < K ? *(const f32x4_t *)(xr + e) : z4;
+            x.gn[i] = e < K ? *(const f32x4_t *)(a.norm.gain + e) : z4;
+        }
+    } else if (WT == W_F32) {
+#pragma unroll
+        for (int i = 0; i < EVM; ++i) {
+            const int e = (tid + TH * i) * 4;
+            x.v[i] = e < K ? *(const f32x4_t *)(a.x.f32 + (size_t)t0 * a.x.ld + e) : z4;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EVM; ++i) {
+            const int e = (tid + TH * i) * 4;
+            const size_t src = (size_t)t0 * a.x.ld + e;
+            x.h[i] = e < K ? *(const u16x4_t *)(a.x.hi + src) : z;
+            x.l[i] = e < K ? *(const u16x4_t *)(a.x.lo + src) : z;
+        }
+    }
+}
+
+template <int WT, int NW, bool NORM>
+__device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const EarlyX<WT, NORM> &x) {
+    constexpr int TH = 64 * NW;
+    __shared__ float red_ss[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K;
+    const size_t plane = (size_t)K;
+    float inv = 1.f;
+    if (NORM) {
+        // the same summation order as the copy above (slices in order,
+        // zeros past the row end)
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < EVM; ++i)
+            ss += x.v[i][0] * x.v[i][0] + x.v[i][1] * x.v[i][1] + x.v[i][2] * x.v[i][2] + x.v[i][3] * x.v[i][3];
+        ss = wave_sum(ss);
+        if (lane == 0) red_ss[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += red_ss[w];
+        inv = 1.0f / sqrtf(tot / (float)K + a.norm.eps);
+    }
+#pragma unroll
+    for (int i = 0; i < EVM; ++i) {
+        const int e = (tid + TH * i) * 4;
+        if (e >= K) continue;
+        if (NORM || WT == W_F32) {
+            const f32x4_t y = NORM ? x.v[i] * inv * x.gn[i] : x.v[i];
+            if (WT == W_F32) {
+                *(f32x4_t *)(lds + (size_t)e * 4) = y;
+            } else {
+                u16x4_t hh, ll;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    hh[k] = f2bf(y[k]);
+                    ll[k] = f2bf(y[k] - bf2f(hh[k]));
+                }
+                *(u16x4_t *)((uint16_t *)lds + e) = hh;
+                *(u16x4_t *)((uint16_t *)lds + plane + e) = ll;
+            }
+        } else {
+            *(u16x4_t *)((uint16_t *)lds + e) = x.h[i];
+            *(u16x4_t *)((uint16_t *)lds + plane + e) = x.l[i];
+        }
+    }
+    __syncthreads();
+    if (WT == W_Q8) {
+        float *xsum = (float *)(lds + 4 * plane);
+        const uint16_t *hi = (const uint16_t *)lds, *lo = hi + plane;
+        for (int p = tid; p < K / 32; p += TH) {
+            const size_t o = (size_t)p * 32;
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < 32; q += 8) {
+                const u16x8_t hh = *(const u16x8_t *)(hi + o + q), ll = *(const u16x8_t *)(lo + o + q);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += bf2f(hh[e]) + bf2f(ll[e]);
+            }
+            xsum[p] = acc;
+        }
+        __syncthreads();
+    }
+}
+
 // q8_0 with gate|up pairs (RB 2) needs more than 128 registers: 2 waves per
 // SIMD for it (at 4 it spilled ~60 registers to scratch, and the spill
 // reloads, counted with the weight loads, stalled every batch: 1.2 TB/s)
@@ -629,7 +769,8 @@ void linear_ldsx_kernel(LinearArgs a) {
     constexpr int KSTEP = WT_<WT>::KSTEP;
     constexpr int UB = WT == W_Q8 ? (RB == 2 ? 4 : 2) : 8 / RB;   // k-steps per weight batch
     extern __shared__ __align__(16) unsigned char dyn_lds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int rb0 = blockIdx.x * RB;
     const int t0 = blockIdx.y * 16;
@@ -646,9 +787,18 @@ void linear_ldsx_kernel(LinearArgs a) {
     // both weight batches go out before the prologue, and each is refilled
     // right after it has been multiplied: two batches stay in flight
     WBatch<WT, RB, UB> bufA, bufB;
-    if (s0 < s1) load_wbatch<WT, RB, UB>(a, rb0, s0, s1, steps, lane, bufA);
-    if (s0 + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s0 + UB, s1, steps, lane, bufB);
-    ldsx_prologue<WT, NW, NORM>(a, dyn_lds, t0, Tb);
+    if (a.early && ldsx_early_fits<NW, UB>(a.K, Tb, steps)) {
+        EarlyX<WT, NORM> x;
+        ldsx_early_load<WT, NW, NORM>(a, t0, x);
+        asm volatile("" ::: "memory");              // activation loads first
+        load_wbatch_whole<WT, RB, UB>(a, rb0, s0, lane, bufA);
+        if (s0 + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s0 + UB, s1, steps, lane, bufB);
+        ldsx_early_store<WT, NW, NORM>(a, dyn_lds, x);
+    } else {
+        if (s0 < s1) load_wbatch<WT, RB, UB>(a, rb0, s0, s1, steps, lane, bufA);
+        if (s0 + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s0 + UB, s1, steps, lane, bufB);
+        ldsx_prologue<WT, NW, NORM>(a, dyn_lds, t0, Tb);
+    }
     for (int s = s0; s < s1; s += 2 * UB) {
         mul_wbatch<WT, RB, UB>(bufA, dyn_lds, Tb, a.K, s, s1, lane, tok, tok_ok, acc);
         if (s + 2 * UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s + 2 * UB, s1, steps, lane, bufA);
@@ -1068,6 +1218,157 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #endif
 }
 
+// Deep variant of the LDS-ring product: weights D stages ahead in D + 1
+// rotating register sets, activations two stages ahead in the 3-deep LDS
+// ring.  The stage loop is unrolled by D + 1 and has no branches inside,
+// so every register set is loaded and consumed at fixed places and no set
+// is ever copied (a copy of a set still in flight makes the compiler wait
+// for it, which leaves one stage's compute to cover a whole memory round
+// trip).  OCC = waves per SIMD (1: the accumulators go to the matrix-core
+// registers, leaving room for more sets).  bf16 weights; the stage count
+// K / 64 must be a multiple of D + 1.
+template <int EPI, int RBW, int TB, int D, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_deep_kernel(
+    LinearArgs a, int n_wtiles, int n_ttiles) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int KS = 64;
+    using C = GemmCfg<W_BF16, RBW, TB, KS>;
+    constexpr int KH = C::KH, NA = C::NA;
+    static_assert(D == 1 || D == 3, "look-ahead");
+    __shared__ u32x4_t xs[C::NX * C::XF * 64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int total = n_wtiles * n_ttiles;
+    const int b = blockIdx.x;
+    const int tile = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
+    const int tt = tile % n_ttiles;
+    const int nt = tile / n_ttiles;
+    const int nrb = a.N / 16;
+    const int rb0 = nt * 4 * RBW + wave * RBW;
+    const int t0 = tt * 16 * TB;
+    const int nst = a.K / KS;
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (size_t)a.N * a.K * 2);
+    const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, (size_t)a.T * a.x.ld * 2);
+    int xoff[C::XW];
+#pragma unroll
+    for (int u = 0; u < C::XW; ++u) {
+        const int f = wave * C::XW + u;
+        const int tb = (f / KH) % TB, j = f % KH;
+        xoff[u] = ((t0 + 16 * tb + r) * a.x.ld + 32 * j + 8 * g) * 2;
+    }
+    int woff[RBW];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) woff[i] = min(rb0 + i, nrb - 1) * 1024 + lane * 16;
+    const int wstep = nrb * 1024;
+    constexpr int NWL = RBW * NA;
+
+    u32x4_t W[D + 1][RBW][NA];
+    f32x4_t acc[RBW][TB];
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // stage s's weights (clamped to the last stage: the loads past the end
+    // keep the issue pattern, and so the wait counts, unchanged)
+    auto issue_w = [&](int s, u32x4_t (&wn)[RBW][NA]) {
+        const int sl = min(s, nst - 1);
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+            const int so = (NA * sl + j) * wstep;
+#pragma unroll
+            for (int i = 0; i < RBW; ++i) wn[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i], so, 0);
+        }
+    };
+    auto issue_x = [&](int s) {
+        const int sl = min(s, nst - 1);
+        u32x4_t *dst = xs + (size_t)((s % C::NX) * C::XF + wave * C::XW) * 64;
+#pragma unroll
+        for (int u = 0; u < C::XW; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxh, (__attribute__((address_space(3))) void *)(dst + u * 64), 16,
+                                                     xoff[u], sl * KS * 2, 0, 0);
+    };
+    // both k halves' activation fragments are read up front: the second
+    // half's reads are in flight while the first half's products run
+    static_assert(KH == 2, "two k halves per stage");
+    auto compute = [&](int s, const u32x4_t (&wc)[RBW][NA]) {
+        const u32x4_t *xb = xs + (size_t)(s % C::NX) * C::XF * 64;
+        u32x4_t B[2][TB];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) B[j][tb] = xb[(tb * KH + j) * 64 + lane];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int i = 0; i < RBW; ++i)
+                    acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wc[i][j]),
+                                                                         __builtin_bit_cast(bf16x8_t, B[j][tb]),
+                                                                         acc[i][tb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // issue order w0 x0 w1 x1 w2 ...: every stage finds at least NWL + XW
+    // loads issued after the ones it needs (XW with one stage of look-ahead)
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        issue_w(k, W[k]);
+        if (k < 2) issue_x(k);
+    }
+    if (D == 1) issue_x(1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < nst; s += D + 1) {
+#pragma unroll
+        for (int k = 0; k <= D; ++k) {
+            wait_vm<D == 1 ? C::XW : C::XW + NWL>();
+            wg_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            issue_w(s + k + D, W[(k + D) % (D + 1)]);
+            issue_x(s + k + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(s + k, W[k]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vm<0>();
+
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+        const int rb = rb0 + i;
+        if (rb >= nrb) continue;
+        if (EPI == EPI_SWIGLU && (i & 1)) continue;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = t0 + tb * 16 + r;
+            if (t >= a.T) continue;
+            if (EPI == EPI_SWIGLU)
+                epilogue4<EPI, false>(a, t, (rb >> 1) * 16 + 4 * g, acc[i][tb], acc[i + 1][tb]);
+            else
+                epilogue4<EPI, false>(a, t, rb * 16 + 4 * g, acc[i][tb], acc[i][tb]);
+        }
+    }
+#endif
+}
+
+// false (nothing launched) unless the stage count is a multiple of D + 1
+template <int EPI, int RBW, int TB, int D, int OCC>
+static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
+    const int nst = a.K / 64;
+    if (a.K % 64 || nst % (D + 1)) return false;
+    const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
+    const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
+    hipLaunchKernelGGL((gemm_deep_kernel<EPI, RBW, TB, D, OCC>), dim3(n_wtiles * n_ttiles), dim3(256), 0, s, a,
+                       n_wtiles, n_ttiles);
+    return true;
+}
+
 // wpd: stages of weight look-ahead (the tuning knob overrides it)
 template <int WT, int EPI, int RBW, int TB, int SPLITK>
 static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
@@ -1101,7 +1402,22 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     case 4: if (WT != W_Q8) { launch_gemm_lds<WT, EPI, WT == W_Q8 ? 2 : 4, 8, 1>(a, s); return; } break;
     case 5: if (EPI != EPI_SWIGLU) { launch_gemm_lds<WT, EPI, 1, 4, 1>(a, s); return; } break;
     case 6: if (EPI != EPI_SWIGLU) { launch_gemm_lds<WT, EPI, 1, 8, 1>(a, s); return; } break;
+    case 7: if (WT == W_BF16 && launch_gemm_deep<EPI, 4, 8, 1, 1>(a, s)) return; break;
+    case 8: if (WT == W_BF16 && launch_gemm_deep<EPI, 4, 8, 3, 1>(a, s)) return; break;
+    case 9: if (WT == W_BF16 && launch_gemm_deep<EPI, 2, 8, 3, 2>(a, s)) return; break;
+    case 10: if (WT == W_BF16 && launch_gemm_deep<EPI, 2, 4, 3, 2>(a, s)) return; break;
+    case 11: if (WT == W_BF16 && launch_gemm_deep<EPI, 4, 4, 3, 2>(a, s)) return; break;
+    case 12: if (WT == W_BF16 && launch_gemm_deep<EPI, 4, 16, 1, 1>(a, s)) return; break;
     default: break;
+    }
+    // bf16 products with enough tiles: the deep variant, weights three
+    // stages ahead (measured at 512 tokens, 8B shape: O 44.4 -> 36.4 us,
+    // FFN down 134.5 -> 108.5 us with 128 x 64 tiles; QKV 62.5 -> 58.2 us
+    // with 128 x 128 tiles).  The wide gate|up tile keeps the kernel above.
+    if (WT == W_BF16 && g_tuning.gemm_deep != 0) {
+        if (EPI == EPI_RESID && tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2>(a, s)) return;
+        if (EPI == EPI_QKV && tiles(4, 8) < 192 && tiles(2, 8) >= 192 && launch_gemm_deep<EPI, 2, 8, 3, 2>(a, s))
+            return;
     }
     // residual products: 128 x 64 tiles, splitting k (atomic partial sums)
     // only when there are too few tiles for the CUs
@@ -1196,12 +1512,14 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
     const size_t ldsx = (size_t)4 * std::min(16, a.T) * a.K + (WT == W_Q8 ? (size_t)std::min(16, a.T) * a.K / 8 : 0);
     if (ldsx <= LDSX_MAX_BYTES && g_tuning.ldsx != 0) {
         const size_t bytes = std::max(ldsx, (size_t)16 * 64 * 16 * 2);   // also holds the wave reduction
-#define UBD_LAUNCH_LDSX(NW_)                                                                               \
-    do {                                                                                                   \
-        if (norm)                                                                                          \
-            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, true>), grid, dim3(64 * NW_), bytes, s, a); \
-        else                                                                                               \
-            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), bytes, s, a); \
+        LinearArgs la = a;
+        la.early = g_tuning.ldsx_early;
+#define UBD_LAUNCH_LDSX(NW_)                                                                                \
+    do {                                                                                                    \
+        if (norm)                                                                                           \
+            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, true>), grid, dim3(64 * NW_), bytes, s, la); \
+        else                                                                                                \
+            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), bytes, s, la); \
     } while (0)
         if (nw == 2)
             UBD_LAUNCH_LDSX(2);

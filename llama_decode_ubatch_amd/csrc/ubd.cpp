@@ -1476,8 +1476,12 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.attn_chunk_min = value;
     } else if (k == "gemm_wpd") {
         g_tuning.gemm_wpd = value;
+    } else if (k == "gemm_deep") {
+        g_tuning.gemm_deep = value;
     } else if (k == "ldsx") {
         g_tuning.ldsx = value;
+    } else if (k == "ldsx_early") {
+        g_tuning.ldsx_early = value;
     } else if (k == "gemm") {
         g_tuning.gemm = value;
     } else if (k == "gemm_split") {

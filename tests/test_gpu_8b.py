@@ -84,6 +84,23 @@ def test_prefill_and_decode_sampled_layers(cfg):
         assert rel(z, zr) < TOL
         tok = ctx.greedy(-1)
         assert tok == int(np.argmax(z))
+    # one-token products with the activation loads issued after the weight
+    # loads: the same arithmetic, so the same logits bit for bit (two
+    # one-token ubatches: no split-k product, whose atomic partial sums
+    # make the order of additions vary from run to run)
+    from llama_decode_ubatch_amd.binding import set_tuning
+    z_early = []
+    for early in (1, 0):
+        set_tuning("ldsx_early", early)
+        try:
+            c2 = Context(model, n_ctx=w.n_ctx, n_batch=w.n_batch, n_ubatch=w.n_ubatch, type_k=w.type_k,
+                         type_v=w.type_v)
+            assert c2.decode(prompt[:1]) == 0 and c2.decode([tok]) == 0
+            z_early.append(c2.logits_ith(-1).copy())
+            c2.free()
+        finally:
+            set_tuning("ldsx_early", 1)
+    assert np.array_equal(z_early[0], z_early[1])
     ctx.free()
     model.free()
 
