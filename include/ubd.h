@@ -481,7 +481,9 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * weight loads, 0 = after; the results are identical), "gemm_wpd"
  * (prefill product weight look-ahead stages, 1 or 2; 0 = per shape),
  * "gemm_deep" (1 = bf16 residual and QKV prefill products use the kernel
- * with weights three stages ahead where the shape allows, 0 = never), "gemm"
+ * with weights three stages ahead where the shape allows, 0 = never),
+ * "act_tiled" (1 = the prefill products read their input activations
+ * stored in matrix-core operand order, 0 = row-major), "gemm"
  * (prefill products: 1 = LDS-ring kernel, 0 = register-staged kernel),
  * "gemm_shape" (0 = automatic LDS-ring tile; 1, 2, 3, 4 force 2x4, 2x8,
  * 4x4, 4x8 blocks of 16 weight rows per wave x 16 tokens; 5, 6 force 1x4,

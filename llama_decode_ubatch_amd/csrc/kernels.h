@@ -47,6 +47,7 @@ struct Tuning {
     int gemm_shape = 0;       // LDS-ring tile (0 = automatic; 1..4 force 2x4, 2x8, 4x4, 4x8 row x token blocks)
     int gemm_wpd = 0;         // LDS-ring product: stages of weight look-ahead (1 or 2; 0 = per shape)
     int gemm_deep = 1;        // bf16 residual / QKV prefill products: 1 = deep look-ahead kernel where it fits
+    int act_tiled = 1;        // prefill products read activations tiled in MFMA operand order (0 = row-major)
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;
@@ -64,6 +65,12 @@ struct Act {
     uint16_t *hi = nullptr;    // HILO format
     uint16_t *lo = nullptr;
     int ld = 0;                // elements per row
+    // HILO planes in MFMA operand order instead of row-major: 1 KB tiles of
+    // 16 tokens x 32 values, tile (t / 16, k / 32) at ((t / 16) * (ld / 32) +
+    // k / 32) * 512 elements, value (t, k) at lane (t % 16) + 16 * ((k / 8) % 4),
+    // element k % 8 of that lane's 8 (ld a multiple of 32; buffers hold whole
+    // 16-token tiles)
+    int tiled = 0;
 };
 
 // Per-ubatch token table on the device (int32 planes of capacity `cap`).
@@ -123,6 +130,10 @@ struct LinearArgs {
 };
 
 void launch_linear(const LinearArgs &a, hipStream_t s);
+// True when launch_linear(a) runs a product that reads its input activations
+// in the tiled layout (the LDS-ring prefill products); the producer of a.x
+// must then write that layout.
+bool linear_reads_tiled(const LinearArgs &a);
 
 // x[t] = dequant(table[token[t]]); also records the position and the
 // sequence mask of each token's cell in the device cell tables
@@ -137,6 +148,8 @@ void launch_embed(int wtype, const void *table, const uint16_t *scales,
                   hipStream_t s);
 
 // out[r] = rmsnorm(x[src_row(r)]) * gain, src_row = row_map ? row_map[r] : r
+// (into a tiled HILO `out` too; the rows of its last tile past `rows` are
+// left as they were)
 void launch_rmsnorm(const float *x, int ldx, const int32_t *row_map, int rows,
                     const float *gain, int d, float eps, const Act &out,
                     hipStream_t s);

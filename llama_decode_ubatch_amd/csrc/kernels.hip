@@ -40,6 +40,12 @@ __device__ __forceinline__ uint16_t f2h(float f) {
     return h;
 }
 
+// element index of activation (token t, value c) in either layout
+__device__ __forceinline__ size_t act_idx(const Act &o, int t, int c) {
+    if (!o.tiled) return (size_t)t * o.ld + c;
+    return ((size_t)(t >> 4) * (o.ld >> 5) + (c >> 5)) * 512 + (size_t)((t & 15) + 16 * ((c >> 3) & 3)) * 8 + (c & 7);
+}
+
 __device__ __forceinline__ void store_act(const Act &o, size_t idx, float v) {
     if (o.f32) {
         o.f32[idx] = v;
@@ -230,7 +236,8 @@ __device__ __forceinline__ void epilogue4(const LinearArgs &a, int t, int n, f32
         const int row = a.row_map[t];
         store4(a.logits + (size_t)row * a.N + n, v);
     } else if (EPI == EPI_SWIGLU) {
-        const size_t o = (size_t)t * a.out.ld + n;
+        // n..n+3 stay contiguous in the tiled layout too (n is a multiple of 4)
+        const size_t o = act_idx(a.out, t, n);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float gt = v[i], up = u[i];
@@ -1070,16 +1077,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     // token rows past T need no clamping).  Every load is a loop-invariant
     // 32-bit lane offset plus a per-stage scalar offset.
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (size_t)a.N * a.K * (Q8 ? 1 : 2));
-    const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, (size_t)a.T * a.x.ld * 2);
-    const __amdgpu_buffer_rsrc_t rxl = make_rsrc(Q8 ? a.x.lo : a.x.hi, (size_t)a.T * a.x.ld * 2);
+    // (tiled activations: whole 16-token tiles, each fragment one
+    // contiguous 1 KB run; row-major: 16 rows x 64 bytes per fragment)
+    const size_t xbytes = (size_t)(a.x.tiled ? (a.T + 15) / 16 * 16 : a.T) * a.x.ld * 2;
+    const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, xbytes);
+    const __amdgpu_buffer_rsrc_t rxl = make_rsrc(Q8 ? a.x.lo : a.x.hi, xbytes);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.wscale, Q8 ? (size_t)a.N * KB * 2 : 0);
+    const int xst = a.x.tiled ? KS * 32 : KS * 2;     // bytes between stages
     // this wave's activation fragments f = wave*XW + u = (plane, token block, k half)
     int xoff[C::XW];
 #pragma unroll
     for (int u = 0; u < C::XW; ++u) {
         const int f = wave * C::XW + u;
         const int tb = (f / KH) % TB, j = f % KH;
-        xoff[u] = ((t0 + 16 * tb + r) * a.x.ld + 32 * j + 8 * g) * 2;
+        xoff[u] = a.x.tiled ? ((t0 / 16 + tb) * (a.x.ld / 32) + j) * 1024 + lane * 16
+                            : ((t0 + 16 * tb + r) * a.x.ld + 32 * j + 8 * g) * 2;
     }
     // weight row blocks past N re-read the last one (never stored)
     int woff[RBW], soff[RBW];
@@ -1126,7 +1138,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
             const bool lo = (wave * C::XW + u) >= TB * KH;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(lo ? rxl : rxh,
                                                      (__attribute__((address_space(3))) void *)(dst + u * 64), 16,
-                                                     xoff[u], sl * KS * 2, 0, 0);
+                                                     xoff[u], sl * xst, 0, 0);
         }
     };
 
@@ -1251,13 +1263,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const int nst = a.K / KS;
 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (size_t)a.N * a.K * 2);
-    const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, (size_t)a.T * a.x.ld * 2);
+    const size_t xbytes = (size_t)(a.x.tiled ? (a.T + 15) / 16 * 16 : a.T) * a.x.ld * 2;
+    const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, xbytes);
+    const int xst = a.x.tiled ? KS * 32 : KS * 2;     // bytes between stages
     int xoff[C::XW];
 #pragma unroll
     for (int u = 0; u < C::XW; ++u) {
         const int f = wave * C::XW + u;
         const int tb = (f / KH) % TB, j = f % KH;
-        xoff[u] = ((t0 + 16 * tb + r) * a.x.ld + 32 * j + 8 * g) * 2;
+        xoff[u] = a.x.tiled ? ((t0 / 16 + tb) * (a.x.ld / 32) + j) * 1024 + lane * 16
+                            : ((t0 + 16 * tb + r) * a.x.ld + 32 * j + 8 * g) * 2;
     }
     int woff[RBW];
 #pragma unroll
@@ -1289,7 +1304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #pragma unroll
         for (int u = 0; u < C::XW; ++u)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rxh, (__attribute__((address_space(3))) void *)(dst + u * 64), 16,
-                                                     xoff[u], sl * KS * 2, 0, 0);
+                                                     xoff[u], sl * xst, 0, 0);
     };
     // both k halves' activation fragments are read up front: the second
     // half's reads are in flight while the first half's products run
@@ -1587,6 +1602,14 @@ static void launch_linear_wt(const LinearArgs &a, hipStream_t s) {
     }
 }
 
+// mirrors the dispatch: try_gemm takes bf16 / q8_0 products of >= 64 tokens
+// with K a multiple of 64, and runs an LDS-ring kernel unless the
+// register-staged one is selected
+bool linear_reads_tiled(const LinearArgs &a) {
+    return g_tuning.act_tiled != 0 && g_tuning.gemm != 0 && (a.wtype == W_BF16 || a.wtype == W_Q8) && a.T >= 64 &&
+           a.K % 64 == 0 && !(a.epi == EPI_SWIGLU && a.N % 32) && a.norm.x == nullptr && a.N > 0;
+}
+
 void launch_linear(const LinearArgs &a, hipStream_t s) {
     if (a.T <= 0 || a.N <= 0) return;
     if (a.norm.x && a.T > NORM_TMAX) return;   // caller contract: fused norm only for few rows
@@ -1685,9 +1708,67 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int ldx, c
     }
 }
 
+// RMSNorm of one row into tiled HILO activations (d a multiple of 32): every
+// thread owns 8-value runs, each one lane's 16 bytes of an operand tile, so
+// the two planes take one 16-byte store per run.
+__global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float *x, int ldx, const int32_t *row_map,
+                                                            const float *gain, int d, float eps, Act out) {
+    const int r = blockIdx.x;
+    const float *xr = x + (size_t)(row_map ? row_map[r] : r) * ldx;
+    constexpr int MAXV = 4;                  // 8-value runs per thread held in registers (d <= 8192)
+    f32x4_t v[MAXV][2];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v[i][h] = e < d ? *(const f32x4_t *)(xr + e + 4 * h) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ss += v[i][h][0] * v[i][h][0] + v[i][h][1] * v[i][h][1] + v[i][h][2] * v[i][h][2] +
+                  v[i][h][3] * v[i][h][3];
+        }
+    }
+    for (int e = (threadIdx.x + 256 * MAXV) * 8; e < d; e += 2048)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4_t w = *(const f32x4_t *)(xr + e + 4 * h);
+            ss += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
+        }
+    __shared__ float part[4];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+    auto put = [&](int e, f32x4_t a0, f32x4_t a1) {
+        const f32x4_t y0 = a0 * inv * *(const f32x4_t *)(gain + e);
+        const f32x4_t y1 = a1 * inv * *(const f32x4_t *)(gain + e + 4);
+        u16x8_t hh, ll;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float y = k < 4 ? y0[k] : y1[k - 4];
+            hh[k] = f2bf(y);
+            ll[k] = f2bf(y - bf2f(hh[k]));
+        }
+        const size_t o = act_idx(out, r, e);
+        *(u16x8_t *)(out.hi + o) = hh;
+        *(u16x8_t *)(out.lo + o) = ll;
+    };
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 8;
+        if (e < d) put(e, v[i][0], v[i][1]);
+    }
+    for (int e = (threadIdx.x + 256 * MAXV) * 8; e < d; e += 2048)
+        put(e, *(const f32x4_t *)(xr + e), *(const f32x4_t *)(xr + e + 4));
+}
+
 void launch_rmsnorm(const float *x, int ldx, const int32_t *row_map, int rows, const float *gain, int d,
                     float eps, const Act &out, hipStream_t s) {
     if (rows <= 0) return;
+    if (out.tiled) {
+        hipLaunchKernelGGL(rmsnorm_tiled_kernel, dim3(rows), dim3(256), 0, s, x, ldx, row_map, gain, d, eps, out);
+        return;
+    }
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, ldx, row_map, gain, d, eps, out);
 }
 
@@ -1853,7 +1934,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
         for (int c = 0; c < nch; ++c)
             if (ml[2 * c] != -INFINITY)
                 o += a.part_o[(((size_t)t * a.n_head + h) * a.max_chunks + c) * HD + d] * expf(ml[2 * c] - M);
-        store_act(a.out, (size_t)t * a.out.ld + h * HD + d, o * invL);
+        store_act(a.out, act_idx(a.out, t, h * HD + d), o * invL);
     }
 }
 
@@ -2240,7 +2321,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
             const int t = t0 + row / G, h = grp * G + row % G;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                store_act(a.out, (size_t)t * a.out.ld + h * HD + 16 * db + r, lrow[i] > 0.f ? O[db][i] / lrow[i] : 0.f);
+                store_act(a.out, act_idx(a.out, t, h * HD + 16 * db + r), lrow[i] > 0.f ? O[db][i] / lrow[i] : 0.f);
         }
         return;
     }
@@ -2312,7 +2393,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < DPL; ++j) {
         const int d = lane + 64 * j;
-        if (d < HD) store_act(a.out, (size_t)t * a.out.ld + h * HD + d, o[j] * invL);
+        if (d < HD) store_act(a.out, act_idx(a.out, t, h * HD + d), o[j] * invL);
     }
 }
 

@@ -604,14 +604,16 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
         return bail("KV cell table init failed");
     const int cap = c->cap;
     const bool f32w = model->wtype == W_F32;
+    // (HILO planes hold whole 16-token tiles: the prefill products read them tiled)
     auto make_act = [&](Act &a, int ld) -> bool {
         a.ld = ld;
         if (f32w) {
             a.f32 = (float *)c->mem.get((size_t)cap * ld * 4);
             return a.f32 != nullptr;
         }
-        a.hi = (uint16_t *)c->mem.get((size_t)cap * ld * 2);
-        a.lo = (uint16_t *)c->mem.get((size_t)cap * ld * 2);
+        const size_t rows = ((size_t)cap + 15) / 16 * 16;
+        a.hi = (uint16_t *)c->mem.get(rows * ld * 2);
+        a.lo = (uint16_t *)c->mem.get(rows * ld * 2);
         return a.hi && a.lo;
     };
     c->x = (float *)c->mem.get((size_t)cap * d * 4);
@@ -872,9 +874,6 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         const auto &L = M.layers[il];
         const bool fuse_norm = T <= NORM_TMAX && g_tuning.fuse_norm != 0;
         const bool fuse_norm_ffn = fuse_norm && g_tuning.fuse_norm == 1;
-        if (!fuse_norm)
-            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, actA, stream); });
-
         LinearArgs la;
         la.wtype = M.wtype;
         la.T = T;
@@ -899,6 +898,10 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         la.qkv.type_k = type_k;
         la.qkv.type_v = type_v;
         if (fuse_norm) la.norm = NormIn{x, nullptr, L.attn_norm, hp.rms_eps, d};
+        // the products that read tiled activations get them from their producer tiled
+        la.x.tiled = linear_reads_tiled(la);
+        if (!fuse_norm)
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, la.x, stream); });
         timed(4 + ph, [&] {
             launch_linear(la, stream);
             if (type_k == KV_Q8) {
@@ -930,7 +933,20 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         aa.n_tiles = n_tiles;
         aa.part_o = part_o;
         aa.part_ml = part_ml;
-        aa.out = actB;
+        LinearArgs lo;
+        lo.wtype = M.wtype;
+        lo.T = T;
+        lo.tok = ti;
+        lo.w = L.o.w;
+        lo.wscale = L.o.scales;
+        lo.N = L.o.rows;
+        lo.K = L.o.cols;
+        lo.x = actB;
+        lo.epi = EPI_RESID;
+        lo.y = x;
+        lo.ldy = d;
+        lo.x.tiled = linear_reads_tiled(lo);
+        aa.out = lo.x;
         if (mfma_attn) {
             aa.split = split;
             aa.max_chunks = max_chunks_mfma;
@@ -949,22 +965,8 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
             timed(6 + ph, [&] { launch_attention(aa, stream); });
         }
 
-        LinearArgs lo;
-        lo.wtype = M.wtype;
-        lo.T = T;
-        lo.tok = ti;
-        lo.w = L.o.w;
-        lo.wscale = L.o.scales;
-        lo.N = L.o.rows;
-        lo.K = L.o.cols;
-        lo.x = actB;
-        lo.epi = EPI_RESID;
-        lo.y = x;
-        lo.ldy = d;
         timed(8 + ph, [&] { launch_linear(lo, stream); });
 
-        if (!fuse_norm_ffn)
-            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, actA, stream); });
         LinearArgs lg = lo;
         lg.w = L.gu.w;
         lg.wscale = L.gu.scales;
@@ -972,10 +974,10 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lg.K = L.gu.cols;
         lg.x = actA;
         lg.epi = EPI_SWIGLU;
-        lg.out = actC;
         if (fuse_norm_ffn) lg.norm = NormIn{x, nullptr, L.ffn_norm, hp.rms_eps, d};
-        timed(10 + ph, [&] { launch_linear(lg, stream); });
-
+        lg.x.tiled = linear_reads_tiled(lg);
+        if (!fuse_norm_ffn)
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, lg.x, stream); });
         LinearArgs ld = lo;
         ld.norm = NormIn{};
         ld.w = L.down.w;
@@ -983,6 +985,9 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         ld.N = L.down.rows;
         ld.K = L.down.cols;
         ld.x = actC;
+        ld.x.tiled = linear_reads_tiled(ld);
+        lg.out = ld.x;
+        timed(10 + ph, [&] { launch_linear(lg, stream); });
         timed(12 + ph, [&] { launch_linear(ld, stream); });
         if (dump)
             hip_ok(hipMemcpyAsync(dump + (size_t)(il + 1) * cap * d, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice,
@@ -990,8 +995,6 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     }
     if (n_out > 0) {
         const bool fuse_norm = n_out <= NORM_TMAX && g_tuning.fuse_norm == 1;
-        if (!fuse_norm)
-            timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, actA, stream); });
         LinearArgs lz;
         lz.wtype = M.wtype;
         lz.w = M.out.w;
@@ -1004,6 +1007,9 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lz.row_map = out_lrow();
         lz.logits = logits_dev;
         if (fuse_norm) lz.norm = NormIn{x, ti.out_tok, M.out_norm, hp.rms_eps, d};
+        lz.x.tiled = linear_reads_tiled(lz);
+        if (!fuse_norm)
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, lz.x, stream); });
         timed(14 + ph, [&] { launch_linear(lz, stream); });
     }
     if (!hip_ok(hipGetLastError(), "kernel launch")) return UBD_COMPUTE_FAILED;
@@ -1478,6 +1484,8 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.gemm_wpd = value;
     } else if (k == "gemm_deep") {
         g_tuning.gemm_deep = value;
+    } else if (k == "act_tiled") {
+        g_tuning.act_tiled = value;
     } else if (k == "ldsx") {
         g_tuning.ldsx = value;
     } else if (k == "ldsx_early") {

@@ -40,11 +40,12 @@ def built():
     return out
 
 
-def gpu_logits(model, tokens, gemm, shape=0):
+def gpu_logits(model, tokens, gemm, shape=0, tiled=1):
     from llama_decode_ubatch_amd import Context
     from llama_decode_ubatch_amd.binding import set_tuning
     set_tuning("gemm", gemm)
     set_tuning("gemm_shape", shape)
+    set_tuning("act_tiled", tiled)
     try:
         ctx = Context(model, n_ctx=512, n_batch=512, n_ubatch=512, n_seq_max=1, type_k="f16", type_v="f16")
         assert ctx.decode(tokens, logits=np.ones(len(tokens))) == 0
@@ -52,6 +53,7 @@ def gpu_logits(model, tokens, gemm, shape=0):
     finally:
         set_tuning("gemm", 1)
         set_tuning("gemm_shape", 0)
+        set_tuning("act_tiled", 1)
 
 
 @pytest.mark.parametrize("key", list(SHAPES))
@@ -70,6 +72,8 @@ def test_prefill_gemm_matches_oracle(built, key, n):
     # the other kernel choices (register-staged kernel; LDS-ring kernel with
     # each forced tile shape; the deep-look-ahead kernel's tiles, bf16 only)
     # must sit within the tolerance too
-    for choice in ((0, 0), (1, 1), (1, 2), (1, 3), (1, 4), (1, 7), (1, 8), (1, 9), (1, 10), (1, 11), (1, 12)):
+    # (activations row-major instead of tiled, as well)
+    for choice in ((0, 0), (1, 1), (1, 2), (1, 3), (1, 4), (1, 7), (1, 8), (1, 9), (1, 10), (1, 11), (1, 12),
+                   (1, 0, 0), (1, 10, 0)):
         zc = gpu_logits(model, tokens, *choice)
         assert float(np.abs(zc - zr).max() / np.abs(zr).max()) < TOL[shape.wtype], choice
