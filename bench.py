@@ -24,6 +24,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILES = {
     "decode.ffn_gate_up": os.path.join(ROOT, "profiles", "decode_ffn_gate_up_8b_bf16_traffic.txt"),
     "decode.attention": os.path.join(ROOT, "profiles", "decode_attention_8b_16seq_32k_traffic.txt"),
+    "prefill.ffn_gate_up": os.path.join(ROOT, "profiles", "prefill_ffn_gate_up_8b_bf16_traffic.txt"),
 }
 KERNEL_SRC = os.path.join(ROOT, "llama_decode_ubatch_amd", "csrc", "kernels.hip")
 
@@ -303,7 +304,9 @@ def main():
         avg_s = kernels["decode.ffn_gate_up"]["avg_us"] * 1e-6
         ach = alg / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(hot),
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    # the committed counter summary covers the bf16 configuration
+                    "traffic": measured_traffic(hot) if shape.wtype == "bf16" and w.n_seqs == 1 else None,
                     "kernel": "decode.ffn_gate_up (linear_ldsx_kernel, fused RMSNorm, SwiGLU epilogue)",
                     "bytes_per_launch": int(alg)}
     roofline_prefill = None
@@ -314,7 +317,9 @@ def main():
         roofline_prefill = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                             "kernel": "prefill.ffn_gate_up (gemm_lds_kernel, SwiGLU epilogue)",
-                            "flops_per_launch": flops}
+                            "flops_per_launch": flops,
+                            "traffic": measured_traffic("prefill.ffn_gate_up")
+                            if shape.wtype == "bf16" and w.n_prompt == 512 else None}
 
     cpu = None
     if not args.no_cpu_baseline and shape.wtype != "f32":
