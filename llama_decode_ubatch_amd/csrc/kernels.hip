@@ -2001,6 +2001,11 @@ __device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src
     for (int db = 0; db < DB; ++db) b.v[db] = *(const f16x8_t *)(vt + db * 16 * 32);
 }
 
+// The MFMA attention works in base 2: the query carries log2(e) / sqrt(hd),
+// so scores, the running max m and the chunk maxima are log2-scaled and every
+// exponential is one native 2^x (exp(s - m) = 2^(log2e s - log2e m)).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Scores of the step's 32 cells for the wave's 16 rows, mask, online-softmax
 // update of (m, l) and O += P V.
 template <int HD>
@@ -2033,7 +2038,7 @@ __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m - m_new);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m - m_new);
     float ps = 0.f;
     f16x8_t ph, pl;
 #pragma unroll
@@ -2041,7 +2046,7 @@ __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float sv = S[b2][i];
-            const float p = sv == -INFINITY ? 0.f : expf(sv - m_new);
+            const float p = sv == -INFINITY ? 0.f : exp2_fast(sv - m_new);
             ps += p;
             const _Float16 h = (_Float16)p;
             ph[4 * b2 + i] = h;
@@ -2148,7 +2153,7 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : expf(m - m_new);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m - m_new);
     float pv[8];
     float ps = 0.f;
 #pragma unroll
@@ -2156,7 +2161,7 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float sv = S[b2][i];
-            const float p = sv == -INFINITY ? 0.f : expf(sv - m_new);
+            const float p = sv == -INFINITY ? 0.f : exp2_fast(sv - m_new);
             ps += p;
             pv[4 * b2 + i] = p;
         }
@@ -2218,7 +2223,7 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
         }
         cend = min(nscan, cbeg + NC);
     }
-    const float scale = 1.0f / sqrtf((float)HD);
+    const float scale = 1.44269504088896341f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
     // this lane's query row (S^T layout: row = r)
     const bool row_ok = r < R;
     const int rt = t0 + (row_ok ? r / G : 0), rh = grp * G + (row_ok ? r % G : 0);
@@ -2367,7 +2372,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
         float wgt = 0.f;
         if (c < nch) {
             const float mc = ml[2 * c];
-            wgt = mc == -INFINITY ? 0.f : expf(mc - M);
+            wgt = mc == -INFINITY ? 0.f : exp2_fast(mc - M);
             L += wgt * ml[2 * c + 1];
         }
         const int n = min(64, nch - c0);
