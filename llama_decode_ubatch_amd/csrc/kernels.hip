@@ -651,9 +651,10 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
 // arrived; issued first, it overlaps them.  Each thread keeps at most EVM
 // float4 slices (and the gain's) in registers; longer rows use the copy
 // above.
-constexpr int EVM = 4;
+// (the 2-wave q8_0 gate|up work-groups hold 8: a 4096-long row)
+template <int WT, int NW> constexpr int evm() { return WT == W_Q8 && NW == 2 ? 8 : 4; }
 
-template <int WT, bool NORM>
+template <int WT, bool NORM, int EVM>
 struct EarlyX {
     f32x4_t v[WT == W_F32 || NORM ? EVM : 1];
     f32x4_t gn[NORM ? EVM : 1];
@@ -662,13 +663,14 @@ struct EarlyX {
 
 // one token, a row short enough for the registers, and a whole first
 // weight batch for every wave
-template <int NW, int UB>
+template <int WT, int NW, int UB>
 __device__ __forceinline__ bool ldsx_early_fits(int K, int Tb, int steps) {
-    return Tb == 1 && (K / 4 + 64 * NW - 1) / (64 * NW) <= EVM && steps >= NW * UB;
+    return Tb == 1 && (K / 4 + 64 * NW - 1) / (64 * NW) <= evm<WT, NW>() && steps >= NW * UB;
 }
 
 template <int WT, int NW, bool NORM>
-__device__ __forceinline__ void ldsx_early_load(const LinearArgs &a, int t0, EarlyX<WT, NORM> &x) {
+__device__ __forceinline__ void ldsx_early_load(const LinearArgs &a, int t0, EarlyX<WT, NORM, evm<WT, NW>()> &x) {
+    constexpr int EVM = evm<WT, NW>();
     constexpr int TH = 64 * NW;
     const int tid = threadIdx.x, K = a.K;
     const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
@@ -699,7 +701,8 @@ __device__ __forceinline__ void ldsx_early_load(const LinearArgs &a, int t0, Ear
 }
 
 template <int WT, int NW, bool NORM>
-__device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const EarlyX<WT, NORM> &x) {
+__device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const EarlyX<WT, NORM, evm<WT, NW>()> &x) {
+    constexpr int EVM = evm<WT, NW>();
     constexpr int TH = 64 * NW;
     __shared__ float red_ss[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -794,8 +797,8 @@ void linear_ldsx_kernel(LinearArgs a) {
     // both weight batches go out before the prologue, and each is refilled
     // right after it has been multiplied: two batches stay in flight
     WBatch<WT, RB, UB> bufA, bufB;
-    if (a.early && ldsx_early_fits<NW, UB>(a.K, Tb, steps)) {
-        EarlyX<WT, NORM> x;
+    if (a.early && ldsx_early_fits<WT, NW, UB>(a.K, Tb, steps)) {
+        EarlyX<WT, NORM, evm<WT, NW>()> x;
         ldsx_early_load<WT, NW, NORM>(a, t0, x);
         asm volatile("" ::: "memory");              // activation loads first
         load_wbatch_whole<WT, RB, UB>(a, rb0, s0, lane, bufA);
@@ -1521,6 +1524,8 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
     // 2 waves per SIMD: keep every wave of the launch resident at once (the
     // second round of work-groups otherwise doubles the time)
     if (ldsx_waves_per_eu<WT, EPI>() == 2) nw = blocks >= 768 ? 2 : blocks >= 384 ? 4 : 8;
+    // gate|up pairs with 16 waves would spill registers to scratch
+    if (EPI == EPI_SWIGLU && nw == 16) nw = 8;
     const bool norm = a.norm.x != nullptr;
     // activations of a 16-token block fit in LDS: the LDS-staged kernel
     // activation planes (+ q8_0 block sums)
