@@ -1162,7 +1162,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
             __builtin_amdgcn_sched_barrier(0);
             issue_w(min(s + WPD, st1 - 1), wn, sn);
             issue_x(s + 2);
-            if (Q8) __builtin_amdgcn_sched_barrier(0);
             const u32x4_t *xb = xs + (size_t)(s % C::NX) * C::XF * 64;
 #pragma unroll
             for (int j = 0; j < KH; ++j) {
@@ -1197,7 +1196,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
                     }
                 }
             }
-            if (!Q8) {
+            {
                 // the stage's loads spread over its first products (2 loads, then
                 // 4 products): issued as one burst by every wave after the
                 // barrier, they filled the address queue and held the matrix
