@@ -491,7 +491,9 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * further ahead in rotating register sets, where K / 64 is a multiple of
  * the set count: 7 = 4x8 one stage ahead and 8 = 4x8 three stages ahead
  * with one wave per SIMD, 9 = 2x8, 10 = 2x4, 11 = 4x4 three stages ahead,
- * 12 = 4x16 one stage ahead with one wave per SIMD),
+ * 12 = 4x16 one stage ahead with one wave per SIMD; three stages ahead
+ * with residual products split in two over k through scratch: 13 = 4x4,
+ * 14 = 2x4, 15 = 2x8),
  * "gemm_split"
  * (residual prefill products: 0 = automatic k split, 2 or 4 forced),
  * "small_rb" (1 =

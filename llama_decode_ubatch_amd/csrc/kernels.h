@@ -127,6 +127,8 @@ struct LinearArgs {
     QKVEpi qkv;
     NormIn norm;                      // set: input is x normalised on the fly (T <= NORM_TMAX)
     int early = 1;                    // LDS-staged product: one-token activation loads may go first
+    float *split_out = nullptr;       // RESID prefill products: scratch for k-slice partial sums,
+                                      // [2][T][N] f32 (null: no k split through scratch)
 };
 
 void launch_linear(const LinearArgs &a, hipStream_t s);

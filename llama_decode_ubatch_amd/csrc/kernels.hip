@@ -1253,7 +1253,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 // trip).  OCC = waves per SIMD (1: the accumulators go to the matrix-core
 // registers, leaving room for more sets).  bf16 weights; the stage count
 // K / 64 must be a multiple of D + 1.
-template <int EPI, int RBW, int TB, int D, int OCC>
+// SPLITK > 1 (residual products): work-group k-slice ks of SPLITK stores its
+// partial sums to a.split_out[ks][t][n]; resid_add_splits_kernel then adds
+// the slices to the residual in order (no atomics: the sums do not depend on
+// timing).
+template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_deep_kernel(
     LinearArgs a, int n_wtiles, int n_ttiles) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1261,20 +1265,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     using C = GemmCfg<W_BF16, RBW, TB, KS>;
     constexpr int KH = C::KH, NA = C::NA;
     static_assert(D == 1 || D == 3, "look-ahead");
+    static_assert(SPLITK == 1 || EPI == EPI_RESID, "k split: residual products only");
     __shared__ u32x4_t xs[C::NX * C::XF * 64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int total = n_wtiles * n_ttiles;
+    const int total = n_wtiles * n_ttiles * SPLITK;
     const int b = blockIdx.x;
     const int tile = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
-    const int tt = tile % n_ttiles;
-    const int nt = tile / n_ttiles;
+    const int ks = tile % SPLITK;
+    const int tt = (tile / SPLITK) % n_ttiles;
+    const int nt = tile / (SPLITK * n_ttiles);
     const int nrb = a.N / 16;
     const int rb0 = nt * 4 * RBW + wave * RBW;
     const int t0 = tt * 16 * TB;
-    const int nst = a.K / KS;
+    const int nst_all = a.K / KS;
+    const int sbeg = ks * (nst_all / SPLITK);          // this slice's stages [sbeg, nst)
+    const int nst = sbeg + nst_all / SPLITK;
 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (size_t)a.N * a.K * 2);
     const size_t xbytes = (size_t)(a.x.tiled ? (a.T + 15) / 16 * 16 : a.T) * a.x.ld * 2;
@@ -1348,12 +1356,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     // loads issued after the ones it needs (XW with one stage of look-ahead)
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-        issue_w(k, W[k]);
-        if (k < 2) issue_x(k);
+        issue_w(sbeg + k, W[k]);
+        if (k < 2) issue_x(sbeg + k);
     }
-    if (D == 1) issue_x(1);
+    if (D == 1) issue_x(sbeg + 1);
     __builtin_amdgcn_sched_barrier(0);
-    for (int s = 0; s < nst; s += D + 1) {
+    for (int s = sbeg; s < nst; s += D + 1) {
 #pragma unroll
         for (int k = 0; k <= D; ++k) {
             wait_vm<D == 1 ? C::XW : C::XW + NWL>();
@@ -1377,7 +1385,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         for (int tb = 0; tb < TB; ++tb) {
             const int t = t0 + tb * 16 + r;
             if (t >= a.T) continue;
-            if (EPI == EPI_SWIGLU)
+            if (SPLITK > 1)
+                store4(a.split_out + ((size_t)ks * a.T + t) * a.N + rb * 16 + 4 * g, acc[i][tb]);
+            else if (EPI == EPI_SWIGLU)
                 epilogue4<EPI, false>(a, t, (rb >> 1) * 16 + 4 * g, acc[i][tb], acc[i + 1][tb]);
             else
                 epilogue4<EPI, false>(a, t, rb * 16 + 4 * g, acc[i][tb], acc[i][tb]);
@@ -1386,15 +1396,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #endif
 }
 
-// false (nothing launched) unless the stage count is a multiple of D + 1
-template <int EPI, int RBW, int TB, int D, int OCC>
+// y[t][n] += the k slices' partial sums, slice 0 first
+__global__ __launch_bounds__(256) void resid_add_splits_kernel(float *y, int ldy, const float *parts, int T, int N,
+                                                               int nsplit) {
+    const int n4 = N / 4;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)T * n4) return;
+    const int t = (int)(i / n4), n = (int)(i % n4) * 4;
+    f32x4_t v = *(const f32x4_t *)(parts + (size_t)t * N + n);
+    for (int k = 1; k < nsplit; ++k) v += *(const f32x4_t *)(parts + ((size_t)k * T + t) * N + n);
+    f32x4_t *o = (f32x4_t *)(y + (size_t)t * ldy + n);
+    *o = *o + v;
+}
+
+// false (nothing launched) unless each k slice's stage count is a multiple
+// of D + 1 (and, split, the product is a residual one with scratch for the
+// slices)
+template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1>
 static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
     const int nst = a.K / 64;
-    if (a.K % 64 || nst % (D + 1)) return false;
+    if (a.K % 64 || nst % SPLITK || (nst / SPLITK) % (D + 1)) return false;
+    if (SPLITK > 1 && (EPI != EPI_RESID || !a.split_out || a.N % 4)) return false;
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
-    hipLaunchKernelGGL((gemm_deep_kernel<EPI, RBW, TB, D, OCC>), dim3(n_wtiles * n_ttiles), dim3(256), 0, s, a,
-                       n_wtiles, n_ttiles);
+    hipLaunchKernelGGL((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(256),
+                       0, s, a, n_wtiles, n_ttiles);
+    if (SPLITK > 1) {
+        const long n = (long)a.T * (a.N / 4);
+        hipLaunchKernelGGL(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
+                           a.split_out, a.T, a.N, SPLITK);
+    }
     return true;
 }
 
@@ -1437,6 +1468,9 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     case 10: if (WT == W_BF16 && launch_gemm_deep<EPI, 2, 4, 3, 2>(a, s)) return; break;
     case 11: if (WT == W_BF16 && launch_gemm_deep<EPI, 4, 4, 3, 2>(a, s)) return; break;
     case 12: if (WT == W_BF16 && launch_gemm_deep<EPI, 4, 16, 1, 1>(a, s)) return; break;
+    case 13: if (WT == W_BF16 && launch_gemm_deep<EPI, 4, 4, 3, 2, EPI == EPI_RESID ? 2 : 1>(a, s)) return; break;
+    case 14: if (WT == W_BF16 && launch_gemm_deep<EPI, 2, 4, 3, 2, EPI == EPI_RESID ? 2 : 1>(a, s)) return; break;
+    case 15: if (WT == W_BF16 && launch_gemm_deep<EPI, 2, 8, 3, 2, EPI == EPI_RESID ? 2 : 1>(a, s)) return; break;
     default: break;
     }
     // bf16 products with enough tiles: the deep variant, weights three
@@ -1444,6 +1478,11 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     // FFN down 134.5 -> 108.5 us with 128 x 64 tiles; QKV 62.5 -> 58.2 us
     // with 128 x 128 tiles).  The wide gate|up tile keeps the kernel above.
     if (WT == W_BF16 && g_tuning.gemm_deep != 0) {
+        // long-k residual products (FFN down): 128 x 128 tiles with k split in
+        // two through scratch, slices added in order (down 93 -> 76 us)
+        if (EPI == EPI_RESID && a.K >= 8192 && tiles(2, 8) * 2 >= 192 &&
+            launch_gemm_deep<EPI, 2, 8, 3, 2, EPI == EPI_RESID ? 2 : 1>(a, s))
+            return;
         if (EPI == EPI_RESID && tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2>(a, s)) return;
         if (EPI == EPI_QKV && tiles(4, 8) < 192 && tiles(2, 8) >= 192 && launch_gemm_deep<EPI, 2, 8, 3, 2>(a, s))
             return;

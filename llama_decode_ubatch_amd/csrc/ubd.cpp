@@ -430,6 +430,7 @@ struct ubd_context : public Executor {
     float *x = nullptr, *q = nullptr;
     Act actA, actB, actC;
     float *part_o = nullptr, *part_ml = nullptr;
+    float *split_scratch = nullptr;         // k-slice partial sums of the residual prefill products [2][cap][d]
     int max_chunks = 0;                     // f32-path chunks (ATTN_CHUNK cells)
     int max_chunks_mfma = 0;                // MFMA split-path chunks (ATTN_DECODE_CHUNK cells)
     bool mfma_attn = false;
@@ -643,6 +644,10 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     c->part_ml = (float *)c->mem.get(part_rows * 2 * 4);
 
     if (!c->part_o || !c->part_ml) return bail("attention scratch allocation failed");
+    if (model->wtype == W_BF16 && cap >= 64) {
+        c->split_scratch = (float *)c->mem.get((size_t)2 * cap * d * 4);
+        if (!c->split_scratch) return bail("product scratch allocation failed");
+    }
     std::vector<double> inv(hd / 2);
     for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)hp.rope_freq_base, -2.0 * i / hd);
     c->inv_freq = (double *)c->mem.get(inv.size() * sizeof(double));
@@ -945,6 +950,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lo.epi = EPI_RESID;
         lo.y = x;
         lo.ldy = d;
+        lo.split_out = split_scratch;
         lo.x.tiled = linear_reads_tiled(lo);
         aa.out = lo.x;
         if (mfma_attn) {

@@ -5,7 +5,8 @@ workloads use f32 weights, which never take the MFMA GEMM path) prefill
 prompts of 64, 100 and 200 tokens with every token flagged for output, so
 the QKV, O, gate|up, down and logits products all run as GEMMs with a
 ragged token tail, weight-row tiles that overhang N, k both a multiple of 128
-and not (n_ff 704), and split-k residual products (n_ff 1408).  All logits
+and not (n_ff 704), and split-k residual products (n_ff 1408; n_ff 1536 for
+the split through scratch).  All logits
 are compared with the float64 oracle; the LDS-ring kernel is also compared
 with the register-staged one.
 """
@@ -22,6 +23,10 @@ SHAPES = {
                               n_vocab=1024, n_ctx_train=2048, rope_base=10000.0, wtype="bf16"),
     "bf16-ff704": ModelShape("small-bf16-b", 11, n_layer=2, n_embd=256, n_head=8, n_head_kv=2, n_ff=704,
                              n_vocab=1024, n_ctx_train=2048, rope_base=10000.0, wtype="bf16"),
+    # k = 1536 splits into two slices of 12 stages: the forced deep shapes
+    # then run the residual products split over k through scratch
+    "bf16-ff1536": ModelShape("small-bf16-c", 13, n_layer=2, n_embd=256, n_head=8, n_head_kv=2, n_ff=1536,
+                              n_vocab=1024, n_ctx_train=2048, rope_base=10000.0, wtype="bf16"),
     "q8_0-ff1408": ModelShape("small-q8-a", 12, n_layer=2, n_embd=256, n_head=8, n_head_kv=2, n_ff=1408,
                               n_vocab=1024, n_ctx_train=2048, rope_base=10000.0, wtype="q8_0"),
 }
@@ -73,7 +78,7 @@ def test_prefill_gemm_matches_oracle(built, key, n):
     # each forced tile shape; the deep-look-ahead kernel's tiles, bf16 only)
     # must sit within the tolerance too
     # (activations row-major instead of tiled, as well)
-    for choice in ((0, 0), (1, 1), (1, 2), (1, 3), (1, 4), (1, 7), (1, 8), (1, 9), (1, 10), (1, 11), (1, 12),
+    for choice in ((0, 0), (1, 1), (1, 2), (1, 3), (1, 4), (1, 7), (1, 8), (1, 9), (1, 10), (1, 11), (1, 12), (1, 13), (1, 14), (1, 15),
                    (1, 0, 0), (1, 10, 0)):
         zc = gpu_logits(model, tokens, *choice)
         assert float(np.abs(zc - zr).max() / np.abs(zr).max()) < TOL[shape.wtype], choice
