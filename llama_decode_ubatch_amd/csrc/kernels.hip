@@ -1484,6 +1484,13 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
             launch_gemm_deep<EPI, 2, 8, 3, 2, EPI == EPI_RESID ? 2 : 1>(a, s))
             return;
         if (EPI == EPI_RESID && tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2>(a, s)) return;
+        // QKV: 64 x 64 tiles of the LDS-ring kernel when they give >= 384
+        // work-groups (52.4 against 55.9 us for the deep 128 x 128 tile at 512
+        // tokens), else the deep kernel
+        if (EPI == EPI_QKV && tiles(4, 8) < 192 && tiles(1, 4) >= 384) {
+            launch_gemm_lds<WT, EPI, 1, 4, 1>(a, s);
+            return;
+        }
         if (EPI == EPI_QKV && tiles(4, 8) < 192 && tiles(2, 8) >= 192 && launch_gemm_deep<EPI, 2, 8, 3, 2>(a, s))
             return;
     }
