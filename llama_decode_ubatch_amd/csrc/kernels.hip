@@ -16,6 +16,7 @@ namespace ubd {
 Tuning g_tuning;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -38,6 +39,20 @@ __device__ __forceinline__ uint16_t f2h(float f) {
     uint16_t h;
     __builtin_memcpy(&h, &v, 2);
     return h;
+}
+
+// Activation planes of the LDS-staged decode products: value = hi + lo,
+// bf16 planes for bf16 weights, f16 planes for q8_0 weights (whose codes
+// enter f16 MFMAs).  The f16 planes hold |value| <= 65504.
+template <int WT>
+__device__ __forceinline__ void split_hilo(float y, uint16_t &h, uint16_t &l) {
+    if (WT == W_Q8) {
+        h = f2h(y);
+        l = f2h(y - h2f(h));
+    } else {
+        h = f2bf(y);
+        l = f2bf(y - bf2f(h));
+    }
 }
 
 // element index of activation (token t, value c) in either layout
@@ -103,9 +118,21 @@ __device__ __forceinline__ bf16x8_t u8x8_to_bf16(uint32_t w0, uint32_t w1) {
     return __builtin_convertvector(f, bf16x8_t);
 }
 
+// Offset code u in [1, 255] -> the f16 value 1024 + u: u is the low mantissa
+// byte under the exponent byte 0x64 (2^10, one unit per mantissa step), so
+// one byte permute makes two values.  v_perm_b32 picks bytes 0-3 from its
+// second operand and 4-7 from its first.
+__device__ __forceinline__ f16x8_t u8x8_to_f16_1024(uint32_t w0, uint32_t w1) {
+    u32x4_t r;
+    r[0] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
+    r[1] = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);
+    r[2] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);
+    r[3] = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
+    return __builtin_bit_cast(f16x8_t, r);
+}
+
 template <int WT, int RB>
 struct StepIn {
-    float xs[2];                        // q8 offset path: sums of this lane's token over blocks 2s, 2s+1
     u32x4_t w[RB];
     u32x4_t xh, xl, xh2, xl2;          // bf16: xh/xl; q8: block 0 (xh, xl), block 1 (xh2, xl2); f32: xh
     u32x2_t sc[RB][2];                  // q8 scales of rows 4g..4g+3, blocks 2s, 2s+1
@@ -152,8 +179,8 @@ __device__ __forceinline__ void load_step(const LinearArgs &a, const unsigned ch
     }
 }
 
-// OFS (q8_0): the products take the codes offset by 128 (cheaper to
-// convert), and 128 times the block's activation sum is taken off again.
+// OFS (q8_0, LDS-staged decode products): the codes enter f16 MFMAs
+// against f16 activation planes.
 template <int WT, int RB, bool OFS = false>
 __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc) {
     if (WT == W_F32) {
@@ -173,6 +200,32 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, xh, acc[j], 0, 0, 0);
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, xl, acc[j], 0, 0, 0);
         }
+    } else if (OFS) {
+        // f16 activation planes; each code q becomes the f16 1024 + (q + 128)
+        // by byte permutes, and q again (exact) by one packed f16 subtract
+        const f16x8_t xh0 = __builtin_bit_cast(f16x8_t, in.xh);
+        const f16x8_t xl0 = __builtin_bit_cast(f16x8_t, in.xl);
+        const f16x8_t xh1 = __builtin_bit_cast(f16x8_t, in.xh2);
+        const f16x8_t xl1 = __builtin_bit_cast(f16x8_t, in.xl2);
+        const f16x8_t ofs = (_Float16)1152.0f;
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            const u32x4_t w = in.w[j] ^ 0x80808080u;
+            const f16x8_t A0 = u8x8_to_f16_1024(w[0], w[1]) - ofs;
+            const f16x8_t A1 = u8x8_to_f16_1024(w[2], w[3]) - ofs;
+            f32x4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, xh0, z, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, xl0, d0, 0, 0, 0);
+            f32x4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, xh1, z, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, xl1, d1, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t s0w = in.sc[j][0][i >> 1], s1w = in.sc[j][1][i >> 1];
+                const float s0 = h2f((uint16_t)(s0w >> (16 * (i & 1))));
+                const float s1 = h2f((uint16_t)(s1w >> (16 * (i & 1))));
+                acc[j][i] = fmaf(s1, d1[i], fmaf(s0, d0[i], acc[j][i]));
+            }
+        }
     } else {
         const bf16x8_t xh0 = __builtin_bit_cast(bf16x8_t, in.xh);
         const bf16x8_t xl0 = __builtin_bit_cast(bf16x8_t, in.xl);
@@ -181,10 +234,8 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            const bf16x8_t A0 = OFS ? u8x8_to_bf16(in.w[j][0] ^ 0x80808080u, in.w[j][1] ^ 0x80808080u)
-                                    : i8x8_to_bf16(in.w[j][0], in.w[j][1]);
-            const bf16x8_t A1 = OFS ? u8x8_to_bf16(in.w[j][2] ^ 0x80808080u, in.w[j][3] ^ 0x80808080u)
-                                    : i8x8_to_bf16(in.w[j][2], in.w[j][3]);
+            const bf16x8_t A0 = i8x8_to_bf16(in.w[j][0], in.w[j][1]);
+            const bf16x8_t A1 = i8x8_to_bf16(in.w[j][2], in.w[j][3]);
             f32x4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, xh0, z, 0, 0, 0);
             d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, xl0, d0, 0, 0, 0);
             f32x4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, xh1, z, 0, 0, 0);
@@ -194,10 +245,7 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
                 const uint32_t s0w = in.sc[j][0][i >> 1], s1w = in.sc[j][1][i >> 1];
                 const float s0 = h2f((uint16_t)(s0w >> (16 * (i & 1))));
                 const float s1 = h2f((uint16_t)(s1w >> (16 * (i & 1))));
-                if (OFS)
-                    acc[j][i] += s0 * (d0[i] - 128.0f * in.xs[0]) + s1 * (d1[i] - 128.0f * in.xs[1]);
-                else
-                    acc[j][i] += s0 * d0[i] + s1 * d1[i];
+                acc[j][i] += s0 * d0[i] + s1 * d1[i];
             }
         }
     }
@@ -504,9 +552,6 @@ __device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const un
             if (WT == W_Q8) {
                 in.xh2 = *(const u32x4_t *)(hi + o + 32);
                 in.xl2 = *(const u32x4_t *)(lo + o + 32);
-                const float2 xs = *(const float2 *)((const float *)(lds + 4 * plane) + (size_t)tok * (K / 32) + 2 * (s + u));
-                in.xs[0] = xs.x;
-                in.xs[1] = xs.y;
 #pragma unroll
                 for (int j = 0; j < RB; ++j) {
                     in.sc[j][0] = b.sc[u][j][0];
@@ -582,8 +627,10 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
                         u16x4_t hh, ll;
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
-                            hh[k] = f2bf(y[k]);
-                            ll[k] = f2bf(y[k] - bf2f(hh[k]));
+                            uint16_t h1, l1;
+                            split_hilo<WT>(y[k], h1, l1);
+                            hh[k] = h1;
+                            ll[k] = l1;
                         }
                         *(u16x4_t *)((uint16_t *)lds + o) = hh;
                         *(u16x4_t *)((uint16_t *)lds + plane + o) = ll;
@@ -617,31 +664,23 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
                     const int e = (tid + TH * (i0 + i)) * 4;
                     if (i0 + i >= nv || e >= K) continue;
                     const size_t o = (size_t)t * K + e;
-                    *(u16x4_t *)((uint16_t *)lds + o) = h[i];
-                    *(u16x4_t *)((uint16_t *)lds + plane + o) = l[i];
+                    u16x4_t hh = h[i], ll = l[i];
+                    if (WT == W_Q8) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            uint16_t h1, l1;
+                            split_hilo<WT>(bf2f(h[i][k]) + bf2f(l[i][k]), h1, l1);
+                            hh[k] = h1;
+                            ll[k] = l1;
+                        }
+                    }
+                    *(u16x4_t *)((uint16_t *)lds + o) = hh;
+                    *(u16x4_t *)((uint16_t *)lds + plane + o) = ll;
                 }
             }
         }
     }
     __syncthreads();
-    if (WT == W_Q8) {
-        // per (token, 32-value block): sum of the staged hi + lo values, for
-        // the offset-code products; stored after the two planes
-        float *xsum = (float *)(lds + 4 * plane);
-        const uint16_t *hi = (const uint16_t *)lds, *lo = hi + plane;
-        for (int p = tid; p < Tb * (K / 32); p += TH) {
-            const size_t o = (size_t)p * 32;
-            float acc = 0.f;
-#pragma unroll
-            for (int q = 0; q < 32; q += 8) {
-                const u16x8_t hh = *(const u16x8_t *)(hi + o + q), ll = *(const u16x8_t *)(lo + o + q);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc += bf2f(hh[e]) + bf2f(ll[e]);
-            }
-            xsum[p] = acc;
-        }
-        __syncthreads();
-    }
 }
 
 // One-token variant of the activation copy, split in two so that the
@@ -736,34 +775,30 @@ __device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const 
                 u16x4_t hh, ll;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    hh[k] = f2bf(y[k]);
-                    ll[k] = f2bf(y[k] - bf2f(hh[k]));
+                    uint16_t h1, l1;
+                    split_hilo<WT>(y[k], h1, l1);
+                    hh[k] = h1;
+                    ll[k] = l1;
                 }
                 *(u16x4_t *)((uint16_t *)lds + e) = hh;
                 *(u16x4_t *)((uint16_t *)lds + plane + e) = ll;
             }
         } else {
-            *(u16x4_t *)((uint16_t *)lds + e) = x.h[i];
-            *(u16x4_t *)((uint16_t *)lds + plane + e) = x.l[i];
+            u16x4_t hh = x.h[i], ll = x.l[i];
+            if (WT == W_Q8) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint16_t h1, l1;
+                    split_hilo<WT>(bf2f(x.h[i][k]) + bf2f(x.l[i][k]), h1, l1);
+                    hh[k] = h1;
+                    ll[k] = l1;
+                }
+            }
+            *(u16x4_t *)((uint16_t *)lds + e) = hh;
+            *(u16x4_t *)((uint16_t *)lds + plane + e) = ll;
         }
     }
     __syncthreads();
-    if (WT == W_Q8) {
-        float *xsum = (float *)(lds + 4 * plane);
-        const uint16_t *hi = (const uint16_t *)lds, *lo = hi + plane;
-        for (int p = tid; p < K / 32; p += TH) {
-            const size_t o = (size_t)p * 32;
-            float acc = 0.f;
-#pragma unroll
-            for (int q = 0; q < 32; q += 8) {
-                const u16x8_t hh = *(const u16x8_t *)(hi + o + q), ll = *(const u16x8_t *)(lo + o + q);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc += bf2f(hh[e]) + bf2f(ll[e]);
-            }
-            xsum[p] = acc;
-        }
-        __syncthreads();
-    }
 }
 
 // q8_0 with gate|up pairs (RB 2) needs more than 128 registers: 2 waves per
@@ -1585,8 +1620,8 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
     if (EPI == EPI_SWIGLU && nw == 16) nw = 8;
     const bool norm = a.norm.x != nullptr;
     // activations of a 16-token block fit in LDS: the LDS-staged kernel
-    // activation planes (+ q8_0 block sums)
-    const size_t ldsx = (size_t)4 * std::min(16, a.T) * a.K + (WT == W_Q8 ? (size_t)std::min(16, a.T) * a.K / 8 : 0);
+    // (hi and lo planes)
+    const size_t ldsx = (size_t)4 * std::min(16, a.T) * a.K;
     if (ldsx <= LDSX_MAX_BYTES && g_tuning.ldsx != 0) {
         const size_t bytes = std::max(ldsx, (size_t)16 * 64 * 16 * 2);   // also holds the wave reduction
         LinearArgs la = a;
@@ -2025,7 +2060,6 @@ void launch_attention(const AttnArgs &a, hipStream_t s) {
 // the cell order {4g..4g+3, 16+4g..16+4g+3}, which the V tile supplies as
 // one contiguous 16-byte run per lane.  Online softmax per row; SPLIT writes the
 // range's (m, l, O) for a combine pass, otherwise O / l is stored.
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 template <int HD> struct KVSrc {
