@@ -690,8 +690,7 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
 // arrived; issued first, it overlaps them.  Each thread keeps at most EVM
 // float4 slices (and the gain's) in registers; longer rows use the copy
 // above.
-// (the 2-wave q8_0 gate|up work-groups hold 8: a 4096-long row)
-template <int WT, int NW> constexpr int evm() { return WT == W_Q8 && NW == 2 ? 8 : 4; }
+template <int WT, int NW> constexpr int evm() { return 4; }
 
 template <int WT, bool NORM, int EVM>
 struct EarlyX {
@@ -801,18 +800,15 @@ __device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const 
     __syncthreads();
 }
 
-// q8_0 with gate|up pairs (RB 2) needs more than 128 registers: 2 waves per
-// SIMD for it (at 4 it spilled ~60 registers to scratch, and the spill
-// reloads, counted with the weight loads, stalled every batch: 1.2 TB/s)
-template <int WT, int EPI>
-constexpr int ldsx_waves_per_eu() { return WT == W_Q8 && EPI == EPI_SWIGLU ? 2 : 4; }
-
+// 4 waves per SIMD (at most 128 registers).  q8_0 weight batches hold 2
+// k-steps: with 4 the gate|up pairs needed 2 waves per SIMD, and that was
+// slower (config 5 gate|up 30.9 against 29.7 us).
 template <int WT, int EPI, int NW, bool NORM>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ldsx_waves_per_eu<WT, EPI>())))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4)))
 void linear_ldsx_kernel(LinearArgs a) {
     constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
     constexpr int KSTEP = WT_<WT>::KSTEP;
-    constexpr int UB = WT == W_Q8 ? (RB == 2 ? 4 : 2) : 8 / RB;   // k-steps per weight batch
+    constexpr int UB = WT == W_Q8 ? 2 : 8 / RB;   // k-steps per weight batch
     extern __shared__ __align__(16) unsigned char dyn_lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1613,9 +1609,6 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
     // k-split waves per work-group: about 4096 waves in flight, all resident
     int nw = blocks >= 768 ? 4 : blocks >= 384 ? 8 : 16;
     if (g_tuning.skinny_nw == 4 || g_tuning.skinny_nw == 8 || g_tuning.skinny_nw == 16) nw = g_tuning.skinny_nw;
-    // 2 waves per SIMD: keep every wave of the launch resident at once (the
-    // second round of work-groups otherwise doubles the time)
-    if (ldsx_waves_per_eu<WT, EPI>() == 2) nw = blocks >= 768 ? 2 : blocks >= 384 ? 4 : 8;
     // gate|up pairs with 16 waves would spill registers to scratch
     if (EPI == EPI_SWIGLU && nw == 16) nw = 8;
     const bool norm = a.norm.x != nullptr;
@@ -1633,9 +1626,7 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
         else                                                                                                \
             hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), bytes, s, la); \
     } while (0)
-        if (nw == 2)
-            UBD_LAUNCH_LDSX(2);
-        else if (nw == 4)
+        if (nw == 4)
             UBD_LAUNCH_LDSX(4);
         else if (nw == 8)
             UBD_LAUNCH_LDSX(8);
