@@ -38,7 +38,7 @@ struct Tuning {
     int skinny_nw = 0;        // waves per work-group of the small-T product
     int fuse_norm = 1;        // ubatches of <= 2 tokens: 1 = RMSNorm fused into the QKV, gate|up and
                               // logits products, -1 = into QKV only, 0 = never
-    int attn_chunk_min = 0;   // smallest cells per wave of split attention
+    int attn_chunk_min = 64;  // smallest cells per wave of split attention (>= 32)
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
     int ldsx_early = 1;       // one-token LDS-staged products: activation loads ahead of the weights
     int small_rb = 1;         // several-token products: 4 row blocks per work-group / split k (0 = off)

@@ -958,7 +958,8 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
             aa.max_chunks = max_chunks_mfma;
             // one round of waves: as many chunks as the GPU holds split-kernel
             // waves at once (a second, partial round cost config 4 ~7 %),
-            // shared by the (tile, KV head) pairs; at least 32 cells each
+            // shared by the (tile, KV head) pairs; at least 64 cells each
+            // (short scans: 32-cell chunks cost config 3 decode ~3 %)
             const int pairs = std::max(1, n_tiles * Hk);
             const int per_pair = std::max(1, attn_wave_slots / pairs);
             const int want = (max_scan + per_pair - 1) / per_pair;
