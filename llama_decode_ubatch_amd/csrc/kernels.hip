@@ -106,18 +106,6 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t w0, uint32_t w1) {
     return __builtin_convertvector(f, bf16x8_t);
 }
 
-// Offset codes: q + 128 as an unsigned byte is an integer in [1, 255],
-// exact in bf16, and converts with one instruction per byte.
-__device__ __forceinline__ bf16x8_t u8x8_to_bf16(uint32_t w0, uint32_t w1) {
-    f32x8_t f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[i] = (float)((w0 >> (8 * i)) & 0xffu);
-        f[4 + i] = (float)((w1 >> (8 * i)) & 0xffu);
-    }
-    return __builtin_convertvector(f, bf16x8_t);
-}
-
 // Offset code u in [1, 255] -> the f16 value 1024 + u: u is the low mantissa
 // byte under the exponent byte 0x64 (2^10, one unit per mantissa step), so
 // one byte permute makes two values.  v_perm_b32 picks bytes 0-3 from its
@@ -2209,7 +2197,7 @@ template <int HD>
 __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0, int cend, const bf16x8_t *qh,
                                                    const bf16x8_t *ql, bool row_ok, int rbit, int rpos, int g,
                                                    float &m, float &l, f32x4_t *O) {
-    constexpr int KK = HD / 32, DB = HD / 16;
+    constexpr int KK = HD / 32;
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
     f32x4_t S[2];
 #pragma unroll
