@@ -119,6 +119,12 @@ __device__ __forceinline__ f16x8_t u8x8_to_f16_1024(uint32_t w0, uint32_t w1) {
     return __builtin_bit_cast(f16x8_t, r);
 }
 
+// Element offset of the q8_0 scales of row block rb, k-step s (blocks 2s,
+// 2s+1), lane group g: 8 f16 values, rows 4g..4g+3 of block 2s then of 2s+1.
+__device__ __forceinline__ size_t q8_scale_ofs(int K, int rb, int s, int g) {
+    return (((size_t)rb * (K / 64) + s) * 4 + g) * 8;
+}
+
 template <int WT, int RB>
 struct StepIn {
     u32x4_t w[RB];
@@ -156,12 +162,11 @@ __device__ __forceinline__ void load_step(const LinearArgs &a, const unsigned ch
         if (WT == W_Q8) {
             in.xh2 = tok_ok ? *(const u32x4_t *)(hi + o + 32) : z;
             in.xl2 = tok_ok ? *(const u32x4_t *)(lo + o + 32) : z;
-            const int KB = a.K / 32;
 #pragma unroll
             for (int j = 0; j < RB; ++j) {
-                const size_t b0 = ((size_t)(rb0 + j) * KB + 2 * s) * 16 + 4 * g;
-                in.sc[j][0] = *(const u32x2_t *)(a.wscale + b0);
-                in.sc[j][1] = *(const u32x2_t *)(a.wscale + b0 + 16);
+                const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb0 + j, s, g));
+                in.sc[j][0] = u32x2_t{sv[0], sv[1]};
+                in.sc[j][1] = u32x2_t{sv[2], sv[3]};
             }
         }
     }
@@ -487,9 +492,9 @@ __device__ __forceinline__ void load_wbatch(const LinearArgs &a, int rb0, int s,
             b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
                                                 ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
             if (WT == W_Q8) {
-                const size_t b0 = ((size_t)(rb0 + j) * (a.K / 32) + 2 * (s + u)) * 16 + 4 * g;
-                b.sc[u][j][0] = *(const u32x2_t *)(a.wscale + b0);
-                b.sc[u][j][1] = *(const u32x2_t *)(a.wscale + b0 + 16);
+                const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb0 + j, s + u, g));
+                b.sc[u][j][0] = u32x2_t{sv[0], sv[1]};
+                b.sc[u][j][1] = u32x2_t{sv[2], sv[3]};
             }
         }
     }
@@ -508,9 +513,9 @@ __device__ __forceinline__ void load_wbatch_whole(const LinearArgs &a, int rb0, 
             b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
                                                 ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
             if (WT == W_Q8) {
-                const size_t b0 = ((size_t)(rb0 + j) * (a.K / 32) + 2 * (s + u)) * 16 + 4 * g;
-                b.sc[u][j][0] = *(const u32x2_t *)(a.wscale + b0);
-                b.sc[u][j][1] = *(const u32x2_t *)(a.wscale + b0 + 16);
+                const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb0 + j, s + u, g));
+                b.sc[u][j][0] = u32x2_t{sv[0], sv[1]};
+                b.sc[u][j][1] = u32x2_t{sv[2], sv[3]};
             }
         }
     }
@@ -901,7 +906,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, i
     const int t0 = tt * BT;
     const int nstage = a.K / 64;
     const int st0 = ks * nstage / SPLITK, st1 = (ks + 1) * nstage / SPLITK;
-    const int KB = a.K / 32;
     const u32x4_t z4 = {0u, 0u, 0u, 0u};
 
     f32x4_t acc[4][TB];
@@ -936,9 +940,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, i
                 } else {
                     wr[i][0] = ldg_nt((const u32x4_t *)((const char *)a.w + ((size_t)st * nrb + rb) * 1024 +
                                                        lane * 16));
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        sc[i][j] = *(const u32x2_t *)(a.wscale + ((size_t)rb * KB + 2 * st + j) * 16 + 4 * g);
+                    const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb, st, g));
+                    sc[i][0] = u32x2_t{sv[0], sv[1]};
+                    sc[i][1] = u32x2_t{sv[2], sv[3]};
                 }
             } else {
                 wr[i][0] = wr[i][1] = z4;
@@ -1121,7 +1125,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     for (int i = 0; i < RBW; ++i) {
         const int rbc = min(rb0 + i, nrb - 1);
         woff[i] = rbc * 1024 + lane * 16;
-        soff[i] = (rbc * KB * 16 + 4 * g) * 2;
+        soff[i] = (int)q8_scale_ofs(a.K, rbc, 0, g) * 2;
     }
     const int wstep = nrb * 1024;   // bytes between consecutive k-steps of the weight tiles
 
@@ -1129,7 +1133,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     // stage of look-ahead, used in turn
     u32x4_t wn0[RBW][NA], wn1[RBW][NA];
     u32x2_t sn0[RBW][KH], sn1[RBW][KH];     // ... and q8_0 scales
-    constexpr int NWL = RBW * NA + (Q8 ? RBW * KH : 0);   // weight loads per stage
+    static_assert(!Q8 || KH % 2 == 0, "q8_0 scales load in pairs of 32-blocks");
+    constexpr int NWL = RBW * NA + (Q8 ? RBW * KH / 2 : 0);   // weight loads per stage
     f32x4_t acc[RBW][TB];
 #pragma unroll
     for (int i = 0; i < RBW; ++i)
@@ -1147,8 +1152,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
             for (int i = 0; i < RBW; ++i)
 #pragma unroll
-                for (int j = 0; j < KH; ++j)
-                    sn[i][j] = __builtin_amdgcn_raw_buffer_load_b64(rsc, soff[i], (KH * s + j) * 32, 0);
+                for (int j = 0; j < KH; j += 2) {
+                    // blocks KH s + j and + 1: 64-wide k-step (KH s + j) / 2
+                    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsc, soff[i], (KH * s + j) / 2 * 64, 0);
+                    sn[i][j] = u32x2_t{v[0], v[1]};
+                    sn[i][j + 1] = u32x2_t{v[2], v[3]};
+                }
         }
     };
     // stage s's activation copies into ring slot s % NX (stage clamped)
@@ -2638,17 +2647,20 @@ __global__ __launch_bounds__(256) void relayout_kernel(RelayoutArgs a) {
     }
 }
 
+// q8_0 scales: per 16-row block rb and 64-wide k-step s (blocks 2s, 2s+1),
+// 32 f16 values ordered [g][h][i] = row 4g + i of block 2s + h, so the
+// scales a lane group g needs for one k-step are one 16-byte run.
 __global__ __launch_bounds__(256) void relayout_scales_kernel(RelayoutArgs a) {
-    const int KB = a.K / 32;
+    const int KB = a.K / 32, KP = KB / 2;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t total = (size_t)a.N * KB;
     if (idx >= total) return;
-    const int r = (int)(idx & 15);
-    const size_t rest = idx >> 4;
-    const int b = (int)(rest % KB), rb = (int)(rest / KB);
+    const int i = (int)(idx & 3), h = (int)((idx >> 2) & 1), g = (int)((idx >> 3) & 3);
+    const size_t rest = idx >> 5;
+    const int p = (int)(rest % KP), rb = (int)(rest / KP);
     int si, sr;
-    map_row(a, rb * 16 + r, &si, &sr);
-    a.dst_scales[idx] = a.src[si].scales[(size_t)sr * KB + b];
+    map_row(a, rb * 16 + 4 * g + i, &si, &sr);
+    a.dst_scales[idx] = a.src[si].scales[(size_t)sr * KB + 2 * p + h];
 }
 
 void launch_relayout(int wtype, const RelayoutSrc *src, int n_src, int mode, int K, void *dst,
