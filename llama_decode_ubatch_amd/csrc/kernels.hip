@@ -106,6 +106,11 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t w0, uint32_t w1) {
     return __builtin_convertvector(f, bf16x8_t);
 }
 
+// Weight codes as relaid at load (q + 128, sign bit flipped) -> bf16 q.
+__device__ __forceinline__ bf16x8_t q8w_to_bf16(uint32_t w0, uint32_t w1) {
+    return i8x8_to_bf16(w0 ^ 0x80808080u, w1 ^ 0x80808080u);
+}
+
 // Offset code u in [1, 255] -> the f16 value 1024 + u: u is the low mantissa
 // byte under the exponent byte 0x64 (2^10, one unit per mantissa step), so
 // one byte permute makes two values.  v_perm_b32 picks bytes 0-3 from its
@@ -172,8 +177,8 @@ __device__ __forceinline__ void load_step(const LinearArgs &a, const unsigned ch
     }
 }
 
-// OFS (q8_0, LDS-staged decode products): the codes enter f16 MFMAs
-// against f16 activation planes.
+// OFS (q8_0, LDS-staged decode products): the codes (stored as q + 128)
+// enter f16 MFMAs against f16 activation planes.
 template <int WT, int RB, bool OFS = false>
 __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc) {
     if (WT == W_F32) {
@@ -204,7 +209,7 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            const u32x4_t w = in.w[j] ^ 0x80808080u;
+            const u32x4_t w = in.w[j];         // codes stored as q + 128
             const f16x8_t A0 = u8x8_to_f16_1024(w[0], w[1]) - ofs;
             const f16x8_t A1 = u8x8_to_f16_1024(w[2], w[3]) - ofs;
             f32x4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, xh0, z, 0, 0, 0);
@@ -227,8 +232,8 @@ __device__ __forceinline__ void mfma_step(const StepIn<WT, RB> &in, f32x4_t *acc
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            const bf16x8_t A0 = i8x8_to_bf16(in.w[j][0], in.w[j][1]);
-            const bf16x8_t A1 = i8x8_to_bf16(in.w[j][2], in.w[j][3]);
+            const bf16x8_t A0 = q8w_to_bf16(in.w[j][0], in.w[j][1]);
+            const bf16x8_t A1 = q8w_to_bf16(in.w[j][2], in.w[j][3]);
             f32x4_t d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, xh0, z, 0, 0, 0);
             d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, xl0, d0, 0, 0, 0);
             f32x4_t d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, xh1, z, 0, 0, 0);
@@ -971,8 +976,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, i
                 A[i][0] = __builtin_bit_cast(bf16x8_t, wr[i][0]);
                 A[i][1] = __builtin_bit_cast(bf16x8_t, wr[i][1]);
             } else {
-                A[i][0] = i8x8_to_bf16(wr[i][0][0], wr[i][0][1]);
-                A[i][1] = i8x8_to_bf16(wr[i][0][2], wr[i][0][3]);
+                A[i][0] = q8w_to_bf16(wr[i][0][0], wr[i][0][1]);
+                A[i][1] = q8w_to_bf16(wr[i][0][2], wr[i][0][3]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1209,7 +1214,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
                     for (int i = 0; i < RBW; ++i) {
                         const u32x4_t w = wc[i][j >> 1];
-                        const bf16x8_t A = (j & 1) ? i8x8_to_bf16(w[2], w[3]) : i8x8_to_bf16(w[0], w[1]);
+                        const bf16x8_t A = (j & 1) ? q8w_to_bf16(w[2], w[3]) : q8w_to_bf16(w[0], w[1]);
                         f32x4_t S;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) S[e] = h2f((uint16_t)(sc[i][j][e >> 1] >> (16 * (e & 1))));
@@ -2641,9 +2646,11 @@ __global__ __launch_bounds__(256) void relayout_kernel(RelayoutArgs a) {
         const uint16_t *row = (const uint16_t *)a.src[si].data + (size_t)sr * a.K;
         *(u32x4_t *)dst = *(const u32x4_t *)(row + 32 * s + 8 * g);
     } else {
+        // codes stored as q + 128 (sign bit flipped): the decode products
+        // take them as offset bytes directly (q8w_to_bf16 flips them back)
         const int8_t *row = (const int8_t *)a.src[si].data + (size_t)sr * a.K;
-        *(u32x2_t *)dst = *(const u32x2_t *)(row + 64 * s + 8 * g);
-        *(u32x2_t *)(dst + 8) = *(const u32x2_t *)(row + 64 * s + 32 + 8 * g);
+        *(u32x2_t *)dst = *(const u32x2_t *)(row + 64 * s + 8 * g) ^ 0x80808080u;
+        *(u32x2_t *)(dst + 8) = *(const u32x2_t *)(row + 64 * s + 32 + 8 * g) ^ 0x80808080u;
     }
 }
 

@@ -1,7 +1,8 @@
 """The q8_0 decode products turn each int8 code into an f16 MFMA operand
-without convert instructions: the byte q ^ 0x80 (= q + 128) is placed under
-the f16 exponent byte 0x64 by a byte permute, giving the f16 1024 + q + 128,
-and one packed f16 subtract of 1152 leaves q.  These tests check that
+without convert instructions: the weights hold each code as the byte q ^ 0x80
+(= q + 128, flipped once at load), a byte permute places it under the f16
+exponent byte 0x64, giving the f16 1024 + q + 128, and one packed f16
+subtract of 1152 leaves q.  These tests check that
 arithmetic on the host for every byte, and the permute selectors the kernel
 source uses, with v_perm_b32's byte selection (selector values 0-3 pick bytes
 of the second operand, 4-7 bytes of the first) modelled in Python."""
