@@ -8,7 +8,8 @@ ragged token tail, weight-row tiles that overhang N, k both a multiple of 128
 and not (n_ff 704), and split-k residual products (n_ff 1408; n_ff 1536 for
 the split through scratch).  All logits
 are compared with the float64 oracle; the LDS-ring kernel is also compared
-with the register-staged one.
+with the register-staged one.  Ubatches of 1, 2, 5 and 16 tokens run the
+same models through the decode products instead.
 """
 import numpy as np
 import pytest
@@ -82,3 +83,23 @@ def test_prefill_gemm_matches_oracle(built, key, n):
                    (1, 0, 0), (1, 10, 0)):
         zc = gpu_logits(model, tokens, *choice)
         assert float(np.abs(zc - zr).max() / np.abs(zr).max()) < TOL[shape.wtype], choice
+
+
+@pytest.mark.parametrize("key", list(SHAPES))
+@pytest.mark.parametrize("n", [1, 2, 5, 16])
+def test_few_token_products_match_oracle(built, key, n):
+    """Fewer than 64 tokens take the decode products instead of the GEMMs:
+    the LDS-staged kernel where a 16-token block's activations fit its stage
+    (k = 256 here; the RMSNorm fused into it for at most 2 tokens) and the
+    kernel that reads the activations from L2 otherwise (the down product,
+    k = n_ff).  Every logits row is compared with the float64 oracle."""
+    shape, tens, model = built[key]
+    tokens = rand_tokens(n, shape.n_vocab, seed=2000 + n)
+    z = gpu_logits(model, tokens, 1)
+    ref = oracle_ctx(shape, tens, np.float64, n_ctx=512, n_batch=512, n_ubatch=512, type_k="f16", type_v="f16")
+    from oracle import Batch
+    assert ref.decode(Batch(tokens, logits=[1] * n)) == 0
+    zr = np.stack([ref.logits_ith(i) for i in range(n)])
+    err = float(np.abs(z - zr).max() / np.abs(zr).max())
+    print(f"{key} T={n}: logits rel err {err:.2e}", flush=True)
+    assert err < TOL[shape.wtype]
