@@ -113,17 +113,20 @@ def test_unified_interleaved_sequences(tiny):
         assert rel_err(ctx.logits(), ref.logits) < TOL
 
 
-def test_ragged_sequences_split_attention(tiny):
+@pytest.mark.parametrize("kv, tol", [("f16", TOL), ("q8_0", 2e-3)])
+def test_ragged_sequences_split_attention(tiny, kv, tol):
     """Three sequences of 20, 150 and 300 cells decode one token each in one
-    ubatch: the split attention launches chunks for the longest scan, so the
-    shorter sequences' tiles carry empty chunks (m = -inf, l = 0) into the
-    combine.  Unified and per-sequence KV streams."""
+    ubatch: the split attention launches chunks for the longest scan, so with
+    per-sequence KV streams the shorter sequences' tiles carry empty chunks
+    (m = -inf, l = 0) into the combine; the unified stream scans all cells
+    with masks.  f16 and q8_0 caches (the q8_0 tolerance is that of the other
+    q8_0 cache tests)."""
     rng = np.random.default_rng(11)
     V = WORKLOADS[1].model.n_vocab
     lens = [20, 150, 300]
     for unified in (True, False):
         ctx, ref = make(tiny, n_ctx=1536, n_batch=512, n_ubatch=512, n_seq_max=3, kv_unified=unified,
-                        type_k="f16", type_v="f16")
+                        type_k=kv, type_v=kv)
         for s, n in enumerate(lens):
             toks = rng.integers(0, V, n)
             assert ctx.decode(toks, seq_id=np.full(n, s)) == 0
@@ -131,8 +134,9 @@ def test_ragged_sequences_split_attention(tiny):
         nxt = rng.integers(0, V, 3)
         assert ctx.decode(nxt, seq_id=[0, 1, 2], logits=[1, 1, 1]) == 0
         assert ref.decode(Batch(nxt, seq_id=[0, 1, 2], logits=[1, 1, 1])) == 0
-        assert rel_err(ctx.logits(), ref.logits) < TOL
-        assert [ctx.greedy(i) for i in range(3)] == [int(np.argmax(ref.logits[i])) for i in range(3)]
+        assert rel_err(ctx.logits(), ref.logits) < tol
+        if kv == "f16":
+            assert [ctx.greedy(i) for i in range(3)] == [int(np.argmax(ref.logits[i])) for i in range(3)]
 
 
 def test_return_codes_abort_and_rollback(tiny):
