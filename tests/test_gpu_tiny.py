@@ -139,6 +139,24 @@ def test_ragged_sequences_split_attention(tiny, kv, tol):
             assert [ctx.greedy(i) for i in range(3)] == [int(np.argmax(ref.logits[i])) for i in range(3)]
 
 
+def test_long_scan_many_chunks(tiny):
+    """One sequence of 4200 cells, then a one-token decode: the split
+    attention cuts the scan into 66 chunks of 64 cells, so the combine pass
+    takes them in two groups (64, then 2)."""
+    rng = np.random.default_rng(12)
+    V = WORKLOADS[1].model.n_vocab
+    ctx, ref = make(tiny, n_ctx=4608, n_batch=512, n_ubatch=512, type_k="f16", type_v="f16")
+    toks = rng.integers(0, V, 4200)
+    for i in range(0, toks.size, 512):
+        assert ctx.decode(toks[i:i + 512]) == 0
+        assert ref.decode(Batch(toks[i:i + 512])) == 0
+    nxt = [int(rng.integers(0, V))]
+    assert ctx.decode(nxt, logits=[1]) == 0
+    assert ref.decode(Batch(nxt, logits=[1])) == 0
+    assert rel_err(ctx.logits(), ref.logits) < TOL
+    assert ctx.greedy(0) == int(np.argmax(ref.logits[0]))
+
+
 def test_return_codes_abort_and_rollback(tiny):
     from llama_decode_ubatch_amd import Context
     shape, tens, model, om = tiny
