@@ -447,19 +447,14 @@ int32_t Planner::decode(const ubd_batch &b, Executor *ex, std::string *err) {
         split_simple(c);
     else
         split_equal(c);
+    // The decode-loop page ("KV cache details") compacts the cache and
+    // searches again after a failed search.  This search takes any free cell
+    // of the stream and compaction keeps the count of free cells, so that
+    // second search cannot succeed: return at once, nothing changed.
     if (!cells.find_slots(ubatches)) {
-        // compact the cache once and search again
-        rc = defrag(ex);
-        if (rc < 0) {
-            if (err) *err = "KV defrag failed";
-            ubatches.clear();
-            return rc;
-        }
-        if (!cells.find_slots(ubatches)) {
-            if (err) *err = "no KV slot for the batch";
-            ubatches.clear();
-            return UBD_NO_KV_SLOT;
-        }
+        if (err) *err = "no KV slot for the batch";
+        ubatches.clear();
+        return UBD_NO_KV_SLOT;
     }
     const int32_t n = b.n_tokens;
     out_row.assign(n, -1);

@@ -186,7 +186,7 @@ class OracleContext:
         index (test hooks)."""
         hp = self.model.hp
         plan = plan_batch(batch, self.mem, hp.n_vocab, self.n_seq_max,
-                          self.n_batch, self.n_ubatch, on_defrag=self._move_cells)
+                          self.n_batch, self.n_ubatch)
         self.last_plan = plan
         self.logits, self.out_row, self.n_outputs = None, None, 0
         if plan.rc != RC_OK:

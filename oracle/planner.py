@@ -371,21 +371,21 @@ class Plan:
 
 
 def plan_batch(batch: Batch, mem: KVMemory, n_vocab: int, n_seq_max: int,
-               n_batch: int, n_ubatch: int, on_defrag=None) -> Plan:
-    """Sanitise, split and find slots.  ``mem`` changes only when the slot
-    search fails: then the cache is defragmented (``on_defrag(src)`` sees
-    the moves) and the search runs once more."""
+               n_batch: int, n_ubatch: int) -> Plan:
+    """Sanitise, split and find slots; ``mem`` is not changed.
+
+    The decode-loop page ("KV cache details") compacts a fragmented cache
+    and searches again when no slot is found.  The slot search here takes
+    any free cell of the stream, and compaction keeps the number of free
+    cells, so a second search cannot succeed: a failed search returns
+    RC_NO_SLOT with the cache as it was (compaction stays available as
+    KVMemory.defrag)."""
     rc, sb = sanitize(batch, n_vocab, n_seq_max, n_batch, mem)
     if rc != RC_OK:
         return Plan(rc)
     ubs = split_simple(sb, n_ubatch) if mem.n_stream == 1 else split_equal(sb, n_ubatch)
     assert sum(u.n_tokens for u in ubs) == sb.token.size
     cells = mem.find_slots(ubs)
-    if cells is None:
-        src = mem.defrag()
-        if on_defrag is not None:
-            on_defrag(src)
-        cells = mem.find_slots(ubs)
     if cells is None:
         return Plan(RC_NO_SLOT)
     out_row = np.full(sb.token.size, -1, np.int64)

@@ -143,19 +143,25 @@ def test_defrag_moves_rows_and_keeps_logits(tiny, kv, unified):
     assert decode_both(ctx, ref, [5, 6], seq_id=[1, 1], logits=[1, 1], tol=tol) == 0
 
 
-def test_full_cache_compacts_then_returns_1(tiny):
-    """A batch with no room: the search fails, the cache is compacted (K/V
-    moved along) and searched again, still no room -> 1; decoding goes on
-    correctly in the compacted cache."""
+def test_full_cache_returns_1_and_changes_nothing(tiny):
+    """A batch with no room in a fragmented cache returns 1 and leaves the
+    cache as it was: cell tables, K/V rows and the logits of a following
+    decode equal those of the oracle, which never ran the failed batch."""
     shape = tiny[0]
     ctx, ref = make(tiny, n_ctx=256, n_batch=256, n_ubatch=64, n_seq_max=2, kv_unified=True,
                     type_k="f16", type_v="f16")
     rng = np.random.default_rng(10)
     toks = rng.integers(0, shape.n_vocab, 200).tolist()
     assert decode_both(ctx, ref, toks, seq_id=[0, 1] * 100, logits=[0] * 199 + [1]) == 0
+    # sequence 1 keeps positions < 50: the free cells are scattered
     assert ctx.seq_rm(1, 50, -1) and ref.seq_rm(1, 50, -1)
-    assert decode_both(ctx, ref, [3] * 120, seq_id=[0] * 120) == 1
-    assert ref.last_defrag_src is not None
+    before = ctx.cells(0)
+    k_before = ctx.kv_read(0, 0, 0, 0, 256)
+    assert ctx.decode([3] * 120, seq_id=[0] * 120) == 1
+    assert ref.decode(Batch([3] * 120, seq_id=[0] * 120)) == 1
+    assert all(np.array_equal(a, b) for a, b in zip(before, ctx.cells(0)))
+    assert np.array_equal(k_before, ctx.kv_read(0, 0, 0, 0, 256))
+    same_tables(ctx, ref)
     assert decode_both(ctx, ref, [4] * 6, seq_id=[0, 1] * 3, logits=[1] * 6) == 0
 
 

@@ -18,8 +18,7 @@ class OraclePlanner:
         self.plan = None
 
     def decode(self, batch, fail_at=-1, fail_code=0):
-        p = plan_batch(batch, self.mem, self.n_vocab, self.n_seq_max, self.n_batch, self.n_ubatch,
-                       on_defrag=lambda src: None)
+        p = plan_batch(batch, self.mem, self.n_vocab, self.n_seq_max, self.n_batch, self.n_ubatch)
         self.plan = p
         if p.rc != 0:
             return p.rc
