@@ -131,7 +131,12 @@ struct LinearArgs {
                                       // [2][T][N] f32 (null: no k split through scratch)
 };
 
-void launch_linear(const LinearArgs &a, hipStream_t s);
+// Enqueues y = W x with the epilogue a.epi.  Returns false, launching
+// nothing, when a fused norm is asked for outside linear_norm_fits.
+bool launch_linear(const LinearArgs &a, hipStream_t s);
+// True when a product over T input rows of K values can take its RMSNorm
+// fused (a.norm): few rows, whose normalised copy fits the LDS stage.
+bool linear_norm_fits(int T, int K);
 // True when launch_linear(a) runs a product that reads its input activations
 // in the tiled layout (the LDS-ring prefill products); the producer of a.x
 // must then write that layout.

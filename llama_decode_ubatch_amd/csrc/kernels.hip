@@ -43,16 +43,29 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 
 // Activation planes of the LDS-staged decode products: value = hi + lo,
 // bf16 planes for bf16 weights, f16 planes for q8_0 weights (whose codes
-// enter f16 MFMAs).  The f16 planes hold |value| <= 65504.
+// enter f16 MFMAs).  The f16 planes hold |value| <= F16_PLANE_MAX; `big`
+// records a value beyond it (the product then rescales its rows, see
+// ldsx_rescale).
+constexpr float F16_PLANE_MAX = 65504.f;
 template <int WT>
-__device__ __forceinline__ void split_hilo(float y, uint16_t &h, uint16_t &l) {
+__device__ __forceinline__ void split_hilo(float y, uint16_t &h, uint16_t &l, int &big) {
     if (WT == W_Q8) {
+        big |= fabsf(y) > F16_PLANE_MAX;
         h = f2h(y);
         l = f2h(y - h2f(h));
     } else {
         h = f2bf(y);
         l = f2bf(y - bf2f(h));
     }
+}
+
+// Barrier that publishes the activation copy; for q8_0 it also tells every
+// thread whether any thread saw a value beyond the f16 planes.
+template <int WT>
+__device__ __forceinline__ int copy_barrier(int big) {
+    if (WT == W_Q8) return __syncthreads_or(big);
+    __syncthreads();
+    return 0;
 }
 
 // element index of activation (token t, value c) in either layout
@@ -566,8 +579,9 @@ __device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const un
 // of a chunk are issued together and waited for once (a per-slice loop
 // waited for every load, and so for the weight batches issued before it).
 template <int WT, int NW, bool NORM>
-__device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, int Tb) {
+__device__ int ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, int Tb) {
     constexpr int TH = 64 * NW, CH = 4;
+    int big = 0;
     __shared__ float red_ss[16][NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K;
@@ -626,7 +640,7 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
                             uint16_t h1, l1;
-                            split_hilo<WT>(y[k], h1, l1);
+                            split_hilo<WT>(y[k], h1, l1, big);
                             hh[k] = h1;
                             ll[k] = l1;
                         }
@@ -667,7 +681,7 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
                             uint16_t h1, l1;
-                            split_hilo<WT>(bf2f(h[i][k]) + bf2f(l[i][k]), h1, l1);
+                            split_hilo<WT>(bf2f(h[i][k]) + bf2f(l[i][k]), h1, l1, big);
                             hh[k] = h1;
                             ll[k] = l1;
                         }
@@ -678,7 +692,7 @@ __device__ void ldsx_prologue(const LinearArgs &a, unsigned char *lds, int t0, i
             }
         }
     }
-    __syncthreads();
+    return copy_barrier<WT>(big);
 }
 
 // One-token variant of the activation copy, split in two so that the
@@ -737,9 +751,10 @@ __device__ __forceinline__ void ldsx_early_load(const LinearArgs &a, int t0, Ear
 }
 
 template <int WT, int NW, bool NORM>
-__device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const EarlyX<WT, NORM, evm<WT, NW>()> &x) {
+__device__ int ldsx_early_store(const LinearArgs &a, unsigned char *lds, const EarlyX<WT, NORM, evm<WT, NW>()> &x) {
     constexpr int EVM = evm<WT, NW>();
     constexpr int TH = 64 * NW;
+    int big = 0;
     __shared__ float red_ss[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K;
@@ -773,7 +788,7 @@ __device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const 
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     uint16_t h1, l1;
-                    split_hilo<WT>(y[k], h1, l1);
+                    split_hilo<WT>(y[k], h1, l1, big);
                     hh[k] = h1;
                     ll[k] = l1;
                 }
@@ -786,7 +801,7 @@ __device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const 
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     uint16_t h1, l1;
-                    split_hilo<WT>(bf2f(x.h[i][k]) + bf2f(x.l[i][k]), h1, l1);
+                    split_hilo<WT>(bf2f(x.h[i][k]) + bf2f(x.l[i][k]), h1, l1, big);
                     hh[k] = h1;
                     ll[k] = l1;
                 }
@@ -795,7 +810,84 @@ __device__ void ldsx_early_store(const LinearArgs &a, unsigned char *lds, const 
             *(u16x4_t *)((uint16_t *)lds + plane + e) = ll;
         }
     }
-    __syncthreads();
+    return copy_barrier<WT>(big);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// q8_0 products whose activation copy met a value beyond the f16 planes
+// (rare: only rows of very large activations).  Every row is formed again
+// from its source, then stored scaled by 2^-e(t), with e(t) >= 0 the
+// smallest exponent that brings the row's largest magnitude to at most
+// 2^15; xs[t] = 2^e(t), by which the epilogue multiplies the token's sums.
+// Scaling by a power of two is exact, so the products stay those of the
+// unscaled values.
+template <int NW, bool NORM>
+__device__ __forceinline__ void ldsx_rescale(const LinearArgs &a, unsigned char *lds, int t0, int Tb, float *xs) {
+    constexpr int TH = 64 * NW;
+    __shared__ float red[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K;
+    const size_t plane = (size_t)Tb * K;
+    for (int t = 0; t < Tb; ++t) {
+        const float *xr = NORM ? a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[t0 + t] : t0 + t) * a.norm.ld
+                               : nullptr;
+        float inv = 1.f;
+        if (NORM) {
+            float ss = 0.f;
+            for (int e = tid * 4; e < K; e += TH * 4) {
+                const f32x4_t v = *(const f32x4_t *)(xr + e);
+                ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+            }
+            ss = wave_sum(ss);
+            if (lane == 0) red[wave] = ss;
+            __syncthreads();
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) tot += red[w];
+            inv = 1.0f / sqrtf(tot / (float)K + a.norm.eps);
+            __syncthreads();
+        }
+        auto row4 = [&](int e) -> f32x4_t {
+            if (NORM) return *(const f32x4_t *)(xr + e) * inv * *(const f32x4_t *)(a.norm.gain + e);
+            const size_t src = (size_t)(t0 + t) * a.x.ld + e;
+            const u16x4_t h = *(const u16x4_t *)(a.x.hi + src), l = *(const u16x4_t *)(a.x.lo + src);
+            return f32x4_t{bf2f(h[0]) + bf2f(l[0]), bf2f(h[1]) + bf2f(l[1]), bf2f(h[2]) + bf2f(l[2]),
+                           bf2f(h[3]) + bf2f(l[3])};
+        };
+        float m = 0.f;
+        for (int e = tid * 4; e < K; e += TH * 4) {
+            const f32x4_t y = row4(e);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))));
+        }
+        m = wave_max(m);
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        float mx = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red[w]);
+        int ex = 0;
+        if (mx < INFINITY) (void)frexpf(mx, &ex);   // mx = f * 2^ex, f in [0.5, 1)
+        const int sh = max(0, ex - 15);
+        const float down = ldexpf(1.f, -sh);
+        if (tid == 0) xs[t] = ldexpf(1.f, sh);
+        for (int e = tid * 4; e < K; e += TH * 4) {
+            const f32x4_t y = row4(e) * down;
+            u16x4_t hh, ll;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                hh[k] = f2h(y[k]);
+                ll[k] = f2h(y[k] - h2f(hh[k]));
+            }
+            *(u16x4_t *)((uint16_t *)lds + (size_t)t * K + e) = hh;
+            *(u16x4_t *)((uint16_t *)lds + plane + (size_t)t * K + e) = ll;
+        }
+        __syncthreads();
+    }
 }
 
 // 4 waves per SIMD (at most 128 registers).  q8_0 weight batches hold 2
@@ -826,17 +918,26 @@ void linear_ldsx_kernel(LinearArgs a) {
     // both weight batches go out before the prologue, and each is refilled
     // right after it has been multiplied: two batches stay in flight
     WBatch<WT, RB, UB> bufA, bufB;
+    int big;                                        // q8_0: a value beyond the f16 planes
     if (a.early && ldsx_early_fits<WT, NW, UB>(a.K, Tb, steps)) {
         EarlyX<WT, NORM, evm<WT, NW>()> x;
         ldsx_early_load<WT, NW, NORM>(a, t0, x);
         asm volatile("" ::: "memory");              // activation loads first
         load_wbatch_whole<WT, RB, UB>(a, rb0, s0, lane, bufA);
         if (s0 + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s0 + UB, s1, steps, lane, bufB);
-        ldsx_early_store<WT, NW, NORM>(a, dyn_lds, x);
+        big = ldsx_early_store<WT, NW, NORM>(a, dyn_lds, x);
     } else {
         if (s0 < s1) load_wbatch<WT, RB, UB>(a, rb0, s0, s1, steps, lane, bufA);
         if (s0 + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s0 + UB, s1, steps, lane, bufB);
-        ldsx_prologue<WT, NW, NORM>(a, dyn_lds, t0, Tb);
+        big = ldsx_prologue<WT, NW, NORM>(a, dyn_lds, t0, Tb);
+    }
+    __shared__ float xs[WT == W_Q8 ? 16 : 1];      // per-token scale of a rescaled copy
+    if (WT == W_Q8 && big) {
+        ldsx_rescale<NW, NORM>(a, dyn_lds, t0, Tb, xs);
+        // both batches are requested again: their first copies are then dead
+        // during the rescale, which can use their registers
+        if (s0 < s1) load_wbatch<WT, RB, UB>(a, rb0, s0, s1, steps, lane, bufA);
+        if (s0 + UB < s1) load_wbatch<WT, RB, UB>(a, rb0, s0 + UB, s1, steps, lane, bufB);
     }
     for (int s = s0; s < s1; s += 2 * UB) {
         mul_wbatch<WT, RB, UB>(bufA, dyn_lds, Tb, a.K, s, s1, lane, tok, tok_ok, acc);
@@ -861,6 +962,11 @@ void linear_ldsx_kernel(LinearArgs a) {
             for (int j = 0; j < RB; ++j) acc[j] += red[(w * RB + j) * 64 + lane];
     }
     if (!tok_ok) return;
+    if (WT == W_Q8 && big) {
+        const float f = xs[r];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) acc[j] *= f;
+    }
     const int t = t0 + r;
     if (EPI == EPI_SWIGLU)
         epilogue4<EPI, false>(a, t, blockIdx.x * 16 + 4 * g, acc[0], acc[RB - 1]);
@@ -1700,15 +1806,22 @@ bool linear_reads_tiled(const LinearArgs &a) {
            a.K % 64 == 0 && !(a.epi == EPI_SWIGLU && a.N % 32) && a.norm.x == nullptr && a.N > 0;
 }
 
-void launch_linear(const LinearArgs &a, hipStream_t s) {
-    if (a.T <= 0 || a.N <= 0) return;
-    if (a.norm.x && a.T > NORM_TMAX) return;   // caller contract: fused norm only for few rows
-    if (a.norm.x && (size_t)4 * a.T * a.K > LDSX_MAX_BYTES) return;
+bool linear_norm_fits(int T, int K) {
+    // the LDS-staged kernel holds T rows of K values (hi + lo planes or f32);
+    // the register-staged one (ldsx off) keeps K <= 8192 values per row
+    return T >= 1 && T <= NORM_TMAX && (size_t)4 * T * K <= LDSX_MAX_BYTES && (g_tuning.ldsx != 0 || K <= 8192);
+}
+
+bool launch_linear(const LinearArgs &a, hipStream_t s) {
+    if (a.T <= 0 || a.N <= 0) return true;
+    if (a.norm.x && !linear_norm_fits(a.T, a.K)) return false;
     switch (a.wtype) {
     case W_F32: launch_linear_wt<W_F32>(a, s); break;
     case W_BF16: launch_linear_wt<W_BF16>(a, s); break;
     case W_Q8: launch_linear_wt<W_Q8>(a, s); break;
+    default: return false;
     }
+    return true;
 }
 
 // ------------------------------------------------------------ embedding

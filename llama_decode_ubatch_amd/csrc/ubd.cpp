@@ -871,13 +871,14 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     const TokInfo ti = tok_info();
     const int n_cells = (int)cell_stride;   // per-stream stride of the device KV and cell tables
     const int ph = T > 16 ? 1 : 0;
+    bool launched = true;     // every product accepted its arguments
     timed(0 + ph, [&] { launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, inv_freq,
                                        hd / 2, rope_cs, stream); });
     if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, stream), "dump");
 
     for (int il = 0; il < hp.n_layer; ++il) {
         const auto &L = M.layers[il];
-        const bool fuse_norm = T <= NORM_TMAX && g_tuning.fuse_norm != 0;
+        const bool fuse_norm = g_tuning.fuse_norm != 0 && linear_norm_fits(T, d);
         const bool fuse_norm_ffn = fuse_norm && g_tuning.fuse_norm == 1;
         LinearArgs la;
         la.wtype = M.wtype;
@@ -908,7 +909,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         if (!fuse_norm)
             timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, la.x, stream); });
         timed(4 + ph, [&] {
-            launch_linear(la, stream);
+            launched &= launch_linear(la, stream);
             if (type_k == KV_Q8) {
                 // the epilogue staged the f32 K / V rows: quantise them into their cells
                 const int ne = Hk * hd;
@@ -972,7 +973,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
             timed(6 + ph, [&] { launch_attention(aa, stream); });
         }
 
-        timed(8 + ph, [&] { launch_linear(lo, stream); });
+        timed(8 + ph, [&] { launched &= launch_linear(lo, stream); });
 
         LinearArgs lg = lo;
         lg.w = L.gu.w;
@@ -994,14 +995,14 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         ld.x = actC;
         ld.x.tiled = linear_reads_tiled(ld);
         lg.out = ld.x;
-        timed(10 + ph, [&] { launch_linear(lg, stream); });
-        timed(12 + ph, [&] { launch_linear(ld, stream); });
+        timed(10 + ph, [&] { launched &= launch_linear(lg, stream); });
+        timed(12 + ph, [&] { launched &= launch_linear(ld, stream); });
         if (dump)
             hip_ok(hipMemcpyAsync(dump + (size_t)(il + 1) * cap * d, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice,
                                   stream), "dump");
     }
     if (n_out > 0) {
-        const bool fuse_norm = n_out <= NORM_TMAX && g_tuning.fuse_norm == 1;
+        const bool fuse_norm = g_tuning.fuse_norm == 1 && linear_norm_fits(n_out, d);
         LinearArgs lz;
         lz.wtype = M.wtype;
         lz.w = M.out.w;
@@ -1017,7 +1018,11 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         lz.x.tiled = linear_reads_tiled(lz);
         if (!fuse_norm)
             timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, lz.x, stream); });
-        timed(14 + ph, [&] { launch_linear(lz, stream); });
+        timed(14 + ph, [&] { launched &= launch_linear(lz, stream); });
+    }
+    if (!launched) {
+        set_err("decode: a matrix product was given a fused norm outside its limits");
+        return UBD_COMPUTE_FAILED;
     }
     if (!hip_ok(hipGetLastError(), "kernel launch")) return UBD_COMPUTE_FAILED;
     perf.n_ubatch += 1;

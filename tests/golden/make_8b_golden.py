@@ -2,13 +2,16 @@
 
 Runs only oracle/ (NumPy, float32 with exactly upcast / dequantised
 weights) on the seeded synthetic inputs of workloads/ and stores, per
-workload, the greedy token sequence and, for every step, the top-16 logits
-and the logits at 256 fixed vocabulary indices.  The GPU tests teacher-force
+workload, the greedy token sequence and, for every step, the top-64 logits
+and the logits at 4096 fixed vocabulary indices.  The GPU tests teacher-force
 these tokens and compare.  No value here comes from the GPU path.
 
-    python tests/golden/make_8b_golden.py [--steps N] [--configs 3 5 4]
+    python tests/golden/make_8b_golden.py [--configs 3 5 4]
 
-Needs about 40 GB of host memory and tens of minutes of CPU time.
+By default every step of each workload is recorded: the prefill logits and
+all 128 (512-token prompt) or 256 (256-token prompt) decode steps, and four
+of the sixteen pre-filled sequences over all 64 steps.  Needs about 40 GB of
+host memory and a few hours of CPU time.
 """
 import argparse
 import os
@@ -25,8 +28,9 @@ from workloads import (WORKLOADS, gen_tensor, gen_tensor_rows, prompt_tokens,  #
                        kv_prefill_block)
 
 OUT_DIR = os.path.dirname(os.path.abspath(__file__))
-N_SAMPLE = 256
-TOPK = 16
+N_SAMPLE = 4096
+TOPK = 64
+MULTI_SEQS = (0, 5, 9, 15)
 
 
 def sample_indices(n_vocab):
@@ -106,18 +110,19 @@ def run_multi(cfg, steps, seqs, log):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--steps", type=int, default=24)
-    ap.add_argument("--multi-steps", type=int, default=6)
+    ap.add_argument("--steps", type=int, default=0, help="decode steps (0: the workload's own count)")
+    ap.add_argument("--multi-steps", type=int, default=0, help="steps with pre-filled KV (0: all)")
     ap.add_argument("--configs", type=int, nargs="+", default=[3, 5, 4])
     args = ap.parse_args()
 
     def log(m):
         print(time.strftime("%H:%M:%S"), m, flush=True)
     for cfg in args.configs:
-        if WORKLOADS[cfg].kv_prefill:
-            run_multi(cfg, args.multi_steps, [0, 9], log)
+        w = WORKLOADS[cfg]
+        if w.kv_prefill:
+            run_multi(cfg, args.multi_steps or w.n_decode, list(MULTI_SEQS), log)
         else:
-            run_single(cfg, args.steps, log)
+            run_single(cfg, args.steps or w.n_decode, log)
 
 
 if __name__ == "__main__":
