@@ -499,9 +499,15 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * (residual prefill products: 0 = automatic k split, 2 or 4 forced),
  * "small_rb" (1 =
  * products of 3..16 tokens share activation fragments over 4 row blocks
- * or split k, 0 = one row block per work-group).
- * Results do not depend on them beyond rounding.  0, or -1 for an unknown
- * key. */
+ * or split k, 0 = one row block per work-group), "prefill_lo" (bf16
+ * prefill products: 1 = the activations' hi and lo bf16 planes both enter
+ * the matrix cores, 0 = the hi plane only, i.e. bf16-rounded activations,
+ * which leaves about 6e-3 of relative error per 8B-shaped layer; with it
+ * the forced shapes are 1, 3, 5, 10 and 14).
+ * Results do not depend on them beyond rounding, except "prefill_lo" 0.
+ * The knobs are process-wide and unsynchronised: set them while no other
+ * thread is inside the library; every context sees the change.  0, or -1
+ * for an unknown key. */
 int32_t ubd_debug_set_tuning(const char *key, int32_t value);
 
 /* Counters in the spirit of llama_perf_context_print ([ARCH] Example 15). */

@@ -48,6 +48,8 @@ struct Tuning {
     int gemm_wpd = 0;         // LDS-ring product: stages of weight look-ahead (1 or 2; 0 = per shape)
     int gemm_deep = 1;        // bf16 residual / QKV prefill products: 1 = deep look-ahead kernel where it fits
     int act_tiled = 1;        // prefill products read activations tiled in MFMA operand order (0 = row-major)
+    int prefill_lo = 1;       // bf16 prefill products: 1 = hi + lo activation planes (two products per
+                              // fragment), 0 = the hi plane only (bf16-rounded activations)
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;

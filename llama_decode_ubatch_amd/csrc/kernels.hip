@@ -1168,9 +1168,9 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int WT, int RBW, int TB, int KS> struct GemmCfg {
+template <int WT, int RBW, int TB, int KS, bool LO = false> struct GemmCfg {
     static constexpr bool Q8 = WT == W_Q8;
-    static constexpr int PL = Q8 ? 2 : 1;         // activation planes: hi (+ lo for q8_0)
+    static constexpr int PL = Q8 || LO ? 2 : 1;   // activation planes: hi (+ lo for q8_0, or bf16 with LO)
     static constexpr int KH = KS / 32;            // 32-wide k halves per stage
     static constexpr int NA = Q8 ? KS / 64 : KH;  // weight tiles per row block per stage
     static constexpr int XF = TB * KH * PL;       // activation fragments per stage
@@ -1179,14 +1179,17 @@ template <int WT, int RBW, int TB, int KS> struct GemmCfg {
     static constexpr int NX = 3;                  // LDS ring depth
 };
 
-template <int WT, int EPI, int RBW, int TB, int SPLITK, int KS, int WPD>
+// LO (bf16 weights): the activations' lo plane enters a second product per
+// fragment, so the product sees about 16 significant bits of the f32
+// activation instead of bf16's 8.
+template <int WT, int EPI, int RBW, int TB, int SPLITK, int KS, int WPD, bool LO = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_lds_kernel(LinearArgs a,
                                                                                              int n_wtiles,
                                                                                              int n_ttiles) {
     // (the host pass only needs the launch stub; the buffer-resource
     // builtins below exist for the device pass alone)
 #if defined(__HIP_DEVICE_COMPILE__)
-    using C = GemmCfg<WT, RBW, TB, KS>;
+    using C = GemmCfg<WT, RBW, TB, KS, LO>;
     constexpr bool Q8 = C::Q8;
     constexpr int KH = C::KH, NA = C::NA;
     __shared__ u32x4_t xs[C::NX * C::XF * 64];
@@ -1218,7 +1221,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     // contiguous 1 KB run; row-major: 16 rows x 64 bytes per fragment)
     const size_t xbytes = (size_t)(a.x.tiled ? (a.T + 15) / 16 * 16 : a.T) * a.x.ld * 2;
     const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, xbytes);
-    const __amdgpu_buffer_rsrc_t rxl = make_rsrc(Q8 ? a.x.lo : a.x.hi, xbytes);
+    const __amdgpu_buffer_rsrc_t rxl = make_rsrc(C::PL == 2 ? a.x.lo : a.x.hi, xbytes);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.wscale, Q8 ? (size_t)a.N * KB * 2 : 0);
     const int xst = a.x.tiled ? KS * 32 : KS * 2;     // bytes between stages
     // this wave's activation fragments f = wave*XW + u = (plane, token block, k half)
@@ -1308,12 +1311,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) Bh[tb] = __builtin_bit_cast(bf16x8_t, xb[(tb * KH + j) * 64 + lane]);
                 if (!Q8) {
+                    bf16x8_t Bl[LO ? TB : 1];
+                    if (LO) {
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb)
+                            Bl[tb] = __builtin_bit_cast(bf16x8_t, xb[((TB + tb) * KH + j) * 64 + lane]);
+                    }
 #pragma unroll
                     for (int i = 0; i < RBW; ++i) {
                         const bf16x8_t A = __builtin_bit_cast(bf16x8_t, wc[i][j]);
 #pragma unroll
-                        for (int tb = 0; tb < TB; ++tb)
+                        for (int tb = 0; tb < TB; ++tb) {
                             acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bh[tb], acc[i][tb], 0, 0, 0);
+                            if (LO)
+                                acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl[tb], acc[i][tb], 0, 0, 0);
+                        }
                     }
                 } else {
                     const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
@@ -1396,12 +1408,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 // partial sums to a.split_out[ks][t][n]; resid_add_splits_kernel then adds
 // the slices to the residual in order (no atomics: the sums do not depend on
 // timing).
-template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1>
+template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1, bool LO = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_deep_kernel(
     LinearArgs a, int n_wtiles, int n_ttiles) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int KS = 64;
-    using C = GemmCfg<W_BF16, RBW, TB, KS>;
+    using C = GemmCfg<W_BF16, RBW, TB, KS, LO>;
     constexpr int KH = C::KH, NA = C::NA;
     static_assert(D == 1 || D == 3, "look-ahead");
     static_assert(SPLITK == 1 || EPI == EPI_RESID, "k split: residual products only");
@@ -1426,7 +1438,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (size_t)a.N * a.K * 2);
     const size_t xbytes = (size_t)(a.x.tiled ? (a.T + 15) / 16 * 16 : a.T) * a.x.ld * 2;
     const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, xbytes);
+    const __amdgpu_buffer_rsrc_t rxl = make_rsrc(LO ? a.x.lo : a.x.hi, xbytes);
     const int xst = a.x.tiled ? KS * 32 : KS * 2;     // bytes between stages
+    // this wave's activation fragments f = wave*XW + u = (plane, token block, k half)
     int xoff[C::XW];
 #pragma unroll
     for (int u = 0; u < C::XW; ++u) {
@@ -1463,20 +1477,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         const int sl = min(s, nst - 1);
         u32x4_t *dst = xs + (size_t)((s % C::NX) * C::XF + wave * C::XW) * 64;
 #pragma unroll
-        for (int u = 0; u < C::XW; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rxh, (__attribute__((address_space(3))) void *)(dst + u * 64), 16,
+        for (int u = 0; u < C::XW; ++u) {
+            const bool lo = (wave * C::XW + u) >= TB * KH;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(lo ? rxl : rxh,
+                                                     (__attribute__((address_space(3))) void *)(dst + u * 64), 16,
                                                      xoff[u], sl * xst, 0, 0);
+        }
     };
     // both k halves' activation fragments are read up front: the second
     // half's reads are in flight while the first half's products run
     static_assert(KH == 2, "two k halves per stage");
     auto compute = [&](int s, const u32x4_t (&wc)[RBW][NA]) {
         const u32x4_t *xb = xs + (size_t)(s % C::NX) * C::XF * 64;
-        u32x4_t B[2][TB];
+        u32x4_t B[C::PL][2][TB];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int pl = 0; pl < C::PL; ++pl)
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) B[j][tb] = xb[(tb * KH + j) * 64 + lane];
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) B[pl][j][tb] = xb[((pl * TB + tb) * KH + j) * 64 + lane];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -1484,9 +1503,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
             for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
                 for (int i = 0; i < RBW; ++i)
-                    acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wc[i][j]),
-                                                                         __builtin_bit_cast(bf16x8_t, B[j][tb]),
-                                                                         acc[i][tb], 0, 0, 0);
+#pragma unroll
+                    for (int pl = 0; pl < C::PL; ++pl)
+                        acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wc[i][j]),
+                                                                             __builtin_bit_cast(bf16x8_t, B[pl][j][tb]),
+                                                                             acc[i][tb], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -1551,15 +1572,15 @@ __global__ __launch_bounds__(256) void resid_add_splits_kernel(float *y, int ldy
 // false (nothing launched) unless each k slice's stage count is a multiple
 // of D + 1 (and, split, the product is a residual one with scratch for the
 // slices)
-template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1>
+template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1, bool LO = false>
 static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
     const int nst = a.K / 64;
     if (a.K % 64 || nst % SPLITK || (nst / SPLITK) % (D + 1)) return false;
     if (SPLITK > 1 && (EPI != EPI_RESID || !a.split_out || a.N % 4)) return false;
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
-    hipLaunchKernelGGL((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(256),
-                       0, s, a, n_wtiles, n_ttiles);
+    hipLaunchKernelGGL((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK, LO>), dim3(n_wtiles * n_ttiles * SPLITK),
+                       dim3(256), 0, s, a, n_wtiles, n_ttiles);
     if (SPLITK > 1) {
         const long n = (long)a.T * (a.N / 4);
         hipLaunchKernelGGL(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
@@ -1569,7 +1590,7 @@ static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
 }
 
 // wpd: stages of weight look-ahead (the tuning knob overrides it)
-template <int WT, int EPI, int RBW, int TB, int SPLITK>
+template <int WT, int EPI, int RBW, int TB, int SPLITK, bool LO = false>
 static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
@@ -1578,21 +1599,60 @@ static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
     // 64-wide stages: the kernel then fits 2 waves per SIMD (two work-groups
     // per CU), which hides the LDS reads and barriers of one behind the other
     if (wpd == 2)
-        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 2>), dim3(total), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 2, LO>), dim3(total), dim3(256), 0, s, a,
                            n_wtiles, n_ttiles);
     else
-        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 1>), dim3(total), dim3(256), 0, s, a,
+        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 1, LO>), dim3(total), dim3(256), 0, s, a,
                            n_wtiles, n_ttiles);
 }
 
 // Shape choice for the LDS-ring product: the largest tile (256 rows x 128
 // tokens) when it yields enough work-groups for the 256 CUs, else narrower
 // tiles; residual products may also split k (partial sums added atomically).
+// bf16 products over hi + lo activation planes (two products per
+// fragment): twice the activation fragments per stage, so the tiles are at
+// most 64 tokens wide.
+template <int EPI>
+static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
+    auto tiles = [&](int rbw, int tb) {
+        return (long)((a.N + 64 * rbw - 1) / (64 * rbw)) * ((a.T + 16 * tb - 1) / (16 * tb));
+    };
+    constexpr int RS = EPI == EPI_RESID ? 2 : 1;
+    // forced shapes for measurements and tests
+    switch (g_tuning.gemm_shape) {
+    case 1: launch_gemm_lds<W_BF16, EPI, 2, 4, 1, true>(a, s); return;
+    case 3: launch_gemm_lds<W_BF16, EPI, 4, 4, 1, true>(a, s); return;
+    case 5: if (EPI != EPI_SWIGLU) { launch_gemm_lds<W_BF16, EPI, 1, 4, 1, true>(a, s); return; } break;
+    case 10: if (launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true>(a, s)) return; break;
+    case 14: if (launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return; break;
+    default: break;
+    }
+    if (EPI == EPI_RESID) {
+        // long k (FFN down): k split in two through scratch
+        if (a.K >= 8192 && tiles(2, 4) * 2 >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return;
+        if (tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true>(a, s)) return;
+        launch_gemm_lds<W_BF16, EPI, 2, 4, 1, true>(a, s);
+        return;
+    }
+    if (EPI == EPI_QKV && tiles(4, 4) < 192 && tiles(1, 4) >= 384) {
+        launch_gemm_lds<W_BF16, EPI, 1, 4, 1, true>(a, s);
+        return;
+    }
+    if (tiles(4, 4) >= 192)
+        launch_gemm_lds<W_BF16, EPI, 4, 4, 1, true>(a, s);
+    else
+        launch_gemm_lds<W_BF16, EPI, 2, 4, 1, true>(a, s);
+}
+
 template <int WT, int EPI>
 static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     auto tiles = [&](int rbw, int tb) {
         return (long)((a.N + 64 * rbw - 1) / (64 * rbw)) * ((a.T + 16 * tb - 1) / (16 * tb));
     };
+    if (WT == W_BF16 && g_tuning.prefill_lo != 0) {
+        launch_gemm_lds_shape_lo<EPI>(a, s);
+        return;
+    }
     // forced shapes for measurements
     switch (g_tuning.gemm_shape) {
     case 1: launch_gemm_lds<WT, EPI, 2, 4, 1>(a, s); return;

@@ -1498,6 +1498,8 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.gemm_deep = value;
     } else if (k == "act_tiled") {
         g_tuning.act_tiled = value;
+    } else if (k == "prefill_lo") {
+        g_tuning.prefill_lo = value;
     } else if (k == "ldsx") {
         g_tuning.ldsx = value;
     } else if (k == "ldsx_early") {

@@ -3,7 +3,8 @@ times (512-token prefill as one ubatch, then single-token decode), on
 sampled outputs the oracle computes one by one: the oracle re-runs sampled
 layers from the GPU's own input to that layer and the output head from the
 GPU's final residual.  Tolerance (bf16 / int8 configs): max |error| within
-3e-2 of the max-norm of the oracle's output."""
+3e-2 of the max-norm of the oracle's output; the prefill layers, whose
+products take the activations as hi + lo planes, within 2e-3."""
 import numpy as np
 import pytest
 
@@ -13,7 +14,8 @@ from tests.helpers import oracle_layer_check
 
 pytestmark = pytest.mark.gpu
 TOL = 3e-2
-LAYERS = (0, 1, 17, 31)
+TOL_PREFILL_LAYER = 2e-3
+PREFILL_LAYERS = tuple(range(0, 32, 4)) + (1, 31)
 
 
 def rel(a, b):
@@ -50,12 +52,12 @@ def test_prefill_and_decode_sampled_layers(cfg):
     T = prompt.size
     print(f"config {cfg}: prefill {T} tokens", flush=True)
     assert ctx.decode(prompt) == 0
-    for il in LAYERS:
+    for il in PREFILL_LAYERS:
         x_in, x_out = ctx.residual(il, T), ctx.residual(il + 1, T)
         y, ref = oracle_layer(om, w, il, x_in, prompt, 0)
         err = rel(x_out, y)
         print(f"  prefill layer {il}: rel err {err:.2e}", flush=True)
-        assert err < TOL, il
+        assert err < TOL_PREFILL_LAYER, il
         # the K/V this layer appended, as stored (f16)
         Kr, Vr = ref.kv(il, 0)
         assert rel(ctx.kv_read(il, 0, 0, 0, T), Kr[:T].astype(np.float32)) < TOL

@@ -1,14 +1,17 @@
 """End-to-end parity of the 8B-shaped workloads against stored oracle runs.
 
-tests/golden/oracle_cfg{3,5,4}.npz hold, per step, the oracle's greedy token,
-its top-16 logits and its logits at 256 fixed vocabulary indices (written by
-tests/golden/make_8b_golden.py, which calls only oracle/).  The GPU path is
-teacher-forced on the oracle's tokens, so every step compares logits of
-identical inputs:
-  * sampled and top-16 logits within 3e-2 of the step's logit max-norm;
-  * top-1 agreement on at least 99 % of the steps, a disagreement counting
-    only where the oracle's top-2 gap exceeds twice the measured logit error
-    (otherwise both picks are correct within the tolerance).
+tests/golden/oracle_cfg{3,5,4}.npz hold, for every step of the workload,
+the oracle's greedy token, its top-64 logits and its logits at 4096 fixed
+vocabulary indices (written by tests/golden/make_8b_golden.py, which calls
+only oracle/).  Two passes on the GPU:
+  * teacher-forced on the oracle's tokens, so every step compares logits of
+    identical inputs: sampled and top-64 logits within 3e-2 of the step's
+    logit max-norm, and the GPU's top-1 equal to the oracle's on at least
+    99 % of the steps, every disagreement counted (the number is printed);
+  * free-running greedy (the GPU feeds its own picks): the token ids equal
+    the oracle's, bit for bit, up to the first step whose oracle top-2 gap
+    lies within twice the measured logit error, if there is one (after such
+    a near tie either pick is correct and the runs go apart).
 """
 import os
 
@@ -57,12 +60,25 @@ def compare_step(z, g, i, k=None):
 def check(results, label):
     errs = np.array([r[0] for r in results])
     n = len(results)
-    hard = [i for i, (e, gap, ok) in enumerate(results) if not ok and gap > 2 * e]
-    soft = [i for i, (e, gap, ok) in enumerate(results) if not ok and gap <= 2 * e]
-    print(f"{label}: {n} steps, max logit err {errs.max():.2e} of max-norm, "
-          f"top-1 disagreements {len(hard)} (+{len(soft)} within tolerance)", flush=True)
+    miss = [(i, gap, e) for i, (e, gap, ok) in enumerate(results) if not ok]
+    print(f"{label}: {n} steps, max logit err {errs.max():.2e} of max-norm (median {np.median(errs):.2e}), "
+          f"top-1 disagreements {len(miss)} of {n}" +
+          "".join(f"\n  step {i}: oracle top-2 gap {gap:.2e}, logit err {e:.2e}" for i, gap, e in miss), flush=True)
     assert errs.max() < TOL
-    assert (n - len(hard)) / n >= 0.99
+    assert (n - len(miss)) / n >= 0.99
+
+
+def check_free_running(ids, g, results, label, k=None):
+    """ids: the GPU's free-running picks (one per step); results: the
+    teacher-forced (err, gap, agree) of the same steps."""
+    ref = np.asarray(g["tokens"] if k is None else g["tokens"][k])
+    n = min(len(ids), len(ref))
+    diff = [i for i in range(n) if int(ids[i]) != int(ref[i])]
+    d = diff[0] if diff else n
+    print(f"{label}: free-running greedy ids equal the oracle's for {d} of {n} steps", flush=True)
+    if diff:
+        e, gap, _ = results[d]
+        assert gap <= 2 * e, f"step {d}: ids differ with an oracle top-2 gap {gap:.2e} > 2 x err {e:.2e}"
 
 
 @pytest.mark.parametrize("cfg", [3, 5])
@@ -79,6 +95,14 @@ def test_single_sequence_teacher_forced(cfg):
         assert ctx.decode([int(toks[i - 1])]) == 0
         res.append(compare_step(ctx.logits_ith(-1), g, i))
     check(res, f"config {cfg}")
+    # free running from the same prompt
+    ctx.seq_rm(-1, -1, -1)
+    assert ctx.decode(g["prompt"]) == 0
+    ids = [ctx.greedy(-1)]
+    for i in range(1, len(toks)):
+        assert ctx.decode([ids[-1]]) == 0
+        ids.append(ctx.greedy(-1))
+    check_free_running(ids, g, res, f"config {cfg}")
 
 
 @pytest.mark.timeout(600)
@@ -97,8 +121,10 @@ def test_prefilled_kv_teacher_forced():
         del kv
     torch.cuda.empty_cache()
     seqs = [int(s) for s in g["seqs"]]
-    toks = np.array(g["first"], np.int32)
     n_steps = g["top_ids"].shape[1]
+    # teacher-forced: the golden sequences take the oracle's tokens, the
+    # others their own greedy picks
+    toks = np.array(g["first"], np.int32)
     res = {s: [] for s in seqs}
     for i in range(n_steps):
         for k, s in enumerate(seqs):
@@ -110,3 +136,16 @@ def test_prefilled_kv_teacher_forced():
         others = [s for s in range(w.n_seqs) if s not in seqs]
         toks[others] = picks[others]
     check([r for s in seqs for r in res[s]], "config 4 (sequences %s)" % seqs)
+    # free running: every sequence feeds its own greedy picks
+    for s in range(w.n_seqs):
+        ctx.seq_rm(s, P, -1)
+    toks = np.array(g["first"], np.int32)
+    ids = {s: [int(toks[s])] for s in seqs}
+    for i in range(n_steps):
+        assert ctx.decode(toks, seq_id=np.arange(w.n_seqs), logits=np.ones(w.n_seqs)) == 0
+        toks = ctx.greedy_all().astype(np.int32)
+        for s in seqs:
+            ids[s].append(int(toks[s]))
+    for k, s in enumerate(seqs):
+        # tokens[k] = [first, pick after step 0, ...]; results index the steps
+        check_free_running(ids[s][1:], {"tokens": g["tokens"][k][1:]}, res[s], f"config 4 sequence {s}")
