@@ -331,6 +331,28 @@ ubd_token ubd_sample_greedy(ubd_context *ctx, int32_t i);
  * Returns the number of rows written, or -1. */
 int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32_t cap);
 
+/* The greedy pick of ubd_sample_greedy_all over caller-owned rows, for
+ * callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the call allocates nothing.  Its
+ * partial results live in a fixed device array of the library (one per GPU,
+ * UBD_GREEDY_STATIC_MAX_ROWS rows, 128 KiB, held until the process ends);
+ * each call overwrites it, so calls that overlap on one GPU (two streams, or
+ * two host threads) race and must be ordered by the caller.
+ *   device  : HIP device ordinal of the rows, the output and the stream
+ *   logits  : device f32 rows [n_rows][ld], 16-byte aligned, read only
+ *   ld      : row stride in floats, a multiple of 4, >= n_vocab
+ *   n_rows  : 0 .. UBD_GREEDY_STATIC_MAX_ROWS
+ *   n_vocab : values per row, a positive multiple of 4
+ *   out     : device int32 [n_rows]: the largest value's index per row,
+ *             the lowest index on ties
+ *   stream  : hipStream_t on `device` (NULL = the null stream); the work is
+ *             enqueued there and the call returns before it finishes
+ * Returns UBD_OK, UBD_INVALID (arguments out of range, nothing enqueued) or
+ * UBD_COMPUTE_FAILED (HIP error). */
+#define UBD_GREEDY_STATIC_MAX_ROWS 256
+int32_t ubd_greedy_rows_static(int32_t device, const float *logits, int32_t ld, int32_t n_rows,
+                               int32_t n_vocab, ubd_token *out, void *stream);
+
 /* Sampler chain ([ENG] Steps 14-16, "Sampler chain"): penalties of the
  * tokens already chosen, then the top-k, top-p and min-p cut-offs, then
  * temperature, then one random token.  Readings where the page gives no

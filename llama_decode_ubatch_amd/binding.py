@@ -19,6 +19,7 @@ UBD_TYPE_F32, UBD_TYPE_F16, UBD_TYPE_BF16, UBD_TYPE_Q8_0 = 0, 1, 2, 3
 UBD_OK, UBD_NO_KV_SLOT, UBD_ABORTED = 0, 1, 2
 UBD_INVALID, UBD_ALLOC_FAILED, UBD_COMPUTE_FAILED = -1, -2, -3
 UBD_MAX_SEQ = 256
+UBD_GREEDY_STATIC_MAX_ROWS = 256
 TYPE_IDS = {"f32": UBD_TYPE_F32, "f16": UBD_TYPE_F16, "bf16": UBD_TYPE_BF16, "q8_0": UBD_TYPE_Q8_0}
 
 
@@ -101,6 +102,8 @@ SIGNATURES = {
     "ubd_get_logits_device": (C.c_void_p, [_P]),
     "ubd_sample_greedy": (C.c_int32, [_P, C.c_int32]),
     "ubd_sample_greedy_all": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_greedy_rows_static": (C.c_int32, [C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                           C.c_void_p]),
     "ubd_sampler_default_params": (SamplerParams, []),
     "ubd_sampler_init": (_P, [_P, SamplerParams]),
     "ubd_sampler_free": (None, [_P]),
@@ -363,6 +366,12 @@ class Model:
         self._finalizer()
 
 
+def greedy_rows_static(device, logits_ptr, ld, n_rows, n_vocab, out_ptr, stream_ptr):
+    """ubd_greedy_rows_static on raw device addresses (ints); returns the
+    library's status code."""
+    return load_library().ubd_greedy_rows_static(device, logits_ptr, ld, n_rows, n_vocab, out_ptr, stream_ptr)
+
+
 def gguf_model_info(path):
     info = GgufInfo()
     if load_library().ubd_gguf_model_info(str(path).encode(), C.byref(info)) != 0:
@@ -471,6 +480,10 @@ class Context:
 
     def n_outputs(self):
         return self.lib.ubd_n_outputs(self.ptr)
+
+    def logits_device_ptr(self):
+        """Device address of the logits rows (ubd_get_logits_device), 0 if none."""
+        return self.lib.ubd_get_logits_device(self.ptr) or 0
 
     def logits(self):
         n = self.n_outputs()

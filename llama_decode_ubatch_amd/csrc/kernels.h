@@ -208,6 +208,10 @@ struct ArgmaxWork {
 };
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows,
                    int n, int32_t *out, const ArgmaxWork &w, hipStream_t s);
+// The same argmax in two kernels and no counter (nothing to keep at zero
+// between calls): pv / pi [n_rows][ARGMAX_BLOCKS] hold the slice winners.
+void launch_argmax_two_pass(const float *logits, int ld, int n_rows, int n, int32_t *out,
+                            float *pv, int32_t *pi, hipStream_t s);
 
 // Sampler chain on one logits row (one work-group): penalties of the
 // history tokens, top-k (1..SAMPLER_KMAX), top-p, min-p, temperature, then

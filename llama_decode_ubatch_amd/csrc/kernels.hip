@@ -2743,6 +2743,14 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int ld
         for (int k = 0; k < 4; ++k) better(bv, bi, v[k], i + k);
     }
     block_best(bv, bi);
+    if (!counter) {
+        // two-pass form: argmax_final_kernel reduces the slices
+        if (threadIdx.x == 0) {
+            pv[row * nb + b] = bv;
+            pi[row * nb + b] = bi;
+        }
+        return;
+    }
     __shared__ int last;
     if (threadIdx.x == 0) {
         pv[row * nb + b] = bv;
@@ -2763,6 +2771,26 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int ld
         out[row] = bi == 0x7fffffff ? 0 : bi;
         counter[row] = 0;
     }
+}
+
+// Second pass of the two-pass argmax: one work-group per row reduces the
+// row's slice winners in slice order (ties: the lowest index).
+__global__ __launch_bounds__(256) void argmax_final_kernel(const float *pv, const int32_t *pi, int nb,
+                                                           int32_t *out) {
+    const int row = blockIdx.x;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int k = threadIdx.x; k < nb; k += blockDim.x) better(bv, bi, pv[row * nb + k], pi[row * nb + k]);
+    block_best(bv, bi);
+    if (threadIdx.x == 0) out[row] = bi == 0x7fffffff ? 0 : bi;
+}
+
+void launch_argmax_two_pass(const float *logits, int ld, int n_rows, int n, int32_t *out, float *pv, int32_t *pi,
+                            hipStream_t s) {
+    if (n_rows <= 0) return;
+    hipLaunchKernelGGL(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld,
+                       (const int32_t *)nullptr, n, out, pv, pi, (int32_t *)nullptr);
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(n_rows), dim3(256), 0, s, pv, pi, ARGMAX_BLOCKS, out);
 }
 
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows, int n, int32_t *out,
