@@ -130,8 +130,11 @@ struct LinearArgs {
     NormIn norm;                      // set: input is x normalised on the fly (T <= NORM_TMAX)
     int early = 1;                    // LDS-staged product: one-token activation loads may go first
     float *split_out = nullptr;       // RESID prefill products: scratch for k-slice partial sums,
-                                      // [2][T][N] f32 (null: no k split through scratch)
+                                      // [MAX_K_SLICES][T][N] f32 (null: no k split)
 };
+// Most k slices a residual prefill product is split into (its partial sums
+// go to scratch and are added to the residual in slice order).
+constexpr int MAX_K_SLICES = 4;
 
 // Enqueues y = W x with the epilogue a.epi.  Returns false, launching
 // nothing, when a fused norm is asked for outside linear_norm_fits.

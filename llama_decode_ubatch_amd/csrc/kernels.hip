@@ -1386,10 +1386,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         for (int tb = 0; tb < TB; ++tb) {
             const int t = t0 + tb * 16 + r;
             if (t >= a.T) continue;
-            if (EPI == EPI_SWIGLU)
+            if (SPLITK > 1)
+                store4(a.split_out + ((size_t)ks * a.T + t) * a.N + rb * 16 + 4 * g, acc[i][tb]);
+            else if (EPI == EPI_SWIGLU)
                 epilogue4<EPI, false>(a, t, (rb >> 1) * 16 + 4 * g, acc[i][tb], acc[i + 1][tb]);
             else
-                epilogue4<EPI, (SPLITK > 1)>(a, t, rb * 16 + 4 * g, acc[i][tb], acc[i][tb]);
+                epilogue4<EPI, false>(a, t, rb * 16 + 4 * g, acc[i][tb], acc[i][tb]);
         }
     }
 #endif
@@ -1592,6 +1594,14 @@ static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
 // wpd: stages of weight look-ahead (the tuning knob overrides it)
 template <int WT, int EPI, int RBW, int TB, int SPLITK, bool LO = false>
 static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
+    if constexpr (SPLITK > 1) {
+        // the k slices go to scratch and are added in slice order: without
+        // scratch (or for a product other than a residual one), no split
+        if (EPI != EPI_RESID || !a.split_out || a.N % 4) {
+            launch_gemm_lds<WT, EPI, RBW, TB, 1, LO>(a, s, wpd);
+            return;
+        }
+    }
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
     const int total = n_wtiles * n_ttiles * SPLITK;
@@ -1604,11 +1614,16 @@ static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
     else
         hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 1, LO>), dim3(total), dim3(256), 0, s, a,
                            n_wtiles, n_ttiles);
+    if (SPLITK > 1) {
+        const long n = (long)a.T * (a.N / 4);
+        hipLaunchKernelGGL(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
+                           a.split_out, a.T, a.N, SPLITK);
+    }
 }
 
 // Shape choice for the LDS-ring product: the largest tile (256 rows x 128
 // tokens) when it yields enough work-groups for the 256 CUs, else narrower
-// tiles; residual products may also split k (partial sums added atomically).
+// tiles; residual products may also split k (slices added in order).
 // bf16 products over hi + lo activation planes (two products per
 // fragment): twice the activation fragments per stage, so the tiles are at
 // most 64 tokens wide.
@@ -1696,8 +1711,8 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
         if (EPI == EPI_QKV && tiles(4, 8) < 192 && tiles(2, 8) >= 192 && launch_gemm_deep<EPI, 2, 8, 3, 2>(a, s))
             return;
     }
-    // residual products: 128 x 64 tiles, splitting k (atomic partial sums)
-    // only when there are too few tiles for the CUs
+    // residual products: 128 x 64 tiles, splitting k (slices through scratch,
+    // added in order) only when there are too few tiles for the CUs
     if (EPI == EPI_RESID) {
         const long t = tiles(2, 4);
         if (g_tuning.gemm_split == 2) {

@@ -430,7 +430,8 @@ struct ubd_context : public Executor {
     float *x = nullptr, *q = nullptr;
     Act actA, actB, actC;
     float *part_o = nullptr, *part_ml = nullptr;
-    float *split_scratch = nullptr;         // k-slice partial sums of the residual prefill products [2][cap][d]
+    float *split_scratch = nullptr;         // k-slice partial sums of the residual prefill products
+                                            // [MAX_K_SLICES][cap][d]
     int max_chunks = 0;                     // f32-path chunks (ATTN_CHUNK cells)
     int max_chunks_mfma = 0;                // MFMA split-path chunks (ATTN_DECODE_CHUNK cells)
     bool mfma_attn = false;
@@ -644,8 +645,8 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     c->part_ml = (float *)c->mem.get(part_rows * 2 * 4);
 
     if (!c->part_o || !c->part_ml) return bail("attention scratch allocation failed");
-    if (model->wtype == W_BF16 && cap >= 64) {
-        c->split_scratch = (float *)c->mem.get((size_t)2 * cap * d * 4);
+    if ((model->wtype == W_BF16 || model->wtype == W_Q8) && cap >= 64) {
+        c->split_scratch = (float *)c->mem.get((size_t)MAX_K_SLICES * cap * d * 4);
         if (!c->split_scratch) return bail("product scratch allocation failed");
     }
     std::vector<double> inv(hd / 2);

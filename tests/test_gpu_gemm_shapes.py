@@ -49,13 +49,14 @@ def built():
     return out
 
 
-def gpu_logits(model, tokens, gemm, shape=0, tiled=1, lo=1):
+def gpu_logits(model, tokens, gemm, shape=0, tiled=1, lo=1, split=0):
     from llama_decode_ubatch_amd import Context
     from llama_decode_ubatch_amd.binding import set_tuning
     set_tuning("gemm", gemm)
     set_tuning("gemm_shape", shape)
     set_tuning("act_tiled", tiled)
     set_tuning("prefill_lo", lo)
+    set_tuning("gemm_split", split)
     try:
         ctx = Context(model, n_ctx=512, n_batch=512, n_ubatch=512, n_seq_max=1, type_k="f16", type_v="f16")
         assert ctx.decode(tokens, logits=np.ones(len(tokens))) == 0
@@ -65,6 +66,7 @@ def gpu_logits(model, tokens, gemm, shape=0, tiled=1, lo=1):
         set_tuning("gemm_shape", 0)
         set_tuning("act_tiled", 1)
         set_tuning("prefill_lo", 1)
+        set_tuning("gemm_split", 0)
 
 
 @pytest.mark.parametrize("key", list(SHAPES))
@@ -89,6 +91,13 @@ def test_prefill_gemm_matches_oracle(built, key, n):
     for choice in lo_choices:
         zc = gpu_logits(model, tokens, *choice)
         assert float(np.abs(zc - zr).max() / np.abs(zr).max()) < TOL[shape.wtype], choice
+    # residual products split over k into 2 and 4 slices (added in slice
+    # order, so two runs give the same logits bit for bit)
+    for split in (2, 4):
+        zc = gpu_logits(model, tokens, 1, split=split, lo=0 if shape.wtype == "bf16" else 1)
+        tol = TOL_HI_ONLY if shape.wtype == "bf16" else TOL[shape.wtype]
+        assert float(np.abs(zc - zr).max() / np.abs(zr).max()) < tol, split
+        assert np.array_equal(zc, gpu_logits(model, tokens, 1, split=split, lo=0 if shape.wtype == "bf16" else 1))
     if shape.wtype == "bf16":
         for choice in ((0, 0), (1, 0), (1, 1), (1, 2), (1, 3), (1, 4), (1, 7), (1, 8), (1, 9), (1, 10), (1, 11), (1, 12),
                        (1, 13), (1, 14), (1, 15), (1, 0, 0), (1, 10, 0)):
