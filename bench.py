@@ -39,11 +39,42 @@ TRAFFIC_FILES = {
     "prefill.ffn_gate_up": os.path.join(ROOT, "profiles", "prefill_ffn_gate_up_8b_bf16_traffic.txt"),
 }
 KERNEL_SRC = os.path.join(ROOT, "llama_decode_ubatch_amd", "csrc", "kernels.hip")
-HEADLINE = 3
+# committed kernel-trace summaries (rocprofv3 --kernel-trace --stats of this
+# script) and the roofline kernels' names in them
+TRACE_FILES = {
+    ("decode.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
+                                     "linear_ldsx_kernel<2, 2, 4, true>"),
+    ("prefill.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
+                                      "gemm_lds_kernel<2, 2, 4, 4, 1, 64, 1, true>"),
+    ("decode.attention", "bf16"): (os.path.join(ROOT, "profiles", "decode_8b_16seq_32k_kernel_stats.md"),
+                                   "attn_mfma_kernel<128, true, false>"),
+    ("decode.ffn_gate_up", "q8_0"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_q8_0_kernel_stats.md"),
+                                     "linear_ldsx_kernel<3, 2, 4, true>"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def _src_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traced_avg_us(kernel_class, wtype):
+    """Average dispatch duration of a roofline kernel in the committed
+    rocprofv3 kernel trace, if kernels.hip is unchanged since then."""
+    try:
+        path, name = TRACE_FILES[(kernel_class, wtype)]
+        text = open(path).read()
+        if f"sha256 prefix {_src_hash()}" not in text:
+            return None
+        for line in text.splitlines():
+            if line.startswith(f"| `{name}` |"):
+                return float(line.split("|")[3])
+    except Exception:
+        return None
+    return None
 
 
 def measured_traffic(kernel_class):
@@ -51,8 +82,7 @@ def measured_traffic(kernel_class):
     rocprofv3 counter summary, if kernels.hip is unchanged since then."""
     try:
         lines = dict(l.split(":", 1) for l in open(TRAFFIC_FILES[kernel_class]).read().splitlines() if ":" in l)
-        src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-        if lines.get("kernels_hip_sha256_16", "").strip() != src_hash:
+        if lines.get("kernels_hip_sha256_16", "").strip() != _src_hash():
             return None
         return int(float(lines["hbm_bytes_per_launch"].strip()))
     except Exception:
@@ -251,10 +281,16 @@ def roofline_of(w, r):
         kernel = "decode.ffn_gate_up (linear_ldsx_kernel, fused RMSNorm, SwiGLU epilogue)"
         traffic = measured_traffic(hot) if shape.wtype == "bf16" and T == 1 else None
     ach = alg / avg_s / 1e9
-    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
-            "bytes_per_launch": int(alg), "avg_us": round(r["hot"][hot]["avg_us"], 2),
-            "timing": "HIP events on the library stream around each launch, one job after the timed region"}
+    out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+           "bytes_per_launch": int(alg), "avg_us": round(r["hot"][hot]["avg_us"], 2),
+           "timing": "HIP events on the library stream around each launch, one job after the timed region "
+                     "(each interval also holds the dispatch of the launch)"}
+    tr = traced_avg_us(hot, shape.wtype)
+    if tr:
+        out["trace_avg_us"] = tr
+        out["trace_frac"] = round(alg / (tr * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    return out
 
 
 def roofline_prefill_of(w, r):
@@ -264,13 +300,19 @@ def roofline_prefill_of(w, r):
     flops = 2.0 * w.n_prompt * 2 * shape.n_ff * shape.n_embd
     avg_us = r["hot"]["prefill.ffn_gate_up"]["avg_us"]
     ach = flops / (avg_us * 1e-6) / 1e12
-    return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-            "kernel": "prefill.ffn_gate_up (gemm_lds_kernel, SwiGLU epilogue)",
-            "flops_per_launch": flops, "avg_us": round(avg_us, 2),
-            "traffic": measured_traffic("prefill.ffn_gate_up")
-            if shape.wtype == "bf16" and w.n_prompt == 512 else None,
-            "timing": "HIP events on the library stream around each launch, one job after the timed region"}
+    out = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+           "kernel": "prefill.ffn_gate_up (gemm_lds_kernel, SwiGLU epilogue; the method's FLOPs, the activations' "
+                     "hi and lo planes make twice that of matrix-core work)",
+           "flops_per_launch": flops, "avg_us": round(avg_us, 2),
+           "traffic": measured_traffic("prefill.ffn_gate_up")
+           if shape.wtype == "bf16" and w.n_prompt == 512 else None,
+           "timing": "HIP events on the library stream around each launch, one job after the timed region"}
+    tr = traced_avg_us("prefill.ffn_gate_up", shape.wtype)
+    if tr:
+        out["trace_avg_us"] = tr
+        out["trace_frac"] = round(flops / (tr * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    return out
 
 
 # -------------------------------------------------------------- CPU baseline
