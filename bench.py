@@ -302,7 +302,7 @@ def roofline_prefill_of(w, r):
     ach = flops / (avg_us * 1e-6) / 1e12
     out = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-           "kernel": "prefill.ffn_gate_up (gemm_lds_kernel, SwiGLU epilogue; the method's FLOPs, the activations' "
+           "kernel": "prefill.ffn_gate_up (gemm_deep_kernel 256 x 64 tiles, SwiGLU epilogue; the method's FLOPs, the activations' "
                      "hi and lo planes make twice that of matrix-core work)",
            "flops_per_launch": flops, "avg_us": round(avg_us, 2),
            "traffic": measured_traffic("prefill.ffn_gate_up")

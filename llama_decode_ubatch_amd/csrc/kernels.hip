@@ -1640,6 +1640,7 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
     case 5: if (EPI != EPI_SWIGLU) { launch_gemm_lds<W_BF16, EPI, 1, 4, 1, true>(a, s); return; } break;
     case 10: if (launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true>(a, s)) return; break;
     case 14: if (launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return; break;
+    case 16: if (launch_gemm_deep<EPI, 4, 4, 1, 2, 1, true>(a, s)) return; break;
     default: break;
     }
     if (EPI == EPI_RESID) {
@@ -1656,6 +1657,11 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
         launch_gemm_lds<W_BF16, EPI, 1, 4, 1, true>(a, s);
         return;
     }
+    // gate|up: the deep 256 x 64 tile with one stage of weight look-ahead
+    // in rotating register sets when there are >= 2 work-groups per CU (8B
+    // shape at 512 tokens: 203.1 us against 215.2 us for the LDS-ring tile;
+    // the same tile on the O and down products is slower)
+    if (EPI == EPI_SWIGLU && tiles(4, 4) >= 512 && launch_gemm_deep<EPI, 4, 4, 1, 2, 1, true>(a, s)) return;
     if (tiles(4, 4) >= 192)
         launch_gemm_lds<W_BF16, EPI, 4, 4, 1, true>(a, s);
     else
