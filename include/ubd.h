@@ -243,6 +243,18 @@ typedef struct ubd_context_params {
     ubd_abort_fn abort_callback;
     void *abort_user_data;
     void *stream;            /* hipStream_t for all work; NULL = null stream */
+    bool graph_reuse;        /* true (default): the first ubatch of a shape
+                                is captured as a HIP graph, and later
+                                ubatches of that shape replay it instead of
+                                launching kernel by kernel (the graph reuse
+                                of [ENG] Step 13a; [ARCH] Example 15).  The
+                                shape: tokens, output rows, attention tiles
+                                and, for ubatches of <= 16 tokens, the scan
+                                length rounded up to 256 cells.  Bypassed
+                                while kernel timing or residual keeping is
+                                on; at most 16 shapes kept, least recently
+                                used first out; results bit-identical to
+                                graph_reuse = false                         */
 } ubd_context_params;
 
 /* n_ctx 0, n_batch 2048, n_ubatch 512, n_seq_max 1, F16/F16, not unified. */
@@ -541,6 +553,10 @@ typedef struct ubd_perf {
     int32_t n_eval;         /* 1-token batches                             */
     int32_t n_ubatch;       /* forward passes enqueued                     */
     int32_t n_decode;       /* ubd_decode calls returning UBD_OK           */
+    int32_t n_graphs;       /* ubatch graphs captured                      */
+    int32_t n_reused;       /* ubatches that replayed a captured graph
+                               (the reuse count of [ARCH] Example 15's
+                               timing summary)                             */
 } ubd_perf;
 void ubd_perf_get(const ubd_context *ctx, ubd_perf *out);
 void ubd_perf_reset(ubd_context *ctx);

@@ -50,7 +50,7 @@ class ContextParams(C.Structure):
     _fields_ = [("n_ctx", C.c_uint32), ("n_batch", C.c_uint32), ("n_ubatch", C.c_uint32),
                 ("n_seq_max", C.c_uint32), ("type_k", C.c_int), ("type_v", C.c_int),
                 ("kv_unified", C.c_bool), ("abort_callback", ABORT_FN),
-                ("abort_user_data", C.c_void_p), ("stream", C.c_void_p)]
+                ("abort_user_data", C.c_void_p), ("stream", C.c_void_p), ("graph_reuse", C.c_bool)]
 
 
 class CBatch(C.Structure):
@@ -76,7 +76,7 @@ class GgufInfo(C.Structure):
 class Perf(C.Structure):
     _fields_ = [("t_load_ms", C.c_double), ("t_p_eval_ms", C.c_double), ("t_eval_ms", C.c_double),
                 ("n_p_eval", C.c_int32), ("n_eval", C.c_int32), ("n_ubatch", C.c_int32),
-                ("n_decode", C.c_int32)]
+                ("n_decode", C.c_int32), ("n_graphs", C.c_int32), ("n_reused", C.c_int32)]
 
 
 # name -> (restype, argtypes); also the list of symbols include/ubd.h declares
@@ -444,7 +444,7 @@ class Gguf:
 
 class Context:
     def __init__(self, model, n_ctx, n_batch=2048, n_ubatch=512, n_seq_max=1, type_k="f16",
-                 type_v="f16", kv_unified=False, abort_callback=None):
+                 type_v="f16", kv_unified=False, abort_callback=None, graph_reuse=True):
         self.lib = model.lib
         self.model = model
         torch = model.torch
@@ -452,6 +452,7 @@ class Context:
         p.n_ctx, p.n_batch, p.n_ubatch, p.n_seq_max = n_ctx, n_batch, n_ubatch, n_seq_max
         p.type_k, p.type_v = TYPE_IDS[type_k], TYPE_IDS[type_v]
         p.kv_unified = kv_unified
+        p.graph_reuse = graph_reuse
         self._abort = None
         if abort_callback is not None:
             self._abort = ABORT_FN(lambda ud: bool(abort_callback()))

@@ -50,6 +50,10 @@ void set_err(const std::string &m) {
     log_line(2, "%s", m.c_str());
 }
 
+// bumped by every tuning change: a captured decode-step graph holds the
+// kernel choices made when it was captured
+uint32_t g_tuning_gen = 0;
+
 }  // namespace
 
 namespace ubd {
@@ -518,6 +522,40 @@ struct ubd_context : public Executor {
     const int32_t *out_lrow() const { return info_dev + 8 * cap; }
     size_t info_ints() const { return (size_t)(13 + n_seq_words) * cap; }
 
+    // ---- decode-step graphs: each ubatch shape is captured once on
+    // cap_stream and replayed on the context stream from then on.  Every kernel of
+    // the step reads the per-ubatch values (tokens, positions, cells, tiles,
+    // scan lengths) from the token table, so a shape's graph stays valid
+    // from step to step; what its launches take by value is in the key.
+    struct GraphKey {
+        int T, n_out, n_tiles, chunk_cells, n_chunks;
+        bool operator<(const GraphKey &o) const {
+            if (T != o.T) return T < o.T;
+            if (n_out != o.n_out) return n_out < o.n_out;
+            if (n_tiles != o.n_tiles) return n_tiles < o.n_tiles;
+            if (chunk_cells != o.chunk_cells) return chunk_cells < o.chunk_cells;
+            return n_chunks < o.n_chunks;
+        }
+    };
+    struct GraphSlot {
+        hipGraphExec_t exec = nullptr;
+        uint64_t last_use = 0;
+    };
+    static constexpr size_t kGraphSlots = 16;
+    std::map<GraphKey, GraphSlot> graphs;
+    uint64_t graph_clock = 0;
+    uint32_t graph_gen = 0;
+    hipStream_t cap_stream = nullptr;
+    bool graphs_on = true;
+    void clear_graphs() {
+        if (graphs.empty()) return;
+        (void)hipStreamSynchronize(stream);
+        for (auto &kv : graphs) (void)hipGraphExecDestroy(kv.second.exec);
+        graphs.clear();
+    }
+    int32_t forward_graph(const GraphKey &key);
+    int32_t enqueue_forward(hipStream_t s, const GraphKey &key);
+
     int32_t reserve_outputs(int32_t n) override;
     int32_t run_ubatch(const UBatch &ub, int32_t k) override;
     int32_t cells_changed(const std::vector<uint8_t> &touched) override;
@@ -535,6 +573,7 @@ extern "C" ubd_context_params ubd_context_default_params(void) {
     p.type_k = UBD_TYPE_F16;
     p.type_v = UBD_TYPE_F16;
     p.kv_unified = false;
+    p.graph_reuse = true;
     return p;
 }
 
@@ -560,6 +599,7 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     c->model = model;
     c->cp = cp;
     c->stream = (hipStream_t)cp.stream;
+    c->graphs_on = cp.graph_reuse;
     c->type_k = kvt(cp.type_k);
     c->type_v = kvt(cp.type_v);
     c->mem.alloc = model->mem.alloc;
@@ -685,6 +725,8 @@ extern "C" void ubd_free(ubd_context *ctx) {
     (void)hipSetDevice(ctx->model->device);
     (void)hipStreamSynchronize(ctx->stream);
     ctx->collect_timing();
+    ctx->clear_graphs();
+    if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
     for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
     ctx->mem.release();
     for (int i = 0; i < 2; ++i) {
@@ -709,6 +751,7 @@ int32_t ubd_context::reserve_outputs(int32_t n) {
         set_err("cannot allocate the logits buffer");
         return UBD_ALLOC_FAILED;
     }
+    clear_graphs();
     logits_dev = p;
     logits_cap = want;
     return UBD_OK;
@@ -810,7 +853,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     const ubd_model &M = *model;
     const ubd_hparams &hp = M.hp;
     const int T = ub.size();
-    const int hd = M.head_dim, H = hp.n_head, Hk = hp.n_head_kv, d = hp.n_embd;
+    const int hd = M.head_dim, H = hp.n_head, Hk = hp.n_head_kv;
     const int G = H / Hk;
 
     // ---- per-ubatch token table (one H2D copy from pinned staging)
@@ -869,13 +912,99 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         return UBD_COMPUTE_FAILED;
     last_ub_idx = ub.idx;
 
+    // split-attention chunk geometry (MFMA path, ubatches of <= 16 tokens):
+    // from the scan length rounded up to a multiple of 256 cells, so
+    // consecutive decode steps launch the same grid (the kernels read each
+    // tile's exact scan length from the token table; chunks past it are
+    // empty).  One round of waves: as many chunks as the GPU holds
+    // split-kernel waves at once (a second, partial round cost config 4
+    // ~7 %), shared by the (tile, KV head) pairs; at least 64 cells each
+    // (short scans: 32-cell chunks cost config 3 decode ~3 %).
+    GraphKey key{T, n_out, n_tiles, 0, 0};
+    if (mfma_attn && split) {
+        const int scan = std::min((max_scan + 255) / 256 * 256, (int)cell_stride);
+        const int pairs = std::max(1, n_tiles * Hk);
+        const int per_pair = std::max(1, attn_wave_slots / pairs);
+        const int want = (scan + per_pair - 1) / per_pair;
+        const int cmin = std::max(ATTN_DECODE_CHUNK, g_tuning.attn_chunk_min / 32 * 32);
+        key.chunk_cells = std::max(cmin, (want + 31) / 32 * 32);
+        key.n_chunks = std::max(1, (scan + key.chunk_cells - 1) / key.chunk_cells);
+    }
+    const bool graph = graphs_on && time_mask == 0 && !dump;
+    const int32_t rc = graph ? forward_graph(key) : enqueue_forward(stream, key);
+    if (rc == UBD_OK) perf.n_ubatch += 1;
+    return rc;
+}
+
+int32_t ubd_context::forward_graph(const GraphKey &key) {
+    if (graph_gen != g_tuning_gen) {
+        clear_graphs();
+        graph_gen = g_tuning_gen;
+    }
+    auto it = graphs.find(key);
+    if (it != graphs.end()) {
+        it->second.last_use = ++graph_clock;
+        perf.n_reused += 1;
+        return hip_ok(hipGraphLaunch(it->second.exec, stream), "graph launch") ? UBD_OK : UBD_COMPUTE_FAILED;
+    }
+    // a new shape: record its kernels on the capture stream (nothing runs
+    // there), then launch the graph on the context stream
+    if (!cap_stream && hipStreamCreateWithFlags(&cap_stream, hipStreamNonBlocking) != hipSuccess) {
+        (void)hipGetLastError();
+        cap_stream = nullptr;
+        graphs_on = false;
+        log_line(1, "decode graphs off: no capture stream");
+        return enqueue_forward(stream, key);
+    }
+    if (hipStreamBeginCapture(cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        (void)hipGetLastError();
+        graphs_on = false;
+        log_line(1, "decode graphs off: stream capture unavailable");
+        return enqueue_forward(stream, key);
+    }
+    const int32_t rc = enqueue_forward(cap_stream, key);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(cap_stream, &g);
+    hipGraphExec_t exec = nullptr;
+    const bool ok = rc == UBD_OK && e == hipSuccess && g && hipGraphInstantiateWithFlags(&exec, g, 0) == hipSuccess;
+    if (g) (void)hipGraphDestroy(g);
+    if (rc != UBD_OK) return rc;     // a refused product: the eager path's error
+    if (!ok) {
+        (void)hipGetLastError();
+        graphs_on = false;
+        log_line(1, "decode graphs off: capture or instantiation failed");
+        return enqueue_forward(stream, key);
+    }
+    if (graphs.size() >= kGraphSlots) {
+        auto lru = graphs.begin();
+        for (auto j = graphs.begin(); j != graphs.end(); ++j)
+            if (j->second.last_use < lru->second.last_use) lru = j;
+        (void)hipStreamSynchronize(stream);
+        (void)hipGraphExecDestroy(lru->second.exec);
+        graphs.erase(lru);
+    }
+    GraphSlot &slot = graphs[key];
+    slot.exec = exec;
+    slot.last_use = ++graph_clock;
+    perf.n_graphs += 1;
+    return hip_ok(hipGraphLaunch(exec, stream), "graph launch") ? UBD_OK : UBD_COMPUTE_FAILED;
+}
+
+// Every kernel of one ubatch's forward pass, enqueued on s (the context
+// stream, or the capture stream while a graph is recorded).
+int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
+    const ubd_model &M = *model;
+    const ubd_hparams &hp = M.hp;
+    const int T = key.T, n_out = key.n_out, n_tiles = key.n_tiles;
+    const int hd = M.head_dim, H = hp.n_head, Hk = hp.n_head_kv, d = hp.n_embd;
+    const bool split = T <= 16;
     const TokInfo ti = tok_info();
-    const int n_cells = (int)cell_stride;   // per-stream stride of the device KV and cell tables
+    const int n_cells = (int)cell_stride;   // per-s stride of the device KV and cell tables
     const int ph = T > 16 ? 1 : 0;
     bool launched = true;     // every product accepted its arguments
     timed(0 + ph, [&] { launch_embed(M.wtype, M.embd, M.embd_scales, d, ti, T, x, cell_pos, cell_seq, n_cells, inv_freq,
-                                       hd / 2, rope_cs, stream); });
-    if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, stream), "dump");
+                                       hd / 2, rope_cs, s); });
+    if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "dump");
 
     for (int il = 0; il < hp.n_layer; ++il) {
         const auto &L = M.layers[il];
@@ -908,16 +1037,16 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         // the products that read tiled activations get them from their producer tiled
         la.x.tiled = linear_reads_tiled(la);
         if (!fuse_norm)
-            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, la.x, stream); });
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, la.x, s); });
         timed(4 + ph, [&] {
-            launched &= launch_linear(la, stream);
+            launched &= launch_linear(la, s);
             if (type_k == KV_Q8) {
                 // the epilogue staged the f32 K / V rows: quantise them into their cells
                 const int ne = Hk * hd;
                 launch_kv_quant(kv_stage, KV_F32, 2 * ne, T, ti.cell, ti.stream, 0, la.qkv.k_cache, false, Hk, hd,
-                                n_cells, kv_layer_elems, stream);
+                                n_cells, kv_layer_elems, s);
                 launch_kv_quant(kv_stage + ne, KV_F32, 2 * ne, T, ti.cell, ti.stream, 0, la.qkv.v_cache, true, Hk, hd,
-                                n_cells, kv_layer_elems, stream);
+                                n_cells, kv_layer_elems, s);
             }
         });
 
@@ -958,23 +1087,15 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         if (mfma_attn) {
             aa.split = split;
             aa.max_chunks = max_chunks_mfma;
-            // one round of waves: as many chunks as the GPU holds split-kernel
-            // waves at once (a second, partial round cost config 4 ~7 %),
-            // shared by the (tile, KV head) pairs; at least 64 cells each
-            // (short scans: 32-cell chunks cost config 3 decode ~3 %)
-            const int pairs = std::max(1, n_tiles * Hk);
-            const int per_pair = std::max(1, attn_wave_slots / pairs);
-            const int want = (max_scan + per_pair - 1) / per_pair;
-            const int cmin = std::max(ATTN_DECODE_CHUNK, g_tuning.attn_chunk_min / 32 * 32);
-            aa.chunk_cells = std::max(cmin, (want + 31) / 32 * 32);
-            aa.n_chunks_launch = std::max(1, (max_scan + aa.chunk_cells - 1) / aa.chunk_cells);
-            timed(6 + ph, [&] { launch_attention_mfma(aa, stream); });
+            aa.chunk_cells = key.chunk_cells;
+            aa.n_chunks_launch = key.n_chunks;
+            timed(6 + ph, [&] { launch_attention_mfma(aa, s); });
         } else {
             aa.max_chunks = max_chunks;
-            timed(6 + ph, [&] { launch_attention(aa, stream); });
+            timed(6 + ph, [&] { launch_attention(aa, s); });
         }
 
-        timed(8 + ph, [&] { launched &= launch_linear(lo, stream); });
+        timed(8 + ph, [&] { launched &= launch_linear(lo, s); });
 
         LinearArgs lg = lo;
         lg.w = L.gu.w;
@@ -986,7 +1107,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         if (fuse_norm_ffn) lg.norm = NormIn{x, nullptr, L.ffn_norm, hp.rms_eps, d};
         lg.x.tiled = linear_reads_tiled(lg);
         if (!fuse_norm_ffn)
-            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, lg.x, stream); });
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, lg.x, s); });
         LinearArgs ld = lo;
         ld.norm = NormIn{};
         ld.w = L.down.w;
@@ -996,11 +1117,11 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         ld.x = actC;
         ld.x.tiled = linear_reads_tiled(ld);
         lg.out = ld.x;
-        timed(10 + ph, [&] { launched &= launch_linear(lg, stream); });
-        timed(12 + ph, [&] { launched &= launch_linear(ld, stream); });
+        timed(10 + ph, [&] { launched &= launch_linear(lg, s); });
+        timed(12 + ph, [&] { launched &= launch_linear(ld, s); });
         if (dump)
             hip_ok(hipMemcpyAsync(dump + (size_t)(il + 1) * cap * d, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice,
-                                  stream), "dump");
+                                  s), "dump");
     }
     if (n_out > 0) {
         const bool fuse_norm = g_tuning.fuse_norm == 1 && linear_norm_fits(n_out, d);
@@ -1018,15 +1139,14 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         if (fuse_norm) lz.norm = NormIn{x, ti.out_tok, M.out_norm, hp.rms_eps, d};
         lz.x.tiled = linear_reads_tiled(lz);
         if (!fuse_norm)
-            timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, lz.x, stream); });
-        timed(14 + ph, [&] { launched &= launch_linear(lz, stream); });
+            timed(2 + ph, [&] { launch_rmsnorm(x, d, ti.out_tok, n_out, M.out_norm, d, hp.rms_eps, lz.x, s); });
+        timed(14 + ph, [&] { launched &= launch_linear(lz, s); });
     }
     if (!launched) {
         set_err("decode: a matrix product was given a fused norm outside its limits");
         return UBD_COMPUTE_FAILED;
     }
     if (!hip_ok(hipGetLastError(), "kernel launch")) return UBD_COMPUTE_FAILED;
-    perf.n_ubatch += 1;
     return UBD_OK;
 }
 
@@ -1516,6 +1636,7 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
     } else {
         return UBD_INVALID;
     }
+    ++g_tuning_gen;
     return UBD_OK;
 }
 

@@ -48,6 +48,7 @@ def test_default_params_and_errors_without_gpu():
     lib = binding.load_library()
     p = lib.ubd_context_default_params()
     assert (p.n_batch, p.n_ubatch, p.n_seq_max, p.type_k, p.type_v) == (2048, 512, 1, 1, 1)
+    assert p.graph_reuse is True and p.kv_unified is False
     st = ctypes.c_int32(7)
     assert not lib.ubd_model_load(None, None, 0, None, ctypes.byref(st))
     assert st.value == -1 and "missing" in binding.last_error()
