@@ -492,30 +492,69 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 // next batch is in flight while the current one is multiplied; B fragments
 // are read from LDS right before use.  k-steps are split over NW waves and
 // reduced through LDS (aliasing the activation copy).
+// q8_0 scales: the batch needs UB * RB groups of 16 words (32 f16 scales of
+// one row block and k-step, in their stored order); lane L holds NWD
+// consecutive words of them (NWD = UB * RB / 4, at least 1: with fewer than
+// 64 words the lanes past them hold none), and each step fetches a lane's
+// 4 words (rows 4g..4g+3 of its two blocks) from the lanes that hold them
+// by cross-lane permutes.  Kept whole in every lane, the scales took as
+// many registers as the codes.
+template <int RB, int UB> constexpr int q8_scale_words() { return UB * RB >= 4 ? UB * RB / 4 : 1; }
+
 template <int WT, int RB, int UB>
 struct WBatch {
+    static constexpr int NWD = WT == W_Q8 ? q8_scale_words<RB, UB>() : 1;
+    static_assert(WT != W_Q8 || ((NWD == 1 || NWD == 2) && UB * RB * 16 <= 64 * NWD), "q8_0: scale words per lane");
     u32x4_t w[UB][RB];
-    u32x2_t sc[WT == W_Q8 ? UB : 1][RB][2];
+    uint32_t sc[NWD];
 };
+
+// this lane's scale words of the batch at k-step s (words past the wave's
+// last step s1 are not loaded: no step reads them)
+template <int RB, int UB>
+__device__ __forceinline__ void load_wbatch_scales(const LinearArgs &a, int rb0, int s, int s1, int lane,
+                                                   uint32_t (&sc)[q8_scale_words<RB, UB>()]) {
+    constexpr int NWD = q8_scale_words<RB, UB>();
+    const int idx = NWD * lane;
+    const int j = idx / (UB * 16), u = (idx / 16) % UB, wd = idx % 16;
+    const bool live = idx < UB * RB * 16 && s + u < s1;
+    const uint16_t *src = a.wscale + q8_scale_ofs(a.K, rb0 + (live ? j : 0), s + (live ? u : 0), 0) + 2 * wd;
+    if (NWD == 2) {
+        u32x2_t v = {0u, 0u};
+        if (live) v = *(const u32x2_t *)src;
+        sc[0] = v[0];
+        sc[NWD - 1] = v[1];
+    } else {
+        sc[0] = live ? *(const uint32_t *)src : 0u;
+    }
+}
+
+// row block j, step u of the batch: this lane's scales (rows 4g..4g+3 of
+// blocks 2s and 2s + 1) are words 16 (j UB + u) + 4g + q, q = 0..3
+template <int RB, int UB>
+__device__ __forceinline__ void wbatch_scales(const uint32_t (&sc)[q8_scale_words<RB, UB>()], int j, int u, int g,
+                                              u32x2_t &b0, u32x2_t &b1) {
+    constexpr int NWD = q8_scale_words<RB, UB>();
+    const int w0 = (j * UB + u) * 16 + 4 * g;
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = (uint32_t)__shfl((int)sc[(w0 + i) % NWD], (w0 + i) / NWD, 64);
+    b0 = u32x2_t{q[0], q[1]};
+    b1 = u32x2_t{q[2], q[3]};
+}
 
 template <int WT, int RB, int UB>
 __device__ __forceinline__ void load_wbatch(const LinearArgs &a, int rb0, int s, int s1, int steps, int lane,
                                             WBatch<WT, RB, UB> &b) {
-    const int g = lane >> 4;
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
         if (s + u >= s1) break;
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
+        for (int j = 0; j < RB; ++j)
             b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
                                                 ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
-            if (WT == W_Q8) {
-                const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb0 + j, s + u, g));
-                b.sc[u][j][0] = u32x2_t{sv[0], sv[1]};
-                b.sc[u][j][1] = u32x2_t{sv[2], sv[3]};
-            }
-        }
     }
+    if constexpr (WT == W_Q8) load_wbatch_scales<RB, UB>(a, rb0, s, s1, lane, b.sc);
 }
 
 // load_wbatch for a batch known to be whole: no per-step exits, so the
@@ -523,20 +562,13 @@ __device__ __forceinline__ void load_wbatch(const LinearArgs &a, int rb0, int s,
 template <int WT, int RB, int UB>
 __device__ __forceinline__ void load_wbatch_whole(const LinearArgs &a, int rb0, int s, int lane,
                                                   WBatch<WT, RB, UB> &b) {
-    const int g = lane >> 4;
 #pragma unroll
-    for (int u = 0; u < UB; ++u) {
+    for (int u = 0; u < UB; ++u)
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
+        for (int j = 0; j < RB; ++j)
             b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
                                                 ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
-            if (WT == W_Q8) {
-                const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb0 + j, s + u, g));
-                b.sc[u][j][0] = u32x2_t{sv[0], sv[1]};
-                b.sc[u][j][1] = u32x2_t{sv[2], sv[3]};
-            }
-        }
-    }
+    if constexpr (WT == W_Q8) load_wbatch_scales<RB, UB>(a, rb0, s, s + UB, lane, b.sc);
 }
 
 template <int WT, int RB, int UB>
@@ -560,14 +592,11 @@ __device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const un
             const uint16_t *hi = (const uint16_t *)lds, *lo = (const uint16_t *)lds + plane;
             in.xh = *(const u32x4_t *)(hi + o);
             in.xl = *(const u32x4_t *)(lo + o);
-            if (WT == W_Q8) {
+            if constexpr (WT == W_Q8) {
                 in.xh2 = *(const u32x4_t *)(hi + o + 32);
                 in.xl2 = *(const u32x4_t *)(lo + o + 32);
 #pragma unroll
-                for (int j = 0; j < RB; ++j) {
-                    in.sc[j][0] = b.sc[u][j][0];
-                    in.sc[j][1] = b.sc[u][j][1];
-                }
+                for (int j = 0; j < RB; ++j) wbatch_scales<RB, UB>(b.sc, j, u, g, in.sc[j][0], in.sc[j][1]);
             }
         }
         mfma_step<WT, RB, WT == W_Q8>(in, acc);
@@ -890,15 +919,18 @@ __device__ __forceinline__ void ldsx_rescale(const LinearArgs &a, unsigned char 
     }
 }
 
-// 4 waves per SIMD (at most 128 registers).  q8_0 weight batches hold 2
-// k-steps: with 4 the gate|up pairs needed 2 waves per SIMD, and that was
-// slower (config 5 gate|up 30.9 against 29.7 us).
+// 4 waves per SIMD (at most 128 registers).
 template <int WT, int EPI, int NW, bool NORM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4)))
 void linear_ldsx_kernel(LinearArgs a) {
     constexpr int RB = EPI == EPI_SWIGLU ? 2 : 1;
     constexpr int KSTEP = WT_<WT>::KSTEP;
-    constexpr int UB = WT == W_Q8 ? 2 : 8 / RB;   // k-steps per weight batch
+    // k-steps per weight batch: 8 tiles per batch; q8_0: 2 k-steps, 4 for the
+    // logits (each wave's k range of the narrower q8_0 products is in flight
+    // whole with two 2-step batches; longer batches made them slower: down
+    // 17.3 -> 21.2 us, O 9.7 -> 11.0, QKV 12.3 -> 13.4 at config 5, logits
+    // 100.4 -> 96.0)
+    constexpr int UB = WT == W_Q8 ? (EPI == EPI_LOGITS ? 4 : 2) : 8 / RB;
     extern __shared__ __align__(16) unsigned char dyn_lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
