@@ -8,10 +8,11 @@ live in HBM before timing starts, and nothing else is recorded while the
 steps run.
 
 The same run then measures, outside the timed region:
-  * kernel durations from HIP events recorded on the library's stream around
-    each launch of the roofline kernels, over one extra job (`roofline`,
-    `roofline_prefill`), and over one more job around every kernel class
-    (`kernels_one_job`);
+  * kernel durations from HIP events tied to the kernel dispatches (the
+    first kernel of a launch records its start, the last its end, as a
+    kernel trace does) on every kernel class over one extra job
+    (`kernels_one_job`; the roofline kernels' figures in `roofline`,
+    `roofline_prefill` come from it);
   * end-to-end fractions: decode tok/s x algorithmic bytes per token against
     8 TB/s of HBM, prefill FLOPs / prefill time against 2.5 PFLOP/s bf16;
   * compact summaries of the 16-sequence 32K-cell decode (`config4`, same
@@ -193,8 +194,8 @@ def build_model(torch, shape):
 
 def measure(torch, model, w, steps, warmup):
     """Times `steps` whole jobs of workload w with nothing else recorded,
-    then runs one job with HIP events around the roofline kernels and one
-    with events around every kernel class."""
+    then runs one job with HIP events on every kernel class (the roofline
+    kernels among them)."""
     import numpy as np
     from llama_decode_ubatch_amd import Context
     from workloads import prompt_tokens
@@ -221,18 +222,15 @@ def measure(torch, model, w, steps, warmup):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
-    # kernel durations outside the timed region
-    hot = "decode.attention" if w.kv_prefill else "decode.ffn_gate_up"
-    ctx.kernel_timing([hot, "prefill.ffn_gate_up"])
-    ctx.kernel_stats()
-    run_job(ctx, w, prompt, first)
-    hot_stats = {k: {"launches": n, "avg_us": 1e3 * ms / n} for k, (n, ms) in ctx.kernel_stats().items()}
+    # kernel durations outside the timed region: one job with events on
+    # every kernel class (the roofline kernels included)
     ctx.kernel_timing(None)
+    ctx.kernel_stats()
     run_job(ctx, w, prompt, first)
     per_class = {k: {"launches": n, "avg_us": 1e3 * ms / n} for k, (n, ms) in ctx.kernel_stats().items()}
     ctx.kernel_timing([])
     ctx.free()
-    log(f"[{w.name}] per-class breakdown of one job (events on every launch):")
+    log(f"[{w.name}] per-class breakdown of one job (kernel execution, events on every launch):")
     for k, v in sorted(per_class.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["launches"]):
         log(f"  {k:22s} {v['launches']:6d} launches  avg {v['avg_us']:9.2f} us  "
             f"total {v['avg_us'] * v['launches'] / 1e3:9.2f} ms")
@@ -243,7 +241,6 @@ def measure(torch, model, w, steps, warmup):
         "ms_per_step": 1e3 * elapsed / steps,
         "prefill_tok_s": w.n_prompt * steps / tp_sum if w.n_prompt else None,
         "decode_tok_s": w.n_decode * w.n_seqs * steps / td_sum,
-        "hot": hot_stats,
         "per_class": per_class,
     }
     # end-to-end fractions of the rooflines
@@ -265,9 +262,9 @@ def roofline_of(w, r):
     shape = w.model
     d, F = shape.n_embd, shape.n_ff
     hot = "decode.attention" if w.kv_prefill else "decode.ffn_gate_up"
-    if hot not in r["hot"]:
+    if hot not in r["per_class"]:
         return None
-    avg_s = r["hot"][hot]["avg_us"] * 1e-6
+    avg_s = r["per_class"][hot]["avg_us"] * 1e-6
     if hot == "decode.attention":
         # each launch reads every sequence's visible K and V cells once; the
         # cache grows by one cell per sequence per step
@@ -283,9 +280,9 @@ def roofline_of(w, r):
     ach = alg / avg_s / 1e9
     out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
-           "bytes_per_launch": int(alg), "avg_us": round(r["hot"][hot]["avg_us"], 2),
-           "timing": "HIP events on the library stream around each launch, one job after the timed region "
-                     "(each interval also holds the dispatch of the launch)"}
+           "bytes_per_launch": int(alg), "avg_us": round(r["per_class"][hot]["avg_us"], 2),
+           "timing": "HIP events tied to the kernel dispatches (start of the first kernel to end of the last), "
+                     "one job after the timed region with every kernel class timed"}
     tr = traced_avg_us(hot, shape.wtype)
     if tr:
         out["trace_avg_us"] = tr
@@ -294,11 +291,11 @@ def roofline_of(w, r):
 
 
 def roofline_prefill_of(w, r):
-    if "prefill.ffn_gate_up" not in r["hot"] or not w.n_prompt:
+    if "prefill.ffn_gate_up" not in r["per_class"] or not w.n_prompt:
         return None
     shape = w.model
     flops = 2.0 * w.n_prompt * 2 * shape.n_ff * shape.n_embd
-    avg_us = r["hot"]["prefill.ffn_gate_up"]["avg_us"]
+    avg_us = r["per_class"]["prefill.ffn_gate_up"]["avg_us"]
     ach = flops / (avg_us * 1e-6) / 1e12
     out = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
@@ -307,7 +304,8 @@ def roofline_prefill_of(w, r):
            "flops_per_launch": flops, "avg_us": round(avg_us, 2),
            "traffic": measured_traffic("prefill.ffn_gate_up")
            if shape.wtype == "bf16" and w.n_prompt == 512 else None,
-           "timing": "HIP events on the library stream around each launch, one job after the timed region"}
+           "timing": "HIP events tied to the kernel dispatches (start of the first kernel to end of the last), "
+                     "one job after the timed region with every kernel class timed"}
     tr = traced_avg_us("prefill.ffn_gate_up", shape.wtype)
     if tr:
         out["trace_avg_us"] = tr

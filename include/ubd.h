@@ -490,7 +490,10 @@ int32_t ubd_debug_get_residual(ubd_context *ctx, int32_t layer, float *out,
 int32_t ubd_debug_last_ubatch(ubd_context *ctx, int32_t *batch_idx,
                               int32_t cap);
 
-/* Kernel timing with HIP events on the context's stream.  Kernels fall in
+/* Kernel timing with HIP events tied to the kernel dispatches (the first
+ * kernel of a timed launch records its start, the last its end, so a
+ * launch's interval is its kernels' execution without their dispatch, the
+ * durations a kernel trace reports).  Kernels fall in
  * classes 2*kind + phase, phase 0 for ubatches of <= 16 tokens (decode) and
  * 1 for larger ones (prefill), kind 0 embed, 1 rmsnorm, 2 qkv (+RoPE and
  * K/V append), 3 attention (partial + combine), 4 attn_output (+residual),
@@ -534,11 +537,12 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * "small_rb" (1 =
  * products of 3..16 tokens share activation fragments over 4 row blocks
  * or split k, 0 = one row block per work-group), "prefill_lo" (bf16
- * prefill products: 1 = the activations' hi and lo bf16 planes both enter
- * the matrix cores, 0 = the hi plane only, i.e. bf16-rounded activations,
- * which leaves about 6e-3 of relative error per 8B-shaped layer; with it
- * the forced shapes are 1, 3, 5, 10 and 14).
- * Results do not depend on them beyond rounding, except "prefill_lo" 0.
+ * prefill products whose activations enter the matrix cores as hi and lo
+ * bf16 planes, a mask of bits 1 QKV, 2 O, 4 gate|up, 8 down, 16 logits;
+ * default 31 = all; the others take the hi plane only, i.e. bf16-rounded
+ * activations, which leaves about 6e-3 of relative error per 8B-shaped
+ * layer; with both planes the forced shapes are 1, 3, 5, 10, 14 and 16).
+ * Results do not depend on them beyond rounding, except "prefill_lo".
  * The knobs are process-wide and unsynchronised: set them while no other
  * thread is inside the library; every context sees the change.  0, or -1
  * for an unknown key. */

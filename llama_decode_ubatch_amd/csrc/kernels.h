@@ -48,12 +48,22 @@ struct Tuning {
     int gemm_wpd = 0;         // LDS-ring product: stages of weight look-ahead (1 or 2; 0 = per shape)
     int gemm_deep = 1;        // bf16 residual / QKV prefill products: 1 = deep look-ahead kernel where it fits
     int act_tiled = 1;        // prefill products read activations tiled in MFMA operand order (0 = row-major)
-    int prefill_lo = 1;       // bf16 prefill products: 1 = hi + lo activation planes (two products per
-                              // fragment), 0 = the hi plane only (bf16-rounded activations)
+    int prefill_lo = 31;      // bf16 prefill products whose activations enter as hi + lo planes (two
+                              // products per fragment), bit 1 << Prod; the others take the hi plane
+                              // only (bf16-rounded activations)
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;
 extern Tuning g_tuning;
+
+// Kernel timing: while stop is set, every launch of this thread records
+// stop when its kernel ends and the first one records start when its
+// kernel begins (events tied to the dispatches themselves, so a timed
+// region spans its kernels' execution, not their dispatch).
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTiming g_launch_timing;
 enum KVType : int { KV_F32 = 0, KV_F16 = 1, KV_Q8 = 2 };
 // One layer of one cache (K or V) holding `elems` values: f32 / f16 values,
 // or for q8_0 the int8 codes (in the f16 layouts) followed by one f16 scale
@@ -87,6 +97,9 @@ struct TokInfo {
 };
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_LOGITS = 4 };
+// The products of a layer and the output head (bit positions of the
+// prefill_lo tuning mask)
+enum Prod : int { PROD_QKV = 0, PROD_O = 1, PROD_GATE_UP = 2, PROD_DOWN = 3, PROD_LOGITS = 4 };
 
 struct QKVEpi {
     int n_q_rows = 0, n_k_rows = 0;   // H*hd, Hk*hd
@@ -129,6 +142,7 @@ struct LinearArgs {
     QKVEpi qkv;
     NormIn norm;                      // set: input is x normalised on the fly (T <= NORM_TMAX)
     int early = 1;                    // LDS-staged product: one-token activation loads may go first
+    int prod = PROD_QKV;              // which product this is (Prod)
     float *split_out = nullptr;       // RESID prefill products: scratch for k-slice partial sums,
                                       // [MAX_K_SLICES][T][N] f32 (null: no k split)
 };

@@ -5,6 +5,7 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -14,6 +15,17 @@
 namespace ubd {
 
 Tuning g_tuning;
+thread_local LaunchTiming g_launch_timing;
+
+#define UBD_LAUNCH(K, G, B, SH, S, ...)                                                                         \
+    do {                                                                                                        \
+        if (g_launch_timing.stop) {                                                                             \
+            hipExtLaunchKernelGGL(K, G, B, SH, S, g_launch_timing.start, g_launch_timing.stop, 0, __VA_ARGS__); \
+            g_launch_timing.start = nullptr;                                                                    \
+        } else {                                                                                                \
+            hipLaunchKernelGGL(K, G, B, SH, S, __VA_ARGS__);                                                    \
+        }                                                                                                       \
+    } while (0)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -1613,11 +1625,11 @@ static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
     if (SPLITK > 1 && (EPI != EPI_RESID || !a.split_out || a.N % 4)) return false;
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
-    hipLaunchKernelGGL((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK, LO>), dim3(n_wtiles * n_ttiles * SPLITK),
+    UBD_LAUNCH((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK, LO>), dim3(n_wtiles * n_ttiles * SPLITK),
                        dim3(256), 0, s, a, n_wtiles, n_ttiles);
     if (SPLITK > 1) {
         const long n = (long)a.T * (a.N / 4);
-        hipLaunchKernelGGL(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
+        UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
                            a.split_out, a.T, a.N, SPLITK);
     }
     return true;
@@ -1641,14 +1653,14 @@ static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
     // 64-wide stages: the kernel then fits 2 waves per SIMD (two work-groups
     // per CU), which hides the LDS reads and barriers of one behind the other
     if (wpd == 2)
-        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 2, LO>), dim3(total), dim3(256), 0, s, a,
+        UBD_LAUNCH((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 2, LO>), dim3(total), dim3(256), 0, s, a,
                            n_wtiles, n_ttiles);
     else
-        hipLaunchKernelGGL((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 1, LO>), dim3(total), dim3(256), 0, s, a,
+        UBD_LAUNCH((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 1, LO>), dim3(total), dim3(256), 0, s, a,
                            n_wtiles, n_ttiles);
     if (SPLITK > 1) {
         const long n = (long)a.T * (a.N / 4);
-        hipLaunchKernelGGL(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
+        UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
                            a.split_out, a.T, a.N, SPLITK);
     }
 }
@@ -1676,8 +1688,14 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
     default: break;
     }
     if (EPI == EPI_RESID) {
-        // long k (FFN down): k split in two through scratch
-        if (a.K >= 8192 && tiles(2, 4) * 2 >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return;
+        // k split over slices through scratch: forced (2 or 4), else in two
+        // for long k (FFN down)
+        constexpr int RS4 = EPI == EPI_RESID ? 4 : 1;
+        if (g_tuning.gemm_split == 4 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS4, true>(a, s)) return;
+        if (g_tuning.gemm_split == 2 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return;
+        if (g_tuning.gemm_split == 0 && a.K >= 8192 && tiles(2, 4) * 2 >= 192 &&
+            launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s))
+            return;
         if (tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true>(a, s)) return;
         launch_gemm_lds<W_BF16, EPI, 2, 4, 1, true>(a, s);
         return;
@@ -1705,7 +1723,7 @@ static void launch_gemm_lds_shape(const LinearArgs &a, hipStream_t s) {
     auto tiles = [&](int rbw, int tb) {
         return (long)((a.N + 64 * rbw - 1) / (64 * rbw)) * ((a.T + 16 * tb - 1) / (16 * tb));
     };
-    if (WT == W_BF16 && g_tuning.prefill_lo != 0) {
+    if (WT == W_BF16 && ((g_tuning.prefill_lo >> a.prod) & 1)) {
         launch_gemm_lds_shape_lo<EPI>(a, s);
         return;
     }
@@ -1787,7 +1805,7 @@ static void launch_gemm(const LinearArgs &a, hipStream_t s) {
     const int n_wtiles = (a.N + 255) / 256;
     const int n_ttiles = (a.T + BT - 1) / BT;
     const int total = n_wtiles * n_ttiles * SPLITK;
-    hipLaunchKernelGGL((gemm_kernel<WT, EPI, BT, SPLITK>), dim3(total), dim3(256), 0, s, a, n_wtiles, n_ttiles);
+    UBD_LAUNCH((gemm_kernel<WT, EPI, BT, SPLITK>), dim3(total), dim3(256), 0, s, a, n_wtiles, n_ttiles);
 }
 
 // True if the product was issued as a GEMM (bf16 / q8_0 weights, >= 64
@@ -1846,9 +1864,9 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
 #define UBD_LAUNCH_LDSX(NW_)                                                                                \
     do {                                                                                                    \
         if (norm)                                                                                           \
-            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, true>), grid, dim3(64 * NW_), bytes, s, la); \
+            UBD_LAUNCH((linear_ldsx_kernel<WT, EPI, NW_, true>), grid, dim3(64 * NW_), bytes, s, la); \
         else                                                                                                \
-            hipLaunchKernelGGL((linear_ldsx_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), bytes, s, la); \
+            UBD_LAUNCH((linear_ldsx_kernel<WT, EPI, NW_, false>), grid, dim3(64 * NW_), bytes, s, la); \
     } while (0)
         if (nw == 4)
             UBD_LAUNCH_LDSX(4);
@@ -1869,30 +1887,30 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
             dim3 g4(nrb / 4, grid.y);
             const int nw4 = nrb / 4 >= 768 ? 4 : 8;
             if (nw4 == 4)
-                hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 4, false, 4, 1>), g4, dim3(256), 0, s, a);
+                UBD_LAUNCH((linear_small_kernel<WT, EPI, 4, false, 4, 1>), g4, dim3(256), 0, s, a);
             else
-                hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 8, false, 4, 1>), g4, dim3(512), 0, s, a);
+                UBD_LAUNCH((linear_small_kernel<WT, EPI, 8, false, 4, 1>), g4, dim3(512), 0, s, a);
             return;
         }
         // narrower products that cannot split k (QKV): 2 row blocks, 16 waves
         if (nrb % 2 == 0 && nrb / 2 >= 192) {
             dim3 g2(nrb / 2, grid.y);
-            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 16, false, 2, 1>), g2, dim3(1024), 0, s, a);
+            UBD_LAUNCH((linear_small_kernel<WT, EPI, 16, false, 2, 1>), g2, dim3(1024), 0, s, a);
             return;
         }
         constexpr int KSPLIT = EPI == EPI_RESID ? 4 : 1;
         if (KSPLIT > 1 && nrb % 4 == 0 && (a.K / WT_<WT>::KSTEP) % 32 == 0) {
             dim3 g4(nrb / 4, grid.y, KSPLIT);
-            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, 8, false, 4, KSPLIT>), g4, dim3(512), 0, s, a);
+            UBD_LAUNCH((linear_small_kernel<WT, EPI, 8, false, 4, KSPLIT>), g4, dim3(512), 0, s, a);
             return;
         }
     }
 #define UBD_LAUNCH_SMALL(NW_)                                                                            \
     do {                                                                                                 \
         if (norm)                                                                                        \
-            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, true, RB, 1>), grid, dim3(64 * NW_), lds, s, a); \
+            UBD_LAUNCH((linear_small_kernel<WT, EPI, NW_, true, RB, 1>), grid, dim3(64 * NW_), lds, s, a); \
         else                                                                                             \
-            hipLaunchKernelGGL((linear_small_kernel<WT, EPI, NW_, false, RB, 1>), grid, dim3(64 * NW_), 0, s, a); \
+            UBD_LAUNCH((linear_small_kernel<WT, EPI, NW_, false, RB, 1>), grid, dim3(64 * NW_), 0, s, a); \
     } while (0)
     if (nw == 4)
         UBD_LAUNCH_SMALL(4);
@@ -1980,7 +1998,7 @@ void launch_embed(int wtype, const void *table, const uint16_t *scales, int d, c
                   float *x, int32_t *cell_pos, uint32_t *cell_seq, int n_cells, const double *inv_freq,
                   int half_dim, float2 *rope_cs, hipStream_t s) {
     if (T <= 0) return;
-    hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, s, wtype, table, scales, d, ti, x, cell_pos,
+    UBD_LAUNCH(embed_kernel, dim3(T), dim3(256), 0, s, wtype, table, scales, d, ti, x, cell_pos,
                        cell_seq, n_cells, inv_freq, half_dim, rope_cs);
 }
 
@@ -2085,10 +2103,10 @@ void launch_rmsnorm(const float *x, int ldx, const int32_t *row_map, int rows, c
                     float eps, const Act &out, hipStream_t s) {
     if (rows <= 0) return;
     if (out.tiled) {
-        hipLaunchKernelGGL(rmsnorm_tiled_kernel, dim3(rows), dim3(256), 0, s, x, ldx, row_map, gain, d, eps, out);
+        UBD_LAUNCH(rmsnorm_tiled_kernel, dim3(rows), dim3(256), 0, s, x, ldx, row_map, gain, d, eps, out);
         return;
     }
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, ldx, row_map, gain, d, eps, out);
+    UBD_LAUNCH(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x, ldx, row_map, gain, d, eps, out);
 }
 
 // ------------------------------------------------------------ attention
@@ -2260,8 +2278,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 template <int HD>
 static void launch_attention_hd(const AttnArgs &a, hipStream_t s) {
     dim3 grid(a.max_chunks, a.n_tiles, a.n_head_kv);
-    hipLaunchKernelGGL(attn_partial_kernel<HD>, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_combine_kernel<HD>, dim3(a.T * a.n_head), dim3(128), 0, s, a);
+    UBD_LAUNCH(attn_partial_kernel<HD>, grid, dim3(256), 0, s, a);
+    UBD_LAUNCH(attn_combine_kernel<HD>, dim3(a.T * a.n_head), dim3(128), 0, s, a);
 }
 
 void launch_attention(const AttnArgs &a, hipStream_t s) {
@@ -2726,16 +2744,16 @@ static void launch_attention_mfma_hd(const AttnArgs &a, hipStream_t s) {
     if (a.split) {
         dim3 grid((unsigned)a.n_chunks_launch, a.n_tiles, a.n_head_kv);
         if (q8)
-            hipLaunchKernelGGL((attn_mfma_kernel<HD, true, true>), grid, dim3(64), 0, s, a);
+            UBD_LAUNCH((attn_mfma_kernel<HD, true, true>), grid, dim3(64), 0, s, a);
         else
-            hipLaunchKernelGGL((attn_mfma_kernel<HD, true, false>), grid, dim3(64), 0, s, a);
-        hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(a.T * a.n_head), dim3(64), 0, s, a);
+            UBD_LAUNCH((attn_mfma_kernel<HD, true, false>), grid, dim3(64), 0, s, a);
+        UBD_LAUNCH((attn_merge_kernel<HD>), dim3(a.T * a.n_head), dim3(64), 0, s, a);
     } else {
         dim3 grid(1, a.n_tiles, a.n_head_kv);
         if (q8)
-            hipLaunchKernelGGL((attn_mfma_kernel<HD, false, true>), grid, dim3(64), 0, s, a);
+            UBD_LAUNCH((attn_mfma_kernel<HD, false, true>), grid, dim3(64), 0, s, a);
         else
-            hipLaunchKernelGGL((attn_mfma_kernel<HD, false, false>), grid, dim3(64), 0, s, a);
+            UBD_LAUNCH((attn_mfma_kernel<HD, false, false>), grid, dim3(64), 0, s, a);
     }
 }
 
@@ -2844,15 +2862,15 @@ __global__ __launch_bounds__(256) void argmax_final_kernel(const float *pv, cons
 void launch_argmax_two_pass(const float *logits, int ld, int n_rows, int n, int32_t *out, float *pv, int32_t *pi,
                             hipStream_t s) {
     if (n_rows <= 0) return;
-    hipLaunchKernelGGL(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld,
+    UBD_LAUNCH(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld,
                        (const int32_t *)nullptr, n, out, pv, pi, (int32_t *)nullptr);
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(n_rows), dim3(256), 0, s, pv, pi, ARGMAX_BLOCKS, out);
+    UBD_LAUNCH(argmax_final_kernel, dim3(n_rows), dim3(256), 0, s, pv, pi, ARGMAX_BLOCKS, out);
 }
 
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows, int n, int32_t *out,
                    const ArgmaxWork &w, hipStream_t s) {
     if (n_rows <= 0) return;
-    hipLaunchKernelGGL(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld, rows, n, out, w.pv,
+    UBD_LAUNCH(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld, rows, n, out, w.pv,
                        w.pi, w.counter);
 }
 
@@ -2944,10 +2962,10 @@ void launch_relayout(int wtype, const RelayoutSrc *src, int n_src, int mode, int
     a.dst = dst;
     a.dst_scales = dst_scales;
     const size_t total = (size_t)(a.N / 16) * a.steps * 64;
-    hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    UBD_LAUNCH(relayout_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     if (wtype == W_Q8) {
         const size_t ts = (size_t)a.N * (K / 32);
-        hipLaunchKernelGGL(relayout_scales_kernel, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, s, a);
+        UBD_LAUNCH(relayout_scales_kernel, dim3((unsigned)((ts + 255) / 256)), dim3(256), 0, s, a);
     }
 }
 
@@ -2999,7 +3017,7 @@ void launch_kv_store(const void *src, int src_type, int n, const int32_t *cells,
     if (n <= 0) return;
     const int W = n_head_kv * hd;
     dim3 grid((n + 63) / 64, (W + 63) / 64);
-    hipLaunchKernelGGL(kv_store_kernel, grid, dim3(256), 0, s, src, src_type, n, cells, cache, type,
+    UBD_LAUNCH(kv_store_kernel, grid, dim3(256), 0, s, src, src_type, n, cells, cache, type,
                        (int)transposed, stream, n_head_kv, hd, n_cells);
 }
 
@@ -3030,7 +3048,7 @@ void launch_kv_load(const void *cache, int type, bool transposed, int stream, in
                     int hd, int n_cells, size_t layer_elems, float *out, hipStream_t s) {
     if (n <= 0) return;
     const size_t total = (size_t)n * n_head_kv * hd;
-    hipLaunchKernelGGL(kv_load_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, cache, type,
+    UBD_LAUNCH(kv_load_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, cache, type,
                        (int)transposed, stream, cell0, n, n_head_kv, hd, n_cells, layer_elems, out);
 }
 
@@ -3081,13 +3099,13 @@ void launch_kv_move(void *cache, int type, bool transposed, int stream, const in
     const size_t total = (size_t)n * n_head_kv * hd;
     const dim3 grid((unsigned)((total + 255) / 256));
     if (type == KV_F32)
-        hipLaunchKernelGGL(kv_move_kernel<uint32_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
+        UBD_LAUNCH(kv_move_kernel<uint32_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
                            n, n_head_kv, hd, n_cells, layer_elems, 0, tmp, (int)to_tmp);
     else if (type == KV_F16)
-        hipLaunchKernelGGL(kv_move_kernel<uint16_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
+        UBD_LAUNCH(kv_move_kernel<uint16_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
                            n, n_head_kv, hd, n_cells, layer_elems, 0, tmp, (int)to_tmp);
     else
-        hipLaunchKernelGGL(kv_move_kernel<uint8_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
+        UBD_LAUNCH(kv_move_kernel<uint8_t>, grid, dim3(256), 0, s, cache, (int)transposed, stream, cells,
                            n, n_head_kv, hd, n_cells, layer_elems, 1, tmp, (int)to_tmp);
 }
 
@@ -3106,7 +3124,7 @@ __global__ __launch_bounds__(256) void q8_blocks_split_kernel(const uint16_t *bl
 void launch_q8_blocks_split(const void *blocks, size_t n_blocks, int8_t *codes, uint16_t *scales,
                             hipStream_t s) {
     if (n_blocks == 0) return;
-    hipLaunchKernelGGL(q8_blocks_split_kernel, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, s,
+    UBD_LAUNCH(q8_blocks_split_kernel, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, s,
                        (const uint16_t *)blocks, n_blocks, codes, scales);
 }
 
@@ -3117,7 +3135,7 @@ __global__ __launch_bounds__(256) void f16_to_f32_kernel(const uint16_t *src, si
 
 void launch_f16_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t s) {
     if (n == 0) return;
-    hipLaunchKernelGGL(f16_to_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, n, dst);
+    UBD_LAUNCH(f16_to_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, n, dst);
 }
 
 // q8_0 quantisation of KV rows into their cells: 32 lanes per 32-value
@@ -3159,7 +3177,7 @@ void launch_kv_quant(const void *src, int src_type, int ld, int n, const int32_t
                      hipStream_t s) {
     if (n <= 0) return;
     const size_t threads = (size_t)n * n_head_kv * hd;   // one lane per value
-    hipLaunchKernelGGL(kv_quant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, src, src_type, ld,
+    UBD_LAUNCH(kv_quant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, src, src_type, ld,
                        n, cells, streams, stream, cache, (int)is_v, n_head_kv, hd, n_cells, layer_elems);
 }
 

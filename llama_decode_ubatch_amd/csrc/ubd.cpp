@@ -484,9 +484,9 @@ struct ubd_context : public Executor {
             return;
         }
         hipEvent_t a = take_event(), b = take_event();
-        (void)hipEventRecord(a, stream);
+        g_launch_timing = {a, b};
         launch();
-        (void)hipEventRecord(b, stream);
+        g_launch_timing = {};
         pending.push_back({cls, a, b});
     }
     void collect_timing() {
@@ -1021,6 +1021,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         la.K = L.qkv.cols;
         la.x = actA;
         la.epi = EPI_QKV;
+        la.prod = PROD_QKV;
         la.qkv.n_q_rows = H * hd;
         la.qkv.n_k_rows = Hk * hd;
         la.qkv.head_dim = hd;
@@ -1079,6 +1080,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         lo.K = L.o.cols;
         lo.x = actB;
         lo.epi = EPI_RESID;
+        lo.prod = PROD_O;
         lo.y = x;
         lo.ldy = d;
         lo.split_out = split_scratch;
@@ -1104,6 +1106,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         lg.K = L.gu.cols;
         lg.x = actA;
         lg.epi = EPI_SWIGLU;
+        lg.prod = PROD_GATE_UP;
         if (fuse_norm_ffn) lg.norm = NormIn{x, nullptr, L.ffn_norm, hp.rms_eps, d};
         lg.x.tiled = linear_reads_tiled(lg);
         if (!fuse_norm_ffn)
@@ -1111,6 +1114,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         LinearArgs ld = lo;
         ld.norm = NormIn{};
         ld.w = L.down.w;
+        ld.prod = PROD_DOWN;
         ld.wscale = L.down.scales;
         ld.N = L.down.rows;
         ld.K = L.down.cols;
@@ -1134,6 +1138,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         lz.x = actA;
         lz.T = n_out;
         lz.epi = EPI_LOGITS;
+        lz.prod = PROD_LOGITS;
         lz.row_map = out_lrow();
         lz.logits = logits_dev;
         if (fuse_norm) lz.norm = NormIn{x, ti.out_tok, M.out_norm, hp.rms_eps, d};

@@ -55,7 +55,7 @@ def gpu_logits(model, tokens, gemm, shape=0, tiled=1, lo=1, split=0):
     set_tuning("gemm", gemm)
     set_tuning("gemm_shape", shape)
     set_tuning("act_tiled", tiled)
-    set_tuning("prefill_lo", lo)
+    set_tuning("prefill_lo", 31 if lo else 0)
     set_tuning("gemm_split", split)
     try:
         ctx = Context(model, n_ctx=512, n_batch=512, n_ubatch=512, n_seq_max=1, type_k="f16", type_v="f16")
@@ -65,7 +65,7 @@ def gpu_logits(model, tokens, gemm, shape=0, tiled=1, lo=1, split=0):
         set_tuning("gemm", 1)
         set_tuning("gemm_shape", 0)
         set_tuning("act_tiled", 1)
-        set_tuning("prefill_lo", 1)
+        set_tuning("prefill_lo", 31)
         set_tuning("gemm_split", 0)
 
 
