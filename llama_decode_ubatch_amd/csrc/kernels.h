@@ -140,7 +140,7 @@ struct LinearArgs {
     float *logits = nullptr;          // LOGITS: [rows][N]
     TokInfo tok;                      // QKV: pos / stream / cell per token
     QKVEpi qkv;
-    NormIn norm;                      // set: input is x normalised on the fly (T <= NORM_TMAX)
+    NormIn norm;                      // set: input is x normalised on the fly (T <= 16)
     int early = 1;                    // LDS-staged product: one-token activation loads may go first
     int prod = PROD_QKV;              // which product this is (Prod)
     float *split_out = nullptr;       // RESID prefill products: scratch for k-slice partial sums,
@@ -154,7 +154,7 @@ constexpr int MAX_K_SLICES = 4;
 // nothing, when a fused norm is asked for outside linear_norm_fits.
 bool launch_linear(const LinearArgs &a, hipStream_t s);
 // True when a product over T input rows of K values can take its RMSNorm
-// fused (a.norm): few rows, whose normalised copy fits the LDS stage.
+// fused (a.norm): the one- and few-token products (T <= 16).
 bool linear_norm_fits(int T, int K);
 // True when launch_linear(a) runs a product that reads its input activations
 // in the tiled layout (the LDS-ring prefill products); the producer of a.x

@@ -202,6 +202,63 @@ __device__ __forceinline__ void load_step(const LinearArgs &a, const unsigned ch
     }
 }
 
+// load_step for a product that normalises its input on the fly (XN): the
+// activations are the raw f32 rows of the residual times the norm gain,
+// split into bf16 hi + lo planes in registers (f32 weights: used as they
+// are); the token's 1/rms, whose sum of squares ss accumulates here over
+// this lane's values, scales the sums in the epilogue.  The rows are
+// a.norm.x (row map a.norm.rows).
+template <int WT, int RB>
+__device__ __forceinline__ void load_step_xn(const LinearArgs &a, int rb0, int s, int lane, int tok, bool tok_ok,
+                                             StepIn<WT, RB> &in, float &ss) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+        const size_t tile = (size_t)s * (a.N / 16) + rb0 + j;
+        in.w[j] = ldg_nt((const u32x4_t *)((const char *)a.w + tile * 1024 + lane * 16));
+    }
+    const float *xr = a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[tok] : tok) * a.norm.ld;
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    // 8 values from k: x * gain as bf16 hi and lo planes
+    auto split8 = [&](int k, u32x4_t &h, u32x4_t &l) {
+        const f32x4_t x0 = tok_ok ? *(const f32x4_t *)(xr + k) : z, x1 = tok_ok ? *(const f32x4_t *)(xr + k + 4) : z;
+        const f32x4_t g0 = *(const f32x4_t *)(a.norm.gain + k), g1 = *(const f32x4_t *)(a.norm.gain + k + 4);
+        ss += x0[0] * x0[0] + x0[1] * x0[1] + x0[2] * x0[2] + x0[3] * x0[3] + x1[0] * x1[0] + x1[1] * x1[1] +
+              x1[2] * x1[2] + x1[3] * x1[3];
+        const f32x4_t y0 = x0 * g0, y1 = x1 * g1;
+        uint16_t hh[8], ll[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float y = e < 4 ? y0[e] : y1[e - 4];
+            hh[e] = f2bf(y);
+            ll[e] = f2bf(y - bf2f(hh[e]));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = (uint32_t)hh[2 * e] | ((uint32_t)hh[2 * e + 1] << 16);
+            l[e] = (uint32_t)ll[2 * e] | ((uint32_t)ll[2 * e + 1] << 16);
+        }
+    };
+    if (WT == W_F32) {
+        const int k = 16 * s + 4 * g;
+        const f32x4_t x = tok_ok ? *(const f32x4_t *)(xr + k) : z;
+        ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+        in.xh = __builtin_bit_cast(u32x4_t, x * *(const f32x4_t *)(a.norm.gain + k));
+    } else {
+        const int k = (WT == W_BF16 ? 32 : 64) * s + 8 * g;
+        split8(k, in.xh, in.xl);
+        if (WT == W_Q8) {
+            split8(k + 32, in.xh2, in.xl2);
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb0 + j, s, g));
+                in.sc[j][0] = u32x2_t{sv[0], sv[1]};
+                in.sc[j][1] = u32x2_t{sv[2], sv[3]};
+            }
+        }
+    }
+}
+
 // OFS (q8_0, LDS-staged decode products): the codes (stored as q + 128)
 // enter f16 MFMAs against f16 activation planes.
 template <int WT, int RB, bool OFS = false>
@@ -417,13 +474,19 @@ __device__ void norm_prologue(const LinearArgs &a, unsigned char *lds) {
 
 // RB row blocks per work-group share each k-step's activation fragment
 // (SWIGLU: RB/2 gate|up pairs); KSPLIT > 1 (residual products only) splits
-// k over grid.z and adds the partial sums atomically.
-template <int WT, int EPI, int NW, bool NORM, int RB, int KSPLIT>
+// k over grid.z and adds the partial sums atomically.  The input's RMSNorm
+// fused: NORM stages the normalised rows in LDS (at most NORM_TMAX rows);
+// XN normalises on the fly (load_step_xn), each work-group covering the
+// whole k range of its rows and so the whole sum of squares of each token.
+template <int WT, int EPI, int NW, bool NORM, int RB, int KSPLIT, bool XN = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void linear_small_kernel(LinearArgs a) {
     static_assert(EPI != EPI_SWIGLU || RB % 2 == 0, "gate|up pairs");
     static_assert(KSPLIT == 1 || EPI == EPI_RESID, "k split only for residual products");
+    static_assert(!XN || (!NORM && KSPLIT == 1), "on-the-fly norm: whole k range per work-group");
     // k-steps per batch: the same 16-byte weight loads in flight per lane
-    constexpr int KSTEP = WT_<WT>::KSTEP, U = WT_<WT>::U / RB > 0 ? WT_<WT>::U / RB : 1;
+    // (half with XN, whose f32 rows and gains take twice the registers)
+    constexpr int U0 = WT_<WT>::U / RB > 0 ? WT_<WT>::U / RB : 1;
+    constexpr int KSTEP = WT_<WT>::KSTEP, U = XN && U0 > 1 ? U0 / 2 : U0;
     extern __shared__ __align__(16) unsigned char dyn_lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -455,11 +518,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
         norm_prologue<WT, NW>(a, dyn_lds);
     }
 
+    float ss = 0.f;                                 // XN: this lane's share of its token's sum of squares
     for (int s = s0; s < s1; s += U) {
         StepIn<WT, RB> in[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (s + u < s1) load_step<WT, RB, NORM>(a, dyn_lds, rb0, s + u, steps, lane, tok, tok_ok, in[u]);
+            if (s + u < s1) {
+                if constexpr (XN)
+                    load_step_xn<WT, RB>(a, rb0, s + u, lane, tok, tok_ok, in[u], ss);
+                else
+                    load_step<WT, RB, NORM>(a, dyn_lds, rb0, s + u, steps, lane, tok, tok_ok, in[u]);
+            }
         if (NORM && s == s0) {
 #pragma unroll
             for (int u = 0; u < HOIST; ++u)
@@ -471,6 +540,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
             if (s + u < s1) mfma_step<WT, RB>(in[u], acc);
     }
 
+    __shared__ float red_ss[XN ? NW : 1][16];
+    if (XN) {
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (lane < 16) red_ss[wave][lane] = ss;
+    }
     if (NW > 1) {
         __shared__ f32x4_t red[NW > 1 ? NW - 1 : 1][RB][64];
         if (wave > 0) {
@@ -479,12 +554,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
         }
         __syncthreads();
         if (wave != 0) return;
-#pragma unroll
+        // one wave's partial sums at a time (all of them at once would need
+        // (NW - 1) * RB * 4 registers)
+#pragma unroll 1
         for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
             for (int j = 0; j < RB; ++j) acc[j] += red[w][j][lane];
+    } else if (XN) {
+        __syncthreads();
     }
     if (!tok_ok) return;
+    if (XN) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += red_ss[w][r];
+        const float inv = 1.0f / sqrtf(tot / (float)a.K + a.norm.eps);
+#pragma unroll
+        for (int j = 0; j < RB; ++j) acc[j] *= inv;
+    }
     const int t = t0 + r;
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
@@ -1877,8 +1964,11 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
 #undef UBD_LAUNCH_LDSX
         return;
     }
-    const size_t lds = norm ? (size_t)4 * a.T * a.K : 0;
-    if (!norm && a.T > 2 && g_tuning.small_rb != 0) {
+    // the norm fused: its normalised rows staged in LDS when they fit (at
+    // most NORM_TMAX rows), else normalised on the fly (XN)
+    const bool norm_lds = norm && a.T <= NORM_TMAX && (size_t)4 * a.T * a.K <= LDSX_MAX_BYTES;
+    const size_t lds = norm_lds ? (size_t)4 * a.T * a.K : 0;
+    if (a.T > 2 && g_tuning.small_rb != 0) {
         // several tokens: 4 row blocks per work-group share each activation
         // fragment when that still gives >= 256 work-groups per token block;
         // narrower products use 2 row blocks or (residual products) split k
@@ -1886,8 +1976,12 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
         if (nrb % 4 == 0 && nrb / 4 >= 256) {
             dim3 g4(nrb / 4, grid.y);
             const int nw4 = nrb / 4 >= 768 ? 4 : 8;
-            if (nw4 == 4)
+            if (nw4 == 4 && norm)
+                UBD_LAUNCH((linear_small_kernel<WT, EPI, 4, false, 4, 1, true>), g4, dim3(256), 0, s, a);
+            else if (nw4 == 4)
                 UBD_LAUNCH((linear_small_kernel<WT, EPI, 4, false, 4, 1>), g4, dim3(256), 0, s, a);
+            else if (norm)
+                UBD_LAUNCH((linear_small_kernel<WT, EPI, 8, false, 4, 1, true>), g4, dim3(512), 0, s, a);
             else
                 UBD_LAUNCH((linear_small_kernel<WT, EPI, 8, false, 4, 1>), g4, dim3(512), 0, s, a);
             return;
@@ -1895,22 +1989,27 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
         // narrower products that cannot split k (QKV): 2 row blocks, 16 waves
         if (nrb % 2 == 0 && nrb / 2 >= 192) {
             dim3 g2(nrb / 2, grid.y);
-            UBD_LAUNCH((linear_small_kernel<WT, EPI, 16, false, 2, 1>), g2, dim3(1024), 0, s, a);
+            if (norm)
+                UBD_LAUNCH((linear_small_kernel<WT, EPI, 16, false, 2, 1, true>), g2, dim3(1024), 0, s, a);
+            else
+                UBD_LAUNCH((linear_small_kernel<WT, EPI, 16, false, 2, 1>), g2, dim3(1024), 0, s, a);
             return;
         }
         constexpr int KSPLIT = EPI == EPI_RESID ? 4 : 1;
-        if (KSPLIT > 1 && nrb % 4 == 0 && (a.K / WT_<WT>::KSTEP) % 32 == 0) {
+        if (KSPLIT > 1 && !norm && nrb % 4 == 0 && (a.K / WT_<WT>::KSTEP) % 32 == 0) {
             dim3 g4(nrb / 4, grid.y, KSPLIT);
             UBD_LAUNCH((linear_small_kernel<WT, EPI, 8, false, 4, KSPLIT>), g4, dim3(512), 0, s, a);
             return;
         }
     }
-#define UBD_LAUNCH_SMALL(NW_)                                                                            \
-    do {                                                                                                 \
-        if (norm)                                                                                        \
-            UBD_LAUNCH((linear_small_kernel<WT, EPI, NW_, true, RB, 1>), grid, dim3(64 * NW_), lds, s, a); \
-        else                                                                                             \
-            UBD_LAUNCH((linear_small_kernel<WT, EPI, NW_, false, RB, 1>), grid, dim3(64 * NW_), 0, s, a); \
+#define UBD_LAUNCH_SMALL(NW_)                                                                                \
+    do {                                                                                                     \
+        if (norm_lds)                                                                                        \
+            UBD_LAUNCH((linear_small_kernel<WT, EPI, NW_, true, RB, 1>), grid, dim3(64 * NW_), lds, s, a);     \
+        else if (norm)                                                                                       \
+            UBD_LAUNCH((linear_small_kernel<WT, EPI, NW_, false, RB, 1, true>), grid, dim3(64 * NW_), 0, s, a); \
+        else                                                                                                 \
+            UBD_LAUNCH((linear_small_kernel<WT, EPI, NW_, false, RB, 1>), grid, dim3(64 * NW_), 0, s, a);     \
     } while (0)
     if (nw == 4)
         UBD_LAUNCH_SMALL(4);
@@ -1941,9 +2040,11 @@ bool linear_reads_tiled(const LinearArgs &a) {
 }
 
 bool linear_norm_fits(int T, int K) {
-    // the LDS-staged kernel holds T rows of K values (hi + lo planes or f32);
-    // the register-staged one (ldsx off) keeps K <= 8192 values per row
-    return T >= 1 && T <= NORM_TMAX && (size_t)4 * T * K <= LDSX_MAX_BYTES && (g_tuning.ldsx != 0 || K <= 8192);
+    // one- and few-token products (the LDS-staged kernel normalises up to 16
+    // rows into its stage; the other few-token kernel stages up to
+    // NORM_TMAX rows or normalises on the fly)
+    (void)K;
+    return T >= 1 && T <= 16;
 }
 
 bool launch_linear(const LinearArgs &a, hipStream_t s) {

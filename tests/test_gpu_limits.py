@@ -1,10 +1,10 @@
 """Decode products at the edges of their fast paths, against the oracle.
 
 * A model 9216 values wide: one token's normalised row (36 KB) fits the
-  LDS stage of the one-token products, two tokens' rows (72 KB) do not, so
-  a two-token ubatch must take the RMSNorm as a kernel of its own.  Every
-  logits row is compared with the float64 oracle (f32 weights, 1e-4 of the
-  logit max-norm).
+  LDS stage of the one-token products, two or three tokens' rows (72 KB,
+  108 KB) do not, so those ubatches normalise their rows on the fly in the
+  few-token products.  Every logits row is compared with the float64 oracle
+  (f32 weights, 1e-4 of the logit max-norm).
 * q8_0 decode products stage their activations as f16 hi + lo planes,
   which end at 65504.  Norm gains of 1e5 on a few channels (attention norm
   of layer 0, FFN norm of layer 1, output norm) make the inputs of the QKV,
@@ -66,7 +66,7 @@ def wide():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("n", [1, 2, 3])
-def test_wide_rows_take_the_norm_unfused_when_the_stage_is_full(wide, n):
+def test_wide_rows_normalised_on_the_fly_when_the_stage_is_full(wide, n):
     tens, model = wide
     assert 4 * 1 * WIDE.n_embd <= 64 * 1024 < 4 * 2 * WIDE.n_embd
     run_both(model, WIDE, tens, rand_tokens(n, WIDE.n_vocab, seed=300 + n), 2, "f32", 1e-4, "wide")
