@@ -125,8 +125,9 @@ typedef struct ubd_model ubd_model;
  * be present exactly once with the expected shape.  Status: 0 ok; -1
  * invalid (missing, duplicate, unknown or mis-shaped tensor, mixed matrix
  * types, unsupported sizes: n_embd, n_head*head_dim, n_ff and n_vocab must
- * be multiples of 16, head_dim must be 32, 64 or 128 and n_head / n_head_kv
- * at most 32); -2 allocation or
+ * be multiples of 16, head_dim must be 32, 64 or 128, n_head / n_head_kv
+ * at most 32, and each fused matrix (Q|K|V, gate|up, O, down, output) at
+ * most 2 GiB); -2 allocation or
  * HIP failure.  Returns NULL on failure.  The model must outlive its
  * contexts. */
 ubd_model *ubd_model_load(const ubd_hparams *hparams,

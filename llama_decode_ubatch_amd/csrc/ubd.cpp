@@ -308,6 +308,15 @@ extern "C" ubd_model *ubd_model_load(const ubd_hparams *hparams, const ubd_tenso
     if (tied && got.count("token_embd.weight")) got["output.weight"] = got["token_embd.weight"];
     for (auto &kv : expect)
         if (!got.count(kv.first)) return fail(-1, "ubd_model_load: missing tensor " + kv.first);
+    {
+        // the products address each (fused) matrix with 32-bit byte offsets
+        const double d = hp.n_embd, kv = (double)hp.n_head_kv * hd, eb = (double)elem_bytes(wtype);
+        const double rows_k[][2] = {{d + 2 * kv, d}, {d, d}, {2.0 * hp.n_ff, d}, {d, (double)hp.n_ff},
+                                    {(double)hp.n_vocab, d}};
+        for (const auto &rk : rows_k)
+            if (rk[0] * rk[1] * eb > 2147483647.0)
+                return fail(-1, "ubd_model_load: a fused weight matrix exceeds 2 GiB");
+    }
 
     ubd_model *m = new ubd_model();
     m->hp = hp;
