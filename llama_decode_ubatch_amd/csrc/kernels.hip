@@ -1965,8 +1965,9 @@ static void launch_linear_wt_epi(const LinearArgs &a, hipStream_t s) {
         return;
     }
     // the norm fused: its normalised rows staged in LDS when they fit (at
-    // most NORM_TMAX rows), else normalised on the fly (XN)
-    const bool norm_lds = norm && a.T <= NORM_TMAX && (size_t)4 * a.T * a.K <= LDSX_MAX_BYTES;
+    // most NORM_TMAX rows of at most 8192 values, what norm_prologue holds),
+    // else normalised on the fly (XN)
+    const bool norm_lds = norm && a.T <= NORM_TMAX && a.K <= 8192 && (size_t)4 * a.T * a.K <= LDSX_MAX_BYTES;
     const size_t lds = norm_lds ? (size_t)4 * a.T * a.K : 0;
     if (a.T > 2 && g_tuning.small_rb != 0) {
         // several tokens: 4 row blocks per work-group share each activation

@@ -72,6 +72,21 @@ def test_wide_rows_normalised_on_the_fly_when_the_stage_is_full(wide, n):
     run_both(model, WIDE, tens, rand_tokens(n, WIDE.n_vocab, seed=300 + n), 2, "f32", 1e-4, "wide")
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("n", [1, 2])
+def test_wide_rows_without_the_lds_stage(wide, n):
+    """With the LDS-staged products switched off, the few-token kernel takes
+    the norm: staged in LDS only for rows of at most 8192 values (what its
+    prologue holds), normalised on the fly beyond that (9216 here)."""
+    from llama_decode_ubatch_amd.binding import set_tuning
+    tens, model = wide
+    set_tuning("ldsx", 0)
+    try:
+        run_both(model, WIDE, tens, rand_tokens(n, WIDE.n_vocab, seed=320 + n), 2, "f32", 1e-4, "wide, ldsx off")
+    finally:
+        set_tuning("ldsx", 1)
+
+
 def planted_tensors():
     tens = {s.name: gen_tensor(BIG, s) for s in tensor_specs(BIG)}
     for name in PLANTED:
