@@ -460,7 +460,7 @@ struct ubd_context : public Executor {
     int32_t logits_cap = 0;
     std::vector<float> logits_host;
     bool logits_host_valid = false;
-    int32_t *argmax_dev = nullptr;
+    int32_t *argmax_host = nullptr;         // pinned, coherent: the argmax kernel writes the picks here
     ArgmaxWork argmax_work;
     std::vector<int32_t> last_ub_idx;
     float *dump = nullptr;
@@ -512,24 +512,27 @@ struct ubd_context : public Executor {
         pending.clear();
     }
 
-    TokInfo tok_info() const {
+    // The token table of a ubatch of T tokens: sections of T ints (tiles: 4
+    // per tile, at most T tiles), so a one-token step uploads a few dozen
+    // bytes; its addresses depend on T alone, which a step's graph fixes.
+    TokInfo tok_info(int T) const {
         TokInfo t;
         const int32_t *b = info_dev;
         t.token = b;
-        t.pos = b + cap;
-        t.seq = b + 2 * cap;
-        t.stream = b + 3 * cap;
-        t.cell = b + 4 * cap;
-        t.out_row = b + 5 * cap;
-        t.tile_of = b + 6 * cap;
-        t.out_tok = b + 7 * cap;
-        t.tiles = b + 9 * cap;
-        t.seqw = (const uint32_t *)(b + 13 * cap);
+        t.pos = b + T;
+        t.seq = b + 2 * T;
+        t.stream = b + 3 * T;
+        t.cell = b + 4 * T;
+        t.out_row = b + 5 * T;
+        t.tile_of = b + 6 * T;
+        t.out_tok = b + 7 * T;
+        t.tiles = b + 9 * T;
+        t.seqw = (const uint32_t *)(b + 13 * T);
         t.n_seq_words = n_seq_words;
         return t;
     }
-    const int32_t *out_lrow() const { return info_dev + 8 * cap; }
-    size_t info_ints() const { return (size_t)(13 + n_seq_words) * cap; }
+    const int32_t *out_lrow(int T) const { return info_dev + 8 * T; }
+    size_t info_ints(int T) const { return (size_t)(13 + n_seq_words) * T; }
 
     // ---- decode-step graphs: each ubatch shape is captured once on
     // cap_stream and replayed on the context stream from then on.  Every kernel of
@@ -627,6 +630,7 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
             if (c->info_host[i]) (void)hipHostFree(c->info_host[i]);
             if (c->info_ev[i]) (void)hipEventDestroy(c->info_ev[i]);
         }
+        if (c->argmax_host) (void)hipHostFree(c->argmax_host);
         delete c;
         return fail(-2, "ubd_init_from_model: " + msg + (g_err.empty() ? "" : ": " + g_err));
     };
@@ -702,13 +706,12 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
     for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)hp.rope_freq_base, -2.0 * i / hd);
     c->inv_freq = (double *)c->mem.get(inv.size() * sizeof(double));
     c->rope_cs = (float2 *)c->mem.get((size_t)cap * (hd / 2) * sizeof(float2));
-    c->info_dev = (int32_t *)c->mem.get(c->info_ints() * 4);
-    c->argmax_dev = (int32_t *)c->mem.get((size_t)std::max<uint32_t>(P.n_batch, 1) * 4);
+    c->info_dev = (int32_t *)c->mem.get(c->info_ints(c->cap) * 4);
     const size_t amax_rows = std::max<uint32_t>(P.n_batch, 1);
     c->argmax_work.pv = (float *)c->mem.get(amax_rows * ARGMAX_BLOCKS * 4);
     c->argmax_work.pi = (int32_t *)c->mem.get(amax_rows * ARGMAX_BLOCKS * 4);
     c->argmax_work.counter = (int32_t *)c->mem.get(amax_rows * 4);
-    if (!c->inv_freq || !c->rope_cs || !c->info_dev || !c->argmax_dev || !c->argmax_work.pv || !c->argmax_work.pi ||
+    if (!c->inv_freq || !c->rope_cs || !c->info_dev || !c->argmax_work.pv || !c->argmax_work.pi ||
         !c->argmax_work.counter)
         return bail("allocation failed");
     if (!hip_ok(hipMemsetAsync(c->argmax_work.counter, 0, amax_rows * 4, c->stream), "memset"))
@@ -717,10 +720,13 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
                                c->stream), "upload"))
         return bail("upload failed");
     for (int i = 0; i < 2; ++i) {
-        if (!hip_ok(hipHostMalloc((void **)&c->info_host[i], c->info_ints() * 4, hipHostMallocDefault), "pinned") ||
+        if (!hip_ok(hipHostMalloc((void **)&c->info_host[i], c->info_ints(c->cap) * 4, hipHostMallocDefault), "pinned") ||
             !hip_ok(hipEventCreateWithFlags(&c->info_ev[i], hipEventDisableTiming), "event"))
             return bail("pinned staging allocation failed");
     }
+    if (!hip_ok(hipHostMalloc((void **)&c->argmax_host, (size_t)std::max<uint32_t>(P.n_batch, 1) * 4,
+                              hipHostMallocCoherent), "pinned"))
+        return bail("pinned argmax buffer allocation failed");
     if (!hip_ok(hipStreamSynchronize(c->stream), "init sync")) return bail("sync failed");
     log_line(1, "context: n_ctx %u (%u streams x %u cells), n_batch %u, n_ubatch %u, KV %.1f MiB", P.n_ctx,
              P.n_stream, P.n_cells, P.n_batch, P.n_ubatch,
@@ -742,6 +748,7 @@ extern "C" void ubd_free(ubd_context *ctx) {
         if (ctx->info_host[i]) (void)hipHostFree(ctx->info_host[i]);
         if (ctx->info_ev[i]) (void)hipEventDestroy(ctx->info_ev[i]);
     }
+    if (ctx->argmax_host) (void)hipHostFree(ctx->argmax_host);
     delete ctx;
 }
 
@@ -870,19 +877,19 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     info_i ^= 1;
     if (!hip_ok(hipEventSynchronize(info_ev[bi]), "staging reuse")) return UBD_COMPUTE_FAILED;
     int32_t *h = info_host[bi];
-    std::fill(h, h + info_ints(), 0);
+    std::fill(h, h + info_ints(T), 0);
     int n_out = 0;
     for (int t = 0; t < T; ++t) {
         h[t] = ub.token[t];
-        h[cap + t] = ub.pos[t];
-        h[2 * cap + t] = ub.seq[t];
-        h[3 * cap + t] = ub.stream[t];
-        h[4 * cap + t] = ub.cell[t];
-        h[5 * cap + t] = ub.out_row[t];
-        for (int w = 0; w < n_seq_words; ++w) h[13 * cap + t * n_seq_words + w] = (int32_t)ub.seqw[(size_t)t * n_seq_words + w];
+        h[T + t] = ub.pos[t];
+        h[2 * T + t] = ub.seq[t];
+        h[3 * T + t] = ub.stream[t];
+        h[4 * T + t] = ub.cell[t];
+        h[5 * T + t] = ub.out_row[t];
+        for (int w = 0; w < n_seq_words; ++w) h[13 * T + t * n_seq_words + w] = (int32_t)ub.seqw[(size_t)t * n_seq_words + w];
         if (ub.out_row[t] >= 0) {
-            h[7 * cap + n_out] = t;
-            h[8 * cap + n_out] = ub.out_row[t];
+            h[7 * T + n_out] = t;
+            h[8 * T + n_out] = ub.out_row[t];
             ++n_out;
         }
     }
@@ -893,7 +900,7 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     for (int t = 0; t < T;) {
         int e = t + 1;
         while (e < T && e - t < qt && ub.stream[e] == ub.stream[t]) ++e;
-        int32_t *tl = h + 9 * cap + 4 * n_tiles;
+        int32_t *tl = h + 9 * T + 4 * n_tiles;
         tl[0] = t;
         tl[1] = e - t;
         tl[2] = ub.stream[t];
@@ -911,12 +918,12 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
             }
             tl[3] = c + 1;
         }
-        for (int j = t; j < e; ++j) h[6 * cap + j] = n_tiles;
+        for (int j = t; j < e; ++j) h[6 * T + j] = n_tiles;
         max_scan = std::max(max_scan, (int)tl[3]);
         ++n_tiles;
         t = e;
     }
-    if (!hip_ok(hipMemcpyAsync(info_dev, h, info_ints() * 4, hipMemcpyHostToDevice, stream), "token table upload") ||
+    if (!hip_ok(hipMemcpyAsync(info_dev, h, info_ints(T) * 4, hipMemcpyHostToDevice, stream), "token table upload") ||
         !hip_ok(hipEventRecord(info_ev[bi], stream), "event"))
         return UBD_COMPUTE_FAILED;
     last_ub_idx = ub.idx;
@@ -1007,7 +1014,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
     const int T = key.T, n_out = key.n_out, n_tiles = key.n_tiles;
     const int hd = M.head_dim, H = hp.n_head, Hk = hp.n_head_kv, d = hp.n_embd;
     const bool split = T <= 16;
-    const TokInfo ti = tok_info();
+    const TokInfo ti = tok_info(T);
     const int n_cells = (int)cell_stride;   // per-s stride of the device KV and cell tables
     const int ph = T > 16 ? 1 : 0;
     bool launched = true;     // every product accepted its arguments
@@ -1148,7 +1155,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         lz.T = n_out;
         lz.epi = EPI_LOGITS;
         lz.prod = PROD_LOGITS;
-        lz.row_map = out_lrow();
+        lz.row_map = out_lrow(T);
         lz.logits = logits_dev;
         if (fuse_norm) lz.norm = NormIn{x, ti.out_tok, M.out_norm, hp.rms_eps, d};
         lz.x.tiled = linear_reads_tiled(lz);
@@ -1243,12 +1250,10 @@ extern "C" ubd_token ubd_sample_greedy(ubd_context *ctx, int32_t i) {
     if (r < 0) return -1;
     (void)hipSetDevice(ctx->model->device);
     const int V = ctx->model->hp.n_vocab;
-    launch_argmax(ctx->logits_dev + (size_t)r * V, V, nullptr, 1, V, ctx->argmax_dev, ctx->argmax_work, ctx->stream);
-    int32_t out = -1;
-    if (!hip_ok(hipMemcpyAsync(&out, ctx->argmax_dev, 4, hipMemcpyDeviceToHost, ctx->stream), "argmax") ||
-        !hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync"))
-        return -1;
-    return out;
+    // the kernel writes the pick into pinned host memory: no copy behind it
+    launch_argmax(ctx->logits_dev + (size_t)r * V, V, nullptr, 1, V, ctx->argmax_host, ctx->argmax_work, ctx->stream);
+    if (!hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync")) return -1;
+    return ctx->argmax_host[0];
 }
 
 extern "C" int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32_t cap) {
@@ -1259,11 +1264,9 @@ extern "C" int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32
     if (P.n_outputs == 0) return 0;
     (void)hipSetDevice(ctx->model->device);
     const int V = ctx->model->hp.n_vocab;
-    launch_argmax(ctx->logits_dev, V, nullptr, P.n_outputs, V, ctx->argmax_dev, ctx->argmax_work, ctx->stream);
-    if (!hip_ok(hipMemcpyAsync(out, ctx->argmax_dev, (size_t)P.n_outputs * 4, hipMemcpyDeviceToHost, ctx->stream),
-                "argmax") ||
-        !hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync"))
-        return -1;
+    launch_argmax(ctx->logits_dev, V, nullptr, P.n_outputs, V, ctx->argmax_host, ctx->argmax_work, ctx->stream);
+    if (!hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync")) return -1;
+    std::memcpy(out, ctx->argmax_host, (size_t)P.n_outputs * 4);
     return P.n_outputs;
 }
 
