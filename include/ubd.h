@@ -514,7 +514,8 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * "fuse_norm" (ubatches of at most 2 tokens: 1 = RMSNorm fused into the
  * QKV, gate|up and logits products, -1 = into QKV only, 0 = never),
  * "attn_chunk_min" (smallest cells per wave of split attention, default
- * 64, at least 32), "ldsx"
+ * 64, at least 32), "attn_pair" (prefill attention: 1 = two waves per
+ * tile, each scanning half its cells, 0 = one wave), "ldsx"
  * (0 = few-token products read activations from global memory),
  * "ldsx_early" (one-token products: 1 = activation loads issued before the
  * weight loads, 0 = after; the results are identical), "gemm_wpd"

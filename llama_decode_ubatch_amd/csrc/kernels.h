@@ -39,6 +39,7 @@ struct Tuning {
     int fuse_norm = 1;        // ubatches of <= 2 tokens: 1 = RMSNorm fused into the QKV, gate|up and
                               // logits products, -1 = into QKV only, 0 = never
     int attn_chunk_min = 64;  // smallest cells per wave of split attention (>= 32)
+    int attn_pair = 1;        // unsplit (prefill) MFMA attention: 1 = two waves per tile, each scanning half
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
     int ldsx_early = 1;       // one-token LDS-staged products: activation loads ahead of the weights
     int small_rb = 1;         // several-token products: 4 row blocks per work-group / split k (0 = off)

@@ -1630,6 +1630,8 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.fuse_norm = value;
     } else if (k == "attn_chunk_min") {
         g_tuning.attn_chunk_min = value;
+    } else if (k == "attn_pair") {
+        g_tuning.attn_pair = value;
     } else if (k == "gemm_wpd") {
         g_tuning.gemm_wpd = value;
     } else if (k == "gemm_deep") {
