@@ -44,13 +44,14 @@ KERNEL_SRC = os.path.join(ROOT, "llama_decode_ubatch_amd", "csrc", "kernels.hip"
 # script) and the roofline kernels' names in them
 TRACE_FILES = {
     ("decode.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
-                                     "linear_ldsx_kernel<2, 2, 4, true>"),
+                                     ("linear_ldsx_kernel<2, 2, 4, true>",)),
     ("prefill.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
-                                      "gemm_lds_kernel<2, 2, 4, 4, 1, 64, 1, true>"),
+                                      ("gemm_deep_kernel<2, 4, 4, 1, 2, 1, true>",)),
+    # split pass + combine pass, as the events span both
     ("decode.attention", "bf16"): (os.path.join(ROOT, "profiles", "decode_8b_16seq_32k_kernel_stats.md"),
-                                   "attn_mfma_kernel<128, true, false>"),
+                                   ("attn_mfma_kernel<128, true, false, false>", "attn_merge_kernel<128>")),
     ("decode.ffn_gate_up", "q8_0"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_q8_0_kernel_stats.md"),
-                                     "linear_ldsx_kernel<3, 2, 4, true>"),
+                                     ("linear_ldsx_kernel<3, 2, 4, true>",)),
 }
 
 
@@ -66,16 +67,18 @@ def traced_avg_us(kernel_class, wtype):
     """Average dispatch duration of a roofline kernel in the committed
     rocprofv3 kernel trace, if kernels.hip is unchanged since then."""
     try:
-        path, name = TRACE_FILES[(kernel_class, wtype)]
+        path, names = TRACE_FILES[(kernel_class, wtype)]
         text = open(path).read()
         if f"sha256 prefix {_src_hash()}" not in text:
             return None
+        avg = {}
         for line in text.splitlines():
-            if line.startswith(f"| `{name}` |"):
-                return float(line.split("|")[3])
+            for name in names:
+                if line.startswith(f"| `{name}` |"):
+                    avg[name] = float(line.split("|")[3])
+        return round(sum(avg.values()), 2) if len(avg) == len(names) else None
     except Exception:
         return None
-    return None
 
 
 def measured_traffic(kernel_class):
