@@ -1772,6 +1772,8 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
     case 10: if (launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true>(a, s)) return; break;
     case 14: if (launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return; break;
     case 16: if (launch_gemm_deep<EPI, 4, 4, 1, 2, 1, true>(a, s)) return; break;
+    case 18: if (launch_gemm_deep<EPI, 4, 4, 1, 2, RS, true>(a, s)) return; break;
+    case 19: if (launch_gemm_deep<EPI, 4, 4, 1, 2, EPI == EPI_RESID ? 4 : 1, true>(a, s)) return; break;
     default: break;
     }
     if (EPI == EPI_RESID) {
@@ -1780,6 +1782,12 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
         constexpr int RS4 = EPI == EPI_RESID ? 4 : 1;
         if (g_tuning.gemm_split == 4 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS4, true>(a, s)) return;
         if (g_tuning.gemm_split == 2 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return;
+        // long k (FFN down): the 256 x 64 tile (one stage of weight look-ahead)
+        // in 4 k slices, else the 128 x 64 tile in 2 (8B shape at 512 tokens:
+        // 110.5 against 130.5 us)
+        if (g_tuning.gemm_split == 0 && a.K >= 8192 && tiles(4, 4) * 4 >= 256 &&
+            launch_gemm_deep<EPI, 4, 4, 1, 2, RS4, true>(a, s))
+            return;
         if (g_tuning.gemm_split == 0 && a.K >= 8192 && tiles(2, 4) * 2 >= 192 &&
             launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s))
             return;
