@@ -1529,28 +1529,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 }
 
 // Deep variant of the LDS-ring product: weights D stages ahead in D + 1
-// rotating register sets, activations two stages ahead in the 3-deep LDS
-// ring.  The stage loop is unrolled by D + 1 and has no branches inside,
+// rotating register sets, activations XA stages ahead in an (XA + 1)-deep
+// LDS ring.  The stage loop is unrolled by D + 1 and has no branches inside,
 // so every register set is loaded and consumed at fixed places and no set
 // is ever copied (a copy of a set still in flight makes the compiler wait
 // for it, which leaves one stage's compute to cover a whole memory round
 // trip).  OCC = waves per SIMD (1: the accumulators go to the matrix-core
 // registers, leaving room for more sets).  bf16 weights; the stage count
-// K / 64 must be a multiple of D + 1.
+// K / 64 must be a multiple of D + 1.  With one work-group per CU a stage's
+// products take about 0.25 us, so the look-ahead has to cover the L2 and
+// HBM latency under load (about 0.5-2 us) by itself: deeper rings and more
+// register sets there, shallower ones where two work-groups share a CU.
 // SPLITK > 1 (residual products): work-group k-slice ks of SPLITK stores its
 // partial sums to a.split_out[ks][t][n]; resid_add_splits_kernel then adds
 // the slices to the residual in order (no atomics: the sums do not depend on
 // timing).
-template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1, bool LO = false>
+template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1, bool LO = false, int XA = 2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void gemm_deep_kernel(
     LinearArgs a, int n_wtiles, int n_ttiles) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int KS = 64;
     using C = GemmCfg<W_BF16, RBW, TB, KS, LO>;
     constexpr int KH = C::KH, NA = C::NA;
-    static_assert(D == 1 || D == 3, "look-ahead");
+    constexpr int NX = XA + 1;                          // LDS ring depth
+    static_assert(D == 1 || D == 3 || D == 7, "look-ahead");
+    static_assert(XA >= 2 && XA <= 7, "activation look-ahead");
     static_assert(SPLITK == 1 || EPI == EPI_RESID, "k split: residual products only");
-    __shared__ u32x4_t xs[C::NX * C::XF * 64];
+    __shared__ u32x4_t xs[NX * C::XF * 64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1608,7 +1613,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     };
     auto issue_x = [&](int s) {
         const int sl = min(s, nst - 1);
-        u32x4_t *dst = xs + (size_t)((s % C::NX) * C::XF + wave * C::XW) * 64;
+        u32x4_t *dst = xs + (size_t)((s % NX) * C::XF + wave * C::XW) * 64;
 #pragma unroll
         for (int u = 0; u < C::XW; ++u) {
             const bool lo = (wave * C::XW + u) >= TB * KH;
@@ -1621,7 +1626,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
     // half's reads are in flight while the first half's products run
     static_assert(KH == 2, "two k halves per stage");
     auto compute = [&](int s, const u32x4_t (&wc)[RBW][NA]) {
-        const u32x4_t *xb = xs + (size_t)(s % C::NX) * C::XF * 64;
+        const u32x4_t *xb = xs + (size_t)(s % NX) * C::XF * 64;
         u32x4_t B[C::PL][2][TB];
 #pragma unroll
         for (int pl = 0; pl < C::PL; ++pl)
@@ -1645,23 +1650,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
         }
     };
 
-    // issue order w0 x0 w1 x1 w2 ...: every stage finds at least NWL + XW
-    // loads issued after the ones it needs (XW with one stage of look-ahead)
+    // Stage t's iteration issues stage t + D's weights, then stage t + XA's
+    // activations.  Loads return in issue order, so stage t may start once
+    // no more are outstanding than were issued after the later of its two:
+    // the weights (D < XA) are followed by one activation batch and D - 1
+    // whole iterations, the activations by XA - 1 whole iterations.  The
+    // prologue replays the iterations before the first stage, issuing only
+    // the loads of stages >= sbeg, which leaves the same counts.
+    constexpr int WAITN = D < XA ? C::XW + (D - 1) * (NWL + C::XW) : (XA - 1) * (NWL + C::XW);
+    static_assert(WAITN + NWL + C::XW < 64, "loads in flight");
+    constexpr int PRE = D > XA ? D : XA;
 #pragma unroll
-    for (int k = 0; k < D; ++k) {
-        issue_w(sbeg + k, W[k]);
-        if (k < 2) issue_x(sbeg + k);
+    for (int v = -PRE; v < 0; ++v) {
+        if (v + D >= 0) issue_w(sbeg + v + D, W[(v + D) % (D + 1)]);
+        if (v + XA >= 0) issue_x(sbeg + v + XA);
     }
-    if (D == 1) issue_x(sbeg + 1);
     __builtin_amdgcn_sched_barrier(0);
     for (int s = sbeg; s < nst; s += D + 1) {
 #pragma unroll
         for (int k = 0; k <= D; ++k) {
-            wait_vm<D == 1 ? C::XW : C::XW + NWL>();
+            wait_vm<WAITN>();
             wg_barrier();
             __builtin_amdgcn_sched_barrier(0);
             issue_w(s + k + D, W[(k + D) % (D + 1)]);
-            issue_x(s + k + 2);
+            issue_x(s + k + XA);
             __builtin_amdgcn_sched_barrier(0);
             compute(s + k, W[k]);
             __builtin_amdgcn_sched_barrier(0);
@@ -1705,14 +1717,14 @@ __global__ __launch_bounds__(256) void resid_add_splits_kernel(float *y, int ldy
 // false (nothing launched) unless each k slice's stage count is a multiple
 // of D + 1 (and, split, the product is a residual one with scratch for the
 // slices)
-template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1, bool LO = false>
+template <int EPI, int RBW, int TB, int D, int OCC, int SPLITK = 1, bool LO = false, int XA = 2>
 static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
     const int nst = a.K / 64;
     if (a.K % 64 || nst % SPLITK || (nst / SPLITK) % (D + 1)) return false;
     if (SPLITK > 1 && (EPI != EPI_RESID || !a.split_out || a.N % 4)) return false;
     const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
-    UBD_LAUNCH((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK, LO>), dim3(n_wtiles * n_ttiles * SPLITK),
+    UBD_LAUNCH((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK, LO, XA>), dim3(n_wtiles * n_ttiles * SPLITK),
                        dim3(256), 0, s, a, n_wtiles, n_ttiles);
     if (SPLITK > 1) {
         const long n = (long)a.T * (a.N / 4);
@@ -1791,7 +1803,11 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
         if (g_tuning.gemm_split == 0 && a.K >= 8192 && tiles(2, 4) * 2 >= 192 &&
             launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s))
             return;
-        if (tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true>(a, s)) return;
+        // short k (O): the 128 x 64 tile with activations three stages ahead
+        // in a 4-deep ring (8B shape at 512 tokens: 40.7 against 43.8 us with
+        // two stages ahead; deeper rings and more weight sets at one wave per
+        // SIMD measured no better)
+        if (tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true, 3>(a, s)) return;
         launch_gemm_lds<W_BF16, EPI, 2, 4, 1, true>(a, s);
         return;
     }
