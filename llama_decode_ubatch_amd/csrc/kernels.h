@@ -199,6 +199,7 @@ struct AttnArgs {
     bool split = false;               // MFMA path: split cells into chunks + combine
     int chunk_cells = 32;             // MFMA split: cells per wave (multiple of 32)
     int n_chunks_launch = 0;          // MFMA split: chunks launched per tile
+    int waves = 1;                    // MFMA, not split: waves per (tile, KV head), 1 or 2
 };
 constexpr int ATTN_CHUNK = 256;       // cells per split-K chunk (f32 path)
 constexpr int ATTN_DECODE_CHUNK = 32; // smallest cells-per-wave chunk of the split MFMA path
@@ -209,8 +210,8 @@ void launch_attention(const AttnArgs &a, hipStream_t s);
 int attn_tile_rows(int head_dim);
 // MFMA attention (f16 K/V): tiles are blocks of 16 / n_gqa tokens; with
 // split (at most 16 tokens), tiles[3] cells are cut into chunk_cells-cell
-// chunks, one wave each, merged by a combine pass; otherwise one wave scans
-// tiles[3] cells.  Partials are indexed with max_chunks = ceil(n_cells /
+// chunks, one wave each, merged by a combine pass; otherwise `waves` waves
+// of one work-group scan tiles[3] cells and merge in LDS.  Partials are indexed with max_chunks = ceil(n_cells /
 // ATTN_DECODE_CHUNK).
 bool attn_mfma_ok(int type_k, int type_v, int head_dim, int n_gqa);
 void launch_attention_mfma(const AttnArgs &a, hipStream_t s);

@@ -2657,19 +2657,23 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
     }
 }
 
-// PAIR (prefill, no split): a work-group of two waves per (tile, KV head);
-// wave 0 scans the first half of the tile's cells and wave 1 the rest, and
-// wave 0 merges the two (m, l, O) through LDS.  The grid is (KV head, tile)
-// with the tiles in reverse order, so the longest causal scans start first.
-template <int HD, bool SPLIT, bool KQ, bool PAIR = false>
-__global__ __launch_bounds__(PAIR ? 128 : 64) void attn_mfma_kernel(AttnArgs a) {
-    static_assert(!(SPLIT && PAIR), "the pair mode merges in the work-group");
+// NW > 1 (no split): a work-group of NW waves per (tile, KV head); wave w
+// scans the w-th of NW runs of 32-cell steps of the tile's cells, and the
+// waves merge their (m, l, O) through LDS, each finishing the dim blocks
+// db = w, w + NW, ...  The grid is (KV head, tile) with the tiles in reverse
+// order, so the longest causal scans start first (prefill: two waves).
+// (For decode steps with short scans, four waves merged this way measured
+// slower than the split pass and its combine kernel: each wave's steps wait
+// on their loads one after another.)
+template <int HD, bool SPLIT, bool KQ, int NW = 1>
+__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
+    static_assert(!(SPLIT && NW > 1), "the multi-wave mode merges in the work-group");
     constexpr int KK = HD / 32, DB = HD / 16;
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    const int wv = PAIR ? (int)(threadIdx.x >> 6) : 0;
-    const int chunk = PAIR ? 0 : blockIdx.x;
-    const int blk = PAIR ? a.n_tiles - 1 - (int)blockIdx.y : (int)blockIdx.y;
-    const int grp = PAIR ? blockIdx.x : blockIdx.z;
+    const int wv = NW > 1 ? (int)(threadIdx.x >> 6) : 0;
+    const int chunk = NW > 1 ? 0 : blockIdx.x;
+    const int blk = NW > 1 ? a.n_tiles - 1 - (int)blockIdx.y : (int)blockIdx.y;
+    const int grp = NW > 1 ? blockIdx.x : blockIdx.z;
     const int t0 = a.tok.tiles[blk * 4 + 0], nt = a.tok.tiles[blk * 4 + 1];
     const int st = a.tok.tiles[blk * 4 + 2], nscan = a.tok.tiles[blk * 4 + 3];
     const int G = a.n_head / a.n_head_kv;
@@ -2693,10 +2697,10 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void attn_mfma_kernel(AttnArgs a) 
         }
         cend = min(nscan, cbeg + NC);
     }
-    if (PAIR) {
-        const int half = min(nscan, (nscan + 63) / 64 * 32);     // a multiple of 32 cells
-        cbeg = wv ? half : 0;
-        cend = wv ? nscan : half;
+    if (NW > 1) {
+        const int per = (nscan + 32 * NW - 1) / (32 * NW) * 32;   // a multiple of 32 cells
+        cbeg = min(nscan, wv * per);
+        cend = min(nscan, cbeg + per);
     }
     const float scale = 1.44269504088896341f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
     // this lane's query row (S^T layout: row = r)
@@ -2789,34 +2793,48 @@ __global__ __launch_bounds__(PAIR ? 128 : 64) void attn_mfma_kernel(AttnArgs a) 
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (PAIR) {
-        // wave 1 hands its (m, l, O) to wave 0, which rescales both halves to
-        // the common maximum
-        __shared__ float pm[16], pl[16];
-        __shared__ f32x4_t po[DB][64];
-        if (wv == 1) {
-            if (g == 0) {
-                pm[r] = m;
-                pl[r] = l;
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) po[db][lane] = O[db];
+    if constexpr (NW > 1) {
+        // every wave publishes its (m, l) per row and its O; each lane then
+        // weights the NW partials of its four rows 4g+i by exp2(m_w - M) and
+        // finishes its wave's dim blocks
+        __shared__ float pm[NW][16], pl[NW][16];
+        __shared__ f32x4_t po[NW][DB][64];
+        if (g == 0) {
+            pm[wv][r] = m;
+            pl[wv][r] = l;
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) po[wv][db][lane] = O[db];
         __syncthreads();
-        if (wv == 1) return;
-        const float m1 = pm[r], l1 = pl[r];
-        const float M = fmaxf(m, m1);
-        const float a0 = m == -INFINITY ? 0.f : exp2_fast(m - M);
-        const float a1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - M);
-        l = l * a0 + l1 * a1;
-        f32x4_t f0, f1;
+        f32x4_t wgt[NW];
+        float L[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f0[i] = __shfl(a0, 4 * g + i, 64);
-            f1[i] = __shfl(a1, 4 * g + i, 64);
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, pm[w][4 * g + i]);
+            L[i] = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = pm[w][4 * g + i];
+                wgt[w][i] = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
+                L[i] += wgt[w][i] * pl[w][4 * g + i];
+            }
         }
 #pragma unroll
-        for (int db = 0; db < DB; ++db) O[db] = O[db] * f0 + po[db][lane] * f1;
+        for (int db = wv; db < DB; db += NW) {
+            f32x4_t o = po[0][db][lane] * wgt[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) o += po[w][db][lane] * wgt[w];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i;
+                if (row >= R) continue;
+                const int t = t0 + row / G, h = grp * G + row % G;
+                store_act(a.out, act_idx(a.out, t, h * HD + 16 * db + r), L[i] > 0.f ? o[i] / L[i] : 0.f);
+            }
+        }
+        return;
     }
     // O: lane (dim r of each 16-dim block, group g) holds rows 4g+i
     if (!SPLIT) {
@@ -2916,12 +2934,12 @@ static void launch_attention_mfma_hd(const AttnArgs &a, hipStream_t s) {
         else
             UBD_LAUNCH((attn_mfma_kernel<HD, true, false>), grid, dim3(64), 0, s, a);
         UBD_LAUNCH((attn_merge_kernel<HD>), dim3(a.T * a.n_head), dim3(64), 0, s, a);
-    } else if (g_tuning.attn_pair) {
+    } else if (a.waves == 2) {
         dim3 grid(a.n_head_kv, a.n_tiles);
         if (q8)
-            UBD_LAUNCH((attn_mfma_kernel<HD, false, true, true>), grid, dim3(128), 0, s, a);
+            UBD_LAUNCH((attn_mfma_kernel<HD, false, true, 2>), grid, dim3(128), 0, s, a);
         else
-            UBD_LAUNCH((attn_mfma_kernel<HD, false, false, true>), grid, dim3(128), 0, s, a);
+            UBD_LAUNCH((attn_mfma_kernel<HD, false, false, 2>), grid, dim3(128), 0, s, a);
     } else {
         dim3 grid(1, a.n_tiles, a.n_head_kv);
         if (q8)

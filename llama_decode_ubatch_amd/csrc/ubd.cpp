@@ -1104,6 +1104,7 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         aa.out = lo.x;
         if (mfma_attn) {
             aa.split = split;
+            aa.waves = g_tuning.attn_pair ? 2 : 1;
             aa.max_chunks = max_chunks_mfma;
             aa.chunk_cells = key.chunk_cells;
             aa.n_chunks_launch = key.n_chunks;
