@@ -133,7 +133,11 @@ def prefill_flops(w):
 
 # ------------------------------------------------------------------- the job
 def run_job(ctx, w, prompt, first_tokens=None):
-    """One pass of the workload.  Returns (t_prefill_s, t_decode_s, ids)."""
+    """One pass of the workload.  Returns (t_prefill_s, t_decode_s, ids).
+    One sequence: the greedy steps run as one chain (ubd_greedy_chain: each
+    pick goes from the argmax kernel straight into the next step's token
+    table, the same picks as decode + greedy step by step); several: one
+    decode of a token per sequence, then the greedy picks, per step."""
     import numpy as np
     if w.kv_prefill:
         for s in range(w.n_seqs):          # back to the pre-filled state
@@ -149,14 +153,15 @@ def run_job(ctx, w, prompt, first_tokens=None):
         tok = first_tokens
     t1 = time.perf_counter()
     ids.append(tok)
-    for _ in range(w.n_decode):
-        if w.n_seqs == 1:
-            assert ctx.decode([tok]) == 0
-            tok = ctx.greedy(-1)
-        else:
+    if w.n_seqs == 1:
+        chain = ctx.greedy_chain(tok, w.n_decode)
+        assert chain.size == w.n_decode
+        ids.extend(int(t) for t in chain)
+    else:
+        for _ in range(w.n_decode):
             assert ctx.decode(tok, seq_id=np.arange(w.n_seqs), logits=np.ones(w.n_seqs)) == 0
             tok = ctx.greedy_all()
-        ids.append(tok)
+            ids.append(tok)
     t2 = time.perf_counter()
     return t1 - t0, t2 - t1, ids
 
@@ -467,7 +472,9 @@ def main():
         "data": "synthetic (seeded counter-based generator; random weights, uniform token ids)",
         "config": {"workload": w.name, "n_prompt": w.n_prompt, "n_decode": w.n_decode,
                    "n_seqs": w.n_seqs, "n_ctx": w.n_ctx, "n_ubatch": w.n_ubatch,
-                   "kv_type": w.type_k, "parallelism": "single-gpu"},
+                   "kv_type": w.type_k, "parallelism": "single-gpu",
+                   "decode_loop": "greedy chain (ubd_greedy_chain)" if w.n_seqs == 1
+                   else "decode + greedy of every sequence per step"},
         "prefill_tok_s": None if r["prefill_tok_s"] is None else round(r["prefill_tok_s"], 1),
         "decode_tok_s": round(r["decode_tok_s"], 2),
         "e2e": r["e2e"],

@@ -102,6 +102,7 @@ SIGNATURES = {
     "ubd_get_logits_device": (C.c_void_p, [_P]),
     "ubd_sample_greedy": (C.c_int32, [_P, C.c_int32]),
     "ubd_sample_greedy_all": (C.c_int32, [_P, C.POINTER(C.c_int32), C.c_int32]),
+    "ubd_greedy_chain": (C.c_int32, [_P, C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
     "ubd_greedy_rows_static": (C.c_int32, [C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                            C.c_void_p]),
     "ubd_sampler_default_params": (SamplerParams, []),
@@ -506,6 +507,18 @@ class Context:
         r = self.lib.ubd_sample_greedy_all(self.ptr, out.ctypes.data_as(C.POINTER(C.c_int32)), out.size)
         if r < 0:
             raise RuntimeError(f"ubd_sample_greedy_all failed: {last_error()}")
+        return out[:r]
+
+    def greedy_chain(self, first, n_steps, seq_id=0):
+        """n_steps greedy single-token steps of one sequence, the first fed
+        `first`, each later one the previous pick (ubd_greedy_chain); returns
+        the picks.  Raises if no step could be done; a shorter array means a
+        later step failed (see last_error())."""
+        out = np.zeros(max(int(n_steps), 1), np.int32)
+        r = self.lib.ubd_greedy_chain(self.ptr, int(first), int(seq_id), int(n_steps),
+                                      out.ctypes.data_as(C.POINTER(C.c_int32)))
+        if r < 0:
+            raise RuntimeError(f"ubd_greedy_chain failed ({r}): {last_error()}")
         return out[:r]
 
     def synchronize(self):

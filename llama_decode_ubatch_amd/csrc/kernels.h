@@ -225,8 +225,9 @@ struct ArgmaxWork {
     int32_t *pi = nullptr;
     int32_t *counter = nullptr;
 };
+// out2 (optional): a second destination of the picks.
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows,
-                   int n, int32_t *out, const ArgmaxWork &w, hipStream_t s);
+                   int n, int32_t *out, const ArgmaxWork &w, hipStream_t s, int32_t *out2 = nullptr);
 // The same argmax in two kernels and no counter (nothing to keep at zero
 // between calls): pv / pi [n_rows][ARGMAX_BLOCKS] hold the slice winners.
 void launch_argmax_two_pass(const float *logits, int ld, int n_rows, int n, int32_t *out,

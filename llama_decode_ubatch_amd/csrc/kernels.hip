@@ -2995,8 +2995,11 @@ __device__ __forceinline__ void block_best(float &bv, int &bi) {
     for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
 }
 
+// out2 (may be null): a second copy of each row's pick (chained greedy
+// steps: the next step's token-table slot on the device).
 __global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int ld, const int32_t *rows, int n,
-                                                     int32_t *out, float *pv, int32_t *pi, int32_t *counter) {
+                                                     int32_t *out, float *pv, int32_t *pi, int32_t *counter,
+                                                     int32_t *out2) {
     const int row = blockIdx.y, b = blockIdx.x, nb = gridDim.x;
     const float *z = logits + (size_t)(rows ? rows[row] : row) * ld;
     const int chunk = ((n + nb - 1) / nb + 3) & ~3;
@@ -3034,7 +3037,9 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int ld
                __hip_atomic_load(pi + row * nb + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     block_best(bv, bi);
     if (threadIdx.x == 0) {
-        out[row] = bi == 0x7fffffff ? 0 : bi;
+        const int32_t pick = bi == 0x7fffffff ? 0 : bi;
+        out[row] = pick;
+        if (out2) out2[row] = pick;
         counter[row] = 0;
     }
 }
@@ -3055,15 +3060,15 @@ void launch_argmax_two_pass(const float *logits, int ld, int n_rows, int n, int3
                             hipStream_t s) {
     if (n_rows <= 0) return;
     UBD_LAUNCH(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld,
-                       (const int32_t *)nullptr, n, out, pv, pi, (int32_t *)nullptr);
+                       (const int32_t *)nullptr, n, out, pv, pi, (int32_t *)nullptr, (int32_t *)nullptr);
     UBD_LAUNCH(argmax_final_kernel, dim3(n_rows), dim3(256), 0, s, pv, pi, ARGMAX_BLOCKS, out);
 }
 
 void launch_argmax(const float *logits, int ld, const int32_t *rows, int n_rows, int n, int32_t *out,
-                   const ArgmaxWork &w, hipStream_t s) {
+                   const ArgmaxWork &w, hipStream_t s, int32_t *out2) {
     if (n_rows <= 0) return;
     UBD_LAUNCH(argmax_kernel, dim3(ARGMAX_BLOCKS, n_rows), dim3(256), 0, s, logits, ld, rows, n, out, w.pv,
-                       w.pi, w.counter);
+                       w.pi, w.counter, out2);
 }
 
 // ------------------------------------------------------------- relayout

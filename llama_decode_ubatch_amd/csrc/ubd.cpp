@@ -461,6 +461,7 @@ struct ubd_context : public Executor {
     std::vector<float> logits_host;
     bool logits_host_valid = false;
     int32_t *argmax_host = nullptr;         // pinned, coherent: the argmax kernel writes the picks here
+    bool chain_tok = false;                 // this ubatch's one token id is already in the device table
     ArgmaxWork argmax_work;
     std::vector<int32_t> last_ub_idx;
     float *dump = nullptr;
@@ -724,7 +725,8 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
             !hip_ok(hipEventCreateWithFlags(&c->info_ev[i], hipEventDisableTiming), "event"))
             return bail("pinned staging allocation failed");
     }
-    if (!hip_ok(hipHostMalloc((void **)&c->argmax_host, (size_t)std::max<uint32_t>(P.n_batch, 1) * 4,
+    if (!hip_ok(hipHostMalloc((void **)&c->argmax_host,
+                              (size_t)std::max<uint32_t>(P.n_batch, UBD_GREEDY_CHAIN_ROUND) * 4,
                               hipHostMallocCoherent), "pinned"))
         return bail("pinned argmax buffer allocation failed");
     if (!hip_ok(hipStreamSynchronize(c->stream), "init sync")) return bail("sync failed");
@@ -923,7 +925,11 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         ++n_tiles;
         t = e;
     }
-    if (!hip_ok(hipMemcpyAsync(info_dev, h, info_ints(T) * 4, hipMemcpyHostToDevice, stream), "token table upload") ||
+    // (a chained greedy step's token id was written into the table by the
+    // previous step's argmax: the upload leaves that word alone)
+    const int skip = chain_tok && T == 1 ? 1 : 0;
+    if (!hip_ok(hipMemcpyAsync(info_dev + skip, h + skip, (info_ints(T) - skip) * 4, hipMemcpyHostToDevice, stream),
+                "token table upload") ||
         !hip_ok(hipEventRecord(info_ev[bi], stream), "event"))
         return UBD_COMPUTE_FAILED;
     last_ub_idx = ub.idx;
@@ -1269,6 +1275,54 @@ extern "C" int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32
     if (!hip_ok(hipStreamSynchronize(ctx->stream), "argmax sync")) return -1;
     std::memcpy(out, ctx->argmax_host, (size_t)P.n_outputs * 4);
     return P.n_outputs;
+}
+
+extern "C" int32_t ubd_greedy_chain(ubd_context *ctx, ubd_token first, ubd_seq_id seq_id, int32_t n_steps,
+                                    ubd_token *out) {
+    if (!ctx || !out || n_steps < 0) return UBD_INVALID;
+    g_err.clear();
+    const int V = ctx->model->hp.n_vocab;
+    if (first < 0 || first >= V) {
+        set_err("ubd_greedy_chain: first token out of range");
+        return UBD_INVALID;
+    }
+    if (!hip_ok(hipSetDevice(ctx->model->device), "hipSetDevice")) return UBD_ALLOC_FAILED;
+    int32_t done = 0, rc = UBD_OK;
+    while (done < n_steps && rc == UBD_OK) {
+        // one round of picks held in pinned memory, then copied out
+        const int n = std::min<int32_t>(n_steps - done, UBD_GREEDY_CHAIN_ROUND);
+        int k = 0;
+        for (; k < n; ++k) {
+            const double t0 = now_ms();
+            // steps after the first embed the previous pick, which the argmax
+            // kernel leaves in the device token table; 0 stands in for it on
+            // the host (a valid id for the batch checks)
+            ubd_token tok = done + k == 0 ? first : 0;
+            ubd_seq_id sid = seq_id;
+            ubd_seq_id *sids = &sid;
+            int32_t nsid = 1;
+            int8_t lg = 1;
+            const ubd_batch b{1, &tok, nullptr, nullptr, &nsid, &sids, &lg};
+            ctx->chain_tok = done + k > 0;
+            std::string err;
+            rc = ctx->planner.decode(b, ctx, &err);
+            ctx->chain_tok = false;
+            if (rc != UBD_OK) {
+                if (g_err.empty()) set_err(err);
+                break;
+            }
+            launch_argmax(ctx->logits_dev, V, nullptr, 1, V, ctx->argmax_host + k, ctx->argmax_work, ctx->stream,
+                          ctx->info_dev);
+            ctx->perf.t_eval_ms += now_ms() - t0;
+            ctx->perf.n_eval += 1;
+            ctx->perf.n_decode += 1;
+        }
+        if (!hip_ok(hipStreamSynchronize(ctx->stream), "greedy chain sync")) return UBD_COMPUTE_FAILED;
+        std::memcpy(out + done, ctx->argmax_host, (size_t)k * 4);
+        done += k;
+    }
+    if (rc != UBD_OK && done == 0) return rc;
+    return done;
 }
 
 // ----------------------------------------------------------------- sampler
