@@ -46,10 +46,10 @@ TRACE_FILES = {
     ("decode.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
                                      ("linear_ldsx_kernel<2, 2, 4, true>",)),
     ("prefill.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
-                                      ("gemm_deep_kernel<2, 4, 4, 1, 2, 1, true>",)),
+                                      ("gemm_deep_kernel<2, 4, 4, 1, 2, 1, true, 2>",)),
     # split pass + combine pass, as the events span both
     ("decode.attention", "bf16"): (os.path.join(ROOT, "profiles", "decode_8b_16seq_32k_kernel_stats.md"),
-                                   ("attn_mfma_kernel<128, true, false, false>", "attn_merge_kernel<128>")),
+                                   ("attn_mfma_kernel<128, true, false, 1>", "attn_merge_kernel<128>")),
     ("decode.ffn_gate_up", "q8_0"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_q8_0_kernel_stats.md"),
                                      ("linear_ldsx_kernel<3, 2, 4, true>",)),
 }
