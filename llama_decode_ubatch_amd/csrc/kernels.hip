@@ -1786,6 +1786,7 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
     case 16: if (launch_gemm_deep<EPI, 4, 4, 1, 2, 1, true>(a, s)) return; break;
     case 18: if (launch_gemm_deep<EPI, 4, 4, 1, 2, RS, true>(a, s)) return; break;
     case 19: if (launch_gemm_deep<EPI, 4, 4, 1, 2, EPI == EPI_RESID ? 4 : 1, true>(a, s)) return; break;
+    case 20: if (launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true, 3>(a, s)) return; break;
     default: break;
     }
     if (EPI == EPI_RESID) {
