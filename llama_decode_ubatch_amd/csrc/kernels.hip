@@ -2175,12 +2175,18 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *x, int ldx, c
 // RMSNorm of one row into tiled HILO activations (d a multiple of 32): every
 // thread owns 8-value runs, each one lane's 16 bytes of an operand tile, so
 // the two planes take one 16-byte store per run.
+// Work-group b takes row (b % 8) * (rows / 8) + b / 8 when rows is a multiple
+// of 8: work-groups go to the 8 XCDs in turn, so each XCD writes whole
+// 16-row blocks of the tiled output, whose 128-byte lines interleave 8 rows.
 __global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float *x, int ldx, const int32_t *row_map,
                                                             const float *gain, int d, float eps, Act out) {
-    const int r = blockIdx.x;
+    const int rows = gridDim.x, b = blockIdx.x;
+    const int r = rows % 8 == 0 ? (b % 8) * (rows / 8) + b / 8 : b;
     const float *xr = x + (size_t)(row_map ? row_map[r] : r) * ldx;
     constexpr int MAXV = 4;                  // 8-value runs per thread held in registers (d <= 8192)
-    f32x4_t v[MAXV][2];
+    // the row and its gains are loaded together, so the gains' round trip
+    // hides under the row's
+    f32x4_t v[MAXV][2], gn[MAXV][2];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
@@ -2188,10 +2194,15 @@ __global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float *x, int 
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             v[i][h] = e < d ? *(const f32x4_t *)(xr + e + 4 * h) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            ss += v[i][h][0] * v[i][h][0] + v[i][h][1] * v[i][h][1] + v[i][h][2] * v[i][h][2] +
-                  v[i][h][3] * v[i][h][3];
+            gn[i][h] = e < d ? *(const f32x4_t *)(gain + e + 4 * h) : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            ss += v[i][h][0] * v[i][h][0] + v[i][h][1] * v[i][h][1] + v[i][h][2] * v[i][h][2] +
+                  v[i][h][3] * v[i][h][3];
     for (int e = (threadIdx.x + 256 * MAXV) * 8; e < d; e += 2048)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -2203,9 +2214,9 @@ __global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float *x, int 
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
-    auto put = [&](int e, f32x4_t a0, f32x4_t a1) {
-        const f32x4_t y0 = a0 * inv * *(const f32x4_t *)(gain + e);
-        const f32x4_t y1 = a1 * inv * *(const f32x4_t *)(gain + e + 4);
+    auto put = [&](int e, f32x4_t a0, f32x4_t a1, f32x4_t g0, f32x4_t g1) {
+        const f32x4_t y0 = a0 * inv * g0;
+        const f32x4_t y1 = a1 * inv * g1;
         u16x8_t hh, ll;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -2220,10 +2231,11 @@ __global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float *x, int 
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
         const int e = (threadIdx.x + 256 * i) * 8;
-        if (e < d) put(e, v[i][0], v[i][1]);
+        if (e < d) put(e, v[i][0], v[i][1], gn[i][0], gn[i][1]);
     }
     for (int e = (threadIdx.x + 256 * MAXV) * 8; e < d; e += 2048)
-        put(e, *(const f32x4_t *)(xr + e), *(const f32x4_t *)(xr + e + 4));
+        put(e, *(const f32x4_t *)(xr + e), *(const f32x4_t *)(xr + e + 4), *(const f32x4_t *)(gain + e),
+            *(const f32x4_t *)(gain + e + 4));
 }
 
 void launch_rmsnorm(const float *x, int ldx, const int32_t *row_map, int rows, const float *gain, int d,
