@@ -1701,6 +1701,137 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 #endif
 }
 
+// Wide prefill product (bf16 weights, activations as hi + lo planes in
+// operand-tiled order): a work-group of 8 waves computes a 256-row x
+// 128-token tile.  Each 32-wide k stage's weights (16 row-block fragments)
+// and activations (8 token blocks x 2 planes) go straight from global memory
+// into a 4-deep LDS ring (buffer_load ... lds, each wave copying 2 + 2
+// fragments), three stages ahead; wave (wr, wc) multiplies row blocks
+// 4wr..4wr+3 by token blocks 4wc..4wc+3 out of LDS.  Every weight and
+// activation byte crosses the load path once per work-group and feeds two
+// waves: 128 bytes per MFMA, where the 256 x 64 tile of the deep kernel
+// (weights straight to registers) needs 192 and waits on that path.  The
+// stage count K / 32 / SPLITK must be whole.  SPLITK > 1 as the deep kernel.
+template <int EPI, int SPLITK = 1>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_wide_kernel(
+    LinearArgs a, int n_wtiles, int n_ttiles) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int NX = 4;                 // ring depth (stages)
+    constexpr int WF = 16, XF = 16;       // weight / activation fragments (1 KB) per stage
+    constexpr int SF = WF + XF;
+    static_assert(SPLITK == 1 || EPI == EPI_RESID, "k split: residual products only");
+    __shared__ u32x4_t ring[NX * SF * 64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave >> 1, wc = wave & 1;
+    const int r = lane & 15, g = lane >> 4;
+    const int total = n_wtiles * n_ttiles * SPLITK;
+    const int b = blockIdx.x;
+    const int tile = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
+    const int ks = tile % SPLITK;
+    const int tt = (tile / SPLITK) % n_ttiles;
+    const int nt = tile / (SPLITK * n_ttiles);
+    const int nrb = a.N / 16;
+    const int rbt = nt * 16;              // the tile's first row block
+    const int t0 = tt * 128;
+    const int nst_all = a.K / 32;
+    const int sbeg = ks * (nst_all / SPLITK), nst = sbeg + nst_all / SPLITK;
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, (size_t)a.N * a.K * 2);
+    const size_t xbytes = (size_t)((a.T + 15) / 16 * 16) * a.x.ld * 2;
+    const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, xbytes);
+    const __amdgpu_buffer_rsrc_t rxl = make_rsrc(a.x.lo, xbytes);
+    // this wave's copies: weight fragments (row blocks) 2 wave + u, clamped
+    // to the last row block (the epilogue skips rows past N), and activation
+    // fragments f = 2 wave + u = (plane f / 8, token block f % 8)
+    int woff[2], xoff[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        woff[u] = min(rbt + 2 * wave + u, nrb - 1) * 1024 + lane * 16;
+        const int tb = (2 * wave + u) % 8;
+        xoff[u] = (t0 / 16 + tb) * (a.x.ld / 32) * 1024 + lane * 16;
+    }
+    const bool xlo = wave >= 4;           // fragments 8..15 are the lo plane
+    const int wstep = nrb * 1024;
+
+    // stage s (clamped to the last: the loads past the end keep the issue
+    // pattern, and so the wait counts, unchanged) into ring slot s % NX
+    auto issue = [&](int s) {
+        const int sl = min(s, nst - 1);
+        u32x4_t *slot = ring + (size_t)(s % NX) * SF * 64;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void *)(slot + (2 * wave + u) * 64), 16, woff[u], sl * wstep,
+                0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xlo ? rxl : rxh, (__attribute__((address_space(3))) void *)(slot + (WF + 2 * wave + u) * 64), 16,
+                xoff[u], sl * 1024, 0, 0);
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // stage s needs its 4 copies landed: 2 later stages (8 copies) may
+    // still be in flight
+#pragma unroll
+    for (int k = 0; k < NX - 1; ++k) issue(sbeg + k);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s = sbeg; s < nst; ++s) {
+        wait_vm<4 * (NX - 2)>();
+        wg_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + NX - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4_t *slot = ring + (size_t)(s % NX) * SF * 64;
+        u32x4_t A[4], B[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[i] = slot[(4 * wr + i) * 64 + lane];
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) B[pl][tb] = slot[(WF + 8 * pl + 4 * wc + tb) * 64 + lane];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+                    acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[i]),
+                                                                         __builtin_bit_cast(bf16x8_t, B[pl][tb]),
+                                                                         acc[i][tb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // the ring's last copies must land before the work-group's LDS is released
+    wait_vm<0>();
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rb = rbt + 4 * wr + i;
+        if (rb >= nrb) continue;
+        if (EPI == EPI_SWIGLU && (i & 1)) continue;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int t = t0 + 64 * wc + 16 * tb + r;
+            if (t >= a.T) continue;
+            if (SPLITK > 1)
+                store4(a.split_out + ((size_t)ks * a.T + t) * a.N + rb * 16 + 4 * g, acc[i][tb]);
+            else if (EPI == EPI_SWIGLU)
+                epilogue4<EPI, false>(a, t, (rb >> 1) * 16 + 4 * g, acc[i][tb], acc[i + 1][tb]);
+            else
+                epilogue4<EPI, false>(a, t, rb * 16 + 4 * g, acc[i][tb], acc[i][tb]);
+        }
+    }
+#endif
+}
+
 // y[t][n] += the k slices' partial sums, slice 0 first
 __global__ __launch_bounds__(256) void resid_add_splits_kernel(float *y, int ldy, const float *parts, int T, int N,
                                                                int nsplit) {
@@ -1730,6 +1861,25 @@ static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
         const long n = (long)a.T * (a.N / 4);
         UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
                            a.split_out, a.T, a.N, SPLITK);
+    }
+    return true;
+}
+
+// false (nothing launched) unless the operands are the tiled hi + lo planes
+// and each k slice's stage count is whole (and, split, the product is a
+// residual one with scratch for the slices)
+template <int EPI, int SPLITK = 1>
+static bool launch_gemm_wide(const LinearArgs &a, hipStream_t s) {
+    if (!a.x.tiled || !a.x.lo || a.K % 32 || (a.K / 32) % SPLITK) return false;
+    if (SPLITK > 1 && (EPI != EPI_RESID || !a.split_out || a.N % 4)) return false;
+    const int n_wtiles = (a.N + 255) / 256;
+    const int n_ttiles = (a.T + 127) / 128;
+    UBD_LAUNCH((gemm_wide_kernel<EPI, SPLITK>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(512), 0, s, a, n_wtiles,
+               n_ttiles);
+    if (SPLITK > 1) {
+        const long n = (long)a.T * (a.N / 4);
+        UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
+                   a.split_out, a.T, a.N, SPLITK);
     }
     return true;
 }
@@ -1787,6 +1937,8 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
     case 18: if (launch_gemm_deep<EPI, 4, 4, 1, 2, RS, true>(a, s)) return; break;
     case 19: if (launch_gemm_deep<EPI, 4, 4, 1, 2, EPI == EPI_RESID ? 4 : 1, true>(a, s)) return; break;
     case 20: if (launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true, 3>(a, s)) return; break;
+    case 21: if (launch_gemm_wide<EPI, 1>(a, s)) return; break;
+    case 22: if (launch_gemm_wide<EPI, EPI == EPI_RESID ? 4 : 1>(a, s)) return; break;
     default: break;
     }
     if (EPI == EPI_RESID) {
@@ -1795,9 +1947,13 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
         constexpr int RS4 = EPI == EPI_RESID ? 4 : 1;
         if (g_tuning.gemm_split == 4 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS4, true>(a, s)) return;
         if (g_tuning.gemm_split == 2 && launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s)) return;
-        // long k (FFN down): the 256 x 64 tile (one stage of weight look-ahead)
-        // in 4 k slices, else the 128 x 64 tile in 2 (8B shape at 512 tokens:
-        // 110.5 against 130.5 us)
+        // long k (FFN down): the wide 256 x 128 tile in 4 k slices when that
+        // gives a work-group per CU (8B shape at 512 tokens: 104 against 113
+        // us), else the deep 256 x 64 tile (one stage of weight look-ahead) in
+        // 4 slices (110.5 against 130.5 us for the 128 x 64 tile in 2)
+        const long wide_tiles = (long)((a.N + 255) / 256) * ((a.T + 127) / 128);
+        if (g_tuning.gemm_split == 0 && a.K >= 8192 && wide_tiles * 4 >= 256 && launch_gemm_wide<EPI, RS4>(a, s))
+            return;
         if (g_tuning.gemm_split == 0 && a.K >= 8192 && tiles(4, 4) * 4 >= 256 &&
             launch_gemm_deep<EPI, 4, 4, 1, 2, RS4, true>(a, s))
             return;
