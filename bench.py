@@ -46,7 +46,7 @@ TRACE_FILES = {
     ("decode.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
                                      ("linear_ldsx_kernel<2, 2, 4, true>",)),
     ("prefill.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
-                                      ("gemm_deep_kernel<2, 4, 4, 1, 2, 1, true, 2>",)),
+                                      ("gemm_wide_kernel<2, 1, 2>",)),
     # split pass + combine pass, as the events span both
     ("decode.attention", "bf16"): (os.path.join(ROOT, "profiles", "decode_8b_16seq_32k_kernel_stats.md"),
                                    ("attn_mfma_kernel<128, true, false, 1>", "attn_merge_kernel<128>")),
@@ -307,7 +307,7 @@ def roofline_prefill_of(w, r):
     ach = flops / (avg_us * 1e-6) / 1e12
     out = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-           "kernel": "prefill.ffn_gate_up (gemm_deep_kernel 256 x 64 tiles, SwiGLU epilogue; the method's FLOPs, the activations' "
+           "kernel": "prefill.ffn_gate_up (gemm_wide_kernel 256 x 128 tiles, SwiGLU epilogue; the method's FLOPs, the activations' "
                      "hi and lo planes make twice that of matrix-core work)",
            "flops_per_launch": flops, "avg_us": round(avg_us, 2),
            "traffic": measured_traffic("prefill.ffn_gate_up")

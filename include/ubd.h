@@ -554,7 +554,8 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * three stages ahead with the activations three stages ahead, the residual
  * short-k products' automatic tile; 21 = the wide 256 x 128 tile of 8 waves
  * with weights and activations staged in LDS, 22 the same with residual
- * products in four k slices),
+ * products in four k slices, 23 the same unsplit with a 2-deep ring, two
+ * work-groups per CU),
  * "gemm_split"
  * (residual prefill products: 0 = automatic k split, 2 or 4 forced),
  * "small_rb" (1 =

@@ -1712,11 +1712,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 // waves: 128 bytes per MFMA, where the 256 x 64 tile of the deep kernel
 // (weights straight to registers) needs 192 and waits on that path.  The
 // stage count K / 32 / SPLITK must be whole.  SPLITK > 1 as the deep kernel.
-template <int EPI, int SPLITK = 1>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_wide_kernel(
+// NX = ring depth: 4 (128 KB, one work-group per CU) or 2 (64 KB, two).
+template <int EPI, int SPLITK = 1, int NX = 4>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NX == 4 ? 2 : 4, NX == 4 ? 2 : 4))) void gemm_wide_kernel(
     LinearArgs a, int n_wtiles, int n_ttiles) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int NX = 4;                 // ring depth (stages)
+    static_assert(NX == 2 || NX == 4, "ring depth");
     constexpr int WF = 16, XF = 16;       // weight / activation fragments (1 KB) per stage
     constexpr int SF = WF + XF;
     static_assert(SPLITK == 1 || EPI == EPI_RESID, "k split: residual products only");
@@ -1868,13 +1869,13 @@ static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
 // false (nothing launched) unless the operands are the tiled hi + lo planes
 // and each k slice's stage count is whole (and, split, the product is a
 // residual one with scratch for the slices)
-template <int EPI, int SPLITK = 1>
+template <int EPI, int SPLITK = 1, int NX = 4>
 static bool launch_gemm_wide(const LinearArgs &a, hipStream_t s) {
     if (!a.x.tiled || !a.x.lo || a.K % 32 || (a.K / 32) % SPLITK) return false;
     if (SPLITK > 1 && (EPI != EPI_RESID || !a.split_out || a.N % 4)) return false;
     const int n_wtiles = (a.N + 255) / 256;
     const int n_ttiles = (a.T + 127) / 128;
-    UBD_LAUNCH((gemm_wide_kernel<EPI, SPLITK>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(512), 0, s, a, n_wtiles,
+    UBD_LAUNCH((gemm_wide_kernel<EPI, SPLITK, NX>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(512), 0, s, a, n_wtiles,
                n_ttiles);
     if (SPLITK > 1) {
         const long n = (long)a.T * (a.N / 4);
@@ -1939,6 +1940,7 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
     case 20: if (launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true, 3>(a, s)) return; break;
     case 21: if (launch_gemm_wide<EPI, 1>(a, s)) return; break;
     case 22: if (launch_gemm_wide<EPI, EPI == EPI_RESID ? 4 : 1>(a, s)) return; break;
+    case 23: if (launch_gemm_wide<EPI, 1, 2>(a, s)) return; break;
     default: break;
     }
     if (EPI == EPI_RESID) {
@@ -1975,10 +1977,15 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
         launch_gemm_lds<W_BF16, EPI, 1, 4, 1, true>(a, s);
         return;
     }
-    // gate|up: the deep 256 x 64 tile with one stage of weight look-ahead
-    // in rotating register sets when there are >= 2 work-groups per CU (8B
-    // shape at 512 tokens: 203.1 us against 215.2 us for the LDS-ring tile;
-    // the same tile on the O and down products is slower)
+    // gate|up: the wide 256 x 128 tile with a 2-deep ring (two work-groups
+    // per CU, so all of them resident at once) when there are >= 384 such
+    // tiles (8B shape at 512 tokens: 195.9 against 205.4 us), else the deep
+    // 256 x 64 tile with one stage of weight look-ahead in rotating register
+    // sets when there are >= 2 work-groups per CU (203.1 us against 215.2 us
+    // for the LDS-ring tile; the same tile on the O and down products is slower)
+    if (EPI == EPI_SWIGLU && (long)((a.N + 255) / 256) * ((a.T + 127) / 128) >= 384 &&
+        launch_gemm_wide<EPI, 1, 2>(a, s))
+        return;
     if (EPI == EPI_SWIGLU && tiles(4, 4) >= 512 && launch_gemm_deep<EPI, 4, 4, 1, 2, 1, true>(a, s)) return;
     if (tiles(4, 4) >= 192)
         launch_gemm_lds<W_BF16, EPI, 4, 4, 1, true>(a, s);
