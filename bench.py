@@ -46,7 +46,7 @@ TRACE_FILES = {
     ("decode.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
                                      ("linear_ldsx_kernel<2, 2, 4, true>",)),
     ("prefill.ffn_gate_up", "bf16"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_bf16_kernel_stats.md"),
-                                      ("gemm_wide_kernel<2, 1, 2>",)),
+                                      ("gemm_wide_kernel<2, 1, 2, 4, 4>",)),
     # split pass + combine pass, as the events span both
     ("decode.attention", "bf16"): (os.path.join(ROOT, "profiles", "decode_8b_16seq_32k_kernel_stats.md"),
                                    ("attn_mfma_kernel<128, true, false, 1>", "attn_merge_kernel<128>")),

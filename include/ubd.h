@@ -555,7 +555,8 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * short-k products' automatic tile; 21 = the wide 256 x 128 tile of 8 waves
  * with weights and activations staged in LDS, 22 the same with residual
  * products in four k slices, 23 the same unsplit with a 2-deep ring, two
- * work-groups per CU),
+ * work-groups per CU; 24 = the wide kernel's 128 x 64 tile, 8 waves of
+ * 32 x 32, 25 the same with residual products in two k slices),
  * "gemm_split"
  * (residual prefill products: 0 = automatic k split, 2 or 4 forced),
  * "small_rb" (1 =
@@ -565,8 +566,8 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * bf16 planes, a mask of bits 1 QKV, 2 O, 4 gate|up, 8 down, 16 logits;
  * default 31 = all; the others take the hi plane only, i.e. bf16-rounded
  * activations, which leaves about 6e-3 of relative error per 8B-shaped
- * layer; with both planes the forced shapes are 1, 3, 5, 10, 14, 16, 18 and
- * 19 to 22).
+ * layer; with both planes the forced shapes are 1, 3, 5, 10, 14, 16 and 18
+ * to 25).
  * Results do not depend on them beyond rounding, except "prefill_lo".
  * The knobs are process-wide and unsynchronised: set them while no other
  * thread is inside the library; every context sees the change.  0, or -1

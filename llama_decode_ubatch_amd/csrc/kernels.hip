@@ -1702,25 +1702,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 }
 
 // Wide prefill product (bf16 weights, activations as hi + lo planes in
-// operand-tiled order): a work-group of 8 waves computes a 256-row x
-// 128-token tile.  Each 32-wide k stage's weights (16 row-block fragments)
-// and activations (8 token blocks x 2 planes) go straight from global memory
-// into a 4-deep LDS ring (buffer_load ... lds, each wave copying 2 + 2
-// fragments), three stages ahead; wave (wr, wc) multiplies row blocks
-// 4wr..4wr+3 by token blocks 4wc..4wc+3 out of LDS.  Every weight and
-// activation byte crosses the load path once per work-group and feeds two
-// waves: 128 bytes per MFMA, where the 256 x 64 tile of the deep kernel
-// (weights straight to registers) needs 192 and waits on that path.  The
-// stage count K / 32 / SPLITK must be whole.  SPLITK > 1 as the deep kernel.
-// NX = ring depth: 4 (128 KB, one work-group per CU) or 2 (64 KB, two).
-template <int EPI, int SPLITK = 1, int NX = 4>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NX == 4 ? 2 : 4, NX == 4 ? 2 : 4))) void gemm_wide_kernel(
-    LinearArgs a, int n_wtiles, int n_ttiles) {
+// operand-tiled order): a work-group of 8 waves in a 4 x 2 grid computes a
+// (64 RBW)-row x (32 TBW)-token tile, wave (wr, wc) multiplying row blocks
+// wr RBW .. + RBW by token blocks wc TBW .. + TBW.  Each 32-wide k stage's
+// weights (4 RBW row-block fragments) and activations (2 TBW token blocks x
+// 2 planes) go straight from global memory into an NX-deep LDS ring
+// (buffer_load ... lds, each wave copying an equal run of fragments), NX - 1
+// stages ahead, and every wave reads its operands out of LDS.  Each weight
+// and activation byte crosses the load path once per work-group and feeds
+// two (weights) or four (activations) waves: RBW = TBW = 4 (256 x 128) needs
+// 128 bytes per MFMA, RBW = TBW = 2 (128 x 64) 256, where the deep kernel's
+// 256 x 64 tile needs 192 and the products wait on that path.  The stage
+// count K / 32 / SPLITK must be whole; SPLITK > 1 as the deep kernel.
+template <int EPI, int SPLITK = 1, int NX = 4, int RBW = 4, int TBW = 4>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(
+    NX * 4 * (RBW + TBW) <= 80 ? 4 : 2, NX * 4 * (RBW + TBW) <= 80 ? 4 : 2))) void
+gemm_wide_kernel(LinearArgs a, int n_wtiles, int n_ttiles) {
+    // (waves per SIMD: two work-groups share a CU when the ring's KB fit 80)
 #if defined(__HIP_DEVICE_COMPILE__)
-    static_assert(NX == 2 || NX == 4, "ring depth");
-    constexpr int WF = 16, XF = 16;       // weight / activation fragments (1 KB) per stage
+    constexpr int WF = 4 * RBW;           // weight fragments (1 KB) per stage
+    constexpr int TBT = 2 * TBW;          // token blocks per tile
+    constexpr int XF = 2 * TBT;           // activation fragments per stage (2 planes)
     constexpr int SF = WF + XF;
+    constexpr int CPW = SF / 8;           // fragments each wave copies per stage
+    static_assert(NX == 2 || NX == 4, "ring depth");
+    static_assert(SF % 8 == 0 && WF % CPW == 0, "each wave copies weights or activations only");
     static_assert(SPLITK == 1 || EPI == EPI_RESID, "k split: residual products only");
+    static_assert(EPI != EPI_SWIGLU || RBW % 2 == 0, "gate and up row blocks in pairs");
     __shared__ u32x4_t ring[NX * SF * 64];
 
     const int lane = threadIdx.x & 63;
@@ -1734,8 +1742,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NX == 4 ? 2
     const int tt = (tile / SPLITK) % n_ttiles;
     const int nt = tile / (SPLITK * n_ttiles);
     const int nrb = a.N / 16;
-    const int rbt = nt * 16;              // the tile's first row block
-    const int t0 = tt * 128;
+    const int rbt = nt * WF;              // the tile's first row block
+    const int t0 = tt * TBT * 16;
     const int nst_all = a.K / 32;
     const int sbeg = ks * (nst_all / SPLITK), nst = sbeg + nst_all / SPLITK;
 
@@ -1743,18 +1751,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NX == 4 ? 2
     const size_t xbytes = (size_t)((a.T + 15) / 16 * 16) * a.x.ld * 2;
     const __amdgpu_buffer_rsrc_t rxh = make_rsrc(a.x.hi, xbytes);
     const __amdgpu_buffer_rsrc_t rxl = make_rsrc(a.x.lo, xbytes);
-    // this wave's copies: weight fragments (row blocks) 2 wave + u, clamped
-    // to the last row block (the epilogue skips rows past N), and activation
-    // fragments f = 2 wave + u = (plane f / 8, token block f % 8)
-    int woff[2], xoff[2];
+    // this wave's copies: fragments f = CPW wave + u; f < WF is row block
+    // rbt + f (clamped to the last row block: the epilogue skips rows past
+    // N), else activation fragment f - WF = (plane, token block)
+    const int f0 = CPW * wave;
+    const bool wcopy = f0 < WF;
+    const bool xlo = !wcopy && f0 - WF >= TBT;
+    int off[CPW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        woff[u] = min(rbt + 2 * wave + u, nrb - 1) * 1024 + lane * 16;
-        const int tb = (2 * wave + u) % 8;
-        xoff[u] = (t0 / 16 + tb) * (a.x.ld / 32) * 1024 + lane * 16;
+    for (int u = 0; u < CPW; ++u) {
+        const int f = f0 + u;
+        off[u] = wcopy ? min(rbt + f, nrb - 1) * 1024 + lane * 16
+                       : (t0 / 16 + (f - WF) % TBT) * (a.x.ld / 32) * 1024 + lane * 16;
     }
-    const bool xlo = wave >= 4;           // fragments 8..15 are the lo plane
-    const int wstep = nrb * 1024;
+    const int sstep = wcopy ? nrb * 1024 : 1024;       // bytes between stages
 
     // stage s (clamped to the last: the loads past the end keep the issue
     // pattern, and so the wait counts, unchanged) into ring slot s % NX
@@ -1762,47 +1772,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NX == 4 ? 2
         const int sl = min(s, nst - 1);
         u32x4_t *slot = ring + (size_t)(s % NX) * SF * 64;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void *)(slot + (2 * wave + u) * 64), 16, woff[u], sl * wstep,
-                0, 0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xlo ? rxl : rxh, (__attribute__((address_space(3))) void *)(slot + (WF + 2 * wave + u) * 64), 16,
-                xoff[u], sl * 1024, 0, 0);
+        for (int u = 0; u < CPW; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wcopy ? rw : xlo ? rxl : rxh,
+                                                     (__attribute__((address_space(3))) void *)(slot + (f0 + u) * 64),
+                                                     16, off[u], sl * sstep, 0, 0);
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[RBW][TBW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RBW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // stage s needs its 4 copies landed: 2 later stages (8 copies) may
-    // still be in flight
+    // stage s needs its CPW copies landed: NX - 2 later stages may still be
+    // in flight
 #pragma unroll
     for (int k = 0; k < NX - 1; ++k) issue(sbeg + k);
     __builtin_amdgcn_sched_barrier(0);
     for (int s = sbeg; s < nst; ++s) {
-        wait_vm<4 * (NX - 2)>();
+        wait_vm<CPW * (NX - 2)>();
         wg_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue(s + NX - 1);
         __builtin_amdgcn_sched_barrier(0);
         const u32x4_t *slot = ring + (size_t)(s % NX) * SF * 64;
-        u32x4_t A[4], B[2][4];
+        u32x4_t A[RBW], B[2][TBW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) A[i] = slot[(4 * wr + i) * 64 + lane];
+        for (int i = 0; i < RBW; ++i) A[i] = slot[(RBW * wr + i) * 64 + lane];
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) B[pl][tb] = slot[(WF + 8 * pl + 4 * wc + tb) * 64 + lane];
+            for (int tb = 0; tb < TBW; ++tb) B[pl][tb] = slot[(WF + TBT * pl + TBW * wc + tb) * 64 + lane];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < TBW; ++tb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < RBW; ++i)
 #pragma unroll
                 for (int pl = 0; pl < 2; ++pl)
                     acc[i][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[i]),
@@ -1814,13 +1819,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NX == 4 ? 2
     wait_vm<0>();
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rb = rbt + 4 * wr + i;
+    for (int i = 0; i < RBW; ++i) {
+        const int rb = rbt + RBW * wr + i;
         if (rb >= nrb) continue;
         if (EPI == EPI_SWIGLU && (i & 1)) continue;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const int t = t0 + 64 * wc + 16 * tb + r;
+        for (int tb = 0; tb < TBW; ++tb) {
+            const int t = t0 + (TBW * wc + tb) * 16 + r;
             if (t >= a.T) continue;
             if (SPLITK > 1)
                 store4(a.split_out + ((size_t)ks * a.T + t) * a.N + rb * 16 + 4 * g, acc[i][tb]);
@@ -1869,14 +1874,14 @@ static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
 // false (nothing launched) unless the operands are the tiled hi + lo planes
 // and each k slice's stage count is whole (and, split, the product is a
 // residual one with scratch for the slices)
-template <int EPI, int SPLITK = 1, int NX = 4>
+template <int EPI, int SPLITK = 1, int NX = 4, int RBW = 4, int TBW = 4>
 static bool launch_gemm_wide(const LinearArgs &a, hipStream_t s) {
     if (!a.x.tiled || !a.x.lo || a.K % 32 || (a.K / 32) % SPLITK) return false;
     if (SPLITK > 1 && (EPI != EPI_RESID || !a.split_out || a.N % 4)) return false;
-    const int n_wtiles = (a.N + 255) / 256;
-    const int n_ttiles = (a.T + 127) / 128;
-    UBD_LAUNCH((gemm_wide_kernel<EPI, SPLITK, NX>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(512), 0, s, a, n_wtiles,
-               n_ttiles);
+    const int n_wtiles = (a.N + 64 * RBW - 1) / (64 * RBW);
+    const int n_ttiles = (a.T + 32 * TBW - 1) / (32 * TBW);
+    UBD_LAUNCH((gemm_wide_kernel<EPI, SPLITK, NX, RBW, TBW>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(512), 0, s, a,
+               n_wtiles, n_ttiles);
     if (SPLITK > 1) {
         const long n = (long)a.T * (a.N / 4);
         UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
@@ -1941,6 +1946,8 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
     case 21: if (launch_gemm_wide<EPI, 1>(a, s)) return; break;
     case 22: if (launch_gemm_wide<EPI, EPI == EPI_RESID ? 4 : 1>(a, s)) return; break;
     case 23: if (launch_gemm_wide<EPI, 1, 2>(a, s)) return; break;
+    case 24: if (launch_gemm_wide<EPI, 1, 4, 2, 2>(a, s)) return; break;
+    case 25: if (launch_gemm_wide<EPI, EPI == EPI_RESID ? 2 : 1, 4, 2, 2>(a, s)) return; break;
     default: break;
     }
     if (EPI == EPI_RESID) {
@@ -1962,17 +1969,22 @@ static void launch_gemm_lds_shape_lo(const LinearArgs &a, hipStream_t s) {
         if (g_tuning.gemm_split == 0 && a.K >= 8192 && tiles(2, 4) * 2 >= 192 &&
             launch_gemm_deep<EPI, 2, 4, 3, 2, RS, true>(a, s))
             return;
-        // short k (O): the 128 x 64 tile with activations three stages ahead
-        // in a 4-deep ring (8B shape at 512 tokens: 40.7 against 43.8 us with
-        // two stages ahead; deeper rings and more weight sets at one wave per
-        // SIMD measured no better)
+        // short k (O): the wide kernel's 128 x 64 tile (8 waves of 32 x 32)
+        // when there are >= 256 tiles (8B shape at 512 tokens: 40.9 against
+        // 42.8 us), else the deep 128 x 64 tile with activations three stages
+        // ahead in a 4-deep ring (40.7 against 43.8 us with two stages ahead;
+        // deeper rings and more weight sets at one wave per SIMD measured no
+        // better)
+        if (tiles(2, 4) >= 256 && launch_gemm_wide<EPI, 1, 4, 2, 2>(a, s)) return;
         if (tiles(2, 4) >= 192 && launch_gemm_deep<EPI, 2, 4, 3, 2, 1, true, 3>(a, s)) return;
         launch_gemm_lds<W_BF16, EPI, 2, 4, 1, true>(a, s);
         return;
     }
-    // QKV: 64 x 64 tiles when they give >= 384 work-groups (8B shape at 512
-    // tokens: 69.9 us against 84.2 us for 256 x 64 and 72.0 us for the deep
-    // 128 x 64 tile)
+    // QKV: the wide kernel's 128 x 64 tile (8 waves of 32 x 32) when there
+    // are >= 256 tiles (8B shape at 512 tokens: 65.1 against 69.5 us), else
+    // 64 x 64 tiles when they give >= 384 work-groups (69.9 us against 84.2
+    // us for 256 x 64 and 72.0 us for the deep 128 x 64 tile)
+    if (EPI == EPI_QKV && tiles(2, 4) >= 256 && launch_gemm_wide<EPI, 1, 4, 2, 2>(a, s)) return;
     if (EPI == EPI_QKV && tiles(1, 4) >= 384) {
         launch_gemm_lds<W_BF16, EPI, 1, 4, 1, true>(a, s);
         return;
