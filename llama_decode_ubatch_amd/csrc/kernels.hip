@@ -1726,7 +1726,8 @@ gemm_wide_kernel(LinearArgs a, int n_wtiles, int n_ttiles) {
     constexpr int SF = WF + XF;
     constexpr int CPW = SF / 8;           // fragments each wave copies per stage
     static_assert(NX == 2 || NX == 4, "ring depth");
-    static_assert(SF % 8 == 0 && WF % CPW == 0, "each wave copies weights or activations only");
+    static_assert(SF % 8 == 0 && WF % CPW == 0 && TBT % CPW == 0,
+                  "each wave copies weights or one activation plane only");
     static_assert(SPLITK == 1 || EPI == EPI_RESID, "k split: residual products only");
     static_assert(EPI != EPI_SWIGLU || RBW % 2 == 0, "gate and up row blocks in pairs");
     __shared__ u32x4_t ring[NX * SF * 64];
