@@ -132,12 +132,14 @@ def prefill_flops(w):
 
 
 # ------------------------------------------------------------------- the job
-def run_job(ctx, w, prompt, first_tokens=None):
+def run_job(ctx, w, prompt, first_tokens=None, chain=True):
     """One pass of the workload.  Returns (t_prefill_s, t_decode_s, ids).
     One sequence: the greedy steps run as one chain (ubd_greedy_chain: each
     pick goes from the argmax kernel straight into the next step's token
-    table, the same picks as decode + greedy step by step); several: one
-    decode of a token per sequence, then the greedy picks, per step."""
+    table, the same picks as decode + greedy step by step), or with
+    chain=False as ubd_decode + ubd_sample_greedy per step; several
+    sequences: one decode of a token per sequence, then the greedy picks,
+    per step."""
     import numpy as np
     if w.kv_prefill:
         for s in range(w.n_seqs):          # back to the pre-filled state
@@ -153,10 +155,15 @@ def run_job(ctx, w, prompt, first_tokens=None):
         tok = first_tokens
     t1 = time.perf_counter()
     ids.append(tok)
-    if w.n_seqs == 1:
-        chain = ctx.greedy_chain(tok, w.n_decode)
-        assert chain.size == w.n_decode
-        ids.extend(int(t) for t in chain)
+    if w.n_seqs == 1 and chain:
+        picks = ctx.greedy_chain(tok, w.n_decode)
+        assert picks.size == w.n_decode
+        ids.extend(int(t) for t in picks)
+    elif w.n_seqs == 1:
+        for _ in range(w.n_decode):
+            assert ctx.decode([tok]) == 0
+            tok = ctx.greedy(-1)
+            ids.append(tok)
     else:
         for _ in range(w.n_decode):
             assert ctx.decode(tok, seq_id=np.arange(w.n_seqs), logits=np.ones(w.n_seqs)) == 0
@@ -237,6 +244,15 @@ def measure(torch, model, w, steps, warmup):
     run_job(ctx, w, prompt, first)
     per_class = {k: {"launches": n, "avg_us": 1e3 * ms / n} for k, (n, ms) in ctx.kernel_stats().items()}
     ctx.kernel_timing([])
+    # one sequence: the same decode steps once more with the host picking each
+    # token (ubd_decode + ubd_sample_greedy per step), for comparison
+    td_steps, same_ids = None, None
+    if w.n_seqs == 1 and w.n_decode:
+        _, _, ids_chain = run_job(ctx, w, prompt, first)
+        _, td_steps, ids_steps = run_job(ctx, w, prompt, first, chain=False)
+        same_ids = ids_chain == ids_steps
+        log(f"[{w.name}] decode step by step (host picks): {w.n_decode / td_steps:.1f} tok/s, "
+            f"ids equal to the chain's: {same_ids}")
     ctx.free()
     log(f"[{w.name}] per-class breakdown of one job (kernel execution, events on every launch):")
     for k, v in sorted(per_class.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["launches"]):
@@ -251,6 +267,9 @@ def measure(torch, model, w, steps, warmup):
         "decode_tok_s": w.n_decode * w.n_seqs * steps / td_sum,
         "per_class": per_class,
     }
+    if td_steps:
+        r["decode_step_by_step"] = {"tok_s": round(w.n_decode / td_steps, 2), "ids_equal": same_ids,
+                                    "loop": "ubd_decode + ubd_sample_greedy per step, one job after the timed region"}
     # end-to-end fractions of the rooflines
     step_bytes = decode_bytes_per_step(w)
     r["e2e"] = {
@@ -392,6 +411,7 @@ def summary(w, r):
     s = {"workload": w.name, "value": round(r["value"], 2), "unit": "tokens/s",
          "ms_per_step": round(r["ms_per_step"], 3),
          "decode_tok_s": round(r["decode_tok_s"], 2), "e2e": r["e2e"],
+         **({"decode_step_by_step": r["decode_step_by_step"]} if "decode_step_by_step" in r else {}),
          "roofline": roofline_of(w, r)}
     if r["prefill_tok_s"] is not None:
         s["prefill_tok_s"] = round(r["prefill_tok_s"], 1)
@@ -477,6 +497,7 @@ def main():
                    else "decode + greedy of every sequence per step"},
         "prefill_tok_s": None if r["prefill_tok_s"] is None else round(r["prefill_tok_s"], 1),
         "decode_tok_s": round(r["decode_tok_s"], 2),
+        "decode_step_by_step": r.get("decode_step_by_step"),
         "e2e": r["e2e"],
         "roofline": roofline_of(w, r),
         "roofline_prefill": roofline_prefill_of(w, r),
