@@ -462,6 +462,7 @@ struct ubd_context : public Executor {
     bool logits_host_valid = false;
     int32_t *argmax_host = nullptr;         // pinned, coherent: the argmax kernel writes the picks here
     bool chain_tok = false;                 // this ubatch's one token id is already in the device table
+    std::vector<int32_t> scan_sufmin;       // run_ubatch's per-stream suffix minima of cell positions
     ArgmaxWork argmax_work;
     std::vector<int32_t> last_ub_idx;
     float *dump = nullptr;
@@ -899,6 +900,10 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
     int max_scan = 0;
     const int qt = mfma_attn ? std::max(1, 16 / G) : std::max(1, attn_tile_rows(hd) / G);
     int n_tiles = 0;
+    // per stream, the smallest position in cells [c, n_kv): no cell past the
+    // last c whose suffix holds a position <= P is visible to a token at P
+    int sufmin_st = -1;
+    std::vector<int32_t> &sufmin = scan_sufmin;
     for (int t = 0; t < T;) {
         int e = t + 1;
         while (e < T && e - t < qt && ub.stream[e] == ub.stream[t]) ++e;
@@ -910,7 +915,20 @@ int32_t ubd_context::run_ubatch(const UBatch &ub, int32_t k) {
         if (mfma_attn && !split && tl[3] <= 8192) {
             // scan only up to the last cell some token of the tile can see
             const int st = ub.stream[t];
-            int c = tl[3] - 1;
+            const int nkv = tl[3];
+            if (sufmin_st != st) {
+                sufmin.assign((size_t)nkv + 1, INT32_MAX);
+                for (int c = nkv - 1; c >= 0; --c) {
+                    const int32_t p = planner.cells.pos_at(st, c);
+                    sufmin[c] = std::min(p < 0 ? INT32_MAX : p, sufmin[c + 1]);
+                }
+                sufmin_st = st;
+            }
+            int32_t pmax = ub.pos[t];
+            for (int j = t + 1; j < e; ++j) pmax = std::max(pmax, ub.pos[j]);
+            // the exact scan starts at the last cell whose position is <= pmax
+            // (the first c with sufmin[c] > pmax, less one: sufmin rises with c)
+            int c = (int)(std::upper_bound(sufmin.begin(), sufmin.begin() + nkv, pmax) - sufmin.begin()) - 1;
             for (; c >= 0; --c) {
                 const int cpp = planner.cells.pos_at(st, c);
                 bool vis = false;
