@@ -531,7 +531,9 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * QKV, gate|up and logits products, -1 = into QKV only, 0 = never),
  * "attn_chunk_min" (smallest cells per wave of split attention, default
  * 64, at least 32), "attn_pair" (prefill attention: 1 = two waves per
- * tile, each scanning half its cells, 0 = one wave), "ldsx"
+ * tile, each scanning half its cells, 0 = one wave), "attn_nt_mb"
+ * (split attention that streams at least this many MB of K/V per launch
+ * loads it non-temporally; default 32, -1 = never), "ldsx"
  * (0 = few-token products read activations from global memory),
  * "ldsx_early" (one-token products: 1 = activation loads issued before the
  * weight loads, 0 = after; the results are identical), "gemm_wpd"

@@ -40,6 +40,8 @@ struct Tuning {
                               // logits products, -1 = into QKV only, 0 = never
     int attn_chunk_min = 64;  // smallest cells per wave of split attention (>= 32)
     int attn_pair = 1;        // unsplit (prefill) MFMA attention: 1 = two waves per tile, each scanning half
+    int attn_nt_mb = 32;      // split attention streaming >= this many MB of K/V per launch loads it
+                              // non-temporally (-1 = never)
     int ldsx = 1;             // stage few-token activations in LDS (decode products)
     int ldsx_early = 1;       // one-token LDS-staged products: activation loads ahead of the weights
     int small_rb = 1;         // several-token products: 4 row blocks per work-group / split k (0 = off)
@@ -200,6 +202,7 @@ struct AttnArgs {
     int chunk_cells = 32;             // MFMA split: cells per wave (multiple of 32)
     int n_chunks_launch = 0;          // MFMA split: chunks launched per tile
     int waves = 1;                    // MFMA, not split: waves per (tile, KV head), 1 or 2
+    bool kv_nt = false;               // MFMA split: K/V codes loaded non-temporally
 };
 constexpr int ATTN_CHUNK = 256;       // cells per split-K chunk (f32 path)
 constexpr int ATTN_DECODE_CHUNK = 32; // smallest cells-per-wave chunk of the split MFMA path

@@ -2633,7 +2633,17 @@ template <int HD> struct KVStep {
     int4 p[2], s[2];
 };
 
-template <int HD>
+// NT: the K/V codes are loaded non-temporally (streams read once per step:
+// long split scans), else through the caches (prefill tiles re-read them).
+template <typename T, bool NT>
+__device__ __forceinline__ T kv_ld(const T *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <int HD, bool NT>
 __device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src, int c0) {
     constexpr int KK = HD / 32, DB = HD / 16;
 #pragma unroll
@@ -2641,7 +2651,7 @@ __device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src
         const int cb = c0 + 16 * b2;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            b.k[b2][kk] = *(const f16x8_t *)(src.K + (size_t)(cb + src.r) * HD + 32 * kk + 8 * src.g);
+            b.k[b2][kk] = kv_ld<f16x8_t, NT>((const f16x8_t *)(src.K + (size_t)(cb + src.r) * HD + 32 * kk + 8 * src.g));
         b.p[b2] = *(const int4 *)(src.cpos + cb + 4 * src.g);
         b.s[b2] = *(const int4 *)(src.cseq + cb + 4 * src.g);
     }
@@ -2649,7 +2659,7 @@ __device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src
     // and this lane's B fragment of dims 16 db + r is slots 8g .. 8g+7
     const _Float16 *vt = src.Vt + (size_t)(c0 >> 5) * HD * 32 + src.r * 32 + 8 * src.g;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) b.v[db] = *(const f16x8_t *)(vt + db * 16 * 32);
+    for (int db = 0; db < DB; ++db) b.v[db] = kv_ld<f16x8_t, NT>((const f16x8_t *)(vt + db * 16 * 32));
 }
 
 // The MFMA attention works in base 2: the query carries log2(e) / sqrt(hd),
@@ -2742,7 +2752,7 @@ template <int HD> struct KVStepQ8 {
     int4 p[2], s[2];
 };
 
-template <int HD>
+template <int HD, bool NT>
 __device__ __forceinline__ void kv_step_load_q8(KVStepQ8<HD> &b, const KVSrcQ8<HD> &src, int c0) {
     constexpr int KK = HD / 32, DB = HD / 16;
 #pragma unroll
@@ -2750,7 +2760,7 @@ __device__ __forceinline__ void kv_step_load_q8(KVStepQ8<HD> &b, const KVSrcQ8<H
         const int cb = c0 + 16 * b2;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            b.k[b2][kk] = *(const u32x2_t *)(src.K + (size_t)(cb + src.r) * HD + 32 * kk + 8 * src.g);
+            b.k[b2][kk] = kv_ld<u32x2_t, NT>((const u32x2_t *)(src.K + (size_t)(cb + src.r) * HD + 32 * kk + 8 * src.g));
             b.ksc[b2][kk] = *(const u32x2_t *)(src.ks + (size_t)kk * src.n_cells + cb + 4 * src.g);
         }
         b.p[b2] = *(const int4 *)(src.cpos + cb + 4 * src.g);
@@ -2758,7 +2768,7 @@ __device__ __forceinline__ void kv_step_load_q8(KVStepQ8<HD> &b, const KVSrcQ8<H
     }
     const int8_t *vt = src.Vt + (size_t)(c0 >> 5) * HD * 32 + src.r * 32 + 8 * src.g;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) b.v[db] = *(const u32x2_t *)(vt + db * 16 * 32);
+    for (int db = 0; db < DB; ++db) b.v[db] = kv_ld<u32x2_t, NT>((const u32x2_t *)(vt + db * 16 * 32));
 #pragma unroll
     for (int kb = 0; kb < KK; ++kb) {
         b.vsc[kb][0] = *(const u32x2_t *)(src.vs + (size_t)kb * src.n_cells + c0 + 4 * src.g);
@@ -2854,7 +2864,8 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
 // (For decode steps with short scans, four waves merged this way measured
 // slower than the split pass and its combine kernel: each wave's steps wait
 // on their loads one after another.)
-template <int HD, bool SPLIT, bool KQ, int NW = 1>
+// NT: K/V codes loaded non-temporally (long split scans).
+template <int HD, bool SPLIT, bool KQ, int NW = 1, bool NT = false>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
     static_assert(!(SPLIT && NW > 1), "the multi-wave mode merges in the work-group");
     constexpr int KK = HD / 32, DB = HD / 16;
@@ -2939,14 +2950,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
         const _Float16 *Vt = (const _Float16 *)a.v_cache + hbase * a.n_cells * HD;
         const KVSrc<HD> src{K, Vt, cpos, cseq, a.n_cells, r, g};
         KVStep<HD> A, B;
-        if (cbeg < cend) kv_step_load(A, src, cbeg);
+        if (cbeg < cend) kv_step_load<HD, NT>(A, src, cbeg);
         for (int c0 = cbeg; c0 < cend; c0 += 64) {
             const int c1 = c0 + 32, c2 = c0 + 64;
-            kv_step_load(B, src, c1 < cend ? c1 : c0);
+            kv_step_load<HD, NT>(B, src, c1 < cend ? c1 : c0);
             __builtin_amdgcn_sched_barrier(0);
             kv_step_compute(A, c0, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
-            kv_step_load(A, src, c2 < cend ? c2 : c0);
+            kv_step_load<HD, NT>(A, src, c2 < cend ? c2 : c0);
             __builtin_amdgcn_sched_barrier(0);
             kv_step_compute(B, c1, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
@@ -2969,14 +2980,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
         const uint16_t *vs = (const uint16_t *)((const int8_t *)a.v_cache + a.layer_elems) + hbase * KK * a.n_cells;
         const KVSrcQ8<HD> src{K, Vt, ks, vs, cpos, cseq, a.n_cells, r, g};
         KVStepQ8<HD> A, B;
-        if (cbeg < cend) kv_step_load_q8(A, src, cbeg);
+        if (cbeg < cend) kv_step_load_q8<HD, NT>(A, src, cbeg);
         for (int c0 = cbeg; c0 < cend; c0 += 64) {
             const int c1 = c0 + 32, c2 = c0 + 64;
-            kv_step_load_q8(B, src, c1 < cend ? c1 : c0);
+            kv_step_load_q8<HD, NT>(B, src, c1 < cend ? c1 : c0);
             __builtin_amdgcn_sched_barrier(0);
             kv_step_compute_q8(A, c0, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
-            kv_step_load_q8(A, src, c2 < cend ? c2 : c0);
+            kv_step_load_q8<HD, NT>(A, src, c2 < cend ? c2 : c0);
             __builtin_amdgcn_sched_barrier(0);
             kv_step_compute_q8(B, c1, cend, qh, ql, row_ok, rbit, rpos, g, m, l, O);
             __builtin_amdgcn_sched_barrier(0);
@@ -3118,8 +3129,12 @@ static void launch_attention_mfma_hd(const AttnArgs &a, hipStream_t s) {
     const bool q8 = a.type_k == KV_Q8;
     if (a.split) {
         dim3 grid((unsigned)a.n_chunks_launch, a.n_tiles, a.n_head_kv);
-        if (q8)
+        if (q8 && a.kv_nt)
+            UBD_LAUNCH((attn_mfma_kernel<HD, true, true, 1, true>), grid, dim3(64), 0, s, a);
+        else if (q8)
             UBD_LAUNCH((attn_mfma_kernel<HD, true, true>), grid, dim3(64), 0, s, a);
+        else if (a.kv_nt)
+            UBD_LAUNCH((attn_mfma_kernel<HD, true, false, 1, true>), grid, dim3(64), 0, s, a);
         else
             UBD_LAUNCH((attn_mfma_kernel<HD, true, false>), grid, dim3(64), 0, s, a);
         UBD_LAUNCH((attn_merge_kernel<HD>), dim3(a.T * a.n_head), dim3(64), 0, s, a);

@@ -1129,6 +1129,13 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         if (mfma_attn) {
             aa.split = split;
             aa.waves = g_tuning.attn_pair ? 2 : 1;
+            // split scans that stream at least attn_nt_mb MB of K/V per launch
+            // (read once, far past any cache) load it non-temporally: at 16 x
+            // 32 K cells 316 against 371 us per layer; short scans and the
+            // prefill tiles, which re-read K/V, keep the cached loads
+            const double kv_mb = (double)n_tiles * Hk * key.chunk_cells * key.n_chunks * hd * 2 *
+                                 (type_k == KV_Q8 ? 1.0625 : 2.0) / 1048576.0;
+            aa.kv_nt = split && g_tuning.attn_nt_mb >= 0 && kv_mb >= g_tuning.attn_nt_mb;
             aa.max_chunks = max_chunks_mfma;
             aa.chunk_cells = key.chunk_cells;
             aa.n_chunks_launch = key.n_chunks;
@@ -1705,6 +1712,8 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.attn_chunk_min = value;
     } else if (k == "attn_pair") {
         g_tuning.attn_pair = value;
+    } else if (k == "attn_nt_mb") {
+        g_tuning.attn_nt_mb = value;
     } else if (k == "gemm_wpd") {
         g_tuning.gemm_wpd = value;
     } else if (k == "gemm_deep") {
