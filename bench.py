@@ -49,7 +49,7 @@ TRACE_FILES = {
                                       ("gemm_wide_kernel<2, 1, 2, 4, 4>",)),
     # split pass + combine pass, as the events span both
     ("decode.attention", "bf16"): (os.path.join(ROOT, "profiles", "decode_8b_16seq_32k_kernel_stats.md"),
-                                   ("attn_mfma_kernel<128, true, false, 1>", "attn_merge_kernel<128>")),
+                                   ("attn_mfma_kernel<128, true, false, 1, true>", "attn_merge_kernel<128>")),
     ("decode.ffn_gate_up", "q8_0"): (os.path.join(ROOT, "profiles", "decode_prefill_8b_q8_0_kernel_stats.md"),
                                      ("linear_ldsx_kernel<3, 2, 4, true>",)),
 }
@@ -297,7 +297,8 @@ def roofline_of(w, r):
         # cache grows by one cell per sequence per step
         cells = w.n_seqs * (w.kv_prefill + (w.n_decode + 1) / 2.0)
         alg = 2 * cells * shape.n_embd_kv * kv_bytes_per_elem(w.type_k) + 2 * w.n_seqs * d * 4
-        kernel = "decode.attention (attn_mfma_kernel split over cells + attn_merge_kernel), per layer-step"
+        kernel = ("decode.attention (attn_mfma_kernel split over cells, K/V loaded non-temporally, + attn_merge_kernel), "
+                  "per layer-step")
         traffic = measured_traffic(hot) if w.type_k == "f16" else None
     else:
         T = w.n_seqs
