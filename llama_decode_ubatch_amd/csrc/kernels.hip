@@ -107,6 +107,17 @@ __device__ __forceinline__ T ldg_nt(const T *p) {
     return __builtin_nontemporal_load(p);
 }
 
+// A 16-byte weight-tile load (non-temporal) at byte offset off of the weight
+// matrix, through a buffer resource: one 32-bit lane offset against a scalar
+// base, where a pointer per lane costs 64-bit address arithmetic per load
+// (one-token O 8.4 -> 7.9 us, QKV 12.6 -> 12.4 us).  Matrices stay below
+// 2 GiB (checked at model load), so off fits the 32-bit offset.
+__device__ __forceinline__ u32x4_t ldw(const void *w, size_t off) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(w), 0, 0x7fffffff, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+
 // --------------------------------------------------------------- matvec
 // "Skinny" product y[t][n] = sum_k W[n][k] x[t][k] for up to 16 tokens per
 // block of grid.y, on the matrix cores: A = a 16-row weight tile straight
@@ -172,7 +183,7 @@ __device__ __forceinline__ void load_step(const LinearArgs &a, const unsigned ch
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
         const size_t tile = (size_t)s * (a.N / 16) + rb0 + j;      // k-step-major tiles
-        in.w[j] = ldg_nt((const u32x4_t *)((const char *)a.w + tile * 1024 + lane * 16));
+        in.w[j] = ldw(a.w, tile * 1024 + lane * 16);
     }
     const u32x4_t z = {0u, 0u, 0u, 0u};
     const size_t plane = (size_t)a.T * a.K;
@@ -215,7 +226,7 @@ __device__ __forceinline__ void load_step_xn(const LinearArgs &a, int rb0, int s
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
         const size_t tile = (size_t)s * (a.N / 16) + rb0 + j;
-        in.w[j] = ldg_nt((const u32x4_t *)((const char *)a.w + tile * 1024 + lane * 16));
+        in.w[j] = ldw(a.w, tile * 1024 + lane * 16);
     }
     const float *xr = a.norm.x + (size_t)(a.norm.rows ? a.norm.rows[tok] : tok) * a.norm.ld;
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -513,8 +524,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
             for (int j = 0; j < RB; ++j)
                 if (s0 + u < s1)
-                    w0[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
-                                                       ((size_t)(s0 + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
+                    w0[u][j] = ldw(a.w, ((size_t)(s0 + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16);
         norm_prologue<WT, NW>(a, dyn_lds);
     }
 
@@ -650,8 +660,7 @@ __device__ __forceinline__ void load_wbatch(const LinearArgs &a, int rb0, int s,
         if (s + u >= s1) break;
 #pragma unroll
         for (int j = 0; j < RB; ++j)
-            b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
-                                                ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
+            b.w[u][j] = ldw(a.w, ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16);
     }
     if constexpr (WT == W_Q8) load_wbatch_scales<RB, UB>(a, rb0, s, s1, lane, b.sc);
 }
@@ -665,8 +674,7 @@ __device__ __forceinline__ void load_wbatch_whole(const LinearArgs &a, int rb0, 
     for (int u = 0; u < UB; ++u)
 #pragma unroll
         for (int j = 0; j < RB; ++j)
-            b.w[u][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
-                                                ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16));
+            b.w[u][j] = ldw(a.w, ((size_t)(s + u) * (a.N / 16) + rb0 + j) * 1024 + lane * 16);
     if constexpr (WT == W_Q8) load_wbatch_scales<RB, UB>(a, rb0, s, s + UB, lane, b.sc);
 }
 
@@ -1177,11 +1185,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int n_wtiles, i
                 if (!Q8) {
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        wr[i][j] = ldg_nt((const u32x4_t *)((const char *)a.w +
-                                                           ((size_t)(2 * st + j) * nrb + rb) * 1024 + lane * 16));
+                        wr[i][j] = ldw(a.w, ((size_t)(2 * st + j) * nrb + rb) * 1024 + lane * 16);
                 } else {
-                    wr[i][0] = ldg_nt((const u32x4_t *)((const char *)a.w + ((size_t)st * nrb + rb) * 1024 +
-                                                       lane * 16));
+                    wr[i][0] = ldw(a.w, ((size_t)st * nrb + rb) * 1024 + lane * 16);
                     const u32x4_t sv = *(const u32x4_t *)(a.wscale + q8_scale_ofs(a.K, rb, st, g));
                     sc[i][0] = u32x2_t{sv[0], sv[1]};
                     sc[i][1] = u32x2_t{sv[2], sv[3]};
