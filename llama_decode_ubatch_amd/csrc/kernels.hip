@@ -2623,11 +2623,13 @@ void launch_attention(const AttnArgs &a, hipStream_t s) {
 // range's (m, l, O) for a combine pass, otherwise O / l is stored.
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
+// Buffer resources over this (stream, KV head)'s K rows, V^T tiles, the
+// stream's cell positions and sequence words, and this lane's byte offsets
+// into them, fixed across steps: a step adds only a scalar offset, so its
+// loads need no per-lane address arithmetic.
 template <int HD> struct KVSrc {
-    const _Float16 *K, *Vt;
-    const int32_t *cpos;
-    const uint32_t *cseq;       // the sequence-mask word of this lane's row
-    int n_cells, r, g;
+    __amdgpu_buffer_rsrc_t k, v, pos, seq;
+    int ko, vo, po, so;         // so: this lane's row's sequence-mask word
 };
 
 // One 32-cell step of K (two 16-cell MFMA A blocks), V^T (the P*V B
@@ -2652,20 +2654,24 @@ __device__ __forceinline__ T kv_ld(const T *p) {
 template <int HD, bool NT>
 __device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src, int c0) {
     constexpr int KK = HD / 32, DB = HD / 16;
+    constexpr int aux = NT ? 2 : 0;     // non-temporal
+    const int cu = __builtin_amdgcn_readfirstlane(c0);
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
-        const int cb = c0 + 16 * b2;
+        const int cb = cu + 16 * b2;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            b.k[b2][kk] = kv_ld<f16x8_t, NT>((const f16x8_t *)(src.K + (size_t)(cb + src.r) * HD + 32 * kk + 8 * src.g));
-        b.p[b2] = *(const int4 *)(src.cpos + cb + 4 * src.g);
-        b.s[b2] = *(const int4 *)(src.cseq + cb + 4 * src.g);
+            b.k[b2][kk] = __builtin_bit_cast(
+                f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(src.k, src.ko + 64 * kk, cb * HD * 2, aux));
+        b.p[b2] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(src.pos, src.po, cb * 4, 0));
+        b.s[b2] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(src.seq, src.so, cb * 4, 0));
     }
     // c0 is a multiple of 32: the step's V is the contiguous tile c0 / 32,
     // and this lane's B fragment of dims 16 db + r is slots 8g .. 8g+7
-    const _Float16 *vt = src.Vt + (size_t)(c0 >> 5) * HD * 32 + src.r * 32 + 8 * src.g;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) b.v[db] = kv_ld<f16x8_t, NT>((const f16x8_t *)(vt + db * 16 * 32));
+    for (int db = 0; db < DB; ++db)
+        b.v[db] = __builtin_bit_cast(f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  src.v, src.vo + db * 16 * 32 * 2, (cu >> 5) * HD * 32 * 2, aux));
 }
 
 // The MFMA attention works in base 2: the query carries log2(e) / sqrt(hd),
@@ -2954,7 +2960,16 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
         }
         const _Float16 *K = (const _Float16 *)a.k_cache + hbase * a.n_cells * HD;
         const _Float16 *Vt = (const _Float16 *)a.v_cache + hbase * a.n_cells * HD;
-        const KVSrc<HD> src{K, Vt, cpos, cseq, a.n_cells, r, g};
+        const size_t kvb = (size_t)a.n_cells * HD * 2;
+        const KVSrc<HD> src{make_rsrc(K, kvb),
+                            make_rsrc(Vt, kvb),
+                            make_rsrc(cpos, (size_t)a.n_cells * 4),
+                            make_rsrc(a.cell_seq + (size_t)st * a.n_seq_words * a.n_cells,
+                                      (size_t)a.n_seq_words * a.n_cells * 4),
+                            (r * HD + 8 * g) * 2,
+                            (r * 32 + 8 * g) * 2,
+                            16 * g,
+                            ((rseq >> 5) * a.n_cells + 4 * g) * 4};
         KVStep<HD> A, B;
         if (cbeg < cend) kv_step_load<HD, NT>(A, src, cbeg);
         for (int c0 = cbeg; c0 < cend; c0 += 64) {
