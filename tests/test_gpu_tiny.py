@@ -157,6 +157,37 @@ def test_long_scan_many_chunks(tiny):
     assert ctx.greedy(0) == int(np.argmax(ref.logits[0]))
 
 
+@pytest.mark.parametrize("kv", ["f16", "q8_0"])
+def test_non_temporal_kv_loads_give_the_same_logits(tiny, kv):
+    """Split attention streams K/V with non-temporal loads only when a launch
+    reads at least attn_nt_mb MB; forcing that path (0) on ragged sequences
+    reads the same values, so the logits equal the cached-load run bit for
+    bit, and both are within the oracle's tolerance."""
+    from llama_decode_ubatch_amd.binding import set_tuning
+    rng = np.random.default_rng(13)
+    V = WORKLOADS[1].model.n_vocab
+    lens = [40, 333, 700]
+    toks = [rng.integers(0, V, n) for n in lens]
+    nxt = rng.integers(0, V, 3)
+    out = []
+    for nt in (32, 0):
+        set_tuning("attn_nt_mb", nt)
+        try:
+            ctx, ref = make(tiny, n_ctx=3072, n_batch=1024, n_ubatch=1024, n_seq_max=3, type_k=kv, type_v=kv)
+            for s, t in enumerate(toks):
+                assert ctx.decode(t, seq_id=np.full(t.size, s)) == 0
+            assert ctx.decode(nxt, seq_id=[0, 1, 2], logits=[1, 1, 1]) == 0
+            out.append(ctx.logits())
+        finally:
+            set_tuning("attn_nt_mb", 32)
+    print(f"{kv}: max |dz| between the load paths {float(np.abs(out[0] - out[1]).max()):.1e}", flush=True)
+    assert np.array_equal(out[0], out[1])
+    for s, t in enumerate(toks):
+        assert ref.decode(Batch(t, seq_id=np.full(t.size, s))) == 0
+    assert ref.decode(Batch(nxt, seq_id=[0, 1, 2], logits=[1, 1, 1])) == 0
+    assert rel_err(out[1], ref.logits) < (TOL if kv == "f16" else 2e-3)
+
+
 def test_return_codes_abort_and_rollback(tiny):
     from llama_decode_ubatch_amd import Context
     shape, tens, model, om = tiny
