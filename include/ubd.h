@@ -352,12 +352,12 @@ int32_t ubd_sample_greedy_all(ubd_context *ctx, ubd_token *out, int32_t cap);
  * ubd_sample_greedy).  Each pick is written by the GPU straight into the
  * next step's token table, so the host plans and enqueues step i+1 while
  * step i runs; results equal ubd_decode + ubd_sample_greedy step by step.
- * The picks come back every UBD_GREEDY_CHAIN_ROUND steps (one
+ * The picks come back every UBD_GREEDY_CHAIN_BLOCK steps (one
  * synchronisation each).  out: host int32 [n_steps].
  * Returns the number of steps done (n_steps, or fewer when a step fails:
  * the error is then in ubd_last_error and the steps before it are kept), or
  * UBD_INVALID / a decode error code when no step was done. */
-#define UBD_GREEDY_CHAIN_ROUND 256
+#define UBD_GREEDY_CHAIN_BLOCK 256
 int32_t ubd_greedy_chain(ubd_context *ctx, ubd_token first, ubd_seq_id seq_id, int32_t n_steps, ubd_token *out);
 
 /* The greedy pick of ubd_sample_greedy_all over caller-owned rows, for

@@ -727,7 +727,7 @@ extern "C" ubd_context *ubd_init_from_model(ubd_model *model, const ubd_context_
             return bail("pinned staging allocation failed");
     }
     if (!hip_ok(hipHostMalloc((void **)&c->argmax_host,
-                              (size_t)std::max<uint32_t>(P.n_batch, UBD_GREEDY_CHAIN_ROUND) * 4,
+                              (size_t)std::max<uint32_t>(P.n_batch, UBD_GREEDY_CHAIN_BLOCK) * 4,
                               hipHostMallocCoherent), "pinned"))
         return bail("pinned argmax buffer allocation failed");
     if (!hip_ok(hipStreamSynchronize(c->stream), "init sync")) return bail("sync failed");
@@ -1314,8 +1314,8 @@ extern "C" int32_t ubd_greedy_chain(ubd_context *ctx, ubd_token first, ubd_seq_i
     if (!hip_ok(hipSetDevice(ctx->model->device), "hipSetDevice")) return UBD_ALLOC_FAILED;
     int32_t done = 0, rc = UBD_OK;
     while (done < n_steps && rc == UBD_OK) {
-        // one round of picks held in pinned memory, then copied out
-        const int n = std::min<int32_t>(n_steps - done, UBD_GREEDY_CHAIN_ROUND);
+        // one block of picks held in pinned memory, then copied out
+        const int n = std::min<int32_t>(n_steps - done, UBD_GREEDY_CHAIN_BLOCK);
         int k = 0;
         for (; k < n; ++k) {
             const double t0 = now_ms();

@@ -14,7 +14,7 @@ section: the new token's K and V are appended first, then Q attends to every
 cached key of its (first) sequence, its own included.
 
 Precision: the arrays are float64 for the tiny model and float32 for the
-8B shape (the pages' graph computes every node in f32; see DESIGN.md).
+8B shape (the pages' graph computes every node in f32).
 Stored K/V are rounded to type_k / type_v.
 """
 from typing import Callable, Dict, Mapping, Optional, Union

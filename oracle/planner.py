@@ -22,7 +22,7 @@ Pages:
   * engine page, Step 10: a token may belong to several sequences
     (n_seq_id > 1); positions are counted per sequence.
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
   * positions given by the caller must be consecutive per sequence in
     batch order and continue from seq_pos_max(s)+1 when the sequence
     already holds cells (an empty sequence may start at any p >= 0),

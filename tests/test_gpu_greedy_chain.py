@@ -1,7 +1,7 @@
 """Chained greedy generation (ubd_greedy_chain) through the C ABI on the
 tiny f32 model: the picks equal the oracle's free-running greedy ids and
 the step-by-step decode + greedy path's, with the same KV cells and the
-same last logits; a chain longer than one round of picks; a chain that
+same last logits; a chain longer than one block of picks; a chain that
 runs out of KV cells part-way; an invalid first token."""
 import numpy as np
 import pytest
@@ -10,7 +10,7 @@ from oracle import OracleModel, OracleContext, Batch
 from workloads import WORKLOADS, gen_tensor, tensor_specs, prompt_tokens
 
 pytestmark = pytest.mark.gpu
-ROUND = 256         # UBD_GREEDY_CHAIN_ROUND
+BLOCK = 256         # UBD_GREEDY_CHAIN_BLOCK
 
 
 @pytest.fixture(scope="module")
@@ -73,11 +73,11 @@ def test_chain_equals_oracle_and_step_by_step(tiny, kv):
     assert a.greedy(-1) == b.greedy(-1)
 
 
-def test_chain_longer_than_one_round(tiny):
+def test_chain_longer_than_one_block(tiny):
     shape, model, om = tiny
     kw = dict(n_ctx=512, n_batch=512, n_ubatch=512, n_seq_max=1, type_k="f16", type_v="f16")
     prompt = prompt_tokens(WORKLOADS[1], 1)
-    n = ROUND + 44
+    n = BLOCK + 44
     print(f"chain of {n} steps", flush=True)
     a, b = prefilled(model, prompt, **kw), prefilled(model, prompt, **kw)
     first = a.greedy(-1)
@@ -95,7 +95,7 @@ def test_chain_stops_when_the_cache_is_full(tiny):
     a, b = prefilled(model, prompt, **kw), prefilled(model, prompt, **kw)
     room = a.n_ctx - prompt.size
     print(f"n_ctx {a.n_ctx}: room for {room} steps", flush=True)
-    assert 0 < room < ROUND
+    assert 0 < room < BLOCK
     first = a.greedy(-1)
     ids = a.greedy_chain(first, room + 5)
     assert ids.size == room
