@@ -2619,8 +2619,11 @@ void launch_attention(const AttnArgs &a, hipStream_t s) {
 // rows' q as f16 hi + lo), so lane (row r, group g) holds S[r][cells 4g+i]
 // of each 16-cell block.  Two blocks give exactly the P fragment of P*V for
 // the cell order {4g..4g+3, 16+4g..16+4g+3}, which the V tile supplies as
-// one contiguous 16-byte run per lane.  Online softmax per row; SPLIT writes the
-// range's (m, l, O) for a combine pass, otherwise O / l is stored.
+// one contiguous 16-byte run per lane.  The product is taken as
+// O^T = V^T P^T, so lane (row r, group g) also holds O[r][dims 4g+i] of
+// each 16-dim block: a row's softmax state (m, l), its rescale factor and
+// its outputs all stay in the row's lanes.  Online softmax per row; SPLIT
+// writes the range's (m, l, O) for a combine pass, otherwise O / l is stored.
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 // Buffer resources over this (stream, KV head)'s K rows, V^T tiles, the
@@ -2679,6 +2682,24 @@ __device__ __forceinline__ void kv_step_load(KVStep<HD> &b, const KVSrc<HD> &src
 // exponential is one native 2^x (exp(s - m) = 2^(log2e s - log2e m)).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum over the four 16-lane rows holding one query row's values
+// (lanes r, r + 16, r + 32, r + 48): the row pairs swap through the gfx950
+// permlane swaps (vector ALU, no LDS round trip).  Each returns a lane's
+// value and its partner's, 16 then 32 lanes apart; max and + commute, so
+// every lane of a row gets the same result.
+__device__ __forceinline__ float row_max(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Scores of the step's 32 cells for the wave's 16 rows, mask, online-softmax
 // update of (m, l) and O += P V.
 template <int HD>
@@ -2706,10 +2727,8 @@ __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int
         }
         S[b2] = acc;
     }
-    float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mx = row_max(fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                                   fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3]))));
     const float m_new = fmaxf(m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m - m_new);
     float ps = 0.f;
@@ -2725,19 +2744,15 @@ __device__ __forceinline__ void kv_step_compute(const KVStep<HD> &b, int c0, int
             ph[4 * b2 + i] = h;
             pl[4 * b2 + i] = (_Float16)(p - (float)h);
         }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l = l * alpha + ps;
+    l = l * alpha + row_sum(ps);
     m = m_new;
-    // O rows are 4g+i in this lane: fetch their rescale factors
-    f32x4_t al;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+    // V^T fragments as A and P^T as B: the output holds this lane's row r
+    // (dims 16 db + 4g + i), whose rescale factor the lane already has
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        f32x4_t o = O[db] * al;
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, b.v[db], o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, b.v[db], o, 0, 0, 0);
+        f32x4_t o = O[db] * alpha;
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.v[db], ph, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(b.v[db], pl, o, 0, 0, 0);
         O[db] = o;
     }
 }
@@ -2821,10 +2836,8 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
         }
         S[b2] = acc;
     }
-    float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mx = row_max(fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                                   fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3]))));
     const float m_new = fmaxf(m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m - m_new);
     float pv[8];
@@ -2838,13 +2851,8 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
             ps += p;
             pv[4 * b2 + i] = p;
         }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l = l * alpha + ps;
+    l = l * alpha + row_sum(ps);
     m = m_new;
-    f32x4_t al;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
     for (int kb = 0; kb < KK; ++kb) {
         // P of this lane's 8 cells times their V scales of dim block kb
@@ -2859,10 +2867,10 @@ __device__ __forceinline__ void kv_step_compute_q8(const KVStepQ8<HD> &b, int c0
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int db = 2 * kb + h2;
-            const bf16x8_t B = i8x8_to_bf16(b.v[db][0], b.v[db][1]);
-            f32x4_t o = O[db] * al;
-            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ph, B, o, 0, 0, 0);
-            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pl, B, o, 0, 0, 0);
+            const bf16x8_t Vf = i8x8_to_bf16(b.v[db][0], b.v[db][1]);
+            f32x4_t o = O[db] * alpha;
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Ph, o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vf, Pl, o, 0, 0, 0);
             O[db] = o;
         }
     }
@@ -3014,10 +3022,12 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // O: lane (row r, group g) holds dims 16 db + 4g + i of its row, and
+    // the row's (m, l)
     if constexpr (NW > 1) {
         // every wave publishes its (m, l) per row and its O; each lane then
-        // weights the NW partials of its four rows 4g+i by exp2(m_w - M) and
-        // finishes its wave's dim blocks
+        // weights the NW partials of its row by exp2(m_w - M) and finishes
+        // its wave's dim blocks
         __shared__ float pm[NW][16], pl[NW][16];
         __shared__ f32x4_t po[NW][DB][64];
         if (g == 0) {
@@ -3027,67 +3037,45 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) po[wv][db][lane] = O[db];
         __syncthreads();
-        f32x4_t wgt[NW];
-        float L[4];
+        float wgt[NW];
+        float M = -INFINITY, L = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float M = -INFINITY;
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, pm[w][r]);
 #pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, pm[w][4 * g + i]);
-            L[i] = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float mw = pm[w][4 * g + i];
-                wgt[w][i] = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
-                L[i] += wgt[w][i] * pl[w][4 * g + i];
-            }
+        for (int w = 0; w < NW; ++w) {
+            const float mw = pm[w][r];
+            wgt[w] = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
+            L += wgt[w] * pl[w][r];
         }
+        if (!row_ok) return;
 #pragma unroll
         for (int db = wv; db < DB; db += NW) {
             f32x4_t o = po[0][db][lane] * wgt[0];
 #pragma unroll
             for (int w = 1; w < NW; ++w) o += po[w][db][lane] * wgt[w];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * g + i;
-                if (row >= R) continue;
-                const int t = t0 + row / G, h = grp * G + row % G;
-                store_act(a.out, act_idx(a.out, t, h * HD + 16 * db + r), L[i] > 0.f ? o[i] / L[i] : 0.f);
-            }
+            for (int i = 0; i < 4; ++i)
+                store_act(a.out, act_idx(a.out, rt, rh * HD + 16 * db + 4 * g + i), L > 0.f ? o[i] / L : 0.f);
         }
         return;
     }
-    // O: lane (dim r of each 16-dim block, group g) holds rows 4g+i
+    if (!row_ok) return;
     if (!SPLIT) {
-        f32x4_t lrow;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l, 4 * g + i, 64);
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * g + i;
-            if (row >= R) continue;
-            const int t = t0 + row / G, h = grp * G + row % G;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                store_act(a.out, act_idx(a.out, t, h * HD + 16 * db + r), lrow[i] > 0.f ? O[db][i] / lrow[i] : 0.f);
-        }
+            for (int i = 0; i < 4; ++i)
+                store_act(a.out, act_idx(a.out, rt, rh * HD + 16 * db + 4 * g + i), l > 0.f ? O[db][i] / l : 0.f);
         return;
     }
     // split: publish this chunk's (m, l, O) for the combine pass
-    if (g == 0 && row_ok) {
-        float *ml = a.part_ml + (((size_t)rt * a.n_head + rh) * a.max_chunks + chunk) * 2;
-        ml[0] = m;
-        ml[1] = l;
+    const size_t pidx = ((size_t)rt * a.n_head + rh) * a.max_chunks + chunk;
+    if (g == 0) {
+        a.part_ml[pidx * 2] = m;
+        a.part_ml[pidx * 2 + 1] = l;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * g + i;
-        if (row >= R) continue;
-        const int t = t0 + row / G, h = grp * G + row % G;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            a.part_o[(((size_t)t * a.n_head + h) * a.max_chunks + chunk) * HD + 16 * db + r] = O[db][i];
-    }
+    for (int db = 0; db < DB; ++db) *(f32x4_t *)(a.part_o + pidx * HD + 16 * db + 4 * g) = O[db];
 }
 
 // Merge the chunks of one (token, head): weights exp(m_c - M) computed
