@@ -602,54 +602,56 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 // are read from LDS right before use.  k-steps are split over NW waves and
 // reduced through LDS (aliasing the activation copy).
 // q8_0 scales: the batch needs UB * RB groups of 16 words (32 f16 scales of
-// one row block and k-step, in their stored order); lane L holds NWD
-// consecutive words of them (NWD = UB * RB / 4, at least 1: with fewer than
-// 64 words the lanes past them hold none), and each step fetches a lane's
-// 4 words (rows 4g..4g+3 of its two blocks) from the lanes that hold them
-// by cross-lane permutes.  Kept whole in every lane, the scales took as
-// many registers as the codes.
-template <int RB, int UB> constexpr int q8_scale_words() { return UB * RB >= 4 ? UB * RB / 4 : 1; }
-
+// one row block and k-step: lane group g's 4 words are rows 4g..4g+3 of the
+// step's two 32-wide blocks).  They are held one word per lane, each 16-lane
+// row g holding its own group's words: lane 16g + 4c + i holds word i of
+// group g for the batch's pair c = j UB + u (row block j, step u), so a step
+// takes its 4 words by DPP row broadcasts, in the vector ALU (cross-lane
+// permutes through LDS took the same 4 instructions per step, each an LDS
+// round trip).  Kept whole in every lane, the scales took as many registers
+// as the codes.
 template <int WT, int RB, int UB>
 struct WBatch {
-    static constexpr int NWD = WT == W_Q8 ? q8_scale_words<RB, UB>() : 1;
-    static_assert(WT != W_Q8 || ((NWD == 1 || NWD == 2) && UB * RB * 16 <= 64 * NWD), "q8_0: scale words per lane");
+    static_assert(WT != W_Q8 || UB * RB <= 4, "q8_0: one scale word per lane");
     u32x4_t w[UB][RB];
-    uint32_t sc[NWD];
+    uint32_t sc;
 };
 
-// this lane's scale words of the batch at k-step s (words past the wave's
+// this lane's scale word of the batch at k-step s (words past the wave's
 // last step s1 are not loaded: no step reads them)
 template <int RB, int UB>
 __device__ __forceinline__ void load_wbatch_scales(const LinearArgs &a, int rb0, int s, int s1, int lane,
-                                                   uint32_t (&sc)[q8_scale_words<RB, UB>()]) {
-    constexpr int NWD = q8_scale_words<RB, UB>();
-    const int idx = NWD * lane;
-    const int j = idx / (UB * 16), u = (idx / 16) % UB, wd = idx % 16;
-    const bool live = idx < UB * RB * 16 && s + u < s1;
-    const uint16_t *src = a.wscale + q8_scale_ofs(a.K, rb0 + (live ? j : 0), s + (live ? u : 0), 0) + 2 * wd;
-    if (NWD == 2) {
-        u32x2_t v = {0u, 0u};
-        if (live) v = *(const u32x2_t *)src;
-        sc[0] = v[0];
-        sc[NWD - 1] = v[1];
-    } else {
-        sc[0] = live ? *(const uint32_t *)src : 0u;
+                                                   uint32_t &sc) {
+    const int g = lane >> 4, c = (lane >> 2) & 3, i = lane & 3;
+    const int j = c / UB, u = c % UB;
+    const bool live = c < UB * RB && s + u < s1;
+    const uint16_t *src = a.wscale + q8_scale_ofs(a.K, rb0 + (live ? j : 0), s + (live ? u : 0), g) + 2 * i;
+    sc = live ? *(const uint32_t *)src : 0u;
+}
+
+// v of lane n (0..15) of this lane's 16-lane row (DPP row_newbcast; n a
+// constant once the callers' loops are unrolled)
+__device__ __forceinline__ uint32_t row_lane(uint32_t v, int n) {
+    switch (n) {
+#define UBD_ROW_LANE(N) \
+    case N: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xF, 0xF, false);
+        UBD_ROW_LANE(0) UBD_ROW_LANE(1) UBD_ROW_LANE(2) UBD_ROW_LANE(3)
+        UBD_ROW_LANE(4) UBD_ROW_LANE(5) UBD_ROW_LANE(6) UBD_ROW_LANE(7)
+        UBD_ROW_LANE(8) UBD_ROW_LANE(9) UBD_ROW_LANE(10) UBD_ROW_LANE(11)
+        UBD_ROW_LANE(12) UBD_ROW_LANE(13) UBD_ROW_LANE(14) UBD_ROW_LANE(15)
+#undef UBD_ROW_LANE
     }
+    return 0u;
 }
 
 // row block j, step u of the batch: this lane's scales (rows 4g..4g+3 of
-// blocks 2s and 2s + 1) are words 16 (j UB + u) + 4g + q, q = 0..3
+// blocks 2s and 2s + 1) are the words of lanes 4 (j UB + u) + q, q = 0..3,
+// of its row
 template <int RB, int UB>
-__device__ __forceinline__ void wbatch_scales(const uint32_t (&sc)[q8_scale_words<RB, UB>()], int j, int u, int g,
-                                              u32x2_t &b0, u32x2_t &b1) {
-    constexpr int NWD = q8_scale_words<RB, UB>();
-    const int w0 = (j * UB + u) * 16 + 4 * g;
-    uint32_t q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = (uint32_t)__shfl((int)sc[(w0 + i) % NWD], (w0 + i) / NWD, 64);
-    b0 = u32x2_t{q[0], q[1]};
-    b1 = u32x2_t{q[2], q[3]};
+__device__ __forceinline__ void wbatch_scales(uint32_t sc, int j, int u, u32x2_t &b0, u32x2_t &b1) {
+    const int c = j * UB + u;
+    b0 = u32x2_t{row_lane(sc, 4 * c), row_lane(sc, 4 * c + 1)};
+    b1 = u32x2_t{row_lane(sc, 4 * c + 2), row_lane(sc, 4 * c + 3)};
 }
 
 template <int WT, int RB, int UB>
@@ -703,7 +705,7 @@ __device__ __forceinline__ void mul_wbatch(const WBatch<WT, RB, UB> &b, const un
                 in.xh2 = *(const u32x4_t *)(hi + o + 32);
                 in.xl2 = *(const u32x4_t *)(lo + o + 32);
 #pragma unroll
-                for (int j = 0; j < RB; ++j) wbatch_scales<RB, UB>(b.sc, j, u, g, in.sc[j][0], in.sc[j][1]);
+                for (int j = 0; j < RB; ++j) wbatch_scales<RB, UB>(b.sc, j, u, in.sc[j][0], in.sc[j][1]);
             }
         }
         mfma_step<WT, RB, WT == W_Q8>(in, acc);
