@@ -569,7 +569,9 @@ int32_t ubd_debug_kernel_stats(ubd_context *ctx, int32_t *launches,
  * default 31 = all; the others take the hi plane only, i.e. bf16-rounded
  * activations, which leaves about 6e-3 of relative error per 8B-shaped
  * layer; with both planes the forced shapes are 1, 3, 5, 10, 14, 16 and 18
- * to 25).
+ * to 25), "post_norm" (1 = a residual prefill product whose k is split
+ * runs the RMSNorm that follows it in the pass adding its k slices, 0 =
+ * the norm in its own kernel; the results are identical).
  * Results do not depend on them beyond rounding, except "prefill_lo".
  * The knobs are process-wide and unsynchronised: set them while no other
  * thread is inside the library; every context sees the change.  0, or -1

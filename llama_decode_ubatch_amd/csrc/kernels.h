@@ -54,6 +54,8 @@ struct Tuning {
     int prefill_lo = 31;      // bf16 prefill products whose activations enter as hi + lo planes (two
                               // products per fragment), bit 1 << Prod; the others take the hi plane
                               // only (bf16-rounded activations)
+    int post_norm = 1;        // residual products with split k: the next RMSNorm runs in the pass that
+                              // adds the slices (0 = its own kernel)
 };
 // LDS bytes the activation copy of the LDS-staged few-token product may use
 constexpr size_t LDSX_MAX_BYTES = 64 * 1024;
@@ -128,6 +130,15 @@ struct NormIn {
     int ld = 0;
 };
 
+// RMSNorm that a residual product runs after its k slices are added (see
+// LinearArgs::post): rows of the updated residual, normalised with gain and
+// eps into out (tiled hi + lo planes).
+struct NormOut {
+    const float *gain = nullptr;
+    float eps = 0.f;
+    Act out;
+};
+
 struct LinearArgs {
     int wtype = W_BF16;
     const void *w = nullptr;          // tiled weights
@@ -148,6 +159,13 @@ struct LinearArgs {
     int prod = PROD_QKV;              // which product this is (Prod)
     float *split_out = nullptr;       // RESID prefill products: scratch for k-slice partial sums,
                                       // [MAX_K_SLICES][T][N] f32 (null: no k split)
+    // RESID products: when post.gain is set and the product's k is split, the
+    // pass that adds the slices into y also normalises each updated row of y
+    // (all T rows, N values each) into post.out (tiled planes, N <= 8192) and
+    // sets *post_done; otherwise *post_done is left false and the caller runs
+    // that norm itself
+    NormOut post;
+    bool *post_done = nullptr;
 };
 // Most k slices a residual prefill product is split into (its partial sums
 // go to scratch and are added to the residual in slice order).

@@ -1860,6 +1860,100 @@ __global__ __launch_bounds__(256) void resid_add_splits_kernel(float *y, int ldy
     *o = *o + v;
 }
 
+__global__ __launch_bounds__(256) void rmsnorm_tiled_kernel(const float *x, int ldx, const int32_t *row_map,
+                                                            const float *gain, int d, float eps, Act out);
+
+// resid_add_splits_kernel and then rmsnorm_tiled_kernel of the updated rows
+// in one pass: a work-group per row (the same row order), each thread adding
+// the NS slices into its 8-value runs of the row (the same additions in the
+// same order as resid_add_splits_kernel), storing them back and normalising
+// them as rmsnorm_tiled_kernel does, so both outputs are those of the two
+// kernels (N <= 8192: the runs stay in registers).  Every load of a thread
+// is issued before the first addition.
+template <int NS>
+__global__ __launch_bounds__(256) void resid_add_norm_kernel(float *y, int ldy, const float *parts, int N,
+                                                             const float *gain, float eps, Act out) {
+    const int rows = gridDim.x, b = blockIdx.x;
+    const int r = rows % 8 == 0 ? (b % 8) * (rows / 8) + b / 8 : b;
+    float *yr = y + (size_t)r * ldy;
+    constexpr int MAXV = 4;
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t v[MAXV][2], gn[MAXV][2], pk[MAXV][2][NS];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v[i][h] = e < N ? *(const f32x4_t *)(yr + e + 4 * h) : z;
+            gn[i][h] = e < N ? *(const f32x4_t *)(gain + e + 4 * h) : z;
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+                pk[i][h][k] = e < N ? *(const f32x4_t *)(parts + ((size_t)k * rows + r) * N + e + 4 * h) : z;
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4_t p = pk[i][h][0];
+#pragma unroll
+            for (int k = 1; k < NS; ++k) p += pk[i][h][k];
+            v[i][h] = v[i][h] + p;
+            if (e < N) *(f32x4_t *)(yr + e + 4 * h) = v[i][h];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            ss += v[i][h][0] * v[i][h][0] + v[i][h][1] * v[i][h][1] + v[i][h][2] * v[i][h][2] +
+                  v[i][h][3] * v[i][h][3];
+    __shared__ float part[4];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)N + eps);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 8;
+        if (e >= N) continue;
+        const f32x4_t y0 = v[i][0] * inv * gn[i][0];
+        const f32x4_t y1 = v[i][1] * inv * gn[i][1];
+        u16x8_t hh, ll;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float yv = k < 4 ? y0[k] : y1[k - 4];
+            hh[k] = f2bf(yv);
+            ll[k] = f2bf(yv - bf2f(hh[k]));
+        }
+        const size_t o = act_idx(out, r, e);
+        *(u16x8_t *)(out.hi + o) = hh;
+        *(u16x8_t *)(out.lo + o) = ll;
+    }
+}
+
+// After a residual product whose k was split into nsplit slices: the slices
+// are added into y, with the post norm fused into that pass when asked for
+// and possible (tiled output planes, rows of at most 8192 values).
+static void finish_k_slices(const LinearArgs &a, int nsplit, hipStream_t s) {
+    if (a.post.gain && a.post_done && g_tuning.post_norm != 0 && a.post.out.tiled && a.post.out.hi &&
+        a.post.out.lo && a.N <= 8192 && a.N % 8 == 0 && (nsplit == 2 || nsplit == 4)) {
+        if (nsplit == 2)
+            UBD_LAUNCH(resid_add_norm_kernel<2>, dim3((unsigned)a.T), dim3(256), 0, s, a.y, a.ldy, a.split_out,
+                       a.N, a.post.gain, a.post.eps, a.post.out);
+        else
+            UBD_LAUNCH(resid_add_norm_kernel<4>, dim3((unsigned)a.T), dim3(256), 0, s, a.y, a.ldy, a.split_out,
+                       a.N, a.post.gain, a.post.eps, a.post.out);
+        *a.post_done = true;
+        return;
+    }
+    const long n = (long)a.T * (a.N / 4);
+    UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
+               a.split_out, a.T, a.N, nsplit);
+}
+
 // false (nothing launched) unless each k slice's stage count is a multiple
 // of D + 1 (and, split, the product is a residual one with scratch for the
 // slices)
@@ -1872,11 +1966,7 @@ static bool launch_gemm_deep(const LinearArgs &a, hipStream_t s) {
     const int n_ttiles = (a.T + 16 * TB - 1) / (16 * TB);
     UBD_LAUNCH((gemm_deep_kernel<EPI, RBW, TB, D, OCC, SPLITK, LO, XA>), dim3(n_wtiles * n_ttiles * SPLITK),
                        dim3(256), 0, s, a, n_wtiles, n_ttiles);
-    if (SPLITK > 1) {
-        const long n = (long)a.T * (a.N / 4);
-        UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
-                           a.split_out, a.T, a.N, SPLITK);
-    }
+    if (SPLITK > 1) finish_k_slices(a, SPLITK, s);
     return true;
 }
 
@@ -1891,11 +1981,7 @@ static bool launch_gemm_wide(const LinearArgs &a, hipStream_t s) {
     const int n_ttiles = (a.T + 32 * TBW - 1) / (32 * TBW);
     UBD_LAUNCH((gemm_wide_kernel<EPI, SPLITK, NX, RBW, TBW>), dim3(n_wtiles * n_ttiles * SPLITK), dim3(512), 0, s, a,
                n_wtiles, n_ttiles);
-    if (SPLITK > 1) {
-        const long n = (long)a.T * (a.N / 4);
-        UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
-                   a.split_out, a.T, a.N, SPLITK);
-    }
+    if (SPLITK > 1) finish_k_slices(a, SPLITK, s);
     return true;
 }
 
@@ -1922,11 +2008,7 @@ static void launch_gemm_lds(const LinearArgs &a, hipStream_t s, int wpd = 1) {
     else
         UBD_LAUNCH((gemm_lds_kernel<WT, EPI, RBW, TB, SPLITK, 64, 1, LO>), dim3(total), dim3(256), 0, s, a,
                            n_wtiles, n_ttiles);
-    if (SPLITK > 1) {
-        const long n = (long)a.T * (a.N / 4);
-        UBD_LAUNCH(resid_add_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.y, a.ldy,
-                           a.split_out, a.T, a.N, SPLITK);
-    }
+    if (SPLITK > 1) finish_k_slices(a, SPLITK, s);
 }
 
 // Shape choice for the LDS-ring product: the largest tile (256 rows x 128

@@ -1046,6 +1046,9 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
                                        hd / 2, rope_cs, s); });
     if (dump) hip_ok(hipMemcpyAsync(dump, x, (size_t)T * d * 4, hipMemcpyDeviceToDevice, s), "dump");
 
+    // set when the previous layer's down product ran this layer's attention
+    // norm in its k-slice pass (LinearArgs::post)
+    bool attn_normed = false;
     for (int il = 0; il < hp.n_layer; ++il) {
         const auto &L = M.layers[il];
         const bool fuse_norm = g_tuning.fuse_norm != 0 && linear_norm_fits(T, d);
@@ -1077,8 +1080,9 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         if (fuse_norm) la.norm = NormIn{x, nullptr, L.attn_norm, hp.rms_eps, d};
         // the products that read tiled activations get them from their producer tiled
         la.x.tiled = linear_reads_tiled(la);
-        if (!fuse_norm)
+        if (!fuse_norm && !attn_normed)
             timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.attn_norm, d, hp.rms_eps, la.x, s); });
+        attn_normed = false;
         timed(4 + ph, [&] {
             launched &= launch_linear(la, s);
             if (type_k == KV_Q8) {
@@ -1145,8 +1149,6 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
             timed(6 + ph, [&] { launch_attention(aa, s); });
         }
 
-        timed(8 + ph, [&] { launched &= launch_linear(lo, s); });
-
         LinearArgs lg = lo;
         lg.w = L.gu.w;
         lg.wscale = L.gu.scales;
@@ -1157,10 +1159,23 @@ int32_t ubd_context::enqueue_forward(hipStream_t s, const GraphKey &key) {
         lg.prod = PROD_GATE_UP;
         if (fuse_norm_ffn) lg.norm = NormIn{x, nullptr, L.ffn_norm, hp.rms_eps, d};
         lg.x.tiled = linear_reads_tiled(lg);
-        if (!fuse_norm_ffn)
+        // the FFN norm: in the O product's k-slice pass when it splits k
+        bool ffn_normed = false;
+        if (!fuse_norm_ffn) {
+            lo.post = NormOut{L.ffn_norm, hp.rms_eps, lg.x};
+            lo.post_done = &ffn_normed;
+        }
+        timed(8 + ph, [&] { launched &= launch_linear(lo, s); });
+        if (!fuse_norm_ffn && !ffn_normed)
             timed(2 + ph, [&] { launch_rmsnorm(x, d, nullptr, T, L.ffn_norm, d, hp.rms_eps, lg.x, s); });
         LinearArgs ld = lo;
         ld.norm = NormIn{};
+        ld.post = NormOut{};
+        ld.post_done = nullptr;
+        if (il + 1 < hp.n_layer && !fuse_norm) {
+            ld.post = NormOut{M.layers[il + 1].attn_norm, hp.rms_eps, la.x};
+            ld.post_done = &attn_normed;
+        }
         ld.w = L.down.w;
         ld.prod = PROD_DOWN;
         ld.wscale = L.down.scales;
@@ -1708,6 +1723,8 @@ extern "C" int32_t ubd_debug_set_tuning(const char *key, int32_t value) {
         g_tuning.skinny_nw = value;
     } else if (k == "fuse_norm") {
         g_tuning.fuse_norm = value;
+    } else if (k == "post_norm") {
+        g_tuning.post_norm = value;
     } else if (k == "attn_chunk_min") {
         g_tuning.attn_chunk_min = value;
     } else if (k == "attn_pair") {

@@ -123,3 +123,47 @@ def test_few_token_products_match_oracle(built, key, n):
     err = float(np.abs(z - zr).max() / np.abs(zr).max())
     print(f"{key} T={n}: logits rel err {err:.2e}", flush=True)
     assert err < TOL[shape.wtype]
+
+
+def prefill_with_norm_counts(model, tokens, split, lo, post_norm):
+    """Logits of a 100-token prefill and the prefill RMSNorm launches that ran
+    as kernels of their own."""
+    from llama_decode_ubatch_amd import Context
+    from llama_decode_ubatch_amd.binding import set_tuning
+    set_tuning("gemm_split", split)
+    set_tuning("prefill_lo", 31 if lo else 0)
+    set_tuning("post_norm", post_norm)
+    try:
+        ctx = Context(model, n_ctx=512, n_batch=512, n_ubatch=512, n_seq_max=1, type_k="f16", type_v="f16")
+        ctx.kernel_timing(None)
+        ctx.kernel_stats()
+        assert ctx.decode(tokens, logits=np.ones(len(tokens))) == 0
+        stats = ctx.kernel_stats()
+        return ctx.logits(), stats.get("prefill.rmsnorm", (0, 0.0))[0]
+    finally:
+        set_tuning("gemm_split", 0)
+        set_tuning("prefill_lo", 31)
+        set_tuning("post_norm", 1)
+
+
+@pytest.mark.parametrize("key", list(SHAPES))
+def test_norm_in_the_k_slice_pass_is_bit_identical(built, key):
+    """A residual product whose k is split adds its slices into the residual
+    in a pass that also runs the RMSNorm after it (the FFN norm after O, the
+    next layer's attention norm after down).  With the products forced into
+    2 and 4 slices, that pass replaces those norm kernels (one attention norm
+    of the first layer and the output norm remain) and the logits equal those
+    with every norm in its own kernel, bit for bit."""
+    shape, tens, model = built[key]
+    tokens = rand_tokens(100, shape.n_vocab, seed=77)
+    # (forced splits reach both residual products on the bf16 hi-plane path
+    # and the q8_0 path at these shapes)
+    lo = 0 if shape.wtype == "bf16" else 1
+    cases = [(2, lo), (4, lo)]
+    for split, lo in cases:
+        print(f"{key}: k in {split} slices, lo plane {lo}", flush=True)
+        fused, n_fused = prefill_with_norm_counts(model, tokens, split, lo, 1)
+        sep, n_sep = prefill_with_norm_counts(model, tokens, split, lo, 0)
+        assert n_sep == 2 * shape.n_layer + 1
+        assert n_fused == 2, n_fused
+        assert np.array_equal(fused, sep), (split, lo)
