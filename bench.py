@@ -342,13 +342,14 @@ def roofline_prefill_of(w, r):
 
 
 # -------------------------------------------------------------- CPU baseline
-def cpu_baseline(w, sample_layers=8, n_decode=48):
+def cpu_baseline(w, sample_layers=8, n_decode=None):
     """The oracle as it stands on a bounded sample of the same job: a
     `sample_layers`-layer model of the same shape (its own seeded weights)
     prefills the whole prompt as one ubatch (so the causal attention costs
-    what it costs in the full job) and then decodes n_decode tokens; layer
-    time is scaled to the full depth and the output head added once per
-    output row."""
+    what it costs in the full job) and then decodes n_decode tokens (default:
+    the job's decode count, so the scans cover the same context lengths);
+    layer time is scaled to the full depth and the output head added once
+    per output row."""
     import numpy as np
     from oracle import OracleModel, OracleContext, Batch
     from workloads import gen_tensor, gen_tensor_rows, prompt_tokens
@@ -374,6 +375,7 @@ def cpu_baseline(w, sample_layers=8, n_decode=48):
     om.w("output_norm.weight")
     om.w("output.weight")
     L = w.model.n_layer
+    n_decode = w.n_decode if n_decode is None else n_decode
     prompt = prompt_tokens(w, 0)
     t0 = time.perf_counter()
     ctx.head(np.zeros((1, shape.n_embd), np.float32))
